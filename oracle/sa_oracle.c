@@ -1,0 +1,446 @@
+/*
+ * sa_oracle.c -- plain, slow CPU oracle for structured sparse prefill attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link,
+ * load or call this file; only the tests, the smoke check and the CPU-baseline
+ * leg of the benchmark use it.  It shares no code, header, table or helper with
+ * the HIP library, and it never uses a value produced by the HIP library.
+ *
+ * Sources (cited by page title and section):
+ *   [DAM]    Pith review of "DAM: Dynamic Attention Mask for Long-Context Large
+ *            Language Model Inference Acceleration" -- sections "What carries the
+ *            argument", "Referee Report" (Summary; minor comment 1), "Circularity
+ *            Check" (steps 1 and 2), "Assumptions & free parameters".
+ *   [Seer]   "SeerAttention: Learning Intrinsic Sparse Attention in Your LLMs",
+ *            abstract (block-level sparsity).
+ *   [Anchor] "AnchorAttention: Difference-Aware Sparse Attention with Stripe
+ *            Granularity", title and abstract (stripe granularity).
+ *
+ * Arithmetic is fp64 throughout.  Build with -O2 -fno-fast-math
+ * -ffp-contract=off so every operation is one IEEE-rounded step.
+ *
+ * Functions and what pins them (pins live in tests/test_oracle_pins.py):
+ *   orc_row_mask         retained predicate of one row        -> numpy brute force
+ *   orc_pair_count       retained pairs per head              -> brute force, row_mask sums
+ *   orc_build_index      canonical index (runs, segments, columns) -> enumeration,
+ *                        hand-worked example (tests/golden/index_example.txt)
+ *   orc_attention_rows   fp64 attention on chosen rows (dense -inf form and
+ *                        sparse-enumeration form) -> textbook causal attention,
+ *                        diagonal-0 identity, V==1, rows sum to one
+ *   orc_capture          Box-Cox / threshold / overlap score / keep -> closed form,
+ *                        hand-worked example (tests/golden/capture_example.txt),
+ *                        planted patterns
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+  int32_t S, H;
+  const int32_t* diag_ptr;  /* [H+1] */
+  const int32_t* diag_off;  /* diagonal offsets r: pair (i, i-r) */
+  const int32_t* vert_ptr;  /* [H+1] */
+  const int32_t* vert_col;  /* vertical columns c: pair (i, c), i >= c */
+  const uint8_t* block_mask; /* NULL or [H][nbq][nbq], nbq = ceil(S/block_size) */
+  int32_t block_size;
+  const int64_t* stripe_ptr; /* NULL or [H*nst+1], nst = ceil(S/stripe_rows) */
+  const int32_t* stripe_col;
+  int32_t stripe_rows;
+} orc_desc;
+
+static int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+/* ------------------------------------------------------------------------ */
+/* Retained predicate.                                                      */
+/* [DAM] "What carries the argument": diagonal pattern j = i - r, vertical  */
+/* pattern j = c with i >= c; the extended mask is the union ("sum") of the */
+/* matched patterns ("Circularity Check", step 1), read as a logical OR.    */
+/* [Seer] abstract: block-level sparsity (64x64 blocks).  [Anchor]: stripe  */
+/* granularity, read as one sorted column list per block of stripe_rows     */
+/* query rows.  Causality (j <= i) applies to every pattern.                */
+/* out[j] = 1 iff (i, j) is retained, for j in [0, i].                       */
+/* ------------------------------------------------------------------------ */
+void orc_row_mask(const orc_desc* d, int32_t h, int32_t i, uint8_t* out) {
+  memset(out, 0, (size_t)i + 1);
+  for (int32_t p = d->diag_ptr[h]; p < d->diag_ptr[h + 1]; ++p) {
+    int32_t r = d->diag_off[p];
+    if (r <= i) out[i - r] = 1;
+  }
+  for (int32_t p = d->vert_ptr[h]; p < d->vert_ptr[h + 1]; ++p) {
+    int32_t c = d->vert_col[p];
+    if (c <= i) out[c] = 1;
+  }
+  if (d->block_mask) {
+    int64_t nbq = cdiv64(d->S, d->block_size);
+    int64_t br = i / d->block_size;
+    const uint8_t* row = d->block_mask + ((int64_t)h * nbq + br) * nbq;
+    for (int32_t j = 0; j <= i; ++j)
+      if (row[j / d->block_size]) out[j] = 1;
+  }
+  if (d->stripe_ptr) {
+    int64_t nst = cdiv64(d->S, d->stripe_rows);
+    int64_t t = i / d->stripe_rows;
+    for (int64_t p = d->stripe_ptr[h * nst + t]; p < d->stripe_ptr[h * nst + t + 1]; ++p) {
+      int32_t c = d->stripe_col[p];
+      if (c <= i) out[c] = 1;
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Retained pairs per head: sum over rows of the number of retained keys.   */
+/* Rows are taken in groups of g rows that lie inside one block row and     */
+/* one stripe, so the column part X (verticals, blocks, stripes) is the same */
+/* for every row of a group; for row i the retained set is                  */
+/*   {j in X : j <= i}  union  {i - r : r in D, r <= i}                     */
+/* and its size is |X <= i| + |{r in D, r <= i : i - r not in X}|.          */
+/* [DAM] "Circularity Check", step 2: the cost is the number of retained    */
+/* keys s per query.                                                         */
+/* ------------------------------------------------------------------------ */
+static int32_t gcd32(int32_t a, int32_t b) { while (b) { int32_t t = a % b; a = b; b = t; } return a; }
+
+static int32_t group_rows(const orc_desc* d) {
+  int32_t g = 64; /* any size works when there are no blocks or stripes */
+  if (d->block_mask && d->stripe_ptr) g = gcd32(d->block_size, d->stripe_rows);
+  else if (d->block_mask) g = d->block_size;
+  else if (d->stripe_ptr) g = d->stripe_rows;
+  return g;
+}
+
+/* inX[j] for j in [0, hiq] for the group that starts at row g0 */
+static void column_part(const orc_desc* d, int32_t h, int32_t g0, int32_t hiq, uint8_t* inX) {
+  memset(inX, 0, (size_t)hiq + 1);
+  for (int32_t p = d->vert_ptr[h]; p < d->vert_ptr[h + 1]; ++p) {
+    int32_t c = d->vert_col[p];
+    if (c <= hiq) inX[c] = 1;
+  }
+  if (d->block_mask) {
+    int64_t nbq = cdiv64(d->S, d->block_size);
+    const uint8_t* row = d->block_mask + ((int64_t)h * nbq + g0 / d->block_size) * nbq;
+    for (int32_t j = 0; j <= hiq; ++j)
+      if (row[j / d->block_size]) inX[j] = 1;
+  }
+  if (d->stripe_ptr) {
+    int64_t nst = cdiv64(d->S, d->stripe_rows);
+    int64_t t = g0 / d->stripe_rows;
+    for (int64_t p = d->stripe_ptr[h * nst + t]; p < d->stripe_ptr[h * nst + t + 1]; ++p) {
+      int32_t c = d->stripe_col[p];
+      if (c <= hiq) inX[c] = 1;
+    }
+  }
+}
+
+void orc_pair_count(const orc_desc* d, int64_t* out /* [H] */) {
+  int32_t S = d->S, g = group_rows(d);
+  for (int32_t h = 0; h < d->H; ++h) out[h] = 0;
+#pragma omp parallel
+  {
+    uint8_t* inX = (uint8_t*)malloc((size_t)S);
+    int64_t* cnt = (int64_t*)malloc(sizeof(int64_t) * (size_t)S);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t task = 0; task < (int64_t)d->H * cdiv64(S, g); ++task) {
+      int32_t h = (int32_t)(task / cdiv64(S, g));
+      int32_t g0 = (int32_t)(task % cdiv64(S, g)) * g;
+      int32_t g1 = g0 + g - 1 < S - 1 ? g0 + g - 1 : S - 1;
+      column_part(d, h, g0, g1, inX);
+      int64_t run = 0;
+      for (int32_t j = 0; j <= g1; ++j) { run += inX[j]; cnt[j] = run; }
+      int64_t total = 0;
+      for (int32_t i = g0; i <= g1; ++i) {
+        int64_t n = cnt[i];
+        for (int32_t p = d->diag_ptr[h]; p < d->diag_ptr[h + 1]; ++p) {
+          int32_t r = d->diag_off[p];
+          if (r <= i && !inX[i - r]) ++n;
+        }
+        total += n;
+      }
+#pragma omp atomic
+      out[h] += total;
+    }
+    free(inX);
+    free(cnt);
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Canonical index.  The pages give no index format; this is the layout the */
+/* kernel consumes, defined by plain set logic so that every array has one  */
+/* correct value.  For row block rb = rows [b0, b1] (BM rows):              */
+/*   runs_h   maximal runs [lo, hi] of the diagonal offsets D_h             */
+/*   U        = { j >= 0 : i - j in D_h for some i in [b0, b1] }            */
+/*              (columns the diagonals touch inside this row block)         */
+/*   segs     maximal intervals of U, ascending                             */
+/*   X        = verticals <= b1, block columns of block row b0/64 (<= b1),  */
+/*              stripe columns of stripe b0/stripe_rows (<= b1)             */
+/*   bcols    X intersect U, ascending;  cols  X minus U, ascending         */
+/* BM must divide block_size and stripe_rows when those are present, so    */
+/* that a row block lies inside one block row and one stripe.               */
+/* Return: 0 ok, 1 capacity too small (sizes are still reported),           */
+/* 3 row block incompatible with the block or stripe granularity.           */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  int64_t n_runs, n_segs, n_bcols, n_cols;
+} orc_sizes;
+
+int orc_build_index(const orc_desc* d, int32_t BM,
+                    int32_t* run_ptr, int32_t* run_lo, int32_t* run_hi, int64_t run_cap,
+                    int64_t* seg_ptr, int32_t* seg_lo, int32_t* seg_hi, int64_t seg_cap,
+                    int64_t* bcol_ptr, int32_t* bcol_idx, int64_t bcol_cap,
+                    int64_t* col_ptr, int32_t* col_idx, int64_t col_cap,
+                    int64_t* pair_count, orc_sizes* sizes) {
+  int32_t S = d->S, H = d->H;
+  int64_t nb = cdiv64(S, BM);
+  int64_t nitems = (int64_t)H * nb;
+  int overflow = 0;
+  if (BM <= 0 || (d->block_mask && d->block_size % BM != 0) || (d->stripe_ptr && d->stripe_rows % BM != 0))
+    return 3;
+
+  /* runs */
+  int64_t nr = 0;
+  for (int32_t h = 0; h < H; ++h) {
+    if (run_ptr) run_ptr[h] = (int32_t)nr;
+    int32_t p = d->diag_ptr[h], e = d->diag_ptr[h + 1];
+    while (p < e) {
+      int32_t lo = d->diag_off[p], hi = lo;
+      while (p + 1 < e && d->diag_off[p + 1] == hi + 1) { ++p; ++hi; }
+      if (nr < run_cap && run_lo) { run_lo[nr] = lo; run_hi[nr] = hi; }
+      ++nr;
+      ++p;
+    }
+  }
+  if (run_ptr) run_ptr[H] = (int32_t)nr;
+  if (nr > run_cap) overflow = 1;
+
+  /* per-item counts first (parallel), then offsets, then fill (parallel) */
+  int64_t* cseg = (int64_t*)calloc((size_t)nitems, sizeof(int64_t));
+  int64_t* cb = (int64_t*)calloc((size_t)nitems, sizeof(int64_t));
+  int64_t* cc = (int64_t*)calloc((size_t)nitems, sizeof(int64_t));
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma omp parallel
+    {
+      uint8_t* inU = (uint8_t*)malloc((size_t)S);
+      uint8_t* inX = (uint8_t*)malloc((size_t)S);
+#pragma omp for schedule(dynamic, 4)
+      for (int64_t it = 0; it < nitems; ++it) {
+        int32_t h = (int32_t)(it / nb);
+        int32_t b0 = (int32_t)((it % nb) * BM);
+        int32_t b1 = b0 + BM - 1 < S - 1 ? b0 + BM - 1 : S - 1;
+        memset(inU, 0, (size_t)b1 + 1);
+        for (int32_t p = d->diag_ptr[h]; p < d->diag_ptr[h + 1]; ++p) {
+          int32_t r = d->diag_off[p];
+          for (int32_t i = b0; i <= b1; ++i)
+            if (i - r >= 0) inU[i - r] = 1;
+        }
+        column_part(d, h, b0, b1, inX);
+        if (pass == 0) {
+          int64_t ns = 0, nbc = 0, nc = 0;
+          for (int32_t j = 0; j <= b1; ++j) {
+            if (inU[j] && (j == 0 || !inU[j - 1])) ++ns;
+            if (inX[j]) { if (inU[j]) ++nbc; else ++nc; }
+          }
+          cseg[it] = ns; cb[it] = nbc; cc[it] = nc;
+        } else {
+          int64_t ps = seg_ptr[it], pb = bcol_ptr[it], pc = col_ptr[it];
+          for (int32_t j = 0; j <= b1; ++j) {
+            if (inU[j] && (j == 0 || !inU[j - 1])) {
+              int32_t e = j;
+              while (e + 1 <= b1 && inU[e + 1]) ++e;
+              if (ps < seg_cap) { seg_lo[ps] = j; seg_hi[ps] = e; }
+              ++ps;
+            }
+            if (inX[j]) {
+              if (inU[j]) { if (pb < bcol_cap) bcol_idx[pb] = j; ++pb; }
+              else { if (pc < col_cap) col_idx[pc] = j; ++pc; }
+            }
+          }
+        }
+      }
+      free(inU);
+      free(inX);
+    }
+    if (pass == 0) {
+      int64_t a = 0, b = 0, c = 0;
+      for (int64_t it = 0; it < nitems; ++it) {
+        seg_ptr[it] = a; bcol_ptr[it] = b; col_ptr[it] = c;
+        a += cseg[it]; b += cb[it]; c += cc[it];
+      }
+      seg_ptr[nitems] = a; bcol_ptr[nitems] = b; col_ptr[nitems] = c;
+      sizes->n_runs = nr; sizes->n_segs = a; sizes->n_bcols = b; sizes->n_cols = c;
+      if (a > seg_cap || b > bcol_cap || c > col_cap) overflow = 1;
+      if (!seg_lo || !bcol_idx || !col_idx) break; /* size query only */
+    }
+  }
+  sizes->n_runs = nr;
+  free(cseg); free(cb); free(cc);
+  if (pair_count) orc_pair_count(d, pair_count);
+  return overflow;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Attention on chosen rows, fp64.                                          */
+/* [DAM] Referee Report, Summary: scores Q K^T / sqrt(d_k), mask applied    */
+/* before softmax; "What carries the argument": all non-retained pairs are  */
+/* zeroed out, read as logit = -inf so they get zero probability.  Softmax  */
+/* and the product with V follow standard attention.                        */
+/*   s_j  = (q . k_j) * scale            (scale = 1/sqrt(d) by default)     */
+/*   m    = max_j s_j over retained j                                       */
+/*   p_j  = exp(s_j - m);  l = sum_j p_j;  o = sum_j p_j v_j / l            */
+/*   lse  = m + ln l                                                        */
+/* A row with no retained key gives o = 0 and lse = -inf.                   */
+/* Inputs: dtype 0 = float32, 1 = bfloat16 bit patterns (uint16); each     */
+/* element is widened exactly to double.  Layout q[b][hq][S][dh],           */
+/* k,v[b][hkv][S][dh]; query head h reads kv head h / (hq/hkv).             */
+/* mode 0: sparse enumeration (sum over retained keys only).                */
+/* mode 1: dense form over all S keys with masked logits = -inf.            */
+/* rows: n_rows triples (b, h, i).  o: [n_rows][dh]; lse: [n_rows].         */
+/* ------------------------------------------------------------------------ */
+static double widen(const void* base, int dtype, int64_t idx) {
+  if (dtype == 0) return (double)((const float*)base)[idx];
+  uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;
+  float f;
+  memcpy(&f, &bits, 4);
+  return (double)f;
+}
+
+void orc_attention_rows(const orc_desc* d, const void* q, const void* k, const void* v, int dtype,
+                        int32_t B, int32_t hq, int32_t hkv, int32_t S, int32_t dh, double scale,
+                        const int32_t* rows, int64_t n_rows, int mode, double* o, double* lse) {
+  (void)B;
+  int32_t group = hq / hkv;
+#pragma omp parallel
+  {
+    uint8_t* keep = (uint8_t*)malloc((size_t)S);
+    double* s = (double*)malloc(sizeof(double) * (size_t)S);
+    double* qi = (double*)malloc(sizeof(double) * (size_t)dh);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t n = 0; n < n_rows; ++n) {
+      int32_t b = rows[3 * n], h = rows[3 * n + 1], i = rows[3 * n + 2];
+      int32_t g = h / group;
+      int64_t qbase = (((int64_t)b * hq + h) * S + i) * dh;
+      int64_t kvbase = ((int64_t)b * hkv + g) * (int64_t)S * dh;
+      for (int32_t c = 0; c < dh; ++c) qi[c] = widen(q, dtype, qbase + c);
+      orc_row_mask(d, h, i, keep);
+      int32_t jend = (mode == 1) ? S - 1 : i;
+      double m = -INFINITY;
+      for (int32_t j = 0; j <= jend; ++j) {
+        int retained = (j <= i) && keep[j];
+        if (mode == 0 && !retained) continue;
+        double acc = 0.0;
+        for (int32_t c = 0; c < dh; ++c) acc += qi[c] * widen(k, dtype, kvbase + (int64_t)j * dh + c);
+        s[j] = retained ? acc * scale : -INFINITY;
+        if (s[j] > m) m = s[j];
+      }
+      double* oi = o + n * dh;
+      for (int32_t c = 0; c < dh; ++c) oi[c] = 0.0;
+      if (m == -INFINITY) { /* no retained key */
+        lse[n] = -INFINITY;
+        continue;
+      }
+      double l = 0.0;
+      for (int32_t j = 0; j <= jend; ++j) {
+        int retained = (j <= i) && keep[j];
+        if (mode == 0 && !retained) continue;
+        double p = exp(s[j] - m); /* exp(-inf) = 0 for masked logits */
+        l += p;
+        if (p != 0.0)
+          for (int32_t c = 0; c < dh; ++c) oi[c] += p * widen(v, dtype, kvbase + (int64_t)j * dh + c);
+      }
+      for (int32_t c = 0; c < dh; ++c) oi[c] = oi[c] / l;
+      lse[n] = m + log(l);
+    }
+    free(keep);
+    free(s);
+    free(qi);
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Pattern capture, fp64, one map at a time.                                */
+/* [DAM] "What carries the argument": Box-Cox transform with lambda = 0.5   */
+/* amplifies small values; thresholding at tau = 0.3 gives the binary true  */
+/* mask M; the pattern pool holds diagonals (i, i-r) and verticals (i, c),  */
+/* i >= c; overlap score gamma_k = sum(M * P_k) / sum(P_k); keep if         */
+/* gamma_k >= mu = 0.8.  Referee Report, minor comment 1: the stabiliser    */
+/* epsilon is 1e-8 in one section and 1e-10 in an appendix (a parameter).   */
+/* Box-Cox (textbook): y = (x^lambda - 1) / lambda, x = A + eps; for        */
+/* lambda = 0.5, x^lambda = sqrt(x).  The pages do not say how y is scaled  */
+/* before comparing with tau; this oracle min-max normalises y per causal   */
+/* row (norm_scope 0) or per map (norm_scope 1).  A row or map whose        */
+/* transformed values are all equal counts as fully retained.               */
+/* Only the causal half (j <= i) of each map is read.                       */
+/* Operation order is fixed: x = A + eps; s = sqrt(x); y = (s - 1) / lambda; */
+/* t = (y - ymin) / (ymax - ymin); M = (t >= tau).                           */
+/* Returns 0, or 2 if lambda != 0.5 (only the square-root case is exact).   */
+/* ------------------------------------------------------------------------ */
+static double boxcox_half(float a, double eps, double lambda) {
+  double x = (double)a + eps;
+  double s = sqrt(x);
+  return (s - 1.0) / lambda;
+}
+
+int orc_capture(const float* maps, int32_t n_maps, int32_t L, double lambda, double eps, double tau,
+                double mu, int32_t norm_scope, uint8_t* keep_diag, uint8_t* keep_vert,
+                int32_t* diag_hits, int32_t* vert_hits, uint8_t* true_mask) {
+  if (lambda != 0.5) return 2;
+#pragma omp parallel
+  {
+    double* y = (double*)malloc(sizeof(double) * (size_t)L);
+    uint8_t* M = (uint8_t*)malloc((size_t)L * (size_t)L);
+    int64_t* hd = (int64_t*)malloc(sizeof(int64_t) * (size_t)L);
+    int64_t* hv = (int64_t*)malloc(sizeof(int64_t) * (size_t)L);
+#pragma omp for schedule(dynamic, 1)
+    for (int32_t mi = 0; mi < n_maps; ++mi) {
+      const float* A = maps + (int64_t)mi * L * L;
+      memset(M, 0, (size_t)L * (size_t)L);
+      double gmin = INFINITY, gmax = -INFINITY;
+      if (norm_scope == 1) {
+        for (int32_t i = 0; i < L; ++i)
+          for (int32_t j = 0; j <= i; ++j) {
+            double t = boxcox_half(A[(int64_t)i * L + j], eps, lambda);
+            if (t < gmin) gmin = t;
+            if (t > gmax) gmax = t;
+          }
+      }
+      for (int32_t i = 0; i < L; ++i) {
+        double ymin = INFINITY, ymax = -INFINITY;
+        for (int32_t j = 0; j <= i; ++j) {
+          y[j] = boxcox_half(A[(int64_t)i * L + j], eps, lambda);
+          if (y[j] < ymin) ymin = y[j];
+          if (y[j] > ymax) ymax = y[j];
+        }
+        if (norm_scope == 1) { ymin = gmin; ymax = gmax; }
+        for (int32_t j = 0; j <= i; ++j) {
+          int keep;
+          if (ymax == ymin) keep = 1;
+          else keep = ((y[j] - ymin) / (ymax - ymin)) >= tau;
+          M[(int64_t)i * L + j] = (uint8_t)keep;
+        }
+      }
+      /* overlap scores over the pool: diagonal r has L - r cells, vertical c has L - c */
+      for (int32_t r = 0; r < L; ++r) {
+        int64_t hit = 0;
+        for (int32_t i = r; i < L; ++i) hit += M[(int64_t)i * L + (i - r)];
+        hd[r] = hit;
+      }
+      for (int32_t c = 0; c < L; ++c) {
+        int64_t hit = 0;
+        for (int32_t i = c; i < L; ++i) hit += M[(int64_t)i * L + c];
+        hv[c] = hit;
+      }
+      for (int32_t r = 0; r < L; ++r) {
+        double gamma = (double)hd[r] / (double)(L - r);
+        keep_diag[(int64_t)mi * L + r] = (uint8_t)(gamma >= mu);
+        if (diag_hits) diag_hits[(int64_t)mi * L + r] = (int32_t)hd[r];
+      }
+      for (int32_t c = 0; c < L; ++c) {
+        double gamma = (double)hv[c] / (double)(L - c);
+        keep_vert[(int64_t)mi * L + c] = (uint8_t)(gamma >= mu);
+        if (vert_hits) vert_hits[(int64_t)mi * L + c] = (int32_t)hv[c];
+      }
+      if (true_mask) memcpy(true_mask + (int64_t)mi * L * L, M, (size_t)L * (size_t)L);
+    }
+    free(y); free(M); free(hd); free(hv);
+  }
+  return 0;
+}

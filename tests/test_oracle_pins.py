@@ -1,0 +1,308 @@
+"""Pins for the CPU oracle: it is checked against things other than itself.
+
+* brute-force whole-matrix numpy twins (tests/brute.py) on tiny inputs,
+* textbook causal attention (torch scaled_dot_product_attention, fp64, CPU),
+* closed forms and special cases (diagonal 0 only -> O = V; V == 1 -> O = 1;
+  one-hot V -> softmax rows that sum to one),
+* hand-worked examples under tests/golden/ (each with its derivation),
+* invariants of pattern capture (monotone threshold, hit-count totals) and the
+  textbook Box-Cox formula (x^lambda - 1) / lambda,
+* planted-pattern maps whose kept sets are known in advance.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from brute import attention_brute, index_brute, mask_matrix
+from golden.load import arr, load
+
+
+def _rand_desc(rng, S, H, kinds):
+    diags, verts = [], []
+    for _ in range(H):
+        d = set()
+        if "diag" in kinds:
+            w = int(rng.integers(1, max(2, S // 4)))
+            d.update(range(w))
+            d.update(int(x) for x in rng.choice(S, size=min(S, int(rng.integers(0, 5))), replace=False))
+        diags.append(np.array(sorted(d), dtype=np.int32))
+        v = set()
+        if "vert" in kinds:
+            v.update(int(x) for x in rng.choice(S, size=min(S, int(rng.integers(0, 7))), replace=False))
+        verts.append(np.array(sorted(v), dtype=np.int32))
+    bm = None
+    if "block" in kinds:
+        nbq = -(-S // 32)
+        bm = (rng.random((H, nbq, nbq)) < 0.3).astype(np.uint8)
+    stripes = None
+    if "stripe" in kinds:
+        nst = -(-S // 32)
+        stripes = [[np.sort(rng.choice(S, size=int(rng.integers(0, S // 3 + 1)), replace=False)) for _ in range(nst)]
+                   for _ in range(H)]
+    return W.desc_from_lists(S, diags, verts, block_mask=bm, block_size=32, stripes=stripes, stripe_rows=32)
+
+
+KINDS = [("diag",), ("vert",), ("block",), ("stripe",), ("diag", "vert"), ("diag", "vert", "block"),
+         ("diag", "stripe"), ("diag", "vert", "block", "stripe")]
+
+
+# ----------------------------------------------------------------------------- masks and counts
+@pytest.mark.parametrize("kinds", KINDS)
+@pytest.mark.parametrize("S", [1, 7, 37, 64])
+def test_row_mask_matches_brute_force(kinds, S):
+    rng = np.random.default_rng([S, len(kinds)])
+    d = _rand_desc(rng, S, 2, kinds)
+    for h in range(2):
+        m = mask_matrix(d, h)
+        for i in range(S):
+            np.testing.assert_array_equal(oracle.row_mask(d, h, i).astype(bool), m[i, :i + 1])
+        assert oracle.pair_count(d)[h] == m.sum()
+
+
+def test_pair_count_matches_row_masks_mid_size():
+    rng = np.random.default_rng(7)
+    d = _rand_desc(rng, 300, 3, ("diag", "vert", "block", "stripe"))
+    pc = oracle.pair_count(d)
+    for h in range(3):
+        assert pc[h] == sum(int(oracle.row_mask(d, h, i).sum()) for i in range(300))
+
+
+# ----------------------------------------------------------------------------- index
+def test_index_hand_worked_example():
+    g = load("index_example.txt")
+    d = W.desc_from_lists(int(arr(g, "S")[0]), [arr(g, "diag")], [arr(g, "vert")])
+    ix = oracle.build_index(d, int(arr(g, "row_block")[0]))
+    for key in ("run_ptr", "run_lo", "run_hi", "seg_ptr", "seg_lo", "seg_hi", "bcol_ptr", "bcol_idx", "col_ptr",
+                "col_idx", "pair_count"):
+        np.testing.assert_array_equal(np.atleast_1d(ix[key]), np.atleast_1d(arr(g, key)), err_msg=key)
+
+
+@pytest.mark.parametrize("kinds", KINDS)
+@pytest.mark.parametrize("S,BM", [(37, 16), (64, 16), (100, 32), (129, 32)])
+def test_index_matches_enumeration(kinds, S, BM):
+    rng = np.random.default_rng([S, BM, len(kinds), 1])
+    d = _rand_desc(rng, S, 2, kinds)
+    ix = oracle.build_index(d, BM)
+    br = index_brute(d, BM)
+    for key in br:
+        np.testing.assert_array_equal(np.asarray(ix[key]).astype(np.int64), br[key].astype(np.int64), err_msg=key)
+
+
+def _expand(d, ix, h):
+    """Pairs the two kernel phases would compute, from the index alone (counts per pair)."""
+    S, BM, nb = d.S, ix["row_block"], ix["n_row_blocks"]
+    offs = set(int(x) for x in d.diags(h))
+    cnt = np.zeros((S, S), dtype=np.int32)
+    for rb in range(nb):
+        b0, b1 = rb * BM, min(S, (rb + 1) * BM) - 1
+        it = h * nb + rb
+        bset = set(ix["bcol_idx"][ix["bcol_ptr"][it]:ix["bcol_ptr"][it + 1]].tolist())
+        for s in range(ix["seg_ptr"][it], ix["seg_ptr"][it + 1]):
+            for j in range(ix["seg_lo"][s], ix["seg_hi"][s] + 1):
+                for i in range(max(j, b0), b1 + 1):
+                    if (i - j) in offs or j in bset:
+                        cnt[i, j] += 1
+        for j in ix["col_idx"][ix["col_ptr"][it]:ix["col_ptr"][it + 1]]:
+            for i in range(max(j, b0), b1 + 1):
+                cnt[i, j] += 1
+    return cnt
+
+
+@pytest.mark.parametrize("kinds", [("diag", "vert"), ("diag", "vert", "block"), ("diag", "stripe"),
+                                   ("diag", "vert", "block", "stripe")])
+def test_index_phases_cover_each_retained_pair_once(kinds):
+    rng = np.random.default_rng([11, len(kinds)])
+    d = _rand_desc(rng, 150, 2, kinds)
+    ix = oracle.build_index(d, 32)
+    for h in range(2):
+        cnt = _expand(d, ix, h)
+        m = mask_matrix(d, h)
+        assert cnt.max() <= 1
+        np.testing.assert_array_equal(cnt.astype(bool), m)
+        assert ix["pair_count"][h] == m.sum()
+
+
+def test_index_rejects_row_block_across_block_rows():
+    rng = np.random.default_rng(12)
+    d = _rand_desc(rng, 100, 1, ("block",))
+    with pytest.raises(ValueError):
+        oracle.build_index(d, 64)
+
+
+# ----------------------------------------------------------------------------- attention
+def _f64(x):
+    return W.bf16_bits_to_f32(x).astype(np.float64) if x.dtype == np.uint16 else x.astype(np.float64)
+
+
+def _all_rows(B, H, S):
+    return np.array([(b, h, i) for b in range(B) for h in range(H) for i in range(S)], dtype=np.int32)
+
+
+@pytest.mark.parametrize("kinds", KINDS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_attention_matches_brute_force(kinds, dtype):
+    S, B, hq, hkv, dh = 48, 2, 4, 2, 16
+    rng = np.random.default_rng([3, len(kinds)])
+    d = _rand_desc(rng, S, hq, kinds)
+    q, k, v = W.qkv(99, B, hq, hkv, S, dh, dtype, seed_extra=len(kinds))
+    rows = _all_rows(B, hq, S)
+    for mode in (0, 1):
+        o, lse = oracle.attention_rows(d, q, k, v, rows, mode=mode)
+        ob, lb = attention_brute(d, _f64(q), _f64(k), _f64(v))
+        np.testing.assert_allclose(o, ob.reshape(-1, dh), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, lb.reshape(-1), rtol=0, atol=1e-12)
+
+
+def test_attention_custom_scale_and_gqa_mapping():
+    S, B, hq, hkv, dh = 40, 1, 6, 3, 8
+    rng = np.random.default_rng(5)
+    d = _rand_desc(rng, S, hq, ("diag", "vert"))
+    q, k, v = W.qkv(98, B, hq, hkv, S, dh, "f32")
+    o, lse = oracle.attention_rows(d, q, k, v, _all_rows(B, hq, S), scale=0.37)
+    ob, lb = attention_brute(d, _f64(q), _f64(k), _f64(v), scale=0.37)
+    np.testing.assert_allclose(o, ob.reshape(-1, dh), atol=1e-12)
+    np.testing.assert_allclose(lse, lb.reshape(-1), atol=1e-12)
+
+
+@pytest.mark.parametrize("variant", ["dense_causal", "all_ones"])
+def test_full_mask_is_textbook_causal_attention(variant):
+    S, dh = 96, 32
+    d = W.tiny(variant, S=S)
+    q, k, v = W.qkv(97, 1, 1, 1, S, dh, "f32")
+    o, lse = oracle.attention_rows(d, q, k, v, _all_rows(1, 1, S))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q.astype(np.float64)), torch.from_numpy(k.astype(np.float64)),
+        torch.from_numpy(v.astype(np.float64)), is_causal=True)
+    np.testing.assert_allclose(o, ref.numpy().reshape(-1, dh), atol=1e-12)
+    s = (q[0, 0].astype(np.float64) @ k[0, 0].astype(np.float64).T) / np.sqrt(dh)
+    s = np.where(np.tril(np.ones((S, S), bool)), s, -np.inf)
+    np.testing.assert_allclose(lse, np.log(np.exp(s).sum(axis=1)), atol=1e-12)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_diagonal_zero_only_returns_v_exactly(dtype):
+    S, dh = 70, 16
+    d = W.tiny("diag0", S=S)
+    q, k, v = W.qkv(96, 1, 1, 1, S, dh, dtype)
+    o, _ = oracle.attention_rows(d, q, k, v, _all_rows(1, 1, S))
+    np.testing.assert_array_equal(o, _f64(v)[0, 0])
+
+
+def test_constant_v_gives_ones_and_one_hot_v_gives_unit_rows():
+    S, dh = 64, 64
+    rng = np.random.default_rng(8)
+    d = _rand_desc(rng, S, 1, ("diag", "vert", "block"))
+    q, k, _ = W.qkv(95, 1, 1, 1, S, dh, "f32")
+    ones = np.ones((1, 1, S, dh), np.float32)
+    o, _ = oracle.attention_rows(d, q, k, ones, _all_rows(1, 1, S))
+    nonempty = mask_matrix(d, 0).any(axis=1)
+    np.testing.assert_allclose(o[nonempty], 1.0, atol=1e-14)
+    eye = np.eye(S, dh, dtype=np.float32)[None, None]
+    p, _ = oracle.attention_rows(d, q, k, eye, _all_rows(1, 1, S))
+    np.testing.assert_allclose(p[nonempty].sum(axis=1), 1.0, atol=1e-14)
+    m = mask_matrix(d, 0)
+    assert np.all(p[~m[:, :dh]] == 0.0)
+
+
+def test_empty_rows_give_zero_output_and_minus_inf_lse():
+    S, dh = 20, 8
+    d = W.desc_from_lists(S, [np.zeros(0)], [np.array([5])])
+    q, k, v = W.qkv(94, 1, 1, 1, S, dh, "f32")
+    o, lse = oracle.attention_rows(d, q, k, v, _all_rows(1, 1, S))
+    assert np.all(o[:5] == 0) and np.all(np.isneginf(lse[:5]))
+    np.testing.assert_array_equal(o[5:], np.repeat(v[0, 0, 5:6].astype(np.float64), S - 5, axis=0))
+
+
+def test_band_and_column_encodings_agree():
+    S, dh = 128, 16
+    q, k, v = W.qkv(93, 1, 1, 1, S, dh, "bf16")
+    a, la = oracle.attention_rows(W.tiny("dense_causal", S), q, k, v, _all_rows(1, 1, S))
+    b, lb = oracle.attention_rows(W.tiny("all_ones", S), q, k, v, _all_rows(1, 1, S))
+    np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(la, lb)
+
+
+# ----------------------------------------------------------------------------- capture
+def test_capture_hand_worked_example():
+    g = load("capture_example.txt")
+    L = int(arr(g, "L")[0])
+    maps = arr(g, "map_row", np.float32).reshape(1, L, L)
+    for scope in (0, 1):
+        c = oracle.capture(maps, norm_scope=scope, want_mask=True)
+        np.testing.assert_array_equal(c["true_mask"][0], arr(g, "true_mask_row"))
+        np.testing.assert_array_equal(c["diag_hits"][0], arr(g, "diag_hits"))
+        np.testing.assert_array_equal(c["vert_hits"][0], arr(g, "vert_hits"))
+        np.testing.assert_array_equal(c["keep_diag"][0], arr(g, "keep_diag"))
+        np.testing.assert_array_equal(c["keep_vert"][0], arr(g, "keep_vert"))
+
+
+def test_capture_true_mask_follows_textbook_boxcox():
+    """M agrees with (x^lambda - 1)/lambda (numpy power), min-max per row, >= tau,
+    except on cells within rounding distance of the threshold."""
+    maps = W.capture_maps(layers=1, heads=3, L=128, n_avg=4)
+    c = oracle.capture(maps, want_mask=True)
+    lam, eps, tau = 0.5, 1e-8, 0.3
+    for n in range(maps.shape[0]):
+        for i in range(128):
+            x = maps[n, i, :i + 1].astype(np.float64) + eps
+            y = (np.power(x, lam) - 1.0) / lam
+            if y.max() == y.min():
+                t = np.ones_like(y)
+            else:
+                t = (y - y.min()) / (y.max() - y.min())
+            sure = np.abs(t - tau) > 1e-12
+            np.testing.assert_array_equal(c["true_mask"][n, i, :i + 1][sure], (t >= tau)[sure])
+            assert not c["true_mask"][n, i, i + 1:].any()
+
+
+def test_capture_invariants_monotone_rows_and_hit_totals():
+    maps = W.capture_maps(layers=1, heads=2, L=64, n_avg=2)
+    for scope in (0, 1):
+        c = oracle.capture(maps, norm_scope=scope, want_mask=True)
+        for n in range(maps.shape[0]):
+            M = c["true_mask"][n]
+            assert c["diag_hits"][n].sum() == M.sum() == c["vert_hits"][n].sum()
+            for i in range(64):
+                row, a = M[i, :i + 1].astype(bool), maps[n, i, :i + 1]
+                if row.any() and (~row).any():
+                    assert a[row].min() > a[~row].max()   # M is an up-set in A within a row
+            L = 64
+            r = np.arange(L)
+            np.testing.assert_array_equal(c["keep_diag"][n], (c["diag_hits"][n] / (L - r) >= 0.8).astype(np.uint8))
+            np.testing.assert_array_equal(c["keep_vert"][n], (c["vert_hits"][n] / (L - r) >= 0.8).astype(np.uint8))
+
+
+@pytest.mark.parametrize("scope", [0, 1])
+def test_capture_planted_patterns(scope):
+    L = 48
+    A = np.full((L, L), 1e-4, dtype=np.float64)
+    for i in range(L):
+        A[i, i] += 0.5
+        if i >= 5:
+            A[i, i - 5] += 0.3
+        if i >= 2:
+            A[i, 2] += 0.15
+    A = np.tril(A).astype(np.float32)[None]
+    c = oracle.capture(A, norm_scope=scope)
+    assert sorted(np.nonzero(c["keep_diag"][0])[0].tolist()) == [0, 5]
+    assert sorted(np.nonzero(c["keep_vert"][0])[0].tolist()) == [2, L - 1]
+
+
+def test_capture_rejects_other_lambda():
+    with pytest.raises(ValueError):
+        oracle.capture(np.ones((1, 4, 4), np.float32), lam=0.25)
+
+
+def test_extension_restricted_to_capture_window_is_the_kept_union():
+    maps = W.capture_maps(layers=1, heads=2, L=64, n_avg=4)
+    c = oracle.capture(maps)
+    diags, verts = oracle.extend(c["keep_diag"], c["keep_vert"], S=200)
+    d = W.desc_from_lists(200, diags, verts)
+    for h in range(2):
+        kd, kv = c["keep_diag"][h].astype(bool), c["keep_vert"][h].astype(bool)
+        for i in range(64):
+            j = np.arange(i + 1)
+            expect = kd[i - j] | kv[j]
+            np.testing.assert_array_equal(oracle.row_mask(d, h, i).astype(bool), expect)
