@@ -1,0 +1,243 @@
+"""Benchmark: structured sparse prefill attention on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input resident in HBM:
+index build (count, scan, fill) from the pattern descriptor, then the sparse
+attention forward.  Default workload: the LLaMA-3-8B-shaped layer (S = 65536,
+32 query / 8 kv heads, d = 128, bf16; half vertical+slash heads, half 64x64
+block-sparse heads).  Also reported: the attention time at S = 131072 (stripe
+masks), the pattern-capture time on 16 x 32 maps of 512 x 512, and the CPU
+oracle timed on a bounded sample of the same workload.
+
+Prints ONE JSON line.  Only one GPU is used; --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+WORKLOADS = {
+    4: dict(name="llama8b_like", S=65536, hq=32, hkv=8, d=128, dtype="bf16", row_block=64),
+    5: dict(name="long_stripes", S=131072, hq=32, hkv=8, d=128, dtype="bf16", row_block=128),
+    2: dict(name="llama1b_like", S=8192, hq=32, hkv=8, d=64, dtype="bf16", row_block=64),
+}
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def make_desc(W, cfg_id, S):
+    if cfg_id == 4:
+        return W.llama8b_like(S=S)
+    if cfg_id == 5:
+        return W.long_stripes(S=S)
+    if cfg_id == 2:
+        return W.llama1b_like(S=S)
+    raise ValueError(cfg_id)
+
+
+def to_dev(torch, x):
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(x).cuda()
+
+
+def setup(cfg_id, B=1):
+    import torch
+    import structured_sparse_attention_amd as sa
+    import workloads as W
+    c = WORKLOADS[cfg_id]
+    t = time.time()
+    desc = make_desc(W, cfg_id, c["S"])
+    q, k, v = W.qkv(cfg_id, B, c["hq"], c["hkv"], c["S"], c["d"], c["dtype"])
+    log("generated workload %d (%s) in %.1fs" % (cfg_id, c["name"], time.time() - t))
+    pat = sa.DevicePatterns.from_host(desc)
+    qd, kd, vd = to_dev(torch, q), to_dev(torch, k), to_dev(torch, v)
+    ix = sa.build_index(pat, c["row_block"])
+    torch.cuda.synchronize()
+    return desc, (q, k, v), pat, (qd, kd, vd), ix
+
+
+def time_attention_only(sa, torch, qkv_dev, ix, reps):
+    qd, kd, vd = qkv_dev
+    o = torch.empty_like(qd)
+    sa.sparse_attn_prefill(qd, kd, vd, ix, out=o)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        sa.sparse_attn_prefill(qd, kd, vd, ix, out=o)
+        b.record()
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+def cpu_baseline(desc, qkv_host, cfg, target_s=15.0):
+    """The oracle as it stands, on a bounded sample of whole row blocks (seeded), all host threads."""
+    import oracle
+    q, k, v = qkv_host
+    S, hq, BM, d = cfg["S"], cfg["hq"], cfg["row_block"], cfg["d"]
+    nb = -(-S // BM)
+    rng = np.random.default_rng(1234)
+
+    def sample(n_per_head):
+        rows = []
+        for h in range(hq):
+            for rb in rng.choice(nb, size=n_per_head, replace=False):
+                rows += [(0, h, i) for i in range(rb * BM, min(S, (rb + 1) * BM))]
+        return np.array(rows, dtype=np.int32)
+
+    t = time.time()
+    rows = sample(1)
+    _, _, cnt = oracle.attention_rows(desc, q, k, v, rows, return_counts=True)
+    dt = time.time() - t
+    n = max(1, min(nb, int(target_s / max(dt, 1e-3))))
+    if n > 1:
+        rows = sample(n)
+        t = time.time()
+        _, _, cnt = oracle.attention_rows(desc, q, k, v, rows, return_counts=True)
+        dt = time.time() - t
+    flops = 4.0 * d * float(cnt.sum())
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=cores, kind="oracle",
+                sample="%d whole row blocks per head (%d rows, %d retained pairs, seeded), fp64 sparse "
+                       "enumeration, %.1f s" % (n, len(rows), int(cnt.sum()), dt),
+                seconds=dt)
+
+
+def capture_ms(sa, torch, reps=5):
+    import workloads as W
+    maps = W.capture_maps(layers=16, heads=32, n_avg=4)
+    md = torch.from_numpy(maps).cuda()
+    sa.pattern_capture(md)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        sa.pattern_capture(md)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    causal_bytes = 4.0 * maps.shape[0] * 512 * 513 / 2
+    return dict(ms=ms, maps=int(maps.shape[0]), L=512, read_GBps=causal_bytes / (ms * 1e-3) / 1e9)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=4, choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the S=131072 and capture measurements")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (see DESIGN.md for how the "
+              "work would shard across GPUs); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import structured_sparse_attention_amd as sa
+
+    cfg = WORKLOADS[args.config]
+    desc, qkv_host, pat, qkv_dev, ix = setup(args.config)
+    qd, kd, vd = qkv_dev
+    o = torch.empty_like(qd)
+    pairs = ix.total_pairs
+    B = qd.shape[0]
+    flops = 4.0 * cfg["d"] * pairs * B
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        sa.refill_index(pat, ix)
+        if ev is not None:
+            ev[1].record()
+        sa.sparse_attn_prefill(qd, kd, vd, ix, out=o)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    attn_ms = float(np.mean([a1.elapsed_time(a2) for _, a1, a2 in evs]))
+    index_ms = float(np.mean([a0.elapsed_time(a1) for a0, a1, _ in evs]))
+    assert int(ix.status.item()) == 0
+    log("step %.3f ms (index %.3f ms, attention %.3f ms), %d retained pairs" % (ms_per_step, index_ms, attn_ms,
+                                                                              pairs))
+
+    prefill_ms = {str(cfg["S"]): attn_ms}
+    extras = {}
+    if not args.no_extras:
+        del o, qd, kd, vd, qkv_dev
+        torch.cuda.empty_cache()
+        other = 5 if args.config != 5 else 4
+        ocfg = WORKLOADS[other]
+        _, _, opat, oqkv, oix = setup(other)
+        oms = time_attention_only(sa, torch, oqkv, oix, reps=5)
+        prefill_ms[str(ocfg["S"])] = oms
+        extras["other_workload"] = dict(workload=ocfg["name"], S=ocfg["S"], attn_ms=oms,
+                                        effective_tflops=4.0 * ocfg["d"] * oix.total_pairs / (oms * 1e-3) / 1e12,
+                                        retained_pairs=oix.total_pairs)
+        log("workload %s: attention %.3f ms" % (ocfg["name"], oms))
+        del oqkv, oix, opat
+        torch.cuda.empty_cache()
+        extras["capture"] = capture_ms(sa, torch)
+        log("capture: %.3f ms" % extras["capture"]["ms"])
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(desc, qkv_host, cfg)
+        log("cpu oracle: %.4f TFLOP/s on %d threads (%s)" % (cpu["value"], cpu["cores"], cpu["sample"]))
+
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    out = {
+        "metric": "effective TFLOP/s (retained pairs) + prefill attn ms at S=64K/131K, 1 GPU",
+        "value": flops / (ms_per_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["dtype"],
+        "data": "synthetic",
+        "config": {"workload": "%s: batch 1, S=%d, %d q / %d kv heads, head_dim %d, row block %d"
+                               % (cfg["name"], cfg["S"], cfg["hq"], cfg["hkv"], cfg["d"], cfg["row_block"]),
+                   "batch": B, "seq_len": cfg["S"], "hq": cfg["hq"], "hkv": cfg["hkv"], "head_dim": cfg["d"]},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None, "kernel": "k_attn (bf16, d=128)"},
+        "cpu_baseline": None if cpu is None else {k2: cpu[k2] for k2 in ("value", "unit", "cores", "kind", "sample")},
+        "prefill_attn_ms": prefill_ms,
+        "index_build_ms": index_ms,
+        "retained_pairs": pairs,
+        "effective_flops_per_step": flops,
+    }
+    out.update(extras)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,229 @@
+/*
+ * sa.h -- C ABI of libsa.so: structured sparse prefill attention on AMD MI355X (gfx950).
+ *
+ * The method: causal prefill attention in which a per-head structured mask is
+ * applied to the logits before softmax, so that only the retained (query i,
+ * key j) pairs are computed.  Sources, cited by page title and section:
+ *   [DAM]    Pith review of "DAM: Dynamic Attention Mask for Long-Context Large
+ *            Language Model Inference Acceleration": "What carries the argument"
+ *            (pattern pool, Box-Cox lambda = 0.5, tau = 0.3, overlap score gamma,
+ *            mu = 0.8, extension to S x S, mask before softmax), "Referee Report"
+ *            (Summary: A' = (Q K^T / sqrt(d_k)) (.) M; minor comment 1: epsilon),
+ *            "Circularity Check" (step 1: extended mask = union of matched
+ *            patterns; step 2: cost O(sL) with s retained keys per query).
+ *   [Seer]   "SeerAttention: Learning Intrinsic Sparse Attention in Your LLMs",
+ *            abstract: block-level (64 x 64) attention sparsity.
+ *   [Anchor] "AnchorAttention: Difference-Aware Sparse Attention with Stripe
+ *            Granularity", abstract: stripe-granularity sparsity for prefill.
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked (host).  Structs are passed by
+ *     host pointer; the device pointers inside them are read by the kernels.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on `stream` and returns, except where a call is documented to
+ *     synchronise `stream`.
+ *   - The library never allocates or frees device memory: the caller owns every
+ *     buffer.  It keeps no state between calls; calls are thread-safe.
+ *   - Arguments are validated on the host before anything is enqueued: a negative
+ *     return value means nothing was launched, except SA_ERR_HIP, which reports a
+ *     failed launch.
+ */
+#ifndef SA_H
+#define SA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t sa_status;
+#define SA_OK 0
+#define SA_ERR_INVALID_ARG (-1)  /* null pointer, bad shape or size, inconsistent sizes */
+#define SA_ERR_UNSUPPORTED (-2)  /* valid request outside what this build implements */
+#define SA_ERR_DESC_INVALID (-3) /* descriptor contents not sorted/unique/in range */
+#define SA_ERR_CAPACITY (-4)     /* an output array is smaller than the result */
+#define SA_ERR_HIP (-5)          /* a HIP runtime call or kernel launch failed */
+
+#define SA_DTYPE_F32 0
+#define SA_DTYPE_BF16 1
+
+/* Bits of sa_index.status (device int32). */
+#define SA_STATUS_OVERFLOW 1     /* a fill stopped at an array's capacity */
+#define SA_STATUS_DESC_INVALID 2 /* a descriptor list was unsorted, repeated or out of range */
+
+/* Flags of sa_build_index. */
+#define SA_BUILD_VALIDATE 1 /* check descriptor contents on the device (reported via sizes query) */
+
+/* Text for a status code (host; static string, never NULL). */
+const char* sa_status_string(sa_status s);
+/* Library version string (host; static string). */
+const char* sa_version(void);
+
+/*
+ * Pattern descriptor, one mask per QUERY head h in [0, n_heads), shared by every
+ * batch element.  Pair (i, j) is retained iff j <= i < S and at least one holds:
+ *   (i - j) in D_h          diagonal patterns  j = i - r        [DAM, pattern pool]
+ *   j in C_h                vertical patterns  j = c, i >= c    [DAM, pattern pool]
+ *   block_mask[h][i/bs][j/bs] != 0   bs = block_size           [Seer, block sparsity]
+ *   j in stripe list (h, i / stripe_rows)                       [Anchor, stripes]
+ * (the extended mask is the union of the patterns [DAM, Circularity Check 1]).
+ *   diag_ptr  int32 [n_heads+1]  CSR row pointers into diag_off (diag_ptr[0] = 0)
+ *   diag_off  int32 [diag_ptr[n_heads]]  per head strictly increasing, in [0, S)
+ *   vert_ptr  int32 [n_heads+1]; vert_col int32 [...]: strictly increasing, in [0, S)
+ *   block_mask  NULL, or uint8 [n_heads][nbq][nbq], nbq = ceil(S / block_size);
+ *               entries above the block diagonal are ignored (causality).
+ *   block_size  multiple of the index row block (64 or 128) when block_mask != NULL.
+ *   stripe_ptr  NULL, or int64 [n_heads * nst + 1], nst = ceil(S / stripe_rows);
+ *               list (h, t) = stripe_col[stripe_ptr[h*nst+t] .. stripe_ptr[h*nst+t+1])
+ *   stripe_col  int32, strictly increasing within each list, in [0, S).
+ *   stripe_rows multiple of the index row block when stripe_ptr != NULL.
+ * The ptr arrays must be consistent with the allocation sizes of the arrays they
+ * index (the library reads diag_off[diag_ptr[h] .. diag_ptr[h+1]) and so on).
+ */
+typedef struct sa_pattern_desc {
+  int32_t S;
+  int32_t n_heads;
+  const int32_t* diag_ptr;
+  const int32_t* diag_off;
+  const int32_t* vert_ptr;
+  const int32_t* vert_col;
+  const uint8_t* block_mask;
+  int32_t block_size;
+  const int64_t* stripe_ptr;
+  const int32_t* stripe_col;
+  int32_t stripe_rows;
+} sa_pattern_desc;
+
+/* Element counts of the variable-length index arrays. */
+typedef struct sa_index_sizes {
+  int64_t n_runs;  /* run_lo / run_hi */
+  int64_t n_segs;  /* seg_lo / seg_hi */
+  int64_t n_bcols; /* bcol_idx */
+  int64_t n_cols;  /* col_idx */
+} sa_index_sizes;
+
+/*
+ * Canonical sparse index for one descriptor and one row block BM (the pages give
+ * no index format; this is the layout the attention kernel consumes).  Row block
+ * rb covers query rows [b0, b1] = [rb*BM, min(S, (rb+1)*BM) - 1]; item it = h*nb + rb.
+ *   run_ptr [n_heads+1], run_lo/run_hi [n_runs]: maximal runs [lo, hi] of D_h.
+ *   U(h, rb) = { j >= 0 : i - j in D_h for some i in [b0, b1] }: the key columns
+ *              the diagonals touch inside the row block.
+ *   seg_ptr [n_items+1] (int64), seg_lo/seg_hi [n_segs]: maximal intervals of U, ascending.
+ *   X(h, rb) = verticals <= b1, columns of the blocks in block row b0/bs (<= b1),
+ *              columns of stripe list (h, b0/stripe_rows) (<= b1).
+ *   bcol_ptr [n_items+1] (int64), bcol_idx: X intersect U, ascending.
+ *   col_ptr  [n_items+1] (int64), col_idx:  X minus U, ascending.
+ *   pair_count [n_heads] (int64): exact number of retained pairs per head
+ *              (the retained keys s per query, summed [DAM, Circularity Check 2]).
+ *   status   int32 [1]: SA_STATUS_* bits raised by the last build (0 = clean).
+ * Every retained pair is computed exactly once by the attention kernel: pairs with
+ * j in U in the segment phase (retained iff (i-j) in D_h or j in bcols), the others
+ * in the gathered phase (j in cols).  S, n_heads, row_block and n_row_blocks are
+ * host values; `capacity` holds the host-side element capacities of run_lo/run_hi,
+ * seg_lo/seg_hi, bcol_idx and col_idx.
+ */
+typedef struct sa_index {
+  int32_t S;
+  int32_t n_heads;
+  int32_t row_block;
+  int32_t n_row_blocks;
+  int32_t* run_ptr;
+  int32_t* run_lo;
+  int32_t* run_hi;
+  int64_t* seg_ptr;
+  int32_t* seg_lo;
+  int32_t* seg_hi;
+  int64_t* bcol_ptr;
+  int32_t* bcol_idx;
+  int64_t* col_ptr;
+  int32_t* col_idx;
+  int64_t* pair_count;
+  int32_t* status;
+  sa_index_sizes capacity;
+} sa_index;
+
+/*
+ * sa_build_index: descriptor -> canonical index (count, exclusive scan, fill; all on
+ * the device).  idx->S, n_heads, row_block (64 or 128), n_row_blocks = ceil(S/BM) and
+ * the fixed-size arrays run_ptr, seg_ptr, bcol_ptr, col_ptr, pair_count and status
+ * must be set.
+ * Size query: if `sizes` (host) is non-NULL, the call synchronises `stream` after the
+ *   counting pass, writes the totals to *sizes and returns SA_ERR_DESC_INVALID if
+ *   validation (flags & SA_BUILD_VALIDATE) found a bad descriptor.  If any of run_lo,
+ *   run_hi, seg_lo, seg_hi, bcol_idx, col_idx is NULL the call stops after the counts
+ *   (sizes must then be non-NULL).
+ * Fill: with every array present the call recounts and fills; it stays asynchronous
+ *   when sizes == NULL.  A fill that would exceed a capacity stops at the capacity and
+ *   raises SA_STATUS_OVERFLOW in idx->status (SA_ERR_CAPACITY is returned directly
+ *   when `sizes` was requested and shows the shortfall).
+ * Limits: 1 <= S <= 262144 (the per-block bitmap lives in LDS), n_heads >= 1.
+ * Errors: SA_ERR_INVALID_ARG (nulls, shapes, row_block not dividing block_size or
+ *   stripe_rows), SA_ERR_UNSUPPORTED (S above the limit), SA_ERR_DESC_INVALID,
+ *   SA_ERR_CAPACITY, SA_ERR_HIP.
+ */
+sa_status sa_build_index(const sa_pattern_desc* desc, sa_index* idx, sa_index_sizes* sizes, int32_t flags,
+                         void* stream);
+
+/*
+ * sa_sparse_attn_prefill: O = softmax(mask(Q K^T * scale)) V over retained pairs
+ * only [DAM, Referee Report Summary; What carries the argument: masked pairs get
+ * zero weight, read as logit -inf].
+ *   q, o  [batch][hq][S][head_dim], k, v [batch][hkv][S][head_dim], contiguous,
+ *         element type `dtype` (SA_DTYPE_BF16 or SA_DTYPE_F32); o has q's type.
+ *   lse   NULL or float [batch][hq][S]: natural-log log-sum-exp of the scaled
+ *         retained logits; -inf for a row without retained keys (whose o row is 0).
+ *   query head h reads kv head h / (hq / hkv) (hq % hkv == 0).
+ *   softmax_scale <= 0 selects 1 / sqrt(head_dim).
+ *   head_dim in {64, 128}.  idx: built for this S with n_heads == hq.
+ * bf16: bf16 MFMA products with fp32 accumulation, fp32 online softmax, probabilities
+ * rounded to bf16 for the P.V product, output rounded to bf16 (nearest even).
+ * f32: fp32 MFMA throughout.
+ * Errors: SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_HIP.
+ */
+sa_status sa_sparse_attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 int32_t batch, int32_t hq, int32_t hkv, int32_t S, int32_t head_dim,
+                                 int32_t dtype, float softmax_scale, const sa_index* idx, void* stream);
+
+/*
+ * sa_pattern_capture [DAM, What carries the argument]: for each averaged attention
+ * map A (float [n_maps][L][L], row-major; entries with j > i are ignored):
+ *   y = (sqrt(A + eps) - 1) / lambda    Box-Cox with lambda = 0.5 (x^0.5 = sqrt x)
+ *   t = (y - ymin) / (ymax - ymin)      min/max over the causal row (norm_scope 0)
+ *                                       or over the causal map (norm_scope 1);
+ *                                       a constant row/map gives t = 1
+ *   M = (t >= tau)                      the binary true mask
+ *   diag_hits[r] = sum_i M[i][i-r], vert_hits[c] = sum_i M[i][c]
+ *   keep_diag[r] = hits / (L - r) >= mu, keep_vert[c] = hits / (L - c) >= mu
+ * All of it in fp64 with correctly rounded sqrt and division, so the keep flags,
+ * hit counts and mask are exact.  eps: 1e-8 in one section of the paper, 1e-10 in
+ * its appendix [DAM, Referee Report minor comment 1] -- a parameter here.
+ * Requires every causal entry finite with A + eps >= 0 (attention probabilities).
+ *   keep_diag, keep_vert  uint8 [n_maps][L];  diag_hits, vert_hits NULL or int32
+ *   [n_maps][L];  true_mask NULL or uint8 [n_maps][L][L] (zeros above the diagonal).
+ * Limits: 1 <= L <= 4096; lambda == 0.5 (else SA_ERR_UNSUPPORTED); norm_scope 0 or 1.
+ */
+sa_status sa_pattern_capture(const float* maps, int32_t n_maps, int32_t L, double lambda, double eps, double tau,
+                             double mu, int32_t norm_scope, uint8_t* keep_diag, uint8_t* keep_vert,
+                             int32_t* diag_hits, int32_t* vert_hits, uint8_t* true_mask, void* stream);
+
+/*
+ * sa_patterns_to_desc [DAM, What carries the argument; Circularity Check 1]: the kept
+ * patterns of each map are pasted into an S x S mask, i.e. the per-head descriptor
+ * lists at length S are D_h = { r : keep_diag[h][r], r < S } and
+ * C_h = { c : keep_vert[h][c], c < S }.
+ *   keep_diag, keep_vert  uint8 [n_maps][L]   (one map per query head)
+ *   diag_ptr, vert_ptr    int32 [n_maps + 1]
+ *   diag_off, vert_col    int32, capacity n_maps * min(L, S) each (always enough)
+ */
+sa_status sa_patterns_to_desc(const uint8_t* keep_diag, const uint8_t* keep_vert, int32_t n_maps, int32_t L,
+                              int32_t S, int32_t* diag_ptr, int32_t* diag_off, int32_t* vert_ptr,
+                              int32_t* vert_col, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SA_H */

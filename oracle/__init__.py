@@ -64,7 +64,8 @@ def _load():
                 [C.c_void_p] * 2 + [C.c_int64] + [C.c_void_p] * 2 + [C.c_int64] + [C.c_void_p, C.POINTER(_Sizes)]
             lib.orc_attention_rows.argtypes = [C.POINTER(_Desc), C.c_void_p, C.c_void_p, C.c_void_p, C.c_int,
                                                C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_double,
-                                               C.c_void_p, C.c_int64, C.c_int, C.c_void_p, C.c_void_p]
+                                               C.c_void_p, C.c_int64, C.c_int, C.c_void_p, C.c_void_p,
+                                               C.c_void_p]
             lib.orc_capture.restype = C.c_int
             lib.orc_capture.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_double, C.c_double, C.c_double,
                                         C.c_double, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
@@ -149,12 +150,13 @@ def build_index(desc, row_block: int, with_pairs: bool = True) -> dict:
                 pair_count=pairs if with_pairs else None)
 
 
-def attention_rows(desc, q, k, v, rows, scale: Optional[float] = None, mode: int = 0):
+def attention_rows(desc, q, k, v, rows, scale: Optional[float] = None, mode: int = 0, return_counts: bool = False):
     """fp64 attention for the (b, h, i) triples in ``rows``.
 
     q [B,hq,S,d], k/v [B,hkv,S,d]: float32 arrays or uint16 bf16 bit patterns.
     mode 0 sums over retained keys only; mode 1 is the dense form with masked
-    logits set to -inf.  Returns (o [n, d] float64, lse [n] float64).
+    logits set to -inf.  Returns (o [n, d] float64, lse [n] float64) and, with
+    return_counts, the number of retained keys of each row (int64 [n]).
     """
     lib = _load()
     hd = _DescHolder(desc)
@@ -171,9 +173,11 @@ def attention_rows(desc, q, k, v, rows, scale: Optional[float] = None, mode: int
     n = rows.shape[0]
     o = np.zeros((n, d), np.float64)
     lse = np.zeros(n, np.float64)
+    cnt = np.zeros(n, np.int64)
     lib.orc_attention_rows(C.byref(hd.c), q.ctypes.data, k.ctypes.data, v.ctypes.data, dtype, B, hq, hkv, S, d,
-                           float(scale), rows.ctypes.data, n, mode, o.ctypes.data, lse.ctypes.data)
-    return o, lse
+                           float(scale), rows.ctypes.data, n, mode, o.ctypes.data, lse.ctypes.data,
+                           cnt.ctypes.data)
+    return (o, lse, cnt) if return_counts else (o, lse)
 
 
 def capture(maps: np.ndarray, lam: float = 0.5, eps: float = 1e-8, tau: float = 0.3, mu: float = 0.8,

@@ -294,6 +294,7 @@ int orc_build_index(const orc_desc* d, int32_t BM,
 /* mode 0: sparse enumeration (sum over retained keys only).                */
 /* mode 1: dense form over all S keys with masked logits = -inf.            */
 /* rows: n_rows triples (b, h, i).  o: [n_rows][dh]; lse: [n_rows].         */
+/* n_keys (optional): the number of retained keys of each row.             */
 /* ------------------------------------------------------------------------ */
 static double widen(const void* base, int dtype, int64_t idx) {
   if (dtype == 0) return (double)((const float*)base)[idx];
@@ -305,7 +306,8 @@ static double widen(const void* base, int dtype, int64_t idx) {
 
 void orc_attention_rows(const orc_desc* d, const void* q, const void* k, const void* v, int dtype,
                         int32_t B, int32_t hq, int32_t hkv, int32_t S, int32_t dh, double scale,
-                        const int32_t* rows, int64_t n_rows, int mode, double* o, double* lse) {
+                        const int32_t* rows, int64_t n_rows, int mode, double* o, double* lse,
+                        int64_t* n_keys /* NULL or [n_rows]: retained keys per row */) {
   (void)B;
   int32_t group = hq / hkv;
 #pragma omp parallel
@@ -321,6 +323,11 @@ void orc_attention_rows(const orc_desc* d, const void* q, const void* k, const v
       int64_t kvbase = ((int64_t)b * hkv + g) * (int64_t)S * dh;
       for (int32_t c = 0; c < dh; ++c) qi[c] = widen(q, dtype, qbase + c);
       orc_row_mask(d, h, i, keep);
+      if (n_keys) {
+        int64_t cnt = 0;
+        for (int32_t j = 0; j <= i; ++j) cnt += keep[j];
+        n_keys[n] = cnt;
+      }
       int32_t jend = (mode == 1) ? S - 1 : i;
       double m = -INFINITY;
       for (int32_t j = 0; j <= jend; ++j) {

@@ -1,0 +1,277 @@
+"""structured_sparse_attention_amd -- Python binding of libsa.so (gfx950).
+
+Argument marshalling only: every step of the path (index build, sparse attention,
+pattern capture, pattern extension) runs in the HIP kernels of ``libsa.so``;
+PyTorch supplies device memory and the current HIP stream.  The C ABI is declared
+in ``include/sa.h``.  Importing this package loads ``libsa.so`` and raises if it
+has not been built (``python -m structured_sparse_attention_amd.build``); there is
+no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import math
+import os
+from typing import Optional
+
+import numpy as np
+import torch
+
+__all__ = ["SAError", "DevicePatterns", "SparseIndex", "build_index", "sparse_attn_prefill", "pattern_capture",
+           "patterns_to_desc", "library_path", "version", "lib"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libsa.so")
+
+SA_DTYPE_F32, SA_DTYPE_BF16 = 0, 1
+SA_BUILD_VALIDATE = 1
+STATUS_OVERFLOW, STATUS_DESC_INVALID = 1, 2
+
+
+class SAError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__("%s failed: %s (%d)" % (where, _lib.sa_status_string(code).decode(), code))
+
+
+class _Desc(C.Structure):
+    _fields_ = [("S", C.c_int32), ("n_heads", C.c_int32),
+                ("diag_ptr", C.c_void_p), ("diag_off", C.c_void_p), ("vert_ptr", C.c_void_p),
+                ("vert_col", C.c_void_p), ("block_mask", C.c_void_p), ("block_size", C.c_int32),
+                ("stripe_ptr", C.c_void_p), ("stripe_col", C.c_void_p), ("stripe_rows", C.c_int32)]
+
+
+class _Sizes(C.Structure):
+    _fields_ = [("n_runs", C.c_int64), ("n_segs", C.c_int64), ("n_bcols", C.c_int64), ("n_cols", C.c_int64)]
+
+
+class _Index(C.Structure):
+    _fields_ = [("S", C.c_int32), ("n_heads", C.c_int32), ("row_block", C.c_int32), ("n_row_blocks", C.c_int32),
+                ("run_ptr", C.c_void_p), ("run_lo", C.c_void_p), ("run_hi", C.c_void_p),
+                ("seg_ptr", C.c_void_p), ("seg_lo", C.c_void_p), ("seg_hi", C.c_void_p),
+                ("bcol_ptr", C.c_void_p), ("bcol_idx", C.c_void_p), ("col_ptr", C.c_void_p),
+                ("col_idx", C.c_void_p), ("pair_count", C.c_void_p), ("status", C.c_void_p),
+                ("capacity", _Sizes)]
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError("libsa.so is not built (%s); run `python -m structured_sparse_attention_amd.build`"
+                          % _LIB_PATH)
+    lib = C.CDLL(_LIB_PATH)
+    lib.sa_status_string.restype = C.c_char_p
+    lib.sa_status_string.argtypes = [C.c_int32]
+    lib.sa_version.restype = C.c_char_p
+    lib.sa_version.argtypes = []
+    lib.sa_build_index.restype = C.c_int32
+    lib.sa_build_index.argtypes = [C.POINTER(_Desc), C.POINTER(_Index), C.POINTER(_Sizes), C.c_int32, C.c_void_p]
+    lib.sa_sparse_attn_prefill.restype = C.c_int32
+    lib.sa_sparse_attn_prefill.argtypes = [C.c_void_p] * 4 + [C.c_void_p] + [C.c_int32] * 6 + \
+        [C.c_float, C.POINTER(_Index), C.c_void_p]
+    lib.sa_pattern_capture.restype = C.c_int32
+    lib.sa_pattern_capture.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_double, C.c_double, C.c_double,
+                                       C.c_double, C.c_int32] + [C.c_void_p] * 5 + [C.c_void_p]
+    lib.sa_patterns_to_desc.restype = C.c_int32
+    lib.sa_patterns_to_desc.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32] + \
+        [C.c_void_p] * 4 + [C.c_void_p]
+    return lib
+
+
+_lib = _load()
+lib = _lib
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def version() -> str:
+    return _lib.sa_version().decode()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _check(code: int, where: str):
+    if code != 0:
+        raise SAError(code, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _dev_array(a, dtype: torch.dtype, device) -> torch.Tensor:
+    """Host or device array -> contiguous device tensor with at least one element."""
+    t = a if isinstance(a, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(a))
+    t = t.to(device=device, dtype=dtype).contiguous()
+    if t.numel() == 0:
+        t = torch.zeros(1, dtype=dtype, device=device)
+    return t
+
+
+class DevicePatterns:
+    """A pattern descriptor (see sa_pattern_desc in include/sa.h) held in device memory."""
+
+    def __init__(self, S: int, n_heads: int, diag_ptr, diag_off, vert_ptr, vert_col, block_mask=None,
+                 block_size: int = 64, stripe_ptr=None, stripe_col=None, stripe_rows: int = 128, device="cuda"):
+        self.S, self.n_heads = int(S), int(n_heads)
+        self.diag_ptr = _dev_array(diag_ptr, torch.int32, device)
+        self.diag_off = _dev_array(diag_off, torch.int32, device)
+        self.vert_ptr = _dev_array(vert_ptr, torch.int32, device)
+        self.vert_col = _dev_array(vert_col, torch.int32, device)
+        self.block_mask = None if block_mask is None else _dev_array(block_mask, torch.uint8, device)
+        self.block_size = int(block_size)
+        self.stripe_ptr = None if stripe_ptr is None else _dev_array(stripe_ptr, torch.int64, device)
+        self.stripe_col = None if stripe_ptr is None else _dev_array(stripe_col, torch.int32, device)
+        self.stripe_rows = int(stripe_rows)
+
+    @classmethod
+    def from_host(cls, desc, device="cuda") -> "DevicePatterns":
+        """From any object with the descriptor fields (S, H or n_heads, diag_ptr, ...)."""
+        H = getattr(desc, "n_heads", None) or getattr(desc, "H")
+        return cls(desc.S, H, desc.diag_ptr, desc.diag_off, desc.vert_ptr, desc.vert_col,
+                   getattr(desc, "block_mask", None), getattr(desc, "block_size", 64),
+                   getattr(desc, "stripe_ptr", None), getattr(desc, "stripe_col", None),
+                   getattr(desc, "stripe_rows", 128), device=device)
+
+    def c_struct(self) -> _Desc:
+        return _Desc(self.S, self.n_heads, _ptr(self.diag_ptr), _ptr(self.diag_off), _ptr(self.vert_ptr),
+                     _ptr(self.vert_col), _ptr(self.block_mask), self.block_size, _ptr(self.stripe_ptr),
+                     _ptr(self.stripe_col), self.stripe_rows)
+
+
+class SparseIndex:
+    """Canonical sparse index (sa_index in include/sa.h) in device memory."""
+
+    KEYS = ("run_ptr", "run_lo", "run_hi", "seg_ptr", "seg_lo", "seg_hi", "bcol_ptr", "bcol_idx", "col_ptr",
+            "col_idx", "pair_count")
+
+    def __init__(self, S, n_heads, row_block, device):
+        self.S, self.n_heads, self.row_block = S, n_heads, row_block
+        self.n_row_blocks = -(-S // row_block)
+        n = n_heads * self.n_row_blocks
+        self.run_ptr = torch.zeros(n_heads + 1, dtype=torch.int32, device=device)
+        self.seg_ptr = torch.zeros(n + 1, dtype=torch.int64, device=device)
+        self.bcol_ptr = torch.zeros(n + 1, dtype=torch.int64, device=device)
+        self.col_ptr = torch.zeros(n + 1, dtype=torch.int64, device=device)
+        self.pair_count = torch.zeros(n_heads, dtype=torch.int64, device=device)
+        self.status = torch.zeros(1, dtype=torch.int32, device=device)
+        self.run_lo = self.run_hi = self.seg_lo = self.seg_hi = self.bcol_idx = self.col_idx = None
+        self.sizes = None
+
+    def _alloc_payload(self, sizes: _Sizes, device):
+        mk = lambda n: torch.zeros(max(1, int(n)), dtype=torch.int32, device=device)
+        self.run_lo, self.run_hi = mk(sizes.n_runs), mk(sizes.n_runs)
+        self.seg_lo, self.seg_hi = mk(sizes.n_segs), mk(sizes.n_segs)
+        self.bcol_idx, self.col_idx = mk(sizes.n_bcols), mk(sizes.n_cols)
+        self.sizes = dict(n_runs=sizes.n_runs, n_segs=sizes.n_segs, n_bcols=sizes.n_bcols, n_cols=sizes.n_cols)
+
+    def c_struct(self) -> _Index:
+        cap = _Sizes(*(self.sizes[k] if self.sizes else 0 for k in ("n_runs", "n_segs", "n_bcols", "n_cols")))
+        return _Index(self.S, self.n_heads, self.row_block, self.n_row_blocks, _ptr(self.run_ptr),
+                      _ptr(self.run_lo), _ptr(self.run_hi), _ptr(self.seg_ptr), _ptr(self.seg_lo),
+                      _ptr(self.seg_hi), _ptr(self.bcol_ptr), _ptr(self.bcol_idx), _ptr(self.col_ptr),
+                      _ptr(self.col_idx), _ptr(self.pair_count), _ptr(self.status), cap)
+
+    def to_numpy(self) -> dict:
+        out = dict(S=self.S, n_heads=self.n_heads, row_block=self.row_block, n_row_blocks=self.n_row_blocks)
+        for k in self.KEYS:
+            t = getattr(self, k).cpu().numpy()
+            size_key = {"run_lo": "n_runs", "run_hi": "n_runs", "seg_lo": "n_segs", "seg_hi": "n_segs",
+                        "bcol_idx": "n_bcols", "col_idx": "n_cols"}.get(k)
+            out[k] = t[:self.sizes[size_key]] if size_key else t
+        return out
+
+    @property
+    def total_pairs(self) -> int:
+        return int(self.pair_count.sum().item())
+
+
+def build_index(patterns: DevicePatterns, row_block: int, validate: bool = False, stream=None) -> SparseIndex:
+    """sa_build_index: size query (synchronises the stream), allocation, then the fill."""
+    dev = patterns.diag_ptr.device
+    ix = SparseIndex(patterns.S, patterns.n_heads, row_block, dev)
+    d = patterns.c_struct()
+    c = ix.c_struct()
+    sizes = _Sizes()
+    flags = SA_BUILD_VALIDATE if validate else 0
+    _check(_lib.sa_build_index(C.byref(d), C.byref(c), C.byref(sizes), flags, _stream(stream)), "sa_build_index")
+    ix._alloc_payload(sizes, dev)
+    refill_index(patterns, ix, stream)
+    ix._patterns = patterns
+    return ix
+
+
+def refill_index(patterns: DevicePatterns, ix: SparseIndex, stream=None):
+    """Re-run the whole build (count, scan, fill) into an existing index without synchronising."""
+    d = patterns.c_struct()
+    c = ix.c_struct()
+    _check(_lib.sa_build_index(C.byref(d), C.byref(c), None, 0, _stream(stream)), "sa_build_index")
+
+
+def sparse_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: SparseIndex,
+                        softmax_scale: Optional[float] = None, return_lse: bool = False,
+                        out: Optional[torch.Tensor] = None, stream=None):
+    """sa_sparse_attn_prefill: q [B,Hq,S,d], k/v [B,Hkv,S,d] (bf16 or fp32, contiguous, on the GPU)."""
+    if q.dtype == torch.bfloat16:
+        dt = SA_DTYPE_BF16
+    elif q.dtype == torch.float32:
+        dt = SA_DTYPE_F32
+    else:
+        raise TypeError("q must be bfloat16 or float32")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q [B,Hq,S,d] and k, v [B,Hkv,S,d] expected")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, hq, S, d = q.shape
+    if k.shape[0] != B or k.shape[2] != S or k.shape[3] != d:
+        raise ValueError("k/v shape does not match q")
+    o = torch.empty_like(q) if out is None else out
+    if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous():
+        raise ValueError("out must match q")
+    lse = torch.empty((B, hq, S), dtype=torch.float32, device=q.device) if return_lse else None
+    c = index.c_struct()
+    scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    _check(_lib.sa_sparse_attn_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse), B, hq,
+                                       k.shape[1], S, d, dt, scale, C.byref(c), _stream(stream)),
+           "sa_sparse_attn_prefill")
+    return (o, lse) if return_lse else o
+
+
+def pattern_capture(maps: torch.Tensor, lam: float = 0.5, eps: float = 1e-8, tau: float = 0.3, mu: float = 0.8,
+                    norm_scope: int = 0, return_hits: bool = True, return_mask: bool = False, stream=None) -> dict:
+    """sa_pattern_capture on float32 maps [n, L, L] in device memory."""
+    if maps.dtype != torch.float32 or maps.dim() != 3 or maps.shape[1] != maps.shape[2] or not maps.is_contiguous():
+        raise ValueError("maps must be a contiguous float32 [n, L, L] tensor")
+    n, L, _ = maps.shape
+    dev = maps.device
+    kd = torch.empty((n, L), dtype=torch.uint8, device=dev)
+    kv = torch.empty((n, L), dtype=torch.uint8, device=dev)
+    hd = torch.empty((n, L), dtype=torch.int32, device=dev) if return_hits else None
+    hv = torch.empty((n, L), dtype=torch.int32, device=dev) if return_hits else None
+    tm = torch.empty((n, L, L), dtype=torch.uint8, device=dev) if return_mask else None
+    _check(_lib.sa_pattern_capture(maps.data_ptr(), n, L, lam, eps, tau, mu, norm_scope, kd.data_ptr(),
+                                   kv.data_ptr(), _ptr(hd), _ptr(hv), _ptr(tm), _stream(stream)),
+           "sa_pattern_capture")
+    return dict(keep_diag=kd, keep_vert=kv, diag_hits=hd, vert_hits=hv, true_mask=tm)
+
+
+def patterns_to_desc(keep_diag: torch.Tensor, keep_vert: torch.Tensor, S: int, stream=None) -> DevicePatterns:
+    """sa_patterns_to_desc: kept patterns of each map (one map per query head) -> descriptor at length S."""
+    n, L = keep_diag.shape
+    dev = keep_diag.device
+    cap = max(1, n * min(L, S))
+    dp = torch.empty(n + 1, dtype=torch.int32, device=dev)
+    vp = torch.empty(n + 1, dtype=torch.int32, device=dev)
+    do = torch.empty(cap, dtype=torch.int32, device=dev)
+    vc = torch.empty(cap, dtype=torch.int32, device=dev)
+    _check(_lib.sa_patterns_to_desc(keep_diag.contiguous().data_ptr(), keep_vert.contiguous().data_ptr(), n, L, S,
+                                    dp.data_ptr(), do.data_ptr(), vp.data_ptr(), vc.data_ptr(), _stream(stream)),
+           "sa_patterns_to_desc")
+    return DevicePatterns(S, n, dp, do, vp, vc, device=dev)

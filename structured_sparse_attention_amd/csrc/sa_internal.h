@@ -1,0 +1,42 @@
+// sa_internal.h -- declarations shared by the host entry points and the kernel files of libsa.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "sa.h"
+
+namespace sa {
+
+// Largest sequence length the index builder accepts: two bitmaps of S bits live in LDS.
+constexpr int32_t kMaxIndexS = 262144;
+// Largest capture window (two int32 hit arrays of L entries live in LDS).
+constexpr int32_t kMaxCaptureL = 4096;
+
+// Index builder (sa_index.hip).  All launches go on `stream`.
+hipError_t launch_index_runs(const sa_pattern_desc& d, const sa_index& ix, int32_t validate, hipStream_t stream);
+hipError_t launch_index_items(const sa_pattern_desc& d, const sa_index& ix, int32_t fill, int32_t validate,
+                              hipStream_t stream);
+hipError_t launch_index_scan(const sa_index& ix, hipStream_t stream);
+
+// Attention (sa_attn.hip).
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int32_t batch, hq, hkv, S, head_dim, dtype;
+  float scale;
+  const sa_index* idx;
+};
+hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
+
+// Pattern capture and extension (sa_capture.hip).
+hipError_t launch_capture(const float* maps, int32_t n_maps, int32_t L, double lambda, double eps, double tau,
+                          double mu, int32_t norm_scope, uint8_t* keep_diag, uint8_t* keep_vert, int32_t* diag_hits,
+                          int32_t* vert_hits, uint8_t* true_mask, hipStream_t stream);
+hipError_t launch_patterns_to_desc(const uint8_t* keep_diag, const uint8_t* keep_vert, int32_t n_maps, int32_t L,
+                                   int32_t S, int32_t* diag_ptr, int32_t* diag_off, int32_t* vert_ptr,
+                                   int32_t* vert_col, hipStream_t stream);
+
+}  // namespace sa

@@ -1,0 +1,118 @@
+"""CPU tests of the C ABI: the library loads, exports every declared entry point, and
+its host-side validation rejects bad arguments before anything touches a GPU."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sa.h")
+
+
+@pytest.fixture(scope="module")
+def m():
+    import structured_sparse_attention_amd as pkg   # raises if libsa.so is not built
+    return pkg
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for f in ("sa_build_index", "sa_sparse_attn_prefill", "sa_pattern_capture", "sa_patterns_to_desc",
+              "sa_status_string", "sa_version"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol(m):
+    lib = C.CDLL(m.library_path())
+    missing = [f for f in declared_functions() if not hasattr(lib, f)]
+    assert not missing, missing
+
+
+def test_status_strings_and_version(m):
+    for code in (0, -1, -2, -3, -4, -5):
+        assert m.lib.sa_status_string(code)
+    assert b"gfx950" in m.lib.sa_version()
+
+
+FAKE = C.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+
+
+def _desc(m, S=512, H=1, **kw):
+    d = m._Desc(S, H, FAKE.value, FAKE.value, FAKE.value, FAKE.value, None, 64, None, None, 128)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def _index(m, S=512, H=1, BM=64, **kw):
+    ix = m._Index(S, H, BM, -(-S // BM), *([FAKE.value] * 12), m._Sizes(10, 10, 10, 10))
+    for k, v in kw.items():
+        setattr(ix, k, v)
+    return ix
+
+
+def test_build_index_validation(m):
+    f = m.lib.sa_build_index
+    sz = m._Sizes()
+    assert f(None, C.byref(_index(m)), C.byref(sz), 0, None) == -1
+    assert f(C.byref(_desc(m)), None, C.byref(sz), 0, None) == -1
+    assert f(C.byref(_desc(m, S=0)), C.byref(_index(m, S=0)), C.byref(sz), 0, None) == -1
+    assert f(C.byref(_desc(m)), C.byref(_index(m, BM=32)), C.byref(sz), 0, None) == -1
+    assert f(C.byref(_desc(m)), C.byref(_index(m, n_row_blocks=3)), C.byref(sz), 0, None) == -1
+    assert f(C.byref(_desc(m, H=2)), C.byref(_index(m)), C.byref(sz), 0, None) == -1
+    assert f(C.byref(_desc(m, diag_off=None)), C.byref(_index(m)), C.byref(sz), 0, None) == -1
+    # block size must be a multiple of the row block
+    assert f(C.byref(_desc(m, block_mask=FAKE.value, block_size=64)), C.byref(_index(m, BM=128)),
+             C.byref(sz), 0, None) == -1
+    assert f(C.byref(_desc(m, stripe_ptr=FAKE.value, stripe_col=FAKE.value, stripe_rows=96)),
+             C.byref(_index(m, BM=64)), C.byref(sz), 0, None) == -1
+    # size query needs `sizes` when the payload arrays are missing
+    assert f(C.byref(_desc(m)), C.byref(_index(m, col_idx=None)), None, 0, None) == -1
+    # too long for the LDS bitmaps
+    S = 300000
+    assert f(C.byref(_desc(m, S=S)), C.byref(_index(m, S=S)), C.byref(sz), 0, None) == -2
+
+
+def test_attention_validation(m):
+    f = m.lib.sa_sparse_attn_prefill
+    ix = _index(m)
+    p = FAKE.value
+    assert f(None, p, p, p, None, 1, 1, 1, 512, 64, 1, 0.0, C.byref(ix), None) == -1
+    assert f(p, p, p, p, None, 1, 3, 2, 512, 64, 1, 0.0, C.byref(ix), None) == -1   # hq % hkv
+    assert f(p, p, p, p, None, 1, 1, 1, 512, 64, 7, 0.0, C.byref(ix), None) == -1   # dtype
+    assert f(p, p, p, p, None, 1, 1, 1, 512, 96, 1, 0.0, C.byref(ix), None) == -2   # head_dim
+    assert f(p, p, p, p, None, 1, 1, 1, 256, 64, 1, 0.0, C.byref(ix), None) == -1   # S != index S
+    assert f(p, p, p, p, None, 1, 2, 1, 512, 64, 1, 0.0, C.byref(ix), None) == -1   # heads != index heads
+    assert f(p, p, p, p, None, 0, 1, 1, 512, 64, 1, 0.0, C.byref(ix), None) == -1   # batch
+    assert f(p, p, p, p, None, 1, 1, 1, 512, 64, 1, 0.0, C.byref(_index(m, col_idx=None)), None) == -1
+
+
+def test_capture_validation(m):
+    f = m.lib.sa_pattern_capture
+    p = FAKE.value
+    assert f(None, 1, 8, 0.5, 1e-8, 0.3, 0.8, 0, p, p, None, None, None, None) == -1
+    assert f(p, 0, 8, 0.5, 1e-8, 0.3, 0.8, 0, p, p, None, None, None, None) == -1
+    assert f(p, 1, 8, 0.5, 1e-8, 0.3, 0.8, 2, p, p, None, None, None, None) == -1
+    assert f(p, 1, 8, 0.25, 1e-8, 0.3, 0.8, 0, p, p, None, None, None, None) == -2
+    assert f(p, 1, 5000, 0.5, 1e-8, 0.3, 0.8, 0, p, p, None, None, None, None) == -2
+    assert f(p, 1, 8, 0.5, float("nan"), 0.3, 0.8, 0, p, p, None, None, None, None) == -1
+    g = m.lib.sa_patterns_to_desc
+    assert g(None, p, 1, 8, 8, p, p, p, p, None) == -1
+    assert g(p, p, 1, 8, 0, p, p, p, p, None) == -1
+
+
+def test_product_package_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "structured_sparse_attention_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert not re.search(r"\boracle\b|sa_oracle|liboracle|workloads", text), fn

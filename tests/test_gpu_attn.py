@@ -1,0 +1,173 @@
+"""GPU parity: sa_sparse_attn_prefill vs the fp64 oracle.
+
+Full parity (every row) at sizes the oracle finishes in seconds that span several
+tiles and a ragged tail; at the full workload sizes (S = 8192, 16384, 65536,
+131072), every row of the first, the last and seeded row blocks of every head,
+in the same launch configuration the benchmark times.
+Tolerances: bf16 max-abs 2e-2 and mean-abs 2e-3; fp32 max-abs 1e-5.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import (all_rows, assert_close_bf16, assert_close_f32, assert_lse, gather_lse, gather_rows, note,
+                      rows_of_blocks, sa, to_dev, widen)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(desc, q, k, v, BM, rows, what, scale=None):
+    m = sa()
+    B, hq, S, d = q.shape
+    note("attn %s S=%d hq=%d hkv=%d d=%d BM=%d dtype=%s rows=%d" % (what, S, hq, k.shape[1], d, BM, q.dtype,
+                                                                     len(rows)))
+    pat = m.DevicePatterns.from_host(desc)
+    ix = m.build_index(pat, BM)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    o, lse = m.sparse_attn_prefill(qd, kd, vd, ix, softmax_scale=scale, return_lse=True)
+    torch.cuda.synchronize()
+    got, got_lse = gather_rows(o, rows), gather_lse(lse, rows)
+    ref, ref_lse = oracle.attention_rows(desc, q, k, v, rows, scale=scale)
+    if q.dtype == np.float32:
+        assert_close_f32(got, ref, what)
+        assert_lse(got_lse, ref_lse, 1e-5, what)
+    else:
+        assert_close_bf16(got, ref, what)
+        assert_lse(got_lse, ref_lse, 1e-3, what)
+    return o, ix
+
+
+# ------------------------------------------------------------------ workload 1 (fp32) and its variants
+@pytest.mark.parametrize("variant", ["base", "dense_causal", "all_ones", "diag0"])
+@pytest.mark.parametrize("BM", [64, 128])
+def test_tiny_fp32(variant, BM):
+    desc = W.tiny(variant)
+    q, k, v = W.qkv(1, 1, 1, 1, 512, 64, "f32")
+    _run(desc, q, k, v, BM, all_rows(1, 1, 512), "tiny-" + variant)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_diagonal_zero_returns_v_exactly(dtype, d):
+    m = sa()
+    S = 300
+    desc = W.tiny("diag0", S=S)
+    q, k, v = W.qkv(11, 1, 1, 1, S, d, dtype)
+    note("diag0 identity dtype=%s d=%d" % (dtype, d))
+    ix = m.build_index(m.DevicePatterns.from_host(desc), 64)
+    o = m.sparse_attn_prefill(to_dev(q), to_dev(k), to_dev(v), ix)
+    torch.cuda.synchronize()
+    assert torch.equal(o.cpu(), to_dev(v, "cpu"))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_band_and_column_encodings_agree(dtype):
+    S, d = 700, 64
+    q, k, v = W.qkv(12, 1, 1, 1, S, d, dtype)
+    rows = all_rows(1, 1, S)
+    oa, _ = _run(W.tiny("dense_causal", S=S), q, k, v, 64, rows, "dense-band")
+    ob, _ = _run(W.tiny("all_ones", S=S), q, k, v, 64, rows, "dense-cols")
+    diff = (oa.float() - ob.float()).abs().max().item()
+    assert diff <= (1e-5 if dtype == "f32" else 2e-2)
+
+
+def test_constant_v_gives_ones():
+    m = sa()
+    S, d = 900, 128
+    desc = W.llama8b_like(S=S, H=4)
+    q, k, _ = W.qkv(13, 1, 4, 2, S, d, "bf16")
+    v = W.bf16_bits(np.ones((1, 2, S, d), np.float32))
+    note("constant v")
+    ix = m.build_index(m.DevicePatterns.from_host(desc), 64)
+    o = m.sparse_attn_prefill(to_dev(q), to_dev(k), to_dev(v), ix)
+    torch.cuda.synchronize()
+    assert (o.float() - 1.0).abs().max().item() <= 2e-2
+
+
+def test_empty_rows_zero_output_minus_inf_lse():
+    S, d = 200, 64
+    desc = W.desc_from_lists(S, [np.zeros(0)], [np.array([70])])
+    for dtype in ("f32", "bf16"):
+        q, k, v = W.qkv(14, 1, 1, 1, S, d, dtype)
+        o, _ = _run(desc, q, k, v, 64, all_rows(1, 1, S), "empty-rows-" + dtype)
+        assert o[0, 0, :70].float().abs().max().item() == 0.0
+
+
+def test_batch_and_gqa_and_custom_scale():
+    S, d = 333, 64
+    desc = W.llama1b_like(S=S, H=6)
+    q, k, v = W.qkv(15, 2, 6, 3, S, d, "bf16")
+    _run(desc, q, k, v, 64, all_rows(2, 6, S), "batch-gqa-scale", scale=0.2)
+
+
+# ------------------------------------------------------------------ workload 2 (1B-like, bf16, d=64)
+@pytest.mark.parametrize("S,BM", [(1000, 64), (1000, 128)])
+def test_llama1b_like_small_full(S, BM):
+    desc = W.llama1b_like(S=S, H=8)
+    q, k, v = W.qkv(2, 1, 8, 2, S, 64, "bf16")
+    _run(desc, q, k, v, BM, all_rows(1, 8, S), "1b-like-small")
+
+
+@pytest.mark.parametrize("BM", [64, 128])
+def test_llama1b_like_full_size_sampled(BM):
+    desc = W.llama1b_like()
+    q, k, v = W.qkv(2, 1, 32, 8, 8192, 64, "bf16")
+    rows = rows_of_blocks(1, 32, 8192, BM, 4, np.random.default_rng(2))
+    _run(desc, q, k, v, BM, rows, "1b-like")
+
+
+# ------------------------------------------------------------------ workload 3 (capture -> S=16384)
+def test_capture_extended_attention_sampled():
+    maps = W.capture_maps(layers=1, heads=32, n_avg=16)
+    c = oracle.capture(maps)
+    diags, verts = oracle.extend(c["keep_diag"], c["keep_vert"], 16384)
+    desc = W.desc_from_lists(16384, diags, verts)
+    q, k, v = W.qkv(3, 1, 32, 8, 16384, 64, "bf16")
+    rows = rows_of_blocks(1, 32, 16384, 64, 3, np.random.default_rng(3))
+    _run(desc, q, k, v, 64, rows, "capture-16k")
+
+
+# ------------------------------------------------------------------ workload 4 (8B-like, d=128)
+def test_llama8b_like_small_full():
+    S = 2500
+    desc = W.llama8b_like(S=S, H=8)
+    q, k, v = W.qkv(4, 1, 8, 2, S, 128, "bf16")
+    _run(desc, q, k, v, 64, all_rows(1, 8, S), "8b-like-small")
+
+
+def test_llama8b_like_full_size_sampled():
+    desc = W.llama8b_like()
+    q, k, v = W.qkv(4, 1, 32, 8, 65536, 128, "bf16")
+    rows = rows_of_blocks(1, 32, 65536, 64, 2, np.random.default_rng(4))
+    _run(desc, q, k, v, 64, rows, "8b-like")
+
+
+# ------------------------------------------------------------------ workload 5 (stripes, S=131072)
+@pytest.mark.parametrize("BM", [64, 128])
+def test_long_stripes_small_full(BM):
+    S = 3000
+    desc = W.long_stripes(S=S, H=4, band=512)
+    q, k, v = W.qkv(5, 1, 4, 2, S, 128, "bf16")
+    _run(desc, q, k, v, BM, all_rows(1, 4, S), "stripes-small")
+
+
+def test_long_stripes_full_size_sampled():
+    desc = W.long_stripes()
+    q, k, v = W.qkv(5, 1, 32, 8, 131072, 128, "bf16")
+    rows = rows_of_blocks(1, 32, 131072, 128, 1, np.random.default_rng(5))
+    _run(desc, q, k, v, 128, rows, "stripes-131k")
+
+
+def test_rejects_bad_arguments():
+    m = sa()
+    desc = W.tiny("base")
+    ix = m.build_index(m.DevicePatterns.from_host(desc), 64)
+    q = torch.zeros(1, 1, 512, 64, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(1, 1, 512, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(m.SAError):   # head_dim 32 unsupported
+        m.sparse_attn_prefill(q[..., :32].contiguous(), k[..., :32].contiguous(), k[..., :32].contiguous(), ix)
+    q2 = torch.zeros(1, 2, 512, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(m.SAError):   # index built for one head
+        m.sparse_attn_prefill(q2, k, k, ix)

@@ -1,0 +1,98 @@
+"""GPU parity: sa_pattern_capture and sa_patterns_to_desc vs the oracle, bit for bit;
+capture -> extension -> index -> attention end to end vs the oracle pipeline."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from golden.load import arr, load
+from gpu_util import assert_close_bf16, note, rows_of_blocks, sa, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _capture_both(maps, **kw):
+    m = sa()
+    got = m.pattern_capture(torch.from_numpy(maps).cuda(), return_hits=True, return_mask=True, **kw)
+    torch.cuda.synchronize()
+    ref = oracle.capture(maps, want_mask=True, **kw)
+    for key in ("keep_diag", "keep_vert", "diag_hits", "vert_hits", "true_mask"):
+        np.testing.assert_array_equal(got[key].cpu().numpy(), ref[key], err_msg=key)
+    return got, ref
+
+
+def test_capture_golden_example():
+    g = load("capture_example.txt")
+    L = int(arr(g, "L")[0])
+    maps = arr(g, "map_row", np.float32).reshape(1, L, L)
+    for scope in (0, 1):
+        got, _ = _capture_both(maps, norm_scope=scope)
+        np.testing.assert_array_equal(got["keep_diag"][0].cpu().numpy(), arr(g, "keep_diag"))
+        np.testing.assert_array_equal(got["keep_vert"][0].cpu().numpy(), arr(g, "keep_vert"))
+
+
+@pytest.mark.parametrize("scope", [0, 1])
+@pytest.mark.parametrize("eps", [1e-8, 1e-10])
+def test_capture_workload_maps(scope, eps):
+    note("capture scope=%d eps=%g" % (scope, eps))
+    maps = W.capture_maps(layers=2, heads=32, n_avg=16)
+    _capture_both(maps, norm_scope=scope, eps=eps)
+
+
+@pytest.mark.parametrize("L", [1, 5, 64, 333, 1024])
+def test_capture_odd_sizes(L):
+    rng = np.random.default_rng(L)
+    A = rng.random((3, L, L)).astype(np.float32)
+    A = np.tril(A) / np.maximum(1, np.tril(A).sum(axis=2, keepdims=True))
+    _capture_both(A.astype(np.float32))
+
+
+def test_capture_thresholds_and_mu():
+    maps = W.capture_maps(layers=1, heads=4, n_avg=4, layer_offset=7)
+    _capture_both(maps, tau=0.55, mu=0.6)
+
+
+def test_capture_rejects_other_lambda():
+    m = sa()
+    with pytest.raises(m.SAError) as e:
+        m.pattern_capture(torch.zeros(1, 8, 8, device="cuda"), lam=0.25)
+    assert e.value.code == -2
+
+
+@pytest.mark.parametrize("S", [300, 512, 16384])
+def test_patterns_to_desc_matches_oracle_extension(S):
+    m = sa()
+    maps = W.capture_maps(layers=1, heads=32, n_avg=8)
+    c = oracle.capture(maps)
+    pat = m.patterns_to_desc(torch.from_numpy(c["keep_diag"]).cuda(), torch.from_numpy(c["keep_vert"]).cuda(), S)
+    torch.cuda.synchronize()
+    diags, verts = oracle.extend(c["keep_diag"], c["keep_vert"], S)
+    dp, do = pat.diag_ptr.cpu().numpy(), pat.diag_off.cpu().numpy()
+    vp, vc = pat.vert_ptr.cpu().numpy(), pat.vert_col.cpu().numpy()
+    for h in range(32):
+        np.testing.assert_array_equal(do[dp[h]:dp[h + 1]], diags[h])
+        np.testing.assert_array_equal(vc[vp[h]:vp[h + 1]], verts[h])
+
+
+def test_capture_to_attention_end_to_end():
+    """All on the GPU: capture -> extension to S=16384 -> index -> attention; vs the oracle pipeline."""
+    m = sa()
+    S = 16384
+    maps = W.capture_maps(layers=1, heads=32, n_avg=16, layer_offset=3)
+    note("end-to-end capture -> attention S=%d" % S)
+    got = m.pattern_capture(torch.from_numpy(maps).cuda())
+    pat = m.patterns_to_desc(got["keep_diag"], got["keep_vert"], S)
+    ix = m.build_index(pat, 64)
+    q, k, v = W.qkv(3, 1, 32, 8, S, 64, "bf16", seed_extra=3)
+    o = m.sparse_attn_prefill(to_dev(q), to_dev(k), to_dev(v), ix)
+    torch.cuda.synchronize()
+    ref = oracle.capture(maps)
+    diags, verts = oracle.extend(ref["keep_diag"], ref["keep_vert"], S)
+    desc = W.desc_from_lists(S, diags, verts)
+    assert int(ix.pair_count.sum().item()) == int(oracle.pair_count(desc).sum())
+    rows = rows_of_blocks(1, 32, S, 64, 2, np.random.default_rng(33))
+    ro, _ = oracle.attention_rows(desc, q, k, v, rows)
+    idx = torch.from_numpy(rows.astype(np.int64)).cuda()
+    go = o[idx[:, 0], idx[:, 1], idx[:, 2]].float().cpu().numpy().astype(np.float64)
+    assert_close_bf16(go, ro, "end-to-end")
