@@ -83,8 +83,15 @@ __device__ inline float mul_then_sub(float a, float b, float c) {
   return a * b - c;
 }
 
-// position of key kk inside the transposed V tile: bits 2 and 3 swapped
+// position of key kk inside the transposed V tile: bits 2 and 3 swapped, so that the 8 keys a
+// lane feeds to one P.V MFMA are 16 contiguous bytes
 __device__ inline int vt_pos(int kk) { return (kk & ~12) | ((kk & 4) << 1) | ((kk & 8) >> 1); }
+
+// Row d of the transposed V tile is 16 units of 8 bytes (4 keys).  Unit u is stored at unit
+// u ^ swz(d), swz(d) = ((d/8) % 8) * 2 + (d/64) % 2: the 16 lanes of one write (rows d = 8c + e,
+// c = 0..15) then hit 16 different units, i.e. all 32 banks once, and 16-byte reads stay
+// aligned pairs of units (swapped when bit 0 of swz(d) is set, i.e. d >= 64 within 128).
+__device__ inline int vt_unit(int u, int d) { return u ^ ((((d >> 3) & 7) << 1) | ((d >> 6) & 1)); }
 
 template <int D, int BM, bool BF16>
 struct Cfg {
@@ -97,6 +104,11 @@ struct Cfg {
   static constexpr int VS = BF16 ? BN + 8 : D + 4;   // bf16: V^T [D][VS]; f32: V [BN][VS]
   static constexpr int K_ELEMS = BN * KS;
   static constexpr int V_ELEMS = BF16 ? D * VS : BN * VS;
+  // tile fetch: a task is 4 consecutive keys x one 16-byte chunk of K and of V
+  static constexpr int EPC = BF16 ? 8 : 4;            // elements per 16-byte chunk
+  static constexpr int CPR = D / EPC;                 // chunks per key row
+  static constexpr int TASKS = (BN / 4) * CPR;
+  static constexpr int NT = (TASKS + T - 1) / T;      // tasks per thread
   using elem = typename std::conditional<BF16, unsigned short, float>::type;
 };
 
@@ -122,13 +134,76 @@ __device__ inline void decode_item(const Params& p, int& b, int& h, int& rb) {
   }
 }
 
+// One key tile of a work item (wave-uniform): kind 1 = contiguous keys j0 .. j0+nvalid-1 of a
+// segment, kind 2 = gathered columns col_idx[pc .. pc+nvalid), kind 0 = past the last tile.
+struct Tile {
+  int kind, j0, shi, nvalid;
+  int64_t seg, pc;
+};
+
+struct TileWalk {
+  int64_t s1, c0, c1;
+  const int32_t* seg_lo;
+  const int32_t* seg_hi;
+
+  __device__ Tile first(int64_t s0) const {
+    Tile t;
+    t.seg = s0;
+    t.pc = c0;
+    if (s0 < s1) {
+      t.kind = 1;
+      t.j0 = seg_lo[s0];
+      t.shi = seg_hi[s0];
+      t.nvalid = min(BN, t.shi - t.j0 + 1);
+    } else {
+      start_gather(t);
+    }
+    return t;
+  }
+  __device__ void start_gather(Tile& t) const {
+    t.j0 = 0;
+    t.shi = 0;
+    if (c0 < c1) {
+      t.kind = 2;
+      t.pc = c0;
+      t.nvalid = (int)min((int64_t)BN, c1 - c0);
+    } else {
+      t.kind = 0;
+      t.nvalid = 0;
+    }
+  }
+  __device__ Tile next(Tile t) const {
+    if (t.kind == 1) {
+      if (t.j0 + BN <= t.shi) {
+        t.j0 += BN;
+      } else if (++t.seg < s1) {
+        t.j0 = seg_lo[t.seg];
+        t.shi = seg_hi[t.seg];
+      } else {
+        start_gather(t);
+        return t;
+      }
+      t.nvalid = min(BN, t.shi - t.j0 + 1);
+    } else if (t.kind == 2) {
+      t.pc += BN;
+      if (t.pc < c1) {
+        t.nvalid = (int)min((int64_t)BN, c1 - t.pc);
+      } else {
+        t.kind = 0;
+        t.nvalid = 0;
+      }
+    }
+    return t;
+  }
+};
+
 template <int D, int BM, bool BF16>
-__global__ void __launch_bounds__(2 * BM) k_attn(Params p) {  // 2*BM threads = BM/32 waves
+__global__ void __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(2))) k_attn(Params p) {  // 2*BM threads = BM/32 waves
   using C = Cfg<D, BM, BF16>;
   using E = typename C::elem;
   __shared__ __attribute__((aligned(16))) E Ks[C::K_ELEMS];
   __shared__ __attribute__((aligned(16))) E Vs[C::V_ELEMS];
-  __shared__ int32_t cols_sh[BN];
+  __shared__ __attribute__((aligned(16))) int32_t cols_sh[3][BN];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, r32 = lane & 31;
@@ -168,61 +243,133 @@ __global__ void __launch_bounds__(2 * BM) k_attn(Params p) {  // 2*BM threads = 
 
   const int64_t item = (int64_t)h * p.nb + rb;
   const int32_t r0 = p.run_ptr[h], r1 = p.run_ptr[h + 1];
+  int64_t bp = p.bcol_ptr[item];
+  const int64_t bp_end = p.bcol_ptr[item + 1];
+  TileWalk walk;
+  walk.s1 = p.seg_ptr[item + 1];
+  walk.c0 = p.col_ptr[item];
+  walk.c1 = p.col_ptr[item + 1];
+  walk.seg_lo = p.seg_lo;
+  walk.seg_hi = p.seg_hi;
 
-  // ---- one tile: keys given by key_of(kk) (kk in [0, 64)), per-lane mask `m`
-  auto load_tile = [&](auto key_of, int nvalid) {
-    if constexpr (BF16) {
-      constexpr int CPR = D / 8;  // 16-byte chunks per row
-      for (int x = tid; x < BN * CPR; x += C::T) {
-        const int kk = x / CPR, c = x % CPR;
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (kk < nvalid) {
-          const int j = key_of(kk);
-          if (j < S) u = *reinterpret_cast<const uint4*>(Kg + (int64_t)j * D + 8 * c);
-        }
-        *reinterpret_cast<uint4*>(&Ks[kk * C::KS + 8 * c]) = u;
-      }
-      for (int x = tid; x < (BN / 4) * CPR; x += C::T) {
-        const int c = x % CPR, q4 = x / CPR;
-        uint4 u[4];
+  // ---- tile fetch: global -> registers (issued one tile ahead), registers -> LDS.
+  // Buffer loads: an offset past the end of the kv head's slab reads as zero, so padding keys
+  // (past nvalid, past S, threads without a task) need no branch.
+  constexpr uint32_t kBufFlags = 0x00020000u;  // raw buffer, 32-bit data format
+  const uint32_t slab_bytes = (uint32_t)S * D * sizeof(E);
+  const __amdgpu_buffer_rsrc_t rsK = __builtin_amdgcn_make_buffer_rsrc((void*)Kg, 0, slab_bytes, kBufFlags);
+  const __amdgpu_buffer_rsrc_t rsV = __builtin_amdgcn_make_buffer_rsrc((void*)Vg, 0, slab_bytes, kBufFlags);
+  uint4 kreg[C::NT][4], vreg[C::NT][4];
+  auto fetch = [&](const Tile& t, const int32_t* cols) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int kk = 4 * q4 + t;
-          u[t] = make_uint4(0, 0, 0, 0);
-          if (kk < nvalid) {
-            const int j = key_of(kk);
-            if (j < S) u[t] = *reinterpret_cast<const uint4*>(Vg + (int64_t)j * D + 8 * c);
-          }
-        }
-        const int pos = vt_pos(4 * q4);
+    for (int it = 0; it < C::NT; ++it) {
+      const int x = tid + it * C::T;
+      const int c = x % C::CPR, q4 = x / C::CPR;
+      const bool task = x < C::TASKS;
+      int key[4];
+      if (t.kind == 2 && task) {
+        const int4 kc = *reinterpret_cast<const int4*>(&cols[4 * q4]);
+        key[0] = kc.x;
+        key[1] = kc.y;
+        key[2] = kc.z;
+        key[3] = kc.w;
+      } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int wsel = e >> 1, sh = (e & 1) * 16;
-          uint32_t a0 = ((&u[0].x)[wsel] >> sh) & 0xffffu, a1 = ((&u[1].x)[wsel] >> sh) & 0xffffu;
-          uint32_t a2 = ((&u[2].x)[wsel] >> sh) & 0xffffu, a3 = ((&u[3].x)[wsel] >> sh) & 0xffffu;
-          uint2 w2 = make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
-          *reinterpret_cast<uint2*>(&Vs[(8 * c + e) * C::VS + pos]) = w2;
-        }
+        for (int u = 0; u < 4; ++u) key[u] = t.j0 + 4 * q4 + u;
       }
-    } else {
-      constexpr int CPR = D / 4;  // float4 chunks per row
-      for (int x = tid; x < BN * CPR; x += C::T) {
-        const int kk = x / CPR, c = x % CPR;
-        float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
-        if (kk < nvalid) {
-          const int j = key_of(kk);
-          if (j < S) {
-            kv = *reinterpret_cast<const float4*>(Kg + (int64_t)j * D + 4 * c);
-            vv = *reinterpret_cast<const float4*>(Vg + (int64_t)j * D + 4 * c);
-          }
-        }
-        Ks[kk * C::KS + 4 * c + 0] = kv.x;
-        Ks[kk * C::KS + 4 * c + 1] = kv.y;
-        Ks[kk * C::KS + 4 * c + 2] = kv.z;
-        Ks[kk * C::KS + 4 * c + 3] = kv.w;
-        *reinterpret_cast<float4*>(&Vs[kk * C::VS + 4 * c]) = vv;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool ok = task && 4 * q4 + u < t.nvalid && key[u] < S;
+        const int off = ok ? key[u] * (D * (int)sizeof(E)) + 16 * c : (int)slab_bytes;
+        auto kv = __builtin_amdgcn_raw_buffer_load_b128(rsK, off, 0, 0);
+        auto vv = __builtin_amdgcn_raw_buffer_load_b128(rsV, off, 0, 0);
+        kreg[it][u] = *reinterpret_cast<uint4*>(&kv);
+        vreg[it][u] = *reinterpret_cast<uint4*>(&vv);
       }
     }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int it = 0; it < C::NT; ++it) {
+      const int x = tid + it * C::T;
+      if (x < C::TASKS) {
+        const int c = x % C::CPR, q4 = x / C::CPR;
+        if constexpr (BF16) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) *reinterpret_cast<uint4*>(&Ks[(4 * q4 + u) * C::KS + 8 * c]) = kreg[it][u];
+          // V^T: element e of the 4 rows -> 4 consecutive keys of row d = 8c + e, at the swizzled
+          // 8-byte unit of that row (see vt_unit)
+          const int unit = vt_pos(4 * q4) >> 2;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int w = e >> 1;
+            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+            const uint32_t lo = __builtin_amdgcn_perm((&vreg[it][1].x)[w], (&vreg[it][0].x)[w], sel);
+            const uint32_t hi = __builtin_amdgcn_perm((&vreg[it][3].x)[w], (&vreg[it][2].x)[w], sel);
+            *reinterpret_cast<uint2*>(&Vs[(8 * c + e) * C::VS + 4 * vt_unit(unit, 8 * c + e)]) = make_uint2(lo, hi);
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int kk = 4 * q4 + u;
+            const float* kf = reinterpret_cast<const float*>(&kreg[it][u]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Ks[kk * C::KS + 4 * c + e] = kf[e];
+            *reinterpret_cast<uint4*>(&Vs[kk * C::VS + 4 * c]) = vreg[it][u];
+          }
+        }
+      }
+    }
+  };
+
+  // ---- per-lane key mask of a tile
+  auto tile_mask = [&](const Tile& t, const int32_t* cols) -> uint64_t {
+    uint64_t m = 0;
+    if (t.kind == 1) {
+      const int j0 = t.j0, nvalid = t.nvalid;
+      // in-segment columns of this tile (sorted list, consumed in order)
+      uint64_t xin = 0;
+      while (bp < bp_end) {
+        const int c = p.bcol_idx[bp];
+        if (c >= j0 + nvalid) break;
+        xin |= 1ull << (c - j0);
+        ++bp;
+      }
+      // runs that can meet this tile have offsets in [b0 - j0 - 63, b1 - j0]; runs are sorted and
+      // disjoint, so the first candidate is found by binary search on run_hi
+      const int omin = b0 - j0 - (BN - 1), omax = b1 - j0;
+      int32_t rf = r0, rl = r1;
+      while (rf < rl) {
+        const int32_t mid = (rf + rl) >> 1;
+        if (p.run_hi[mid] < omin) rf = mid + 1;
+        else rl = mid;
+      }
+      const int base = i - j0;  // key kk of this lane's row has offset base - kk
+      for (int32_t r = rf; r < r1; ++r) {
+        const int lo = p.run_lo[r];
+        if (lo > omax) break;
+        const int hi = p.run_hi[r];
+        const int a = max(0, base - hi), e = min(BN - 1, base - lo);
+        if (a <= e) m |= range_mask(a, e);
+      }
+      m |= xin;
+      m &= prefix_mask(nvalid) & prefix_mask(base + 1);
+    } else {
+      // gathered: the list is sorted, so the causal keys of row i are a prefix
+      const int nvalid = t.nvalid;
+      int cnt = nvalid;
+      if (cols[nvalid - 1] > i) {
+        int lo = 0, hi = nvalid;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (cols[mid] <= i) lo = mid + 1;
+          else hi = mid;
+        }
+        cnt = lo;
+      }
+      m = prefix_mask(cnt);
+    }
+    return row_ok ? m : 0ull;
   };
 
   auto compute_tile = [&](uint64_t m) {
@@ -246,8 +393,7 @@ __global__ void __launch_bounds__(2 * BM) k_attn(Params p) {  // 2*BM threads = 
       }
     }
     // mask: value v of block kb is key kb*32 + 8*(v/4) + 4*g + v%4
-    const bool full = (m == ~0ull);
-    if (!__all(full)) {
+    if (!__all(m == ~0ull)) {
       const uint64_t mg = m >> (4 * g);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -255,50 +401,60 @@ __global__ void __launch_bounds__(2 * BM) k_attn(Params p) {  // 2*BM threads = 
         for (int v = 0; v < 16; ++v)
           if (!((mg >> (kb * 32 + 8 * (v >> 2) + (v & 3))) & 1ull)) sacc[kb][v] = -INFINITY;
     }
-    // online softmax (log2 domain)
+    // online softmax in the log2 domain.  The reference maximum moves only when the tile maximum
+    // exceeds it by more than kLazy (probabilities up to 2^kLazy are exact enough in fp32 and keep
+    // bf16's relative precision), so the O rescale is rare.
+    constexpr float kLazy = 8.0f;
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
-    mx = pair_max(mx);
-    const float m_new = fmaxf(m_run, mx * p.scale_log2);
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    mx = pair_max(mx) * p.scale_log2;
+    const bool move = mx > m_run + kLazy;
+    if (__any(move)) {
+      const float m_new = move ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.0f : m_new));
+      l_run *= alpha;
+#pragma unroll
+      for (int x = 0; x < C::OB; ++x)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[x][v] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
     float lsum = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        // bf16: one fma per score.  fp32: scale first, so the row maximum maps to exp2(0) = 1 exactly.
+        // bf16: one fma per score.  fp32: scale first, so a row maximum that sets the reference
+        // maps to exp2(0) = 1 exactly.
         const float arg = BF16 ? __builtin_fmaf(sacc[kb][v], p.scale_log2, -m_use)
                                : mul_then_sub(sacc[kb][v], p.scale_log2, m_use);
         const float e = __builtin_amdgcn_exp2f(arg);
         sacc[kb][v] = e;
         lsum += e;
       }
-    l_run = l_run * alpha + lsum;
-    if (__any(alpha != 1.0f)) {
-#pragma unroll
-      for (int x = 0; x < C::OB; ++x)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) oacc[x][v] *= alpha;
-    }
-    m_run = m_new;
+    l_run += lsum;
     // O^T += V^T P^T
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       if constexpr (BF16) {
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
-          bf16x8 pf;
+          bf16x8 pf, pf_sw;
 #pragma unroll
           for (int t = 0; t < 8; ++t) pf[t] = (__bf16)sacc[kb][8 * mm + t];
 #pragma unroll
+          for (int t = 0; t < 8; ++t) pf_sw[t] = pf[t ^ 4];
+#pragma unroll
           for (int x = 0; x < C::OB; ++x) {
-            const bf16x8 vf =
-                *reinterpret_cast<const bf16x8*>(&Vs[(32 * x + r32) * C::VS + kb * 32 + 16 * mm + 8 * g]);
-            oacc[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[x], 0, 0, 0);
+            const int d = 32 * x + r32;
+            const int unit = 2 * (4 * kb + 2 * mm + g);  // first 8-byte unit of this lane's 8 keys
+            const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&Vs[d * C::VS + 4 * (vt_unit(unit, d) & ~1)]);
+            // rows with bit 3 of d/8 set hold the two 4-key halves swapped (see vt_unit)
+            oacc[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, (x & 2) ? pf_sw : pf, oacc[x], 0, 0, 0);
           }
         }
       } else {
@@ -315,80 +471,36 @@ __global__ void __launch_bounds__(2 * BM) k_attn(Params p) {  // 2*BM threads = 
     }
   };
 
-  // ---------------- segment phase
-  {
-    int64_t bp = p.bcol_ptr[item];
-    const int64_t bp_end = p.bcol_ptr[item + 1];
-    const int64_t s0 = p.seg_ptr[item], s1 = p.seg_ptr[item + 1];
-    for (int64_t s = s0; s < s1; ++s) {
-      const int slo = p.seg_lo[s], shi = p.seg_hi[s];
-      for (int j0 = slo; j0 <= shi; j0 += BN) {
-        const int nvalid = min(BN, shi - j0 + 1);
-        // in-segment columns of this tile (sorted list, consumed in order)
-        uint64_t xin = 0;
-        while (bp < bp_end) {
-          const int c = p.bcol_idx[bp];
-          if (c >= j0 + nvalid) break;
-          xin |= 1ull << (c - j0);
-          ++bp;
-        }
-        // per-lane key mask: diagonals, in-segment columns, valid range, causality.
-        // Runs that can meet this tile have offsets in [b0 - j0 - 63, b1 - j0]; runs are sorted and
-        // disjoint, so the first candidate is found by binary search on run_hi.
-        const int omin = b0 - j0 - (BN - 1), omax = b1 - j0;
-        int32_t rf = r0, rl = r1;
-        while (rf < rl) {
-          const int32_t mid = (rf + rl) >> 1;
-          if (p.run_hi[mid] < omin) rf = mid + 1;
-          else rl = mid;
-        }
-        uint64_t m = 0;
-        const int base = i - j0;  // key kk of this lane's row has offset base - kk
-        for (int32_t r = rf; r < r1; ++r) {
-          const int lo = p.run_lo[r];
-          if (lo > omax) break;
-          const int hi = p.run_hi[r];
-          const int a = max(0, base - hi), e = min(BN - 1, base - lo);
-          if (a <= e) m |= range_mask(a, e);
-        }
-        m |= xin;
-        m &= prefix_mask(nvalid) & prefix_mask(base + 1);
-        if (!row_ok) m = 0;
-        __syncthreads();
-        load_tile([&](int kk) { return j0 + kk; }, nvalid);
-        __syncthreads();
-        compute_tile(m);
-      }
-    }
+  // ---- software pipeline: K/V of tile t+1 and the column list of tile t+2 are loaded while
+  // tile t is computed.  cols_sh[n % 3] holds the columns of gathered tile n.
+  auto load_cols = [&](const Tile& t, int32_t* dst) {
+    if (t.kind == 2 && tid < BN) dst[tid] = tid < t.nvalid ? p.col_idx[t.pc + tid] : 0;
+  };
+  Tile cur = walk.first(p.seg_ptr[item]);
+  Tile nxt = walk.next(cur);
+  Tile nn = walk.next(nxt);
+  load_cols(cur, cols_sh[0]);
+  load_cols(nxt, cols_sh[1]);
+  __syncthreads();
+  if (cur.kind != 0) {
+    fetch(cur, cols_sh[0]);
+    store();
   }
-  // ---------------- gathered phase
-  {
-    const int64_t c0 = p.col_ptr[item], c1 = p.col_ptr[item + 1];
-    for (int64_t pc = c0; pc < c1; pc += BN) {
-      const int nvalid = (int)min((int64_t)BN, c1 - pc);
-      __syncthreads();
-      if (tid < BN) cols_sh[tid] = tid < nvalid ? p.col_idx[pc + tid] : 0;
-      __syncthreads();
-      load_tile([&](int kk) { return cols_sh[kk]; }, nvalid);
-      __syncthreads();
-      uint64_t m = 0;
-      if (row_ok) {
-        int cnt;
-        if (cols_sh[nvalid - 1] <= i) {
-          cnt = nvalid;
-        } else {
-          int lo = 0, hi = nvalid;
-          while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (cols_sh[mid] <= i) lo = mid + 1;
-            else hi = mid;
-          }
-          cnt = lo;
-        }
-        m = prefix_mask(cnt);
-      }
-      compute_tile(m);
-    }
+  __syncthreads();
+  for (int n = 0; cur.kind != 0; ++n) {
+    const int bc = n % 3, bx = (n + 1) % 3, bz = (n + 2) % 3;
+    if (nxt.kind != 0) fetch(nxt, cols_sh[bx]);
+    int32_t ncol = 0;
+    if (nn.kind == 2 && tid < BN && tid < nn.nvalid) ncol = p.col_idx[nn.pc + tid];
+    const uint64_t m = tile_mask(cur, cols_sh[bc]);
+    compute_tile(m);
+    __syncthreads();
+    if (nxt.kind != 0) store();
+    if (nn.kind == 2 && tid < BN) cols_sh[bz][tid] = ncol;
+    __syncthreads();
+    cur = nxt;
+    nxt = nn;
+    nn = walk.next(nn);
   }
 
   // ---------------- epilogue
