@@ -118,6 +118,8 @@ typedef struct sa_index_sizes {
  *   col_ptr  [n_items+1] (int64), col_idx:  X minus U, ascending.
  *   pair_count [n_heads] (int64): exact number of retained pairs per head
  *              (the retained keys s per query, summed [DAM, Circularity Check 2]).
+ *   dbits    uint32 [n_heads][ceil(S/32)]: bit r of head h (word r/32, bit r%32) is set
+ *              iff r is in D_h (the diagonal offsets as a bitmap).
  *   status   int32 [1]: SA_STATUS_* bits raised by the last build (0 = clean).
  * Every retained pair is computed exactly once by the attention kernel: pairs with
  * j in U in the segment phase (retained iff (i-j) in D_h or j in bcols), the others
@@ -141,6 +143,7 @@ typedef struct sa_index {
   int64_t* col_ptr;
   int32_t* col_idx;
   int64_t* pair_count;
+  uint32_t* dbits;
   int32_t* status;
   sa_index_sizes capacity;
 } sa_index;
@@ -148,8 +151,8 @@ typedef struct sa_index {
 /*
  * sa_build_index: descriptor -> canonical index (count, exclusive scan, fill; all on
  * the device).  idx->S, n_heads, row_block (64 or 128), n_row_blocks = ceil(S/BM) and
- * the fixed-size arrays run_ptr, seg_ptr, bcol_ptr, col_ptr, pair_count and status
- * must be set.
+ * the fixed-size arrays run_ptr, seg_ptr, bcol_ptr, col_ptr, pair_count, dbits and
+ * status must be set.
  * Size query: if `sizes` (host) is non-NULL, the call synchronises `stream` after the
  *   counting pass, writes the totals to *sizes and returns SA_ERR_DESC_INVALID if
  *   validation (flags & SA_BUILD_VALIDATE) found a bad descriptor.  If any of run_lo,

@@ -143,7 +143,12 @@ def build_index(desc, row_block: int, with_pairs: bool = True) -> dict:
                              col_ptr.ctypes.data, col.ctypes.data, col.size,
                              pairs.ctypes.data if with_pairs else None, C.byref(sz))
     assert rc == 0
-    return dict(S=desc.S, n_heads=desc.H, row_block=row_block, n_row_blocks=nb,
+    nwords = -(-desc.S // 32)
+    dbits = np.zeros((desc.H, nwords), np.uint32)
+    for h in range(desc.H):
+        for r in desc.diags(h):   # bit r of head h: r is a diagonal offset
+            dbits[h, r // 32] |= np.uint32(1) << np.uint32(r % 32)
+    return dict(S=desc.S, n_heads=desc.H, row_block=row_block, n_row_blocks=nb, dbits=dbits.reshape(-1),
                 run_ptr=run_ptr, run_lo=run_lo[:sz.n_runs], run_hi=run_hi[:sz.n_runs],
                 seg_ptr=seg_ptr, seg_lo=seg_lo[:sz.n_segs], seg_hi=seg_hi[:sz.n_segs],
                 bcol_ptr=bcol_ptr, bcol_idx=bcol[:sz.n_bcols], col_ptr=col_ptr, col_idx=col[:sz.n_cols],

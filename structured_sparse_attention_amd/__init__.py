@@ -4,7 +4,7 @@ Argument marshalling only: every step of the path (index build, sparse attention
 pattern capture, pattern extension) runs in the HIP kernels of ``libsa.so``;
 PyTorch supplies device memory and the current HIP stream.  The C ABI is declared
 in ``include/sa.h``.  Importing this package loads ``libsa.so`` and raises if it
-has not been built (``python -m structured_sparse_attention_amd.build``); there is
+has not been built (``python structured_sparse_attention_amd/build.py``); there is
 no fallback implementation.
 """
 from __future__ import annotations
@@ -50,13 +50,13 @@ class _Index(C.Structure):
                 ("run_ptr", C.c_void_p), ("run_lo", C.c_void_p), ("run_hi", C.c_void_p),
                 ("seg_ptr", C.c_void_p), ("seg_lo", C.c_void_p), ("seg_hi", C.c_void_p),
                 ("bcol_ptr", C.c_void_p), ("bcol_idx", C.c_void_p), ("col_ptr", C.c_void_p),
-                ("col_idx", C.c_void_p), ("pair_count", C.c_void_p), ("status", C.c_void_p),
-                ("capacity", _Sizes)]
+                ("col_idx", C.c_void_p), ("pair_count", C.c_void_p), ("dbits", C.c_void_p),
+                ("status", C.c_void_p), ("capacity", _Sizes)]
 
 
 def _load():
     if not os.path.exists(_LIB_PATH):
-        raise ImportError("libsa.so is not built (%s); run `python -m structured_sparse_attention_amd.build`"
+        raise ImportError("libsa.so is not built (%s); run `python structured_sparse_attention_amd/build.py`"
                           % _LIB_PATH)
     lib = C.CDLL(_LIB_PATH)
     lib.sa_status_string.restype = C.c_char_p
@@ -148,7 +148,7 @@ class SparseIndex:
     """Canonical sparse index (sa_index in include/sa.h) in device memory."""
 
     KEYS = ("run_ptr", "run_lo", "run_hi", "seg_ptr", "seg_lo", "seg_hi", "bcol_ptr", "bcol_idx", "col_ptr",
-            "col_idx", "pair_count")
+            "col_idx", "pair_count", "dbits")
 
     def __init__(self, S, n_heads, row_block, device):
         self.S, self.n_heads, self.row_block = S, n_heads, row_block
@@ -159,6 +159,7 @@ class SparseIndex:
         self.bcol_ptr = torch.zeros(n + 1, dtype=torch.int64, device=device)
         self.col_ptr = torch.zeros(n + 1, dtype=torch.int64, device=device)
         self.pair_count = torch.zeros(n_heads, dtype=torch.int64, device=device)
+        self.dbits = torch.zeros(n_heads * (-(-S // 32)), dtype=torch.int32, device=device)
         self.status = torch.zeros(1, dtype=torch.int32, device=device)
         self.run_lo = self.run_hi = self.seg_lo = self.seg_hi = self.bcol_idx = self.col_idx = None
         self.sizes = None
@@ -175,7 +176,7 @@ class SparseIndex:
         return _Index(self.S, self.n_heads, self.row_block, self.n_row_blocks, _ptr(self.run_ptr),
                       _ptr(self.run_lo), _ptr(self.run_hi), _ptr(self.seg_ptr), _ptr(self.seg_lo),
                       _ptr(self.seg_hi), _ptr(self.bcol_ptr), _ptr(self.bcol_idx), _ptr(self.col_ptr),
-                      _ptr(self.col_idx), _ptr(self.pair_count), _ptr(self.status), cap)
+                      _ptr(self.col_idx), _ptr(self.pair_count), _ptr(self.dbits), _ptr(self.status), cap)
 
     def to_numpy(self) -> dict:
         out = dict(S=self.S, n_heads=self.n_heads, row_block=self.row_block, n_row_blocks=self.n_row_blocks)
@@ -184,6 +185,7 @@ class SparseIndex:
             size_key = {"run_lo": "n_runs", "run_hi": "n_runs", "seg_lo": "n_segs", "seg_hi": "n_segs",
                         "bcol_idx": "n_bcols", "col_idx": "n_cols"}.get(k)
             out[k] = t[:self.sizes[size_key]] if size_key else t
+        out["dbits"] = out["dbits"].view(np.uint32)
         return out
 
     @property

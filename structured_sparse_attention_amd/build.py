@@ -1,4 +1,8 @@
-"""Build libsa.so (HIP, gfx950) in-tree with hipcc."""
+"""Build libsa.so (HIP, gfx950) in-tree with hipcc.
+
+Run as a script (``python structured_sparse_attention_amd/build.py``) or load this
+file by path: importing it through the package would first load the library.
+"""
 from __future__ import annotations
 
 import os
@@ -38,6 +42,13 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + errs)
     if verbose and errs.strip():
         print(errs, file=sys.stderr)
+    # every symbol must resolve (a kernel whose host stub was not emitted shows up here, not at run time)
+    import ctypes
+    try:
+        ctypes.CDLL(tmp, mode=os.RTLD_NOW)
+    except OSError as e:
+        os.unlink(tmp)
+        raise RuntimeError("libsa.so does not load: %s" % e)
     os.replace(tmp, LIB)
     return LIB
 

@@ -13,7 +13,7 @@ sa_status hip_status(hipError_t e) { return e == hipSuccess ? SA_OK : SA_ERR_HIP
 
 bool index_arrays_ok(const sa_index& ix) {
   return ix.run_ptr && ix.run_lo && ix.run_hi && ix.seg_ptr && ix.seg_lo && ix.seg_hi && ix.bcol_ptr &&
-         ix.bcol_idx && ix.col_ptr && ix.col_idx;
+         ix.bcol_idx && ix.col_ptr && ix.col_idx && ix.dbits;
 }
 
 }  // namespace
@@ -46,7 +46,8 @@ sa_status sa_build_index(const sa_pattern_desc* desc, sa_index* idx, sa_index_si
   if (idx->n_row_blocks != cdiv(d.S, BM)) return SA_ERR_INVALID_ARG;
   if (d.block_mask && (d.block_size < BM || d.block_size % BM != 0)) return SA_ERR_INVALID_ARG;
   if (d.stripe_ptr && (!d.stripe_col || d.stripe_rows < BM || d.stripe_rows % BM != 0)) return SA_ERR_INVALID_ARG;
-  if (!idx->run_ptr || !idx->seg_ptr || !idx->bcol_ptr || !idx->col_ptr || !idx->pair_count || !idx->status)
+  if (!idx->run_ptr || !idx->seg_ptr || !idx->bcol_ptr || !idx->col_ptr || !idx->pair_count || !idx->dbits ||
+      !idx->status)
     return SA_ERR_INVALID_ARG;
   if ((int64_t)d.n_heads * idx->n_row_blocks > 0x7fffffffLL) return SA_ERR_UNSUPPORTED;
   if (d.S > sa::kMaxIndexS) return SA_ERR_UNSUPPORTED;
@@ -88,7 +89,9 @@ sa_status sa_build_index(const sa_pattern_desc* desc, sa_index* idx, sa_index_si
       return SA_ERR_CAPACITY;
   }
   if (!payload) return SA_OK;
-  return hip_status(sa::launch_index_items(d, ix, 1, 0, st));
+  e = sa::launch_index_dbits(d, ix, st);
+  if (e == hipSuccess) e = sa::launch_index_items(d, ix, 1, 0, st);
+  return hip_status(e);
 }
 
 sa_status sa_sparse_attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int32_t batch,

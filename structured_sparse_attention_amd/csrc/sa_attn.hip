@@ -55,9 +55,8 @@ struct Params {
   const int32_t* bcol_idx;
   const int64_t* col_ptr;
   const int32_t* col_idx;
-  const int32_t* run_ptr;
-  const int32_t* run_lo;
-  const int32_t* run_hi;
+  const uint32_t* dbits;  // [hq][nwords] diagonal offsets as bits
+  int32_t nwords;
 };
 
 __device__ inline uint64_t prefix_mask(int n) {  // bits [0, n), n clamped to [0, 64]
@@ -233,6 +232,8 @@ __global__ void __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
     for (int s = 0; s < C::QS; ++s) qf[s] = row_ok ? Qg[(int64_t)i * D + 2 * s + g] : 0.0f;
   }
+  // Q is complete before the pipelined loop, so the loop's waits only ever cover the prefetch
+  __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
 
   f32x16 oacc[C::OB];
 #pragma unroll
@@ -242,7 +243,6 @@ __global__ void __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(2))
   float m_run = -INFINITY, l_run = 0.0f;
 
   const int64_t item = (int64_t)h * p.nb + rb;
-  const int32_t r0 = p.run_ptr[h], r1 = p.run_ptr[h + 1];
   int64_t bp = p.bcol_ptr[item];
   const int64_t bp_end = p.bcol_ptr[item + 1];
   TileWalk walk;
@@ -265,7 +265,7 @@ __global__ void __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(2))
     for (int it = 0; it < C::NT; ++it) {
       const int x = tid + it * C::T;
       const int c = x % C::CPR, q4 = x / C::CPR;
-      const bool task = x < C::TASKS;
+      const bool task = (C::TASKS % C::T == 0) || x < C::TASKS;
       int key[4];
       if (t.kind == 2 && task) {
         const int4 kc = *reinterpret_cast<const int4*>(&cols[4 * q4]);
@@ -279,7 +279,7 @@ __global__ void __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(2))
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const bool ok = task && 4 * q4 + u < t.nvalid && key[u] < S;
+        const bool ok = task & (4 * q4 + u < t.nvalid) & (key[u] < S);
         const int off = ok ? key[u] * (D * (int)sizeof(E)) + 16 * c : (int)slab_bytes;
         auto kv = __builtin_amdgcn_raw_buffer_load_b128(rsK, off, 0, 0);
         auto vv = __builtin_amdgcn_raw_buffer_load_b128(rsV, off, 0, 0);
@@ -322,39 +322,53 @@ __global__ void __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(2))
     }
   };
 
-  // ---- per-lane key mask of a tile
-  auto tile_mask = [&](const Tile& t, const int32_t* cols) -> uint64_t {
-    uint64_t m = 0;
+  // ---- per-lane key mask of a tile, in two steps so that its loads overlap other work:
+  // mask_loads issues the three diagonal-bitmap words that cover this lane's 64 offsets and
+  // collects the tile's in-segment columns; mask_finish combines them with causality.
+  const uint32_t* dbh = p.dbits + (int64_t)h * p.nwords;
+  struct MaskIn {
+    uint32_t w0, w1, w2;
+    uint64_t xin;
+  };
+  auto mask_loads = [&](const Tile& t) -> MaskIn {
+    MaskIn mi{0u, 0u, 0u, 0ull};
     if (t.kind == 1) {
-      const int j0 = t.j0, nvalid = t.nvalid;
-      // in-segment columns of this tile (sorted list, consumed in order)
+      // offsets of keys j0 + 63 .. j0 of row i are base - 63 .. base (base = i - j0); the words
+      // below offset 0 read as zero (out of the buffer)
+      // (each word is loaded from a clamped index and zeroed when the index was out of range; the
+      // three loads must stay separate, a merged wide buffer load would drop all three words when one
+      // of them is out of range)
+      const int wl = i - t.j0 - (BN - 1);
+      const int wi = wl >> 5;
+      const int c0 = min(max(wi, 0), p.nwords - 1), c1 = min(max(wi + 1, 0), p.nwords - 1),
+                c2 = min(max(wi + 2, 0), p.nwords - 1);
+      const uint32_t a0 = dbh[c0], a1 = dbh[c1], a2 = dbh[c2];
+      mi.w0 = (c0 == wi) ? a0 : 0u;
+      mi.w1 = (c1 == wi + 1) ? a1 : 0u;
+      mi.w2 = (c2 == wi + 2) ? a2 : 0u;
+      // in-segment columns of this tile (sorted list, consumed in tile order)
       uint64_t xin = 0;
       while (bp < bp_end) {
         const int c = p.bcol_idx[bp];
-        if (c >= j0 + nvalid) break;
-        xin |= 1ull << (c - j0);
+        if (c >= t.j0 + t.nvalid) break;
+        xin |= 1ull << (c - t.j0);
         ++bp;
       }
-      // runs that can meet this tile have offsets in [b0 - j0 - 63, b1 - j0]; runs are sorted and
-      // disjoint, so the first candidate is found by binary search on run_hi
-      const int omin = b0 - j0 - (BN - 1), omax = b1 - j0;
-      int32_t rf = r0, rl = r1;
-      while (rf < rl) {
-        const int32_t mid = (rf + rl) >> 1;
-        if (p.run_hi[mid] < omin) rf = mid + 1;
-        else rl = mid;
-      }
-      const int base = i - j0;  // key kk of this lane's row has offset base - kk
-      for (int32_t r = rf; r < r1; ++r) {
-        const int lo = p.run_lo[r];
-        if (lo > omax) break;
-        const int hi = p.run_hi[r];
-        const int a = max(0, base - hi), e = min(BN - 1, base - lo);
-        if (a <= e) m |= range_mask(a, e);
-      }
-      m |= xin;
-      m &= prefix_mask(nvalid) & prefix_mask(base + 1);
-    } else {
+      mi.xin = xin;
+    }
+    return mi;
+  };
+  auto mask_finish = [&](const Tile& t, const MaskIn& mi, const int32_t* cols) -> uint64_t {
+    uint64_t m = 0;
+    if (t.kind == 1) {
+      const int base = i - t.j0;
+      const int sh = (base - (BN - 1)) & 31;
+      const uint64_t lo = ((uint64_t)mi.w1 << 32) | mi.w0;
+      const uint64_t win = sh ? ((lo >> sh) | ((uint64_t)mi.w2 << (64 - sh))) : lo;
+      // window bit q is offset base - 63 + q, i.e. key kk = 63 - q
+      m = __builtin_bitreverse64(win) | mi.xin;
+      m &= prefix_mask(t.nvalid) & prefix_mask(base + 1);
+    } else if (t.kind == 2) {
       // gathered: the list is sorted, so the causal keys of row i are a prefix
       const int nvalid = t.nvalid;
       int cnt = nvalid;
@@ -471,8 +485,8 @@ __global__ void __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(2))
     }
   };
 
-  // ---- software pipeline: K/V of tile t+1 and the column list of tile t+2 are loaded while
-  // tile t is computed.  cols_sh[n % 3] holds the columns of gathered tile n.
+  // ---- software pipeline: the K/V tile and the mask inputs of tile t+1 and the column list of
+  // tile t+2 are loaded while tile t is computed.  cols_sh[n % 3] holds the columns of gathered tile n.
   auto load_cols = [&](const Tile& t, int32_t* dst) {
     if (t.kind == 2 && tid < BN) dst[tid] = tid < t.nvalid ? p.col_idx[t.pc + tid] : 0;
   };
@@ -482,22 +496,31 @@ __global__ void __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(2))
   load_cols(cur, cols_sh[0]);
   load_cols(nxt, cols_sh[1]);
   __syncthreads();
+  uint64_t m_cur = 0;
   if (cur.kind != 0) {
+    const MaskIn mi = mask_loads(cur);
     fetch(cur, cols_sh[0]);
+    m_cur = mask_finish(cur, mi, cols_sh[0]);
     store();
   }
   __syncthreads();
   for (int n = 0; cur.kind != 0; ++n) {
     const int bc = n % 3, bx = (n + 1) % 3, bz = (n + 2) % 3;
-    if (nxt.kind != 0) fetch(nxt, cols_sh[bx]);
+    (void)bc;
+    MaskIn mi{0u, 0u, 0u, 0ull};
+    if (nxt.kind != 0) {
+      mi = mask_loads(nxt);
+      fetch(nxt, cols_sh[bx]);
+    }
     int32_t ncol = 0;
     if (nn.kind == 2 && tid < BN && tid < nn.nvalid) ncol = p.col_idx[nn.pc + tid];
-    const uint64_t m = tile_mask(cur, cols_sh[bc]);
-    compute_tile(m);
+    compute_tile(m_cur);
+    const uint64_t m_next = nxt.kind != 0 ? mask_finish(nxt, mi, cols_sh[bx]) : 0ull;
     __syncthreads();
     if (nxt.kind != 0) store();
     if (nn.kind == 2 && tid < BN) cols_sh[bz][tid] = ncol;
     __syncthreads();
+    m_cur = m_next;
     cur = nxt;
     nxt = nn;
     nn = walk.next(nn);
@@ -529,6 +552,396 @@ __global__ void __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(2))
           l_tot > 0.0f ? m_run * 0.69314718055994530942f + logf(l_tot) : -INFINITY;
     }
   }
+}
+
+// ============================================================================
+// bf16 kernel.  Four waves per workgroup.  BM = 128: wave w owns rows 32w..32w+31
+// and all 64 keys of a tile.  BM = 64: the two 32-row halves are split again by
+// key halves (waves 2, 3 take keys 32..63 of every tile, with their own softmax
+// state), and the two halves of each row are merged at the end -- so four waves
+// share every K/V tile either way.
+// K and V tiles travel global -> LDS with buffer_load ... lds (no register
+// staging), double-buffered: the loads of tile t+1 are in flight while tile t is
+// computed, one barrier per tile.  Tiles are stored key-row-major with the
+// 16-byte chunks of row R XOR-swizzled (K: chunk ^ (R % 8); V: chunk ^ 2(R % 4))
+// so that the MFMA operand reads are free of bank conflicts.  The V operand of
+// O^T = V^T P^T is read with ds_read_b64_tr_b16, which transposes 4x4 blocks of
+// 16-bit values across each group of 16 lanes: source lane a + 4e supplies 4
+// consecutive d values of key row key0 + e, and lane 4a + b receives column b of
+// those rows, i.e. 4 consecutive keys of one d -- the layout the MFMA A operand
+// needs.  Row sums come from v_dot2_f32_bf16 on the packed probabilities.
+// ============================================================================
+// Chunk swizzle of row R of a V tile (16-byte chunks XOR'ed with vswz(R % 4)): the 16 lanes of one
+// transposed read take 32 bytes from each of 4 consecutive key rows, and with this swizzle the
+// 8 such segments of a half-wave land on 8 different 32-byte bank groups (measured free of bank
+// conflicts on gfx950 for 256-byte rows; 128-byte rows pair up two rows per 256 bytes).
+template <int D>
+__device__ inline int vswz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+
+template <int D, int BM, int KS>
+struct Cfg3 {
+  static constexpr int KSPLIT = KS;
+  static constexpr int NW = (BM / 32) * KS;
+  static constexpr int T = 64 * NW;
+  static constexpr int NKB = (BN / KSPLIT) / 32;      // 32-key blocks per wave per tile
+  static constexpr int QS = D / 16;
+  static constexpr int OB = D / 32;
+  static constexpr int ROWB = D * 2;                  // bytes per key row
+  static constexpr int CPR = D / 8;                   // 16-byte chunks per key row
+  static constexpr int RPL = 64 / CPR;                // key rows per 1 KB load instruction
+  static constexpr int LPW = (BN / RPL) / NW;         // load instructions per wave per matrix
+  static constexpr int MAT = BN * ROWB;               // bytes of one K (or V) tile
+  static constexpr int STAGE = 2 * MAT;
+};
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+template <int D, int BM, int KS>
+__global__ void __launch_bounds__(64 * (BM / 32) * KS) __attribute__((amdgpu_waves_per_eu(2)))
+k_attn_bf16(Params p) {
+  using C = Cfg3<D, BM, KS>;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * C::STAGE];
+  __shared__ __attribute__((aligned(16))) int32_t cols_sh[3][BN];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, r32 = lane & 31;
+  const int rh = wave % (BM / 32), kh = wave / (BM / 32);  // row half (32 rows), key half
+  int b, h, rb;
+  decode_item(p, b, h, rb);
+  const int S = p.S;
+  const int b0 = rb * BM, b1 = min(S, b0 + BM) - 1;
+  const int i = b0 + rh * 32 + r32;
+  const bool row_ok = i <= b1;
+  const int kvh = h / (p.hq / p.hkv);
+  using E = unsigned short;
+  const E* Qg = static_cast<const E*>(p.q) + ((int64_t)(b * p.hq + h) * S) * D;
+  const E* Kg = static_cast<const E*>(p.k) + ((int64_t)(b * p.hkv + kvh) * S) * D;
+  const E* Vg = static_cast<const E*>(p.v) + ((int64_t)(b * p.hkv + kvh) * S) * D;
+
+  bf16x8 qf[C::QS];
+#pragma unroll
+  for (int s = 0; s < C::QS; ++s) {
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (row_ok) u = *reinterpret_cast<const uint4*>(Qg + (int64_t)i * D + 16 * s + 8 * g);
+    qf[s] = *reinterpret_cast<bf16x8*>(&u);
+  }
+  __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): Q is in registers before the pipelined loop
+
+  f32x16 oacc[C::OB];
+#pragma unroll
+  for (int x = 0; x < C::OB; ++x)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) oacc[x][v] = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  const int64_t item = (int64_t)h * p.nb + rb;
+  int64_t bp = p.bcol_ptr[item];
+  const int64_t bp_end = p.bcol_ptr[item + 1];
+  TileWalk walk;
+  walk.s1 = p.seg_ptr[item + 1];
+  walk.c0 = p.col_ptr[item];
+  walk.c1 = p.col_ptr[item + 1];
+  walk.seg_lo = p.seg_lo;
+  walk.seg_hi = p.seg_hi;
+
+  constexpr uint32_t kBufFlags = 0x00020000u;
+  const uint32_t slab_bytes = (uint32_t)S * D * 2u;
+  const __amdgpu_buffer_rsrc_t rsK = __builtin_amdgcn_make_buffer_rsrc((void*)Kg, 0, slab_bytes, kBufFlags);
+  const __amdgpu_buffer_rsrc_t rsV = __builtin_amdgcn_make_buffer_rsrc((void*)Vg, 0, slab_bytes, kBufFlags);
+
+  // ---- tile loads straight into LDS stage `st`: wave w fills key rows [w*LPW*RPL, (w+1)*LPW*RPL)
+  // lane constants of the tile loads: key row R = R0 + lane / CPR, chunk slot P = lane % CPR.
+  // R0 is a multiple of RPL (4 or 8) and the wave's first row a multiple of 16, so R % 8 is
+  // (k * RPL) % 8 + lane / CPR with no carry, and R % 4 == (lane / CPR) % 4.
+  const int ld_r = lane / C::CPR, ld_p = lane % C::CPR;
+  const int ld_ck = 16 * (ld_p ^ ld_r), ld_cv = 16 * (ld_p ^ vswz<D>(ld_r));
+  auto issue_tile = [&](const Tile& t, int st, const int32_t* cols) {
+    unsigned char* Kst = lds + st * C::STAGE;
+    unsigned char* Vst = Kst + C::MAT;
+    int key[C::LPW];
+#pragma unroll
+    for (int k = 0; k < C::LPW; ++k) key[k] = t.j0 + (wave * C::LPW + k) * C::RPL + ld_r;
+    if (t.kind == 2) {
+#pragma unroll
+      for (int k = 0; k < C::LPW; ++k) key[k] = cols[(wave * C::LPW + k) * C::RPL + ld_r];
+    }
+    // rows of the tile that hold keys (< S for a band tile; list entries are always < S)
+    const int lim = t.kind == 2 ? t.nvalid : min(t.nvalid, S - t.j0);
+#pragma unroll
+    for (int k = 0; k < C::LPW; ++k) {
+      const int R0 = (wave * C::LPW + k) * C::RPL;
+      const int base = R0 + ld_r < lim ? key[k] * C::ROWB : (int)slab_bytes;  // past the slab: zeros
+      const int ck = ld_ck ^ (16 * ((k * C::RPL) & 7));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsK, (lds_void_ptr)(Kst + R0 * C::ROWB), 16, base + ck, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsV, (lds_void_ptr)(Vst + R0 * C::ROWB), 16, base + ld_cv, 0, 0, 0);
+    }
+  };
+
+  // ---- per-lane 64-bit key mask of a tile (see the fp32 kernel for the derivation)
+  const uint32_t* dbh = p.dbits + (int64_t)h * p.nwords;
+  struct MaskIn {
+    uint32_t w0, w1, w2;
+    uint64_t xin;
+    bool full;  // every key of the tile is retained for every row of the block (wave-uniform)
+  };
+  auto mask_loads = [&](const Tile& t, const int32_t* cols) -> MaskIn {
+    MaskIn mi{0u, 0u, 0u, 0ull, false};
+    if (t.kind == 2) mi.full = (t.nvalid == BN) && (cols[BN - 1] <= b0);
+    if (t.kind == 1) {
+      // full when the whole tile is at or below the block's first row and every offset any row of
+      // the block sees in it, [b0 - j0 - 63, b1 - j0], is a diagonal (checked on the bitmap words)
+      if (t.nvalid == BN && t.j0 + BN - 1 <= b0) {
+        // the offsets span at most BM + 63 bits, i.e. at most (BM + 94) / 32 words from word
+        // omin/32; all of them are read at once (scalar loads) and checked without branches
+        const int omin = b0 - t.j0 - (BN - 1), omax = b1 - t.j0;
+        const int w0 = omin >> 5;
+        constexpr int kWords = (BM + BN - 1 + 31) / 32 + 1;
+        bool f = true;
+#pragma unroll
+        for (int k = 0; k < kWords; ++k) {
+          const int w = w0 + k;
+          const int a = max(omin - 32 * w, 0), e = min(omax - 32 * w, 31);
+          const uint32_t need =
+              a <= e ? ((e == 31 ? 0xffffffffu : ((1u << (e + 1)) - 1u)) & ~((1u << a) - 1u)) : 0u;
+          const uint32_t word = dbh[min(w, p.nwords - 1)];
+          f = f & ((word & need) == need);
+        }
+        mi.full = f;
+      }
+      const int wl = i - t.j0 - (BN - 1);
+      const int wi = wl >> 5;
+      const int c0 = min(max(wi, 0), p.nwords - 1), c1 = min(max(wi + 1, 0), p.nwords - 1),
+                c2 = min(max(wi + 2, 0), p.nwords - 1);
+      const uint32_t a0 = dbh[c0], a1 = dbh[c1], a2 = dbh[c2];
+      mi.w0 = (c0 == wi) ? a0 : 0u;
+      mi.w1 = (c1 == wi + 1) ? a1 : 0u;
+      mi.w2 = (c2 == wi + 2) ? a2 : 0u;
+      uint64_t xin = 0;
+      while (bp < bp_end) {
+        const int c = p.bcol_idx[bp];
+        if (c >= t.j0 + t.nvalid) break;
+        xin |= 1ull << (c - t.j0);
+        ++bp;
+      }
+      mi.xin = xin;
+    }
+    return mi;
+  };
+  auto mask_finish = [&](const Tile& t, const MaskIn& mi, const int32_t* cols) -> uint64_t {
+    if (mi.full) return ~0ull;
+    uint64_t m = 0;
+    if (t.kind == 1) {
+      const int base = i - t.j0;
+      const int sh = (base - (BN - 1)) & 31;
+      const uint64_t lo = ((uint64_t)mi.w1 << 32) | mi.w0;
+      const uint64_t win = sh ? ((lo >> sh) | ((uint64_t)mi.w2 << (64 - sh))) : lo;
+      m = __builtin_bitreverse64(win) | mi.xin;
+      m &= prefix_mask(t.nvalid) & prefix_mask(base + 1);
+    } else if (t.kind == 2) {
+      const int nvalid = t.nvalid;
+      int cnt = nvalid;
+      if (cols[nvalid - 1] > i) {
+        int lo = 0, hi = nvalid;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (cols[mid] <= i) lo = mid + 1;
+          else hi = mid;
+        }
+        cnt = lo;
+      }
+      m = prefix_mask(cnt);
+    }
+    return row_ok ? m : 0ull;
+  };
+
+  // per-lane LDS offsets that do not change from tile to tile
+  int koff[4];  // K row r32, logical chunk 2s + g for s = 0..3 (s + 4 adds 128 bytes)
+#pragma unroll
+  for (int s = 0; s < 4; ++s) koff[s] = r32 * C::ROWB + 16 * ((2 * s + g) ^ (r32 & 7));
+  const int q16 = lane >> 4, t16 = lane & 15, es = t16 >> 2, as = t16 & 3;
+  int voff[C::OB];  // transposed-read source address for d block x (key row key0 + es)
+#pragma unroll
+  for (int x = 0; x < C::OB; ++x) {
+    const int d = 32 * x + 16 * (q16 & 1) + 4 * as;
+    voff[x] = (4 * (q16 >> 1) + es) * C::ROWB + 16 * ((d >> 3) ^ vswz<D>(es)) + 8 * ((d >> 2) & 1);
+  }
+
+  auto compute_tile = [&](int st, uint64_t m) {
+    const unsigned char* Kst = lds + st * C::STAGE;
+    const unsigned char* Vst = Kst + C::MAT;
+    f32x16 sacc[C::NKB];
+    // all K fragments of the tile first, so that the MFMA burst below waits for LDS only once
+    bf16x8 kf[C::NKB][C::QS];
+#pragma unroll
+    for (int kbl = 0; kbl < C::NKB; ++kbl)
+#pragma unroll
+      for (int s = 0; s < C::QS; ++s)
+        kf[kbl][s] = *reinterpret_cast<const bf16x8*>(Kst + (kh * C::NKB + kbl) * 32 * C::ROWB + koff[s & 3] +
+                                                      (s >> 2) * 128);
+#pragma unroll
+    for (int kbl = 0; kbl < C::NKB; ++kbl) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sacc[kbl][v] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < C::QS; ++s)
+        sacc[kbl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kbl][s], qf[s], sacc[kbl], 0, 0, 0);
+    }
+    // all V fragments (transposed reads) next; they do not depend on the softmax and their
+    // latency hides behind it
+    v8i16 vfr[C::NKB][2][C::OB];
+#pragma unroll
+    for (int kbl = 0; kbl < C::NKB; ++kbl)
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        const int kbase = ((kh * C::NKB + kbl) * 32 + 16 * mm) * C::ROWB;
+#pragma unroll
+        for (int x = 0; x < C::OB; ++x) {
+          const v4i16 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(Vst + kbase + voff[x]));
+          const v4i16 vb =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(Vst + kbase + 8 * C::ROWB + voff[x]));
+          vfr[kbl][mm][x] = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+      }
+    // mask: value v of local block kbl is key (kh*NKB + kbl)*32 + 8*(v/4) + 4*g + v%4
+    const uint64_t mw = (m >> (kh * C::NKB * 32)) >> (4 * g);
+    if (!__all(m == ~0ull)) {
+#pragma unroll
+      for (int kbl = 0; kbl < C::NKB; ++kbl)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (!((mw >> (kbl * 32 + 8 * (v >> 2) + (v & 3))) & 1ull)) sacc[kbl][v] = -INFINITY;
+    }
+    constexpr float kLazy = 8.0f;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kbl = 0; kbl < C::NKB; ++kbl)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kbl][v]);
+    mx = pair_max(mx) * p.scale_log2;
+    const bool move = mx > m_run + kLazy;
+    if (__any(move)) {
+      const float m_new = move ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.0f : m_new));
+      l_run *= alpha;
+#pragma unroll
+      for (int x = 0; x < C::OB; ++x)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[x][v] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int kbl = 0; kbl < C::NKB; ++kbl) {
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        bf16x8 pf;
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          pf[t] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kbl][8 * mm + t], p.scale_log2, -m_use));
+#pragma unroll
+        for (int t = 0; t < 8; t += 2) l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[t], pf[t + 1]}, ones, l_run, false);
+#pragma unroll
+        for (int x = 0; x < C::OB; ++x)
+          oacc[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vfr[kbl][mm][x]), pf, oacc[x],
+                                                            0, 0, 0);
+      }
+    }
+  };
+
+  // ---- pipeline
+  auto load_cols = [&](const Tile& t, int32_t* dst) {
+    if (t.kind == 2 && tid < BN) dst[tid] = tid < t.nvalid ? p.col_idx[t.pc + tid] : 0;
+  };
+  Tile cur = walk.first(p.seg_ptr[item]);
+  Tile nxt = walk.next(cur);
+  Tile nn = walk.next(nxt);
+  load_cols(cur, cols_sh[0]);
+  load_cols(nxt, cols_sh[1]);
+  __syncthreads();
+  uint64_t m_cur = 0;
+  if (cur.kind != 0) {
+    const MaskIn mi = mask_loads(cur, cols_sh[0]);
+    issue_tile(cur, 0, cols_sh[0]);
+    m_cur = mask_finish(cur, mi, cols_sh[0]);
+  }
+  __builtin_amdgcn_s_waitcnt(0xF70);  // this thread's tile loads have landed in LDS
+  __syncthreads();
+  for (int n = 0; cur.kind != 0; ++n) {
+    const int bx = (n + 1) % 3, bz = (n + 2) % 3;
+    MaskIn mi{0u, 0u, 0u, 0ull, false};
+    if (nxt.kind != 0) {
+      mi = mask_loads(nxt, cols_sh[bx]);
+      issue_tile(nxt, (n + 1) & 1, cols_sh[bx]);
+    }
+    int32_t ncol = 0;
+    if (nn.kind == 2 && tid < BN && tid < nn.nvalid) ncol = p.col_idx[nn.pc + tid];
+    compute_tile(n & 1, m_cur);
+    const uint64_t m_next = nxt.kind != 0 ? mask_finish(nxt, mi, cols_sh[bx]) : 0ull;
+    if (nn.kind == 2 && tid < BN) cols_sh[bz][tid] = ncol;
+    __builtin_amdgcn_s_waitcnt(0xF70);
+    __syncthreads();
+    m_cur = m_next;
+    cur = nxt;
+    nxt = nn;
+    nn = walk.next(nn);
+  }
+
+  // ---- merge the key halves (BM = 64), then normalise and store
+  if constexpr (C::KSPLIT == 2) {
+    float* xch = reinterpret_cast<float*>(lds) + rh * (C::OB * 16 + 2) * 64;
+    if (kh == 1) {
+#pragma unroll
+      for (int x = 0; x < C::OB; ++x)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) xch[(x * 16 + v) * 64 + lane] = oacc[x][v];
+      xch[(C::OB * 16) * 64 + lane] = m_run;
+      xch[(C::OB * 16 + 1) * 64 + lane] = l_run;
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    const float m_o = xch[(C::OB * 16) * 64 + lane];
+    const float l_o = xch[(C::OB * 16 + 1) * 64 + lane];
+    const float m_new = fmaxf(m_run, m_o);
+    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+    const float fa = __builtin_amdgcn_exp2f(m_run - m_use), fb = __builtin_amdgcn_exp2f(m_o - m_use);
+#pragma unroll
+    for (int x = 0; x < C::OB; ++x)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) oacc[x][v] = oacc[x][v] * fa + xch[(x * 16 + v) * 64 + lane] * fb;
+    l_run = l_run * fa + l_o * fb;
+    m_run = m_new;
+  }
+  const float l_tot = pair_sum(l_run);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  if (row_ok) {
+    E* Og = static_cast<E*>(p.o) + ((int64_t)(b * p.hq + h) * S + i) * D;
+#pragma unroll
+    for (int x = 0; x < C::OB; ++x)
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const int d0 = 32 * x + 8 * qd + 4 * g;
+        __bf16 t4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t4[e] = (__bf16)(oacc[x][4 * qd + e] * inv);
+        *reinterpret_cast<uint2*>(Og + d0) = *reinterpret_cast<uint2*>(t4);
+      }
+    if (p.lse != nullptr && g == 0) {
+      p.lse[(int64_t)(b * p.hq + h) * S + i] =
+          l_tot > 0.0f ? m_run * 0.69314718055994530942f + logf(l_tot) : -INFINITY;
+    }
+  }
+}
+
+template <int D, int BM, int KS>
+hipError_t launch_bf16(const Params& p, hipStream_t stream) {
+  const int64_t blocks = (int64_t)p.B * p.hq * p.nb;
+  k_attn_bf16<D, BM, KS><<<dim3((unsigned)blocks), dim3(Cfg3<D, BM, KS>::T), 0, stream>>>(p);
+  return hipGetLastError();
 }
 
 template <int D, int BM, bool BF16>
@@ -566,12 +979,15 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
   p.bcol_idx = a.idx->bcol_idx;
   p.col_ptr = a.idx->col_ptr;
   p.col_idx = a.idx->col_idx;
-  p.run_ptr = a.idx->run_ptr;
-  p.run_lo = a.idx->run_lo;
-  p.run_hi = a.idx->run_hi;
-  const bool bf = a.dtype == SA_DTYPE_BF16;
-  if (a.head_dim == 64) return bf ? launch_bm<64, true>(p, stream) : launch_bm<64, false>(p, stream);
-  return bf ? launch_bm<128, true>(p, stream) : launch_bm<128, false>(p, stream);
+  p.dbits = a.idx->dbits;
+  p.nwords = ((a.S - 1) >> 5) + 1;
+  // bf16: 128-row blocks run the LDS-direct kernel; 64-row blocks (two waves per block) run the
+  // register-staged kernel, which keeps four blocks per CU and measured faster at that size.
+  if (a.dtype == SA_DTYPE_BF16) {
+    if (p.BM == 128) return a.head_dim == 64 ? launch_bf16<64, 128, 1>(p, stream) : launch_bf16<128, 128, 1>(p, stream);
+    return a.head_dim == 64 ? launch_t<64, 64, true>(p, stream) : launch_t<128, 64, true>(p, stream);
+  }
+  return a.head_dim == 64 ? launch_bm<64, false>(p, stream) : launch_bm<128, false>(p, stream);
 }
 
 }  // namespace sa

@@ -333,6 +333,23 @@ __global__ void __launch_bounds__(kThreads) k_items(sa_pattern_desc d, sa_index 
 }
 
 // ---------------------------------------------------------------------------
+// Diagonal offsets as a bitmap: one thread per 32-bit word; the word's offsets
+// [32w, 32w + 31] are a contiguous slice of the sorted list, found by binary search.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kThreads) k_dbits(sa_pattern_desc d, uint32_t* dbits, int32_t nwords) {
+  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (gid >= (int64_t)d.n_heads * nwords) return;
+  const int32_t h = (int32_t)(gid / nwords), w = (int32_t)(gid % nwords);
+  const int32_t* D = d.diag_off + d.diag_ptr[h];
+  const int32_t n = d.diag_ptr[h + 1] - d.diag_ptr[h];
+  int32_t p = upper_bound_i32(D, n, w * 32 - 1);  // first offset >= 32w
+  uint32_t bits = 0;
+  for (; p < n && D[p] < w * 32 + 32; ++p)
+    if (D[p] >= w * 32) bits |= 1u << (D[p] - w * 32);
+  dbits[gid] = bits;
+}
+
+// ---------------------------------------------------------------------------
 // In-place inclusive scan of entries 1..n of the three item pointer arrays
 // (entry 0 is 0), so that ptr[it] is the first element of item it.
 // ---------------------------------------------------------------------------
@@ -377,6 +394,14 @@ hipError_t launch_index_items(const sa_pattern_desc& d, const sa_index& ix, int3
   const int64_t items = (int64_t)ix.n_heads * ix.n_row_blocks;
   const size_t lds = 2 * sizeof(uint32_t) * (size_t)(((d.S - 1) >> 5) + 1);
   hipLaunchKernelGGL(k_items, dim3((unsigned)items), dim3(kThreads), lds, stream, d, ix, fill, validate);
+  return hipGetLastError();
+}
+
+hipError_t launch_index_dbits(const sa_pattern_desc& d, const sa_index& ix, hipStream_t stream) {
+  const int32_t nwords = ((d.S - 1) >> 5) + 1;
+  const int64_t total = (int64_t)d.n_heads * nwords;
+  hipLaunchKernelGGL(k_dbits, dim3((unsigned)((total + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream, d,
+                     ix.dbits, nwords);
   return hipGetLastError();
 }
 

@@ -17,6 +17,7 @@ hipError_t launch_index_runs(const sa_pattern_desc& d, const sa_index& ix, int32
 hipError_t launch_index_items(const sa_pattern_desc& d, const sa_index& ix, int32_t fill, int32_t validate,
                               hipStream_t stream);
 hipError_t launch_index_scan(const sa_index& ix, hipStream_t stream);
+hipError_t launch_index_dbits(const sa_pattern_desc& d, const sa_index& ix, hipStream_t stream);
 
 // Attention (sa_attn.hip).
 struct AttnArgs {

@@ -53,7 +53,7 @@ def _desc(m, S=512, H=1, **kw):
 
 
 def _index(m, S=512, H=1, BM=64, **kw):
-    ix = m._Index(S, H, BM, -(-S // BM), *([FAKE.value] * 12), m._Sizes(10, 10, 10, 10))
+    ix = m._Index(S, H, BM, -(-S // BM), *([FAKE.value] * 13), m._Sizes(10, 10, 10, 10))
     for k, v in kw.items():
         setattr(ix, k, v)
     return ix

@@ -12,7 +12,7 @@ from gpu_util import note, sa
 pytestmark = pytest.mark.gpu
 
 KEYS = ("run_ptr", "run_lo", "run_hi", "seg_ptr", "seg_lo", "seg_hi", "bcol_ptr", "bcol_idx", "col_ptr", "col_idx",
-        "pair_count")
+        "pair_count", "dbits")
 
 
 def _compare(desc, BM, what):
