@@ -134,6 +134,24 @@ def capture_ms(sa, torch, reps=5):
     return dict(ms=ms, maps=int(maps.shape[0]), L=512, read_GBps=causal_bytes / (ms * 1e-3) / 1e9)
 
 
+def measured_traffic(cfg):
+    """HBM bytes per launch of the attention kernel, from profiles/traffic.json (hardware counters
+    FETCH_SIZE + WRITE_SIZE, scaled by a 1 GiB copy), or None when the kernel source has changed
+    since those counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    src = os.path.join(ROOT, "structured_sparse_attention_amd", "csrc", "sa_attn.hip")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    entry = rec.get(cfg["name"])
+    if not entry or entry.get("sa_attn_sha256") != digest:
+        return None
+    return entry.get("bytes_per_launch")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,6 +160,8 @@ def main():
     ap.add_argument("--config", type=int, default=4, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the S=131072 and capture measurements")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one device copy of 1 GiB (reference for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (see DESIGN.md for how the "
@@ -210,6 +230,13 @@ def main():
         cpu = cpu_baseline(desc, qkv_host, cfg)
         log("cpu oracle: %.4f TFLOP/s on %d threads (%s)" % (cpu["value"], cpu["cores"], cpu["sample"]))
 
+    if args.calibrate_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     achieved = flops / (attn_ms * 1e-3) / 1e12
     out = {
         "metric": "effective TFLOP/s (retained pairs) + prefill attn ms at S=64K/131K, 1 GPU",
@@ -228,7 +255,8 @@ def main():
                                % (cfg["name"], cfg["S"], cfg["hq"], cfg["hkv"], cfg["d"], cfg["row_block"]),
                    "batch": B, "seq_len": cfg["S"], "hq": cfg["hq"], "hkv": cfg["hkv"], "head_dim": cfg["d"]},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None, "kernel": "k_attn (bf16, d=128)"},
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(cfg),
+                     "kernel": "attention forward, bf16, head_dim %d, row block %d" % (cfg["d"], cfg["row_block"])},
         "cpu_baseline": None if cpu is None else {k2: cpu[k2] for k2 in ("value", "unit", "cores", "kind", "sample")},
         "prefill_attn_ms": prefill_ms,
         "index_build_ms": index_ms,
