@@ -157,7 +157,8 @@ typedef struct sa_index {
  *   counting pass, writes the totals to *sizes and returns SA_ERR_DESC_INVALID if
  *   validation (flags & SA_BUILD_VALIDATE) found a bad descriptor.  If any of run_lo,
  *   run_hi, seg_lo, seg_hi, bcol_idx, col_idx is NULL the call stops after the counts
- *   (sizes must then be non-NULL).
+ *   (sizes must then be non-NULL); pair_count and dbits are then not yet valid (the
+ *   counting pass uses dbits as scratch; the fill writes both).
  * Fill: with every array present the call recounts and fills; it stays asynchronous
  *   when sizes == NULL.  A fill that would exceed a capacity stops at the capacity and
  *   raises SA_STATUS_OVERFLOW in idx->status (SA_ERR_CAPACITY is returned directly

@@ -63,7 +63,7 @@ sa_status sa_build_index(const sa_pattern_desc* desc, sa_index* idx, sa_index_si
   if (!payload) {
     ix.run_lo = ix.run_hi = ix.seg_lo = ix.seg_hi = ix.bcol_idx = ix.col_idx = nullptr;
   }
-  hipError_t e = sa::launch_index_runs(d, ix, validate, st);
+  hipError_t e = sa::launch_index_heads(d, ix, validate, st);
   if (e == hipSuccess) e = sa::launch_index_items(d, ix, 0, validate, st);
   if (e == hipSuccess) e = sa::launch_index_scan(ix, st);
   if (e != hipSuccess) return SA_ERR_HIP;
@@ -89,8 +89,8 @@ sa_status sa_build_index(const sa_pattern_desc* desc, sa_index* idx, sa_index_si
       return SA_ERR_CAPACITY;
   }
   if (!payload) return SA_OK;
-  e = sa::launch_index_dbits(d, ix, st);
-  if (e == hipSuccess) e = sa::launch_index_items(d, ix, 1, 0, st);
+  e = sa::launch_index_items(d, ix, 1, 0, st);
+  if (e == hipSuccess) e = sa::launch_index_heads_fill(d, ix, st);
   return hip_status(e);
 }
 

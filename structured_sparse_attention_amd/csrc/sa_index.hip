@@ -9,14 +9,31 @@
 // part X (verticals, blocks, stripe lists) split into X & U and X \ U.  Its exact
 // definition is in include/sa.h.
 //
-// Work layout: one 256-thread workgroup per (head, row block).  The workgroup
-// builds two bitmaps over key columns [0, b1] in LDS -- X and U -- with one word
-// per thread per step (blocks, interval fills) and LDS atomics (vertical and stripe
-// lists).  Everything after that is word-parallel: popcounts give the counts,
-// a block-wide scan gives write positions, and segment starts/ends are the rising
-// and falling edges of U.  The pass runs twice per build: counting (then a device
-// scan turns counts into offsets) and filling.  HBM traffic: the stripe lists and
-// block-mask rows in, the index out; everything else stays in LDS.
+// A build is nine launches, all on one stream:
+//   k_heads         one workgroup per head: validation of D and C, the run count of D,
+//                   reset of status
+//   k_items_lists   one workgroup per (head, row block), count pass: classifies the item
+//                   and counts the items that need no bitmap (block columns only, a stripe
+//                   list only, or diagonals and verticals)
+//   k_items         count pass of the other items (bitmaps in LDS)
+//   k_scan_local  |
+//   k_scan_offset | exclusive scans of the per-item counts and of the per-head run
+//   k_scan_fix    | counts (three passes, no workspace: the arrays are scanned in place)
+//   k_items_lists   fill pass
+//   k_items         fill pass
+//   k_heads_fill    one workgroup per head: pair_count, the D bitmap (dbits), the runs of D
+// Between the passes each item keeps its kind and retained-pair count in its slot of
+// dbits, which k_heads_fill overwrites with the bitmap at the end.
+// Bitmap path: X and U over key columns [0, b1] in LDS, with one word per thread per
+// step (blocks, interval fills) and LDS atomics (vertical and stripe lists);
+// everything after that is word-parallel: popcounts give the counts, a block-wide scan
+// gives write positions, and segment starts/ends are the rising and falling edges of U.
+// Without bitmaps: block columns are whole blocks in order; the columns <= b1 of a
+// sorted stripe list are a prefix of it; a vertical c lies in U iff some offset of D
+// falls in [max(b0, c) - c, b1 - c]; the segments of U are the merged column intervals
+// of the runs of D.  The head's diagonal offsets are staged in LDS (when they fit) for
+// the binary searches.  HBM traffic: the descriptor lists and block-mask rows in, the
+// index out.
 #include "sa_internal.h"
 
 namespace sa {
@@ -24,10 +41,15 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+constexpr int kDsh = 2048;                      // diagonal offsets of one head staged in LDS (also the fill's stage)
+constexpr int kScanPer = 16;                    // scan entries per thread
+constexpr int kScanChunk = kThreads * kScanPer; // scan entries per workgroup
+constexpr int32_t kBadHead = 1 << 30;           // run_ptr marker from k_heads to k_scan_fix
+constexpr size_t kDefaultLds = 65536;           // dynamic LDS usable without raising the function's limit
 
 __device__ inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// number of elements <= x in the sorted array a[0, n)
+// number of elements <= x in the sorted array a[0, n) (a may point to LDS or global memory)
 __device__ inline int32_t upper_bound_i32(const int32_t* a, int32_t n, int32_t x) {
   int32_t lo = 0, hi = n;
   while (lo < hi) {
@@ -44,64 +66,39 @@ __device__ inline uint32_t bit_range(int a, int b) {
   return hi & ~((1u << a) - 1u);
 }
 
-// ---------------------------------------------------------------------------
-// Runs of D_h (maximal runs of consecutive offsets), validation of the D and C
-// lists, and reset of pair_count / status.  A single workgroup: heads are few.
-// ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(kThreads) k_runs(sa_pattern_desc d, sa_index ix, int32_t validate) {
-  const int tid = threadIdx.x;
-  if (tid == 0) ix.status[0] = 0;
+// true iff offset r does not continue the run of its predecessor (wrap-safe for invalid lists)
+__device__ inline bool starts_run(int32_t r, int32_t prev) { return (uint32_t)r != (uint32_t)prev + 1u; }
+
+// Workgroup-wide exclusive scan of one value per thread; *total receives the sum.  Contains
+// two barriers, so every read a thread made before the call precedes every write after it.
+template <typename T>
+__device__ inline T block_exscan(T x, T* total, T* sh /* [kWaves] */) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  T inc = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    T y = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += y;
+  }
+  if (lane == 63) sh[wave] = inc;
   __syncthreads();
-  for (int h = tid; h < d.n_heads; h += kThreads) {
-    ix.pair_count[h] = 0;
-    const int32_t p0 = d.diag_ptr[h], p1 = d.diag_ptr[h + 1];
-    int32_t n = 0, prev = -1;
-    bool bad = false;
-    for (int32_t p = p0; p < p1; ++p) {
-      int32_t r = d.diag_off[p];
-      if (validate && (r < 0 || r >= d.S || r <= prev)) bad = true;
-      if (p == p0 || r != prev + 1) ++n;
-      prev = r;
-    }
-    if (validate) {
-      int32_t pv = -1;
-      for (int32_t p = d.vert_ptr[h]; p < d.vert_ptr[h + 1]; ++p) {
-        int32_t c = d.vert_col[p];
-        if (c < 0 || c >= d.S || c <= pv) bad = true;
-        pv = c;
-      }
-    }
-    if (bad) atomicOr(ix.status, SA_STATUS_DESC_INVALID);
-    ix.run_ptr[h + 1] = n;
+  T before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    T t = sh[w];
+    if (w < wave) before += t;
+    all += t;
   }
   __syncthreads();
-  if (tid == 0) {
-    int32_t acc = 0;
-    ix.run_ptr[0] = 0;
-    for (int h = 0; h < d.n_heads; ++h) {
-      acc += ix.run_ptr[h + 1];
-      ix.run_ptr[h + 1] = acc;
-    }
-  }
-  __syncthreads();
-  if (ix.run_lo == nullptr || ix.run_hi == nullptr) return;
-  for (int h = tid; h < d.n_heads; h += kThreads) {
-    const int32_t p0 = d.diag_ptr[h], p1 = d.diag_ptr[h + 1];
-    int64_t out = ix.run_ptr[h];
-    int32_t p = p0;
-    while (p < p1) {
-      int32_t lo = d.diag_off[p], hi = lo;
-      while (p + 1 < p1 && d.diag_off[p + 1] == hi + 1) { ++p; ++hi; }
-      if (out < ix.capacity.n_runs) {
-        ix.run_lo[out] = lo;
-        ix.run_hi[out] = hi;
-      } else {
-        atomicOr(ix.status, SA_STATUS_OVERFLOW);
-      }
-      ++out;
-      ++p;
-    }
-  }
+  *total = all;
+  return before + inc - x;
+}
+
+template <typename T>
+__device__ inline T block_sum(T x, T* sh /* [kWaves] */) {
+  T tot;
+  block_exscan<T>(x, &tot, sh);
+  return tot;
 }
 
 // Block-wide exclusive scan of four counters; returns the totals in tot[].
@@ -138,106 +135,541 @@ __device__ inline void block_scan4(int32_t v[4], int32_t tot[4], int32_t* sh /* 
 }
 
 // ---------------------------------------------------------------------------
-// Per (head, row block): build X and U bitmaps, then count (fill = 0) or write
-// (fill = 1) segments, in-segment columns and gathered columns.
+// Per head, before the count: reset status and run_ptr[0] (once); validate the D
+// and C lists; count the maximal runs of D into run_ptr[h + 1] (kBadHead marks an
+// invalid head until k_scan_fix folds it into status).
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(kThreads) k_items(sa_pattern_desc d, sa_index ix, int32_t fill, int32_t validate) {
-  extern __shared__ uint32_t lds[];
-  __shared__ int32_t scan_sh[kWaves * 4];
-  __shared__ long long red_sh[kWaves * 4];
-
+__global__ void __launch_bounds__(kThreads) k_heads(sa_pattern_desc d, sa_index ix, int32_t validate) {
+  __shared__ int32_t red[kWaves];
   const int tid = threadIdx.x;
-  const int32_t S = d.S, BM = ix.row_block, nb = ix.n_row_blocks;
-  const int64_t it = blockIdx.x;
-  const int32_t h = (int32_t)(it / nb), rb = (int32_t)(it % nb);
-  const int32_t b0 = rb * BM, b1 = min(S, b0 + BM) - 1;
-  const int32_t nw = (b1 >> 5) + 1;          // words covering columns [0, b1]
-  const int32_t nw_alloc = ((S - 1) >> 5) + 1;
-  uint32_t* X = lds;
-  uint32_t* U = lds + nw_alloc;
-
-  // --- X from the block row, U cleared
-  const uint8_t* brow = nullptr;
-  int64_t nbq = 0;
-  if (d.block_mask != nullptr) {
-    nbq = cdiv64(S, d.block_size);
-    brow = d.block_mask + ((int64_t)h * nbq + b0 / d.block_size) * nbq;
+  const int32_t h = blockIdx.x, S = d.S;
+  if (h == 0 && tid == 0) {
+    ix.status[0] = 0;
+    ix.run_ptr[0] = 0;
   }
-  for (int32_t w = tid; w < nw; w += kThreads) {
-    uint32_t x = 0;
-    if (brow != nullptr && brow[(w * 32) / d.block_size]) x = 0xffffffffu;
-    if (w == nw - 1) x &= bit_range(0, b1 & 31);
-    X[w] = x;
-    U[w] = 0;
+  const int32_t p0 = d.diag_ptr[h], p1 = d.diag_ptr[h + 1];
+  int32_t runs = 0, bad = 0;
+  for (int32_t pb = p0; pb < p1; pb += 4 * kThreads) {
+    int32_t r[4], prev[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int32_t p = pb + u * kThreads + tid;
+      r[u] = p < p1 ? d.diag_off[p] : 0;
+      prev[u] = (p < p1 && p > p0) ? d.diag_off[p - 1] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int32_t p = pb + u * kThreads + tid;
+      if (p >= p1) continue;
+      if (validate && (r[u] < 0 || r[u] >= S || (p > p0 && r[u] <= prev[u]))) bad = 1;
+      if (p == p0 || starts_run(r[u], prev[u])) ++runs;
+    }
+  }
+  if (validate) {
+    const int32_t q0 = d.vert_ptr[h], q1 = d.vert_ptr[h + 1];
+    for (int32_t p = q0 + tid; p < q1; p += kThreads) {
+      const int32_t c = d.vert_col[p];
+      if (c < 0 || c >= S || (p > q0 && d.vert_col[p - 1] >= c)) bad = 1;
+    }
+  }
+  runs = block_sum<int32_t>(runs, red);
+  bad = block_sum<int32_t>(bad, red);
+  if (tid == 0) ix.run_ptr[h + 1] = runs | (bad ? kBadHead : 0);
+}
+
+// Launch constants of the item kernels, computed on the host (32-bit: S <= 262144, items < 2^31).
+struct ItemConsts {
+  int32_t nbq;        // block-mask row length, ceil(S / block_size) (0 without a block mask)
+  int32_t rb_per_br;  // row blocks per block row, block_size / BM
+  int32_t wpb_shift;  // log2(block_size / 32) when that is a power of two, else -1
+  int32_t wpb;        // block_size / 32
+  int32_t bs;         // block_size (a multiple of 64)
+  int32_t nst;        // stripes per head, ceil(S / stripe_rows) (0 without stripes)
+  int32_t rb_per_st;  // row blocks per stripe, stripe_rows / BM
+  int32_t dcap;       // diagonal offsets that fit the LDS staging area
+  int32_t nwords;     // ceil(S / 32): length of one dbits row
+};
+
+// How an item is built.  The count pass of k_items_lists decides it and keeps it in the two top
+// bits of the item's scratch slot dbits[h][rb] (the low bits hold its retained-pair count); every
+// later item pass reads it from there.
+//   kKindBlocks   only block-mask columns (no diagonal, vertical or stripe list)
+//   kKindStripes  only a stripe list
+//   kKindLists    diagonals and verticals, no block or stripe column, the diagonals fit in LDS
+//   kKindGeneral  anything else: the bitmap path of k_items
+constexpr uint32_t kKindBlocks = 0, kKindStripes = 1, kKindLists = 2, kKindGeneral = 3;
+constexpr int kKindShift = 30;
+constexpr uint32_t kPairsMask = (1u << kKindShift) - 1u;  // an item holds at most BM * S <= 2^25 pairs
+
+struct Item {
+  int32_t it, h, rb, b0, b1, nw;
+  int32_t nD, vp0, vp1;
+  int64_t sp0, sp1;
+  const int32_t* D;     // the head's diagonal offsets (global)
+  const uint8_t* brow;  // the block row of this row block, or null
+  int32_t cb1;          // block column that holds column b1
+};
+
+__device__ inline Item load_item(const sa_pattern_desc& d, const sa_index& ix, const ItemConsts& kc, int32_t it) {
+  Item m;
+  const int32_t S = d.S, BM = ix.row_block, nb = ix.n_row_blocks;
+  m.it = it;
+  m.h = m.it / nb;
+  m.rb = m.it - m.h * nb;
+  m.b0 = m.rb * BM;
+  m.b1 = min(S, m.b0 + BM) - 1;
+  m.nw = (m.b1 >> 5) + 1;
+  // every list bound this item needs, loaded together
+  const int32_t dp0 = d.diag_ptr[m.h], dp1 = d.diag_ptr[m.h + 1];
+  m.vp0 = d.vert_ptr[m.h];
+  m.vp1 = d.vert_ptr[m.h + 1];
+  m.sp0 = m.sp1 = 0;
+  if (d.stripe_ptr != nullptr) {
+    const int64_t st = (int64_t)m.h * kc.nst + m.rb / kc.rb_per_st;
+    m.sp0 = d.stripe_ptr[st];
+    m.sp1 = d.stripe_ptr[st + 1];
+  }
+  m.nD = dp1 - dp0;
+  m.D = d.diag_off + dp0;
+  m.brow = nullptr;
+  m.cb1 = 0;
+  if (d.block_mask != nullptr) {
+    m.brow = d.block_mask + ((int64_t)m.h * kc.nbq + m.rb / kc.rb_per_br) * kc.nbq;
+    m.cb1 = kc.wpb_shift >= 0 ? ((m.b1 >> 5) >> kc.wpb_shift) : (m.b1 >> 5) / kc.wpb;
+  }
+  return m;
+}
+
+__device__ inline uint32_t* scratch_slot(const sa_index& ix, const ItemConsts& kc, const Item& m) {
+  return ix.dbits + (int64_t)m.h * kc.nwords + m.rb;
+}
+
+// Workgroup reduction of the four item counters; thread 0 stores them and the scratch slot.
+__device__ inline void store_counts(const sa_index& ix, const ItemConsts& kc, const Item& m, long long cnt[4],
+                                    uint32_t kind, long long* red_sh /* [kWaves * 4] */) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    long long x = cnt[c];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_down(x, o, 64);
+    if (lane == 0) red_sh[wave * 4 + c] = x;
   }
   __syncthreads();
+  if (threadIdx.x == 0) {
+    long long t[4] = {0, 0, 0, 0};
+    for (int w = 0; w < kWaves; ++w)
+      for (int c = 0; c < 4; ++c) t[c] += red_sh[w * 4 + c];
+    ix.seg_ptr[m.it + 1] = t[0];
+    ix.bcol_ptr[m.it + 1] = t[1];
+    ix.col_ptr[m.it + 1] = t[2];
+    *scratch_slot(ix, kc, m) = ((uint32_t)t[3] & kPairsMask) | (kind << kKindShift);
+  }
+}
 
-  // --- verticals and stripe columns into X
-  {
-    const int32_t p0 = d.vert_ptr[h], p1 = d.vert_ptr[h + 1];
-    for (int32_t p = p0 + tid; p < p1; p += kThreads) {
-      int32_t c = d.vert_col[p];
-      if (c >= 0 && c <= b1) atomicOr(&X[c >> 5], 1u << (c & 31));
+// Retained pairs of gathered columns c0..c1 (all rows max(j, b0) .. b1 retained), 0 <= c0 <= c1 <= b1.
+__device__ inline long long column_pairs(int32_t c0, int32_t c1, int32_t b0, int32_t b1) {
+  long long p = 0;
+  const int32_t below = min(c1, b0 - 1);  // columns under the row block: every row
+  if (below >= c0) p += (long long)(below - c0 + 1) * (b1 - b0 + 1);
+  const int32_t a = max(c0, b0);          // columns inside: rows j .. b1
+  if (c1 >= a) {
+    const long long n = c1 - a + 1;
+    p += n * (b1 + 1) - (long long)(a + c1) * n / 2;
+  }
+  return p;
+}
+
+// Number of entries <= x of the sorted global array a[0, n), found by one wave: each round probes
+// 64 evenly spaced entries and keeps the gap between the last probe <= x and the next one (a
+// round per factor of 64 in n).  Every lane returns the result.
+__device__ inline int64_t wave_upper_bound(const int32_t* a, int64_t n, int32_t x) {
+  const int lane = threadIdx.x & 63;
+  int64_t lo = 0, hi = n;  // invariant: a[i] <= x for i < lo, a[i] > x for i >= hi
+  while (hi > lo) {
+    const int64_t step = (hi - lo + 63) / 64;
+    const int64_t p = lo + lane * step;
+    const bool le = p < hi && a[p] <= x;
+    const int k = __popcll(__ballot(le));  // probes 0 .. k-1 are <= x (the array is sorted)
+    if (k == 0) {
+      hi = lo;
+    } else {
+      const int64_t pk = lo + (int64_t)k * step;  // first probe > x, if it exists
+      lo += (int64_t)(k - 1) * step + 1;
+      if (pk < hi) hi = pk;
     }
   }
-  if (d.stripe_ptr != nullptr) {
-    const int64_t nst = cdiv64(S, d.stripe_rows);
-    const int64_t t = b0 / d.stripe_rows;
-    const int64_t p0 = d.stripe_ptr[h * nst + t], p1 = d.stripe_ptr[h * nst + t + 1];
-    bool bad = false;
-    for (int64_t p = p0 + tid; p < p1; p += kThreads) {
-      int32_t c = d.stripe_col[p];
-      if (validate && (c < 0 || c >= S || (p > p0 && d.stripe_col[p - 1] >= c))) bad = true;
-      if (c >= 0 && c <= b1) atomicOr(&X[c >> 5], 1u << (c & 31));
+  return lo;
+}
+
+// Lists path helpers: number of offsets of D (sorted, in LDS) in [lo, hi]
+__device__ inline int32_t count_in(const int32_t* D, int32_t nD, int32_t lo, int32_t hi) {
+  return hi < lo ? 0 : upper_bound_i32(D, nD, hi) - upper_bound_i32(D, nD, lo - 1);
+}
+
+// ---------------------------------------------------------------------------
+// Item kinds with no bitmap (blocks only, stripes only, diagonals + verticals).
+// One workgroup per (head, row block); the count pass (fill = 0) classifies the
+// item and, for a kKindGeneral item, only records that in its scratch slot.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kThreads) k_items_lists(sa_pattern_desc d, sa_index ix, int32_t fill,
+                                                          int32_t validate, ItemConsts kc) {
+  __shared__ int32_t Dsh[kDsh];
+  __shared__ int32_t list_sh[kThreads * 4];
+  __shared__ long long red_sh[kWaves * 4];
+  __shared__ int32_t sh32[kWaves];
+  __shared__ int64_t bound_sh[2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const Item m = load_item(d, ix, kc, blockIdx.x);
+  const int32_t S = d.S, b0 = m.b0, b1 = m.b1;
+
+  uint32_t kind;
+  if (!fill) {
+    int any = 0;
+    if (m.brow != nullptr)
+      for (int32_t cb = tid; cb <= m.cb1; cb += kThreads) any |= m.brow[cb];
+    const bool has_blk = __syncthreads_or(any) != 0;
+    const bool has_vert = m.vp1 > m.vp0, has_str = m.sp1 > m.sp0, has_diag = m.nD > 0;
+    if (has_blk && !has_diag && !has_vert && !has_str) kind = kKindBlocks;
+    else if (has_str && !has_blk && !has_diag && !has_vert) kind = kKindStripes;
+    else if (!has_blk && !has_str && m.nD <= kc.dcap) kind = kKindLists;
+    else kind = kKindGeneral;
+    if (kind == kKindGeneral) {
+      if (tid == 0) *scratch_slot(ix, kc, m) = kKindGeneral << kKindShift;
+      return;
     }
-    if (bad) atomicOr(ix.status, SA_STATUS_DESC_INVALID);
+  } else {
+    kind = *scratch_slot(ix, kc, m) >> kKindShift;
+    if (kind == kKindGeneral) return;
+  }
+
+  long long cnt[4] = {0, 0, 0, 0};  // segments, in-segment columns, gathered columns, retained pairs
+  bool bad = false, overflow = false;
+
+  if (kind == kKindBlocks) {
+    const int32_t bs = kc.bs;
+    if (!fill) {
+      for (int32_t cb = tid; cb <= m.cb1; cb += kThreads) {
+        if (m.brow[cb]) {
+          const int32_t c0 = cb * bs, c1 = min(b1, c0 + bs - 1);
+          cnt[2] += c1 - c0 + 1;
+          cnt[3] += column_pairs(c0, c1, b0, b1);
+        }
+      }
+      store_counts(ix, kc, m, cnt, kind, red_sh);
+      return;
+    }
+    // fill: every set block but the last is full, so block k of the row (in order) starts at k * bs;
+    // the set blocks of each chunk are listed in LDS and each wave writes whole blocks, lane by column
+    int64_t base = ix.col_ptr[m.it];
+    const int64_t cap = ix.capacity.n_cols;
+    for (int32_t cbase = 0; cbase <= m.cb1; cbase += 4 * kThreads) {
+      int32_t mine = 0;
+      uint8_t f[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int32_t cb = cbase + 4 * tid + u;
+        f[u] = cb <= m.cb1 ? m.brow[cb] : 0;
+        mine += f[u] ? 1 : 0;
+      }
+      int32_t tot;
+      int32_t r = block_exscan<int32_t>(mine, &tot, sh32);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (f[u]) list_sh[r++] = cbase + 4 * tid + u;
+      __syncthreads();
+      for (int32_t e = wave; e < tot; e += kWaves) {
+        const int32_t c0 = list_sh[e] * bs, c1 = min(b1, c0 + bs - 1);
+        const int64_t out = base + (int64_t)e * bs;
+        for (int32_t c = c0 + lane; c <= c1; c += 64) {
+          const int64_t pos = out + (c - c0);
+          if (pos < cap) ix.col_idx[pos] = c; else overflow = true;
+        }
+      }
+      __syncthreads();
+      base += (int64_t)tot * bs;
+    }
+  } else if (kind == kKindStripes) {
+    if (!fill && !validate) {
+      // sorted list: entries below b0 each give every row; the few in [b0, b1] are summed one by one
+      const int64_t len = m.sp1 - m.sp0;
+      if (wave < 2) {
+        const int64_t n = wave_upper_bound(d.stripe_col + m.sp0, len, wave == 0 ? b1 : b0 - 1);
+        if (lane == 0) bound_sh[wave] = n;
+      }
+      __syncthreads();
+      const int64_t n_le = bound_sh[0], n_lt = bound_sh[1];
+      if (tid == 0) {
+        cnt[2] = n_le;
+        cnt[3] = n_lt * (long long)(b1 - b0 + 1);
+      }
+      for (int64_t q = n_lt + tid; q < n_le; q += kThreads) {
+        const int32_t c = d.stripe_col[m.sp0 + q];
+        cnt[3] += b1 - max(c, b0) + 1;
+      }
+      store_counts(ix, kc, m, cnt, kind, red_sh);
+      return;
+    }
+    if (!fill) {
+      for (int64_t pb = m.sp0; pb < m.sp1; pb += 8 * kThreads) {
+        int32_t c[8], prev[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int64_t p = pb + u * kThreads + tid;
+          c[u] = p < m.sp1 ? d.stripe_col[p] : -1;
+          prev[u] = (validate && p < m.sp1 && p > m.sp0) ? d.stripe_col[p - 1] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int64_t p = pb + u * kThreads + tid;
+          if (validate && p < m.sp1 && (c[u] < 0 || c[u] >= S || (p > m.sp0 && prev[u] >= c[u]))) bad = true;
+          if (c[u] >= 0 && c[u] <= b1) {
+            cnt[2] += 1;
+            cnt[3] += b1 - max(c[u], b0) + 1;
+          }
+        }
+      }
+      if (bad) atomicOr(ix.status, SA_STATUS_DESC_INVALID);
+      store_counts(ix, kc, m, cnt, kind, red_sh);
+      return;
+    }
+    // fill: the columns <= b1 of a sorted list are its first n entries
+    const int64_t base = ix.col_ptr[m.it], n = ix.col_ptr[m.it + 1] - base;
+    const int64_t cap = ix.capacity.n_cols;
+    for (int64_t qb = 0; qb < n; qb += 8 * kThreads) {
+      int32_t c[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t q = qb + u * kThreads + tid;
+        c[u] = q < n ? d.stripe_col[m.sp0 + q] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t q = qb + u * kThreads + tid;
+        if (q < n) {
+          int32_t col = c[u];
+          if (col < 0 || col > b1) {  // only an unsorted list gets here; keep every column in range
+            bad = true;
+            col = min(max(col, 0), b1);
+          }
+          if (base + q < cap) ix.col_idx[base + q] = col; else overflow = true;
+        }
+      }
+    }
+  } else {  // kKindLists
+    const int32_t nD = m.nD;
+    for (int32_t pb = 0; pb < nD; pb += 8 * kThreads) {
+      int32_t r[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int32_t p = pb + u * kThreads + tid;
+        r[u] = p < nD ? m.D[p] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int32_t p = pb + u * kThreads + tid;
+        if (p < nD) Dsh[p] = r[u];
+      }
+    }
+    __syncthreads();
+    // A run [lo, hi] of D (lo <= b1) touches key columns I = [max(0, b0 - hi), b1 - lo] (clipped to
+    // [0, b1]); runs in descending offset order give intervals in ascending column order, and U's
+    // segments are the merged intervals.  The run with the next larger offsets starts at index q + 1
+    // (q: this run's last index); the one with the next smaller offsets ends at index p - 1.
+    auto run_of = [&](int32_t p, int32_t& lo, int32_t& hi, int32_t& q) {
+      lo = Dsh[p];
+      int32_t qa = p, qb = nD - 1;
+      while (qa < qb) {
+        const int32_t mid = (qa + qb + 1) >> 1;
+        if (Dsh[mid] - mid == lo - p) qa = mid;
+        else qb = mid - 1;
+      }
+      q = qa;
+      hi = Dsh[qa];
+    };
+    auto is_run_start = [&](int32_t p) { return p == 0 || starts_run(Dsh[p], Dsh[p - 1]); };
+    auto seg_flags = [&](int32_t p, bool& st, bool& en, int32_t& s0, int32_t& s1) {
+      st = en = false;
+      if (p < 0 || p >= nD || !is_run_start(p)) return;
+      int32_t lo, hi, q;
+      run_of(p, lo, hi, q);
+      if (lo > b1) return;
+      s0 = max(0, b0 - hi);
+      s1 = min(b1, b1 - lo);
+      st = !(q + 1 < nD && Dsh[q + 1] <= b1 && s0 <= min(b1, b1 - Dsh[q + 1]) + 1);
+      en = !(p > 0 && max(0, b0 - Dsh[p - 1]) <= s1 + 1);
+    };
+
+    if (!fill) {
+      for (int32_t p = tid; p < nD; p += kThreads) {
+        bool st, en;
+        int32_t s0, s1;
+        seg_flags(p, st, en, s0, s1);
+        cnt[0] += st ? 1 : 0;
+      }
+      for (int32_t pb = m.vp0; pb < m.vp1; pb += 8 * kThreads) {
+        int32_t c[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int32_t p = pb + u * kThreads + tid;
+          c[u] = p < m.vp1 ? d.vert_col[p] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (c[u] < 0 || c[u] > b1) continue;
+          const int32_t a = max(b0, c[u]);
+          const int32_t dc = count_in(Dsh, nD, a - c[u], b1 - c[u]);
+          if (dc > 0) {
+            cnt[1] += 1;
+            cnt[3] += (b1 - a + 1) - dc;
+          } else {
+            cnt[2] += 1;
+            cnt[3] += b1 - a + 1;
+          }
+        }
+      }
+      // diagonal pairs of each row: offsets r in D_h with r <= i
+      if (nD > 0)
+        for (int32_t i = b0 + tid; i <= b1; i += kThreads) cnt[3] += upper_bound_i32(Dsh, nD, i);
+      store_counts(ix, kc, m, cnt, kind, red_sh);
+      return;
+    }
+    // fill: segments in ascending column order = runs in descending offset order
+    int64_t bs_lo = ix.seg_ptr[m.it], bs_hi = bs_lo;
+    for (int32_t cbase = 0; cbase < nD; cbase += kThreads) {
+      const int32_t p = nD - 1 - (cbase + tid);
+      bool st, en;
+      int32_t s0 = 0, s1 = 0;
+      seg_flags(p, st, en, s0, s1);
+      int32_t tst, ten;
+      const int32_t rst = block_exscan<int32_t>(st ? 1 : 0, &tst, sh32);
+      const int32_t ren = block_exscan<int32_t>(en ? 1 : 0, &ten, sh32);
+      if (st) {
+        if (bs_lo + rst < ix.capacity.n_segs) ix.seg_lo[bs_lo + rst] = s0; else overflow = true;
+      }
+      if (en) {
+        if (bs_hi + ren < ix.capacity.n_segs) ix.seg_hi[bs_hi + ren] = s1; else overflow = true;
+      }
+      bs_lo += tst;
+      bs_hi += ten;
+    }
+    // verticals in list order, split into in-segment and gathered columns
+    int64_t b_in = ix.bcol_ptr[m.it], b_out = ix.col_ptr[m.it];
+    for (int32_t pb = m.vp0; pb < m.vp1; pb += kThreads) {
+      const int32_t p = pb + tid;
+      const int32_t c = p < m.vp1 ? d.vert_col[p] : -1;
+      bool in = false, out = false;
+      if (c >= 0 && c <= b1) {
+        const int32_t a = max(b0, c);
+        if (count_in(Dsh, nD, a - c, b1 - c) > 0) in = true;
+        else out = true;
+      }
+      int32_t tin, tout;
+      const int32_t rin = block_exscan<int32_t>(in ? 1 : 0, &tin, sh32);
+      const int32_t rout = block_exscan<int32_t>(out ? 1 : 0, &tout, sh32);
+      if (in) {
+        if (b_in + rin < ix.capacity.n_bcols) ix.bcol_idx[b_in + rin] = c; else overflow = true;
+      }
+      if (out) {
+        if (b_out + rout < ix.capacity.n_cols) ix.col_idx[b_out + rout] = c; else overflow = true;
+      }
+      b_in += tin;
+      b_out += tout;
+    }
+  }
+  if (bad) atomicOr(ix.status, SA_STATUS_DESC_INVALID);
+  if (overflow) atomicOr(ix.status, SA_STATUS_OVERFLOW);
+}
+
+// Gathered-column slots per thread and round of the bitmap fill: thread t expands slots
+// [kSlots t, kSlots t + kSlots) of the round into an LDS stage, then the workgroup stores the
+// round's kSlots * kThreads slots coalesced.
+constexpr int kSlots = 8;
+static_assert(kSlots * kThreads <= kDsh, "the fill stage lives in the diagonal staging area");
+
+// ---------------------------------------------------------------------------
+// Bitmap path (items of kind kKindGeneral; the others return at once): build X
+// and U bitmaps over key columns [0, b1], then count (fill = 0) or write (fill = 1)
+// segments, in-segment columns and gathered columns.
+// STAGED: the head's diagonal offsets are in LDS (searched with LDS reads).
+// ---------------------------------------------------------------------------
+template <bool STAGED>
+__device__ inline void items_body(const sa_pattern_desc& d, const sa_index& ix, int32_t fill, int32_t validate,
+                                  const ItemConsts& kc, const Item& m, const int32_t* Dq, uint32_t* X, uint32_t* U,
+                                  int32_t* scan_sh, long long* red_sh, int32_t* off_sh, int32_t* stage) {
+  const int tid = threadIdx.x;
+  const int32_t S = d.S, b0 = m.b0, b1 = m.b1, nw = m.nw, nD = m.nD;
+  // --- verticals and stripe columns into X (eight loads in flight per thread)
+  for (int32_t pb = m.vp0; pb < m.vp1; pb += 8 * kThreads) {
+    int32_t c[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int32_t p = pb + u * kThreads + tid;
+      c[u] = p < m.vp1 ? d.vert_col[p] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (c[u] >= 0 && c[u] <= b1) atomicOr(&X[c[u] >> 5], 1u << (c[u] & 31));
+  }
+  if (m.sp1 > m.sp0) {
+    bool bad = false;
+    for (int64_t pb = m.sp0; pb < m.sp1; pb += 8 * kThreads) {
+      int32_t c[8], prev[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t p = pb + u * kThreads + tid;
+        c[u] = p < m.sp1 ? d.stripe_col[p] : -1;
+        prev[u] = (validate && p < m.sp1 && p > m.sp0) ? d.stripe_col[p - 1] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t p = pb + u * kThreads + tid;
+        if (validate && p < m.sp1 && (c[u] < 0 || c[u] >= S || (p > m.sp0 && prev[u] >= c[u]))) bad = true;
+        if (c[u] >= 0 && c[u] <= b1) atomicOr(&X[c[u] >> 5], 1u << (c[u] & 31));
+      }
+    }
+    if (bad && !fill) atomicOr(ix.status, SA_STATUS_DESC_INVALID);
   }
   // --- U: columns i - r for i in [b0, b1] and r in a run [lo, hi] of D_h: [b0 - hi, b1 - lo], clipped
   // to [0, b1].  A thread that holds the first offset of a run finds the run's end by binary search:
-  // diag_off[q] - q is non-decreasing and constant exactly along a run.
-  {
-    const int32_t p0 = d.diag_ptr[h], p1 = d.diag_ptr[h + 1];
-    for (int32_t p = p0 + tid; p < p1; p += kThreads) {
-      const int32_t lo = d.diag_off[p];
-      if (p > p0 && d.diag_off[p - 1] == lo - 1) continue;  // not the first offset of a run
-      if (lo > b1) continue;
-      int32_t qa = p, qb = p1 - 1;
-      while (qa < qb) {
-        const int32_t mid = (qa + qb + 1) >> 1;
-        if (d.diag_off[mid] - mid == lo - p) qa = mid;
-        else qb = mid - 1;
-      }
-      const int32_t hi = d.diag_off[qa];
-      const int32_t a = max(0, b0 - hi), e = min(b1, b1 - lo);
-      for (int32_t w = a >> 5; a <= e && w <= (e >> 5); ++w) {
-        const int32_t ba = max(a, w * 32) - w * 32, be = min(e, w * 32 + 31) - w * 32;
-        atomicOr(&U[w], bit_range(ba, be));
-      }
+  // D[q] - q is non-decreasing and constant exactly along a run.
+  for (int32_t p = tid; p < nD; p += kThreads) {
+    const int32_t lo = Dq[p];
+    if (p > 0 && !starts_run(lo, Dq[p - 1])) continue;  // not the first offset of a run
+    if (lo > b1) continue;
+    int32_t qa = p, qb = nD - 1;
+    while (qa < qb) {
+      const int32_t mid = (qa + qb + 1) >> 1;
+      if (Dq[mid] - mid == lo - p) qa = mid;
+      else qb = mid - 1;
+    }
+    const int32_t hi = Dq[qa];
+    const int32_t a = max(0, b0 - hi), e = min(b1, b1 - lo);
+    for (int32_t w = a >> 5; a <= e && w <= (e >> 5); ++w) {
+      const int32_t ba = max(a, w * 32) - w * 32, be = min(e, w * 32 + 31) - w * 32;
+      atomicOr(&U[w], bit_range(ba, be));
     }
   }
   __syncthreads();
 
-  const int32_t* Dh = d.diag_off + d.diag_ptr[h];
-  const int32_t nD = d.diag_ptr[h + 1] - d.diag_ptr[h];
-
   if (!fill) {
-    int64_t n_seg = 0, n_in = 0, n_out = 0, pairs = 0;
+    long long cnt[4] = {0, 0, 0, 0};  // segments, in-segment columns, gathered columns, retained pairs
     for (int32_t w = tid; w < nw; w += kThreads) {
       const uint32_t u = U[w], x = X[w];
       const uint32_t prev_msb = (w > 0) ? (U[w - 1] >> 31) : 0u;
-      n_seg += __popc(u & ~((u << 1) | prev_msb));
+      cnt[0] += __popc(u & ~((u << 1) | prev_msb));
       uint32_t in = x & u, out = x & ~u;
-      n_in += __popc(in);
-      n_out += __popc(out);
+      cnt[1] += __popc(in);
+      cnt[2] += __popc(out);
       // gathered columns: rows max(j, b0) .. b1, all retained
       if (w * 32 + 31 < b0) {
-        pairs += (int64_t)__popc(out) * (int64_t)(b1 - b0 + 1);
+        cnt[3] += (long long)__popc(out) * (long long)(b1 - b0 + 1);
       } else {
         while (out) {
           int bit = __ffs(out) - 1;
           out &= out - 1;
           int32_t j = w * 32 + bit;
-          pairs += b1 - max(j, b0) + 1;
+          cnt[3] += b1 - max(j, b0) + 1;
         }
       }
       // in-segment columns of X: every causal row minus the rows whose offset is a diagonal
@@ -246,84 +678,123 @@ __global__ void __launch_bounds__(kThreads) k_items(sa_pattern_desc d, sa_index 
         in &= in - 1;
         int32_t j = w * 32 + bit;
         int32_t a = max(j, b0);
-        int32_t dcount = upper_bound_i32(Dh, nD, b1 - j) - upper_bound_i32(Dh, nD, a - j - 1);
-        pairs += (b1 - a + 1) - dcount;
+        int32_t dcount = upper_bound_i32(Dq, nD, b1 - j) - upper_bound_i32(Dq, nD, a - j - 1);
+        cnt[3] += (b1 - a + 1) - dcount;
       }
     }
     // diagonal pairs of each row: offsets r in D_h with r <= i
-    for (int32_t i = b0 + tid; i <= b1; i += kThreads) pairs += upper_bound_i32(Dh, nD, i);
-
-    // block reduction of the four counters
-    const int lane = tid & 63, wave = tid >> 6;
-    long long vals[4] = {(long long)n_seg, (long long)n_in, (long long)n_out, (long long)pairs};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      long long x = vals[c];
-      for (int o = 32; o > 0; o >>= 1) x += __shfl_down(x, o, 64);
-      if (lane == 0) red_sh[wave * 4 + c] = x;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      long long t[4] = {0, 0, 0, 0};
-      for (int w = 0; w < kWaves; ++w)
-        for (int c = 0; c < 4; ++c) t[c] += red_sh[w * 4 + c];
-      ix.seg_ptr[it + 1] = t[0];
-      ix.bcol_ptr[it + 1] = t[1];
-      ix.col_ptr[it + 1] = t[2];
-      if (it == 0) {
-        ix.seg_ptr[0] = 0;
-        ix.bcol_ptr[0] = 0;
-        ix.col_ptr[0] = 0;
-      }
-      atomicAdd((unsigned long long*)&ix.pair_count[h], (unsigned long long)t[3]);
-    }
+    if (nD > 0)
+      for (int32_t i = b0 + tid; i <= b1; i += kThreads) cnt[3] += upper_bound_i32(Dq, nD, i);
+    store_counts(ix, kc, m, cnt, kKindGeneral, red_sh);
     return;
   }
 
-  // --- fill: word-per-thread chunks, block scan for write positions
-  int64_t base_rise = ix.seg_ptr[it], base_fall = ix.seg_ptr[it], base_in = ix.bcol_ptr[it],
-          base_out = ix.col_ptr[it];
+  // --- fill: four consecutive words per thread per chunk, block scan for write positions.  Segment
+  // ends and in-segment columns are few and each thread writes its own.  Gathered columns are many:
+  // thread t expands the kSlots consecutive output slots starting at slot kSlots * t of the round (one
+  // search over the per-thread offsets, then a walk along the chunk's words) into the LDS stage, which
+  // the workgroup then stores with consecutive threads on consecutive slots.  The stage reuses the
+  // diagonal staging area: the fill reads no diagonal offset after U is built.
+  int64_t base_rise = ix.seg_ptr[m.it], base_fall = base_rise, base_in = ix.bcol_ptr[m.it],
+          base_out = ix.col_ptr[m.it];
   bool overflow = false;
-  for (int32_t w0 = 0; w0 < nw; w0 += kThreads) {
-    const int32_t w = w0 + tid;
-    uint32_t rise = 0, fall = 0, in = 0, out = 0;
-    if (w < nw) {
-      const uint32_t u = U[w], x = X[w];
-      const uint32_t prev_msb = (w > 0) ? (U[w - 1] >> 31) : 0u;
-      const uint32_t next_lsb = (w + 1 < nw) ? (U[w + 1] & 1u) : 0u;
-      rise = u & ~((u << 1) | prev_msb);
-      fall = u & ~((u >> 1) | (next_lsb << 31));
-      in = x & u;
-      out = x & ~u;
+  const int64_t cap_out = ix.capacity.n_cols;
+  for (int32_t w0 = 0; w0 < nw; w0 += 4 * kThreads) {
+    const int32_t wt = w0 + 4 * tid;
+    const int32_t wend = min(nw, w0 + 4 * kThreads);  // words of this chunk: [w0, wend)
+    uint32_t rise[4], fall[4], in[4];
+    int32_t v[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int32_t w = wt + u;
+      rise[u] = fall[u] = in[u] = 0;
+      if (w < nw) {
+        const uint32_t uu = U[w], x = X[w];
+        const uint32_t prev_msb = (w > 0) ? (U[w - 1] >> 31) : 0u;
+        const uint32_t next_lsb = (w + 1 < nw) ? (U[w + 1] & 1u) : 0u;
+        rise[u] = uu & ~((uu << 1) | prev_msb);
+        fall[u] = uu & ~((uu >> 1) | (next_lsb << 31));
+        in[u] = x & uu;
+        v[3] += __popc(x & ~uu);
+      }
+      v[0] += __popc(rise[u]);
+      v[1] += __popc(fall[u]);
+      v[2] += __popc(in[u]);
     }
-    int32_t v[4] = {(int32_t)__popc(rise), (int32_t)__popc(fall), (int32_t)__popc(in), (int32_t)__popc(out)};
     int32_t tot[4];
     block_scan4(v, tot, scan_sh);
-    int64_t pr = base_rise + v[0], pf = base_fall + v[1], pi = base_in + v[2], po = base_out + v[3];
-    while (rise) {
-      int bit = __ffs(rise) - 1;
-      rise &= rise - 1;
-      if (pr < ix.capacity.n_segs) ix.seg_lo[pr] = w * 32 + bit; else overflow = true;
-      ++pr;
+    off_sh[tid] = v[3];
+    int64_t pr = base_rise + v[0], pf = base_fall + v[1], pi = base_in + v[2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int32_t wcol = (wt + u) * 32;
+      uint32_t mk = rise[u];
+      while (mk) {
+        int bit = __ffs(mk) - 1;
+        mk &= mk - 1;
+        if (pr < ix.capacity.n_segs) ix.seg_lo[pr] = wcol + bit; else overflow = true;
+        ++pr;
+      }
+      mk = fall[u];
+      while (mk) {
+        int bit = __ffs(mk) - 1;
+        mk &= mk - 1;
+        if (pf < ix.capacity.n_segs) ix.seg_hi[pf] = wcol + bit; else overflow = true;
+        ++pf;
+      }
+      mk = in[u];
+      while (mk) {
+        int bit = __ffs(mk) - 1;
+        mk &= mk - 1;
+        if (pi < ix.capacity.n_bcols) ix.bcol_idx[pi] = wcol + bit; else overflow = true;
+        ++pi;
+      }
     }
-    while (fall) {
-      int bit = __ffs(fall) - 1;
-      fall &= fall - 1;
-      if (pf < ix.capacity.n_segs) ix.seg_hi[pf] = w * 32 + bit; else overflow = true;
-      ++pf;
+    __syncthreads();  // off_sh complete
+    for (int32_t qb = 0; qb < tot[3]; qb += kSlots * kThreads) {
+      const int32_t q0 = qb + kSlots * tid;
+      if (q0 < tot[3]) {
+        // owner of slot q0: the last thread t with off_sh[t] <= q0
+        int32_t lo = 0, hi = kThreads - 1;
+        while (lo < hi) {
+          const int32_t mid = (lo + hi + 1) >> 1;
+          if (off_sh[mid] <= q0) lo = mid;
+          else hi = mid - 1;
+        }
+        int32_t k = q0 - off_sh[lo];
+        int32_t w = w0 + 4 * lo;
+        uint32_t cur = X[w] & ~U[w];
+        while (k >= __popc(cur)) {  // the slot lies in one of the owner's four words
+          k -= __popc(cur);
+          ++w;
+          cur = (w < wend) ? (X[w] & ~U[w]) : 0u;
+        }
+        for (; k > 0; --k) cur &= cur - 1;
+        const int32_t n = min(kSlots, tot[3] - q0);
+#pragma unroll
+        for (int e = 0; e < kSlots; ++e) {
+          if (e < n) {
+            while (cur == 0 && w + 1 < wend) {
+              ++w;
+              cur = X[w] & ~U[w];
+            }
+            stage[kSlots * tid + e] = w * 32 + __ffs(cur) - 1;
+            cur &= cur - 1;
+          }
+        }
+      }
+      __syncthreads();  // the round's slots are in stage, in slot order
+      const int64_t pos = base_out + qb;
+#pragma unroll
+      for (int e = 0; e < kSlots; ++e) {
+        const int32_t sidx = e * kThreads + tid;
+        if (qb + sidx < tot[3]) {
+          if (pos + sidx < cap_out) ix.col_idx[pos + sidx] = stage[sidx]; else overflow = true;
+        }
+      }
+      __syncthreads();  // stage reused by the next round
     }
-    while (in) {
-      int bit = __ffs(in) - 1;
-      in &= in - 1;
-      if (pi < ix.capacity.n_bcols) ix.bcol_idx[pi] = w * 32 + bit; else overflow = true;
-      ++pi;
-    }
-    while (out) {
-      int bit = __ffs(out) - 1;
-      out &= out - 1;
-      if (po < ix.capacity.n_cols) ix.col_idx[po] = w * 32 + bit; else overflow = true;
-      ++po;
-    }
+    __syncthreads();  // off_sh reused by the next chunk
     base_rise += tot[0];
     base_fall += tot[1];
     base_in += tot[2];
@@ -332,82 +803,291 @@ __global__ void __launch_bounds__(kThreads) k_items(sa_pattern_desc d, sa_index 
   if (overflow) atomicOr(ix.status, SA_STATUS_OVERFLOW);
 }
 
-// ---------------------------------------------------------------------------
-// Diagonal offsets as a bitmap: one thread per 32-bit word; the word's offsets
-// [32w, 32w + 31] are a contiguous slice of the sorted list, found by binary search.
-// ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(kThreads) k_dbits(sa_pattern_desc d, uint32_t* dbits, int32_t nwords) {
-  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (gid >= (int64_t)d.n_heads * nwords) return;
-  const int32_t h = (int32_t)(gid / nwords), w = (int32_t)(gid % nwords);
-  const int32_t* D = d.diag_off + d.diag_ptr[h];
-  const int32_t n = d.diag_ptr[h + 1] - d.diag_ptr[h];
-  int32_t p = upper_bound_i32(D, n, w * 32 - 1);  // first offset >= 32w
-  uint32_t bits = 0;
-  for (; p < n && D[p] < w * 32 + 32; ++p)
-    if (D[p] >= w * 32) bits |= 1u << (D[p] - w * 32);
-  dbits[gid] = bits;
+// Items per workgroup of k_items: the kinds of kGenBatch items (strided by the grid) are read at
+// once, and the workgroup builds the general ones among them one after another.
+constexpr int kGenBatch = 16;
+
+__global__ void __launch_bounds__(kThreads) k_items(sa_pattern_desc d, sa_index ix, int32_t fill, int32_t validate,
+                                                    ItemConsts kc, int32_t n_items) {
+  extern __shared__ uint32_t lds[];
+  __shared__ int32_t scan_sh[kWaves * 4];
+  __shared__ long long red_sh[kWaves * 4];
+  __shared__ int32_t off_sh[kThreads];
+
+  const int tid = threadIdx.x;
+  uint32_t* X = lds;
+  uint32_t* U = lds + kc.nwords;
+  int32_t* Dsh = reinterpret_cast<int32_t*>(lds + 2 * kc.nwords);
+  const int32_t nbatch = (int32_t)gridDim.x;
+  bool general = false;
+  if (tid < kGenBatch) {
+    const int32_t it = (int32_t)blockIdx.x + tid * nbatch;
+    if (it < n_items) {
+      const int32_t h = it / ix.n_row_blocks, rb = it - h * ix.n_row_blocks;
+      general = (ix.dbits[(int64_t)h * kc.nwords + rb] >> kKindShift) == kKindGeneral;
+    }
+  }
+  uint64_t todo = __ballot(general);  // bits of wave 0 (tid < kGenBatch <= 64)
+  __shared__ uint64_t todo_sh;
+  if (tid == 0) todo_sh = todo;
+  __syncthreads();
+  todo = todo_sh;
+
+  while (todo) {
+    const int j = __ffsll((unsigned long long)todo) - 1;
+    todo &= todo - 1;
+    const Item m = load_item(d, ix, kc, (int32_t)blockIdx.x + j * nbatch);
+    const int32_t b1 = m.b1, nw = m.nw, nD = m.nD;
+    const bool staged = nD <= kc.dcap;
+
+    // --- X from the block row, U cleared, D staged in LDS
+    for (int32_t wb = 0; wb < nw; wb += 4 * kThreads) {
+      uint32_t x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int32_t w = wb + u * kThreads + tid;
+        const int32_t blk = kc.wpb_shift >= 0 ? (w >> kc.wpb_shift) : w / kc.wpb;
+        x[u] = (m.brow != nullptr && w < nw && m.brow[blk]) ? 0xffffffffu : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int32_t w = wb + u * kThreads + tid;
+        if (w < nw) {
+          X[w] = (w == nw - 1) ? (x[u] & bit_range(0, b1 & 31)) : x[u];
+          U[w] = 0;
+        }
+      }
+    }
+    if (staged) {
+      for (int32_t pb = 0; pb < nD; pb += 8 * kThreads) {
+        int32_t r[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int32_t p = pb + u * kThreads + tid;
+          r[u] = p < nD ? m.D[p] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int32_t p = pb + u * kThreads + tid;
+          if (p < nD) Dsh[p] = r[u];
+        }
+      }
+    }
+    __syncthreads();
+    if (staged)
+      items_body<true>(d, ix, fill, validate, kc, m, Dsh, X, U, scan_sh, red_sh, off_sh, Dsh);
+    else
+      items_body<false>(d, ix, fill, validate, kc, m, m.D, X, U, scan_sh, red_sh, off_sh, Dsh);
+    __syncthreads();  // LDS reused by the next item
+  }
 }
 
 // ---------------------------------------------------------------------------
-// In-place inclusive scan of entries 1..n of the three item pointer arrays
-// (entry 0 is 0), so that ptr[it] is the first element of item it.
+// Scans of the item pointer arrays: entries 1..n hold per-item counts (entry 0
+// becomes 0); afterwards ptr[it] is the first element of item it.  Three passes
+// over chunks of kScanChunk entries, in place:
+//   local   each chunk scanned on its own (its last entry is then the chunk total)
+//   offset  every entry but a chunk's last gets the sum of the earlier chunk totals
+//   fix     one workgroup adds the same sums to the chunks' last entries, scans the
+//           per-head run counts into run_ptr and folds invalid-head marks into status
 // ---------------------------------------------------------------------------
-constexpr int kScanThreads = 1024;
+__device__ inline int64_t* pick(int64_t* a0, int64_t* a1, int64_t* a2, int which) {
+  return which == 0 ? a0 : (which == 1 ? a1 : a2);
+}
 
-__global__ void __launch_bounds__(kScanThreads) k_scan(int64_t* a0, int64_t* a1, int64_t* a2, int64_t n) {
-  __shared__ long long part[kScanThreads];
-  int64_t* arrs[3] = {a0, a1, a2};
-  const int tid = threadIdx.x;
-  const int64_t per = cdiv64(n, kScanThreads);
-  const int64_t s = 1 + tid * per, e = min(n + 1, s + per);
-  for (int c = 0; c < 3; ++c) {
-    int64_t* a = arrs[c];
-    long long local = 0;
-    for (int64_t p = s; p < e; ++p) local += a[p];
-    part[tid] = local;
-    __syncthreads();
-    for (int o = 1; o < kScanThreads; o <<= 1) {
-      long long y = (tid >= o) ? part[tid - o] : 0;
-      __syncthreads();
-      part[tid] += y;
-      __syncthreads();
-    }
-    long long run = part[tid] - local;
-    for (int64_t p = s; p < e; ++p) {
-      run += a[p];
-      a[p] = run;
-    }
-    __syncthreads();
+__global__ void __launch_bounds__(kThreads) k_scan_local(int64_t* a0, int64_t* a1, int64_t* a2, int64_t n) {
+  __shared__ long long sh[kWaves];
+  int64_t* a = pick(a0, a1, a2, blockIdx.y);
+  const int64_t c = blockIdx.x;
+  const int64_t end = min(n, (c + 1) * kScanChunk);
+  const int64_t base = 1 + c * kScanChunk + (int64_t)threadIdx.x * kScanPer;
+  long long v[kScanPer], s = 0;
+#pragma unroll
+  for (int u = 0; u < kScanPer; ++u) v[u] = (base + u <= end) ? a[base + u] : 0;
+#pragma unroll
+  for (int u = 0; u < kScanPer; ++u) s += v[u];
+  long long tot;
+  long long run = block_exscan<long long>(s, &tot, sh);
+#pragma unroll
+  for (int u = 0; u < kScanPer; ++u) {
+    run += v[u];
+    if (base + u <= end) a[base + u] = run;
   }
+}
+
+__global__ void __launch_bounds__(kThreads) k_scan_offset(int64_t* a0, int64_t* a1, int64_t* a2, int64_t n) {
+  __shared__ long long sh[kWaves];
+  const int64_t c = blockIdx.x;
+  if (c == 0) return;
+  int64_t* a = pick(a0, a1, a2, blockIdx.y);
+  long long part = 0;
+  for (int64_t cc = threadIdx.x; cc < c; cc += kThreads) part += a[(cc + 1) * kScanChunk];  // full chunks
+  const long long off = block_sum<long long>(part, sh);
+  const int64_t end = min(n, (c + 1) * kScanChunk);
+  const int64_t base = 1 + c * kScanChunk + (int64_t)threadIdx.x * kScanPer;
+#pragma unroll
+  for (int u = 0; u < kScanPer; ++u)
+    if (base + u < end) a[base + u] += off;
+}
+
+__global__ void __launch_bounds__(kThreads) k_scan_fix(int64_t* a0, int64_t* a1, int64_t* a2, int64_t n,
+                                                       int32_t* run_ptr, int32_t n_heads, int32_t* status) {
+  __shared__ long long sh[kWaves];
+  __shared__ int32_t sh32[kWaves];
+  const int tid = threadIdx.x;
+  const int64_t C = cdiv64(n, kScanChunk);
+  for (int which = 0; which < 3; ++which) {
+    int64_t* a = pick(a0, a1, a2, which);
+    long long carry = 0;
+    for (int64_t cb = 0; cb < C; cb += kThreads) {
+      const int64_t c = cb + tid;
+      const int64_t e = min(n, (c + 1) * kScanChunk);
+      const long long t = c < C ? a[e] : 0;
+      long long tot;
+      const long long ex = block_exscan<long long>(t, &tot, sh);
+      if (c < C) a[e] = carry + ex + t;
+      carry += tot;
+    }
+    if (tid == 0) a[0] = 0;
+  }
+  int32_t carry = 0, bad = 0;
+  for (int32_t hb = 0; hb < n_heads; hb += kThreads) {
+    const int32_t hh = hb + tid;
+    int32_t v = hh < n_heads ? run_ptr[hh + 1] : 0;
+    bad |= v & kBadHead;
+    v &= ~kBadHead;
+    int32_t tot;
+    const int32_t ex = block_exscan<int32_t>(v, &tot, sh32);
+    if (hh < n_heads) run_ptr[hh + 1] = carry + ex + v;
+    carry += tot;
+  }
+  bad = block_sum<int32_t>(bad ? 1 : 0, sh32);
+  if (tid == 0 && bad) atomicOr(status, SA_STATUS_DESC_INVALID);
+}
+
+// ---------------------------------------------------------------------------
+// Per head, after the fill: pair_count[h] from the items' scratch slots in dbits
+// row h, then the D bitmap over that row (built in LDS), then the maximal runs of
+// D at run_ptr[h] (run_ptr already scanned).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kThreads) k_heads_fill(sa_pattern_desc d, sa_index ix, int32_t nwords) {
+  extern __shared__ uint32_t bits[];  // [nwords]
+  __shared__ int32_t sh[kWaves];
+  __shared__ long long shl[kWaves];
+  const int tid = threadIdx.x;
+  const int32_t h = blockIdx.x, S = d.S, nb = ix.n_row_blocks;
+  uint32_t* row = ix.dbits + (int64_t)h * nwords;
+  long long pairs = 0;
+  for (int32_t rb = tid; rb < nb; rb += kThreads) pairs += row[rb] & kPairsMask;
+  for (int32_t w = tid; w < nwords; w += kThreads) bits[w] = 0;
+  pairs = block_sum<long long>(pairs, shl);  // its barriers: every slot read, bitmap cleared
+  if (tid == 0) ix.pair_count[h] = pairs;
+
+  const int32_t p0 = d.diag_ptr[h], p1 = d.diag_ptr[h + 1];
+  for (int32_t p = p0 + tid; p < p1; p += kThreads) {
+    const int32_t r = d.diag_off[p];
+    if (r >= 0 && r < S) atomicOr(&bits[r >> 5], 1u << (r & 31));
+  }
+  __syncthreads();
+  for (int32_t w = tid; w < nwords; w += kThreads) row[w] = bits[w];
+
+  int64_t base = ix.run_ptr[h];
+  bool overflow = false;
+  for (int32_t pb = p0; pb < p1; pb += kThreads) {
+    const int32_t p = pb + tid;
+    const bool in = p < p1;
+    int32_t r = 0, prev = 0, next = 0;
+    if (in) {
+      r = d.diag_off[p];
+      if (p > p0) prev = d.diag_off[p - 1];
+      if (p + 1 < p1) next = d.diag_off[p + 1];
+    }
+    const bool st = in && (p == p0 || starts_run(r, prev));
+    const bool en = in && (p + 1 == p1 || starts_run(next, r));
+    int32_t tot;
+    const int32_t ex = block_exscan<int32_t>(st ? 1 : 0, &tot, sh);
+    const int64_t idx = base + ex + (st ? 1 : 0) - 1;  // the run that holds offset p
+    if (st) {
+      if (idx < ix.capacity.n_runs) ix.run_lo[idx] = r; else overflow = true;
+    }
+    if (en) {
+      if (idx >= 0 && idx < ix.capacity.n_runs) ix.run_hi[idx] = r; else overflow = true;
+    }
+    base += tot;
+  }
+  if (overflow) atomicOr(ix.status, SA_STATUS_OVERFLOW);
 }
 
 }  // namespace
 
-hipError_t launch_index_runs(const sa_pattern_desc& d, const sa_index& ix, int32_t validate, hipStream_t stream) {
-  hipLaunchKernelGGL(k_runs, dim3(1), dim3(kThreads), 0, stream, d, ix, validate);
+hipError_t launch_index_heads(const sa_pattern_desc& d, const sa_index& ix, int32_t validate, hipStream_t stream) {
+  hipLaunchKernelGGL(k_heads, dim3(d.n_heads), dim3(kThreads), 0, stream, d, ix, validate);
   return hipGetLastError();
 }
 
 hipError_t launch_index_items(const sa_pattern_desc& d, const sa_index& ix, int32_t fill, int32_t validate,
                               hipStream_t stream) {
   const int64_t items = (int64_t)ix.n_heads * ix.n_row_blocks;
-  const size_t lds = 2 * sizeof(uint32_t) * (size_t)(((d.S - 1) >> 5) + 1);
-  hipLaunchKernelGGL(k_items, dim3((unsigned)items), dim3(kThreads), lds, stream, d, ix, fill, validate);
-  return hipGetLastError();
-}
-
-hipError_t launch_index_dbits(const sa_pattern_desc& d, const sa_index& ix, hipStream_t stream) {
-  const int32_t nwords = ((d.S - 1) >> 5) + 1;
-  const int64_t total = (int64_t)d.n_heads * nwords;
-  hipLaunchKernelGGL(k_dbits, dim3((unsigned)((total + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream, d,
-                     ix.dbits, nwords);
+  ItemConsts kc{};
+  kc.nwords = ((d.S - 1) >> 5) + 1;
+  const size_t bitmaps = 2 * sizeof(uint32_t) * (size_t)kc.nwords;
+  kc.dcap = kDsh;  // staged diagonal offsets (count pass) / gathered-column stage (fill pass)
+  kc.nbq = 0;
+  kc.rb_per_br = 1;
+  kc.wpb = 1;
+  kc.wpb_shift = 0;
+  kc.bs = 64;
+  if (d.block_mask != nullptr) {
+    kc.bs = d.block_size;
+    kc.nbq = (d.S + d.block_size - 1) / d.block_size;
+    kc.rb_per_br = d.block_size / ix.row_block;
+    kc.wpb = d.block_size / 32;
+    kc.wpb_shift = -1;
+    for (int s = 0; s < 31; ++s)
+      if ((1 << s) == kc.wpb) kc.wpb_shift = s;
+  }
+  kc.nst = 0;
+  kc.rb_per_st = 1;
+  if (d.stripe_ptr != nullptr) {
+    kc.nst = (d.S + d.stripe_rows - 1) / d.stripe_rows;
+    kc.rb_per_st = d.stripe_rows / ix.row_block;
+  }
+  const size_t lds = bitmaps + sizeof(int32_t) * (size_t)kDsh;
+  if (lds > kDefaultLds) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_items),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_items_lists, dim3((unsigned)items), dim3(kThreads), 0, stream, d, ix, fill, validate, kc);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned gen_grid = (unsigned)((items + kGenBatch - 1) / kGenBatch);
+  hipLaunchKernelGGL(k_items, dim3(gen_grid), dim3(kThreads), lds, stream, d, ix, fill, validate, kc, (int32_t)items);
   return hipGetLastError();
 }
 
 hipError_t launch_index_scan(const sa_index& ix, hipStream_t stream) {
   const int64_t items = (int64_t)ix.n_heads * ix.n_row_blocks;
-  hipLaunchKernelGGL(k_scan, dim3(1), dim3(kScanThreads), 0, stream, ix.seg_ptr, ix.bcol_ptr, ix.col_ptr, items);
+  const unsigned chunks = (unsigned)((items + kScanChunk - 1) / kScanChunk);
+  hipLaunchKernelGGL(k_scan_local, dim3(chunks, 3), dim3(kThreads), 0, stream, ix.seg_ptr, ix.bcol_ptr, ix.col_ptr,
+                     items);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (chunks > 1) {
+    hipLaunchKernelGGL(k_scan_offset, dim3(chunks, 3), dim3(kThreads), 0, stream, ix.seg_ptr, ix.bcol_ptr,
+                       ix.col_ptr, items);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_scan_fix, dim3(1), dim3(kThreads), 0, stream, ix.seg_ptr, ix.bcol_ptr, ix.col_ptr, items,
+                     ix.run_ptr, ix.n_heads, ix.status);
+  return hipGetLastError();
+}
+
+hipError_t launch_index_heads_fill(const sa_pattern_desc& d, const sa_index& ix, hipStream_t stream) {
+  const int32_t nwords = ((d.S - 1) >> 5) + 1;
+  hipLaunchKernelGGL(k_heads_fill, dim3(d.n_heads), dim3(kThreads), sizeof(uint32_t) * (size_t)nwords, stream, d,
+                     ix, nwords);
   return hipGetLastError();
 }
 

@@ -12,12 +12,13 @@ constexpr int32_t kMaxIndexS = 262144;
 // Largest capture window (two int32 hit arrays of L entries live in LDS).
 constexpr int32_t kMaxCaptureL = 4096;
 
-// Index builder (sa_index.hip).  All launches go on `stream`.
-hipError_t launch_index_runs(const sa_pattern_desc& d, const sa_index& ix, int32_t validate, hipStream_t stream);
+// Index builder (sa_index.hip).  All launches go on `stream`.  Order of a build: heads, items (count),
+// scan, [size query], items (fill), heads (fill).
+hipError_t launch_index_heads(const sa_pattern_desc& d, const sa_index& ix, int32_t validate, hipStream_t stream);
 hipError_t launch_index_items(const sa_pattern_desc& d, const sa_index& ix, int32_t fill, int32_t validate,
                               hipStream_t stream);
 hipError_t launch_index_scan(const sa_index& ix, hipStream_t stream);
-hipError_t launch_index_dbits(const sa_pattern_desc& d, const sa_index& ix, hipStream_t stream);
+hipError_t launch_index_heads_fill(const sa_pattern_desc& d, const sa_index& ix, hipStream_t stream);
 
 // Attention (sa_attn.hip).
 struct AttnArgs {

@@ -16,17 +16,20 @@ KEYS = ("run_ptr", "run_lo", "run_hi", "seg_ptr", "seg_lo", "seg_hi", "bcol_ptr"
 
 
 def _compare(desc, BM, what):
+    """Both build modes (with and without descriptor validation) against the oracle index."""
     note("index %s S=%d H=%d BM=%d" % (what, desc.S, desc.H, BM))
     m = sa()
     pat = m.DevicePatterns.from_host(desc)
-    ix = m.build_index(pat, BM, validate=True)
-    torch.cuda.synchronize()
-    assert int(ix.status.item()) == 0
-    got = ix.to_numpy()
     ref = oracle.build_index(desc, BM)
-    for k in KEYS:
-        np.testing.assert_array_equal(np.asarray(got[k]).astype(np.int64), np.asarray(ref[k]).astype(np.int64),
-                                      err_msg="%s: %s" % (what, k))
+    for validate in (True, False):
+        ix = m.build_index(pat, BM, validate=validate)
+        m.refill_index(pat, ix)   # a second build into the same arrays gives the same index
+        torch.cuda.synchronize()
+        assert int(ix.status.item()) == 0
+        got = ix.to_numpy()
+        for k in KEYS:
+            np.testing.assert_array_equal(np.asarray(got[k]).astype(np.int64), np.asarray(ref[k]).astype(np.int64),
+                                          err_msg="%s (validate=%s): %s" % (what, validate, k))
 
 
 @pytest.mark.parametrize("variant", ["base", "dense_causal", "all_ones", "diag0"])
@@ -79,6 +82,71 @@ def test_index_mixed_all_kinds():
     d = W.desc_from_lists(S, diags, verts, block_mask=bm, block_size=128, stripes=stripes, stripe_rows=256)
     for BM in (64, 128):
         _compare(d, BM, "mixed")
+
+
+@pytest.mark.parametrize("BM", [64, 128])
+def test_index_block_only_heads(BM):
+    """Heads whose rows hold only block-mask columns: block size 128 over 64-row blocks, a ragged last
+    block, rows with no set block below the diagonal, and an all-zero head next to a dense one."""
+    rng = np.random.default_rng(31)
+    S, H, bs = 2000, 4, 128
+    nbq = -(-S // bs)
+    bm = np.tril(rng.random((H, nbq, nbq)) < 0.3).astype(np.uint8)
+    bm[1] = 0
+    bm[2] = np.tril(np.ones((nbq, nbq), np.uint8))
+    bm[3, 5] = 0
+    d = W.desc_from_lists(S, [np.zeros(0)] * H, [np.zeros(0)] * H, block_mask=bm, block_size=bs)
+    _compare(d, BM, "blocks-only")
+
+
+@pytest.mark.parametrize("BM", [64, 128])
+def test_index_stripe_only_heads(BM):
+    """Stripe lists longer than the row block: with 256-row stripes, the first row block of a stripe sees
+    only the list's columns up to its own last row; empty lists and lists of a single column."""
+    rng = np.random.default_rng(32)
+    S, H, sr = 3000, 3, 256
+    nst = -(-S // sr)
+    stripes = []
+    for h in range(H):
+        per = []
+        for t in range(nst):
+            top = min(S, (t + 1) * sr) - 1
+            k = int(rng.integers(0, 3)) if h == 1 else int(rng.integers(1, top + 2))
+            per.append(np.sort(rng.choice(top + 1, size=min(k, top + 1), replace=False)))
+        stripes.append(per)
+    d = W.desc_from_lists(S, [np.zeros(0)] * H, [np.zeros(0)] * H, stripes=stripes, stripe_rows=sr)
+    _compare(d, BM, "stripes-only")
+
+
+@pytest.mark.parametrize("BM", [64, 128])
+def test_index_diagonal_runs_merge(BM):
+    """Diagonal runs whose column intervals merge or stay apart by one column, runs clipped at column 0,
+    verticals inside and outside the band, and a head with more offsets than fit in LDS."""
+    S = 5000
+    diags = [np.concatenate([np.arange(0, 10), np.arange(10 + BM, 20 + BM), np.arange(21 + 2 * BM, 30 + 2 * BM),
+                             [700, 701, 900]]),
+             np.arange(0, S, 3),
+             np.arange(S),
+             np.array([4999])]
+    verts = [np.array([0, 5, 100, 2500, 4999]), np.array([1, 2, 3]), np.arange(0, S, 7), np.zeros(0)]
+    d = W.desc_from_lists(S, diags, verts)
+    _compare(d, BM, "diag-runs")
+
+
+def test_index_unsorted_stripe_list_stays_in_range():
+    """An unsorted stripe list (an invalid descriptor) built without validation: every column the index
+    holds is still a valid key column of its row block."""
+    m = sa()
+    S = 512
+    stripes = [[np.array([300, 5, 100]), np.array([1, 2]), np.array([400, 3]), np.array([7])]]
+    d = W.desc_from_lists(S, [np.zeros(0)], [np.zeros(0)], stripes=stripes, stripe_rows=128)
+    pat = m.DevicePatterns.from_host(d)
+    ix = m.build_index(pat, 128)
+    torch.cuda.synchronize()
+    got = ix.to_numpy()
+    for rb in range(4):
+        cols = got["col_idx"][got["col_ptr"][rb]:got["col_ptr"][rb + 1]]
+        assert np.all((cols >= 0) & (cols <= min(S, 128 * rb + 128) - 1))
 
 
 def test_index_rejects_invalid_descriptor():
