@@ -25,9 +25,8 @@
 // that each lane's 8 keys are 16 contiguous bytes.  Softmax is the online
 // (running max / running sum) form in fp32 with exp2 and a pre-multiplied
 // log2(e) scale; the O rescale is skipped when no row max moved.
-// Block order: row blocks in descending order (longest causal work first), and,
-// when batch*hkv is a multiple of 8, the work of one kv head stays on one XCD
-// (workgroup k runs on XCD k % 8), so one XCD's L2 serves one kv head's K/V.
+// Block order (decode_item): kv groups one after another across the whole chip,
+// neighbouring row blocks of a group on one XCD, heaviest row blocks first.
 #include <type_traits>
 
 #include "sa_internal.h"
@@ -111,12 +110,28 @@ struct Cfg {
   using elem = typename std::conditional<BF16, unsigned short, float>::type;
 };
 
-// Work-item decode: blockIdx -> (batch, head, row block).
+// Work-item decode: blockIdx -> (batch, head, row block).  Workgroup k runs on XCD k % 8.
+// When the row blocks split into 8 * kChunk-block pieces, the kv groups are taken one after
+// another by all eight XCDs together (one group's K/V, 32 MiB at S = 64K and d = 128, is what the
+// whole chip reads at a time), each XCD taking chunks of kChunk neighbouring row blocks (which
+// share band tiles in its L2), chunks dealt round-robin, heaviest (last) row blocks first, and
+// the heads of a group innermost.  Otherwise, when batch * hkv is a multiple of 8, each XCD owns
+// whole kv groups; else plain descending row-block order.
+constexpr int kChunk = 4;
+
 __device__ inline void decode_item(const Params& p, int& b, int& h, int& rb) {
   const int k = blockIdx.x;
   const int G = p.B * p.hkv, hpg = p.hq / p.hkv;
-  if ((G & 7) == 0) {
-    const int x = k & 7, s = k >> 3;
+  const int x = k & 7, s = k >> 3;
+  if (p.nb % (8 * kChunk) == 0) {
+    const int per_xcd_group = (p.nb / 8) * hpg;  // items of one kv group on one XCD
+    const int g = s / per_xcd_group, r = s % per_xcd_group;
+    const int cl = r / (kChunk * hpg), rr = r % (kChunk * hpg);
+    const int c = p.nb / kChunk - 1 - (cl * 8 + x);
+    rb = c * kChunk + (kChunk - 1 - rr / hpg);
+    b = g / p.hkv;
+    h = (g % p.hkv) * hpg + rr % hpg;
+  } else if ((G & 7) == 0) {
     const int gper = G >> 3;
     const int per_rb = gper * hpg;
     rb = p.nb - 1 - s / per_rb;
