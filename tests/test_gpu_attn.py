@@ -104,6 +104,16 @@ def test_batch_and_gqa_and_custom_scale():
     _run(desc, q, k, v, 64, all_rows(2, 6, S), "batch-gqa-scale", scale=0.2)
 
 
+@pytest.mark.parametrize("dtype,d,BM", [("bf16", 64, 64), ("bf16", 128, 128), ("f32", 64, 64)])
+def test_group_major_schedule_every_row(dtype, d, BM):
+    """Row-block counts that are a multiple of 32 take the kv-group-major workgroup order: with two batch
+    elements, GQA 6/3 and every row checked, each (batch, head, row block) must be computed exactly once."""
+    S = 32 * BM
+    desc = W.llama1b_like(S=S, H=6)
+    q, k, v = W.qkv(17, 2, 6, 3, S, d, dtype)
+    _run(desc, q, k, v, BM, all_rows(2, 6, S), "group-major")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("BM", [64, 128])
 def test_band_edges_partial_tiles(d, BM):
