@@ -12,9 +12,9 @@
 // A build is nine launches, all on one stream:
 //   k_heads         one workgroup per head: validation of D and C, the run count of D,
 //                   reset of status
-//   k_items_lists   one workgroup per (head, row block), count pass: classifies the item
-//                   and counts the items that need no bitmap (block columns only, a stripe
-//                   list only, or diagonals and verticals)
+//   k_items_lists   one wave per (head, row block), count pass: classifies the item and
+//                   counts the items that need no bitmap (block columns only, a stripe list
+//                   only, or diagonals and verticals)
 //   k_items         count pass of the other items (bitmaps in LDS)
 //   k_scan_local  |
 //   k_scan_offset | exclusive scans of the per-item counts and of the per-head run
@@ -307,35 +307,90 @@ __device__ inline int32_t count_in(const int32_t* D, int32_t nD, int32_t lo, int
   return hi < lo ? 0 : upper_bound_i32(D, nD, hi) - upper_bound_i32(D, nD, lo - 1);
 }
 
+// Wave-level helpers of k_items_lists (one item per wave, no workgroup barrier).
+__device__ inline long long wave_sum(long long x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+// number of lanes below this one whose flag is set
+__device__ inline int lanes_below(uint64_t mask) {
+  const int lane = threadIdx.x & 63;
+  return __popcll(mask & ((1ull << lane) - 1ull));
+}
+// LDS written by some lanes of this wave becomes visible to every lane of it
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Items per workgroup of k_items_lists (one per wave) and diagonal offsets staged per wave.
+constexpr int kListWaves = 4;
+constexpr int kDshWave = 1536;
+
+// Lane 0 stores the four item counters and the scratch slot.
+__device__ inline void store_counts_wave(const sa_index& ix, const ItemConsts& kc, const Item& m, long long cnt[4],
+                                         uint32_t kind) {
+  long long t[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) t[c] = wave_sum(cnt[c]);
+  if ((threadIdx.x & 63) == 0) {
+    ix.seg_ptr[m.it + 1] = t[0];
+    ix.bcol_ptr[m.it + 1] = t[1];
+    ix.col_ptr[m.it + 1] = t[2];
+    *scratch_slot(ix, kc, m) = ((uint32_t)t[3] & kPairsMask) | (kind << kKindShift);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Item kinds with no bitmap (blocks only, stripes only, diagonals + verticals).
-// One workgroup per (head, row block); the count pass (fill = 0) classifies the
-// item and, for a kKindGeneral item, only records that in its scratch slot.
+// One wave per (head, row block), kListWaves items per workgroup; the waves never
+// wait for each other.  The count pass (fill = 0) classifies the item and, for a
+// kKindGeneral item, only records that in its scratch slot.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(kThreads) k_items_lists(sa_pattern_desc d, sa_index ix, int32_t fill,
-                                                          int32_t validate, ItemConsts kc) {
-  __shared__ int32_t Dsh[kDsh];
-  __shared__ int32_t list_sh[kThreads * 4];
-  __shared__ long long red_sh[kWaves * 4];
-  __shared__ int32_t sh32[kWaves];
-  __shared__ int64_t bound_sh[2];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const Item m = load_item(d, ix, kc, blockIdx.x);
+__global__ void __launch_bounds__(64 * kListWaves) k_items_lists(sa_pattern_desc d, sa_index ix, int32_t fill,
+                                                                 int32_t validate, ItemConsts kc, int32_t n_items) {
+  __shared__ int32_t Dsh_all[kListWaves][kDshWave];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int32_t it = (int32_t)blockIdx.x * kListWaves + wave;
+  if (it >= n_items) return;  // the whole wave leaves; nothing below waits for other waves
+  const Item m = load_item(d, ix, kc, it);
   const int32_t S = d.S, b0 = m.b0, b1 = m.b1;
+  int32_t* Dsh = Dsh_all[wave];
 
   uint32_t kind;
+  long long blk_cols = 0, blk_pairs = 0;  // the block-mask columns' counts, used if the item is block-only
   if (!fill) {
     int any = 0;
-    if (m.brow != nullptr)
-      for (int32_t cb = tid; cb <= m.cb1; cb += kThreads) any |= m.brow[cb];
-    const bool has_blk = __syncthreads_or(any) != 0;
+    if (m.brow != nullptr) {
+      const int32_t bs = kc.bs;
+      for (int32_t cbase = 0; cbase <= m.cb1; cbase += 8 * 64) {  // eight loads in flight per lane
+        uint8_t f[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int32_t cb = cbase + u * 64 + lane;
+          f[u] = cb <= m.cb1 ? m.brow[cb] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (f[u]) {
+            const int32_t c0 = (cbase + u * 64 + lane) * bs, c1 = min(b1, c0 + bs - 1);
+            any = 1;
+            blk_cols += c1 - c0 + 1;
+            blk_pairs += column_pairs(c0, c1, b0, b1);
+          }
+        }
+      }
+    }
+    const bool has_blk = __ballot(any != 0) != 0ull;
     const bool has_vert = m.vp1 > m.vp0, has_str = m.sp1 > m.sp0, has_diag = m.nD > 0;
     if (has_blk && !has_diag && !has_vert && !has_str) kind = kKindBlocks;
     else if (has_str && !has_blk && !has_diag && !has_vert) kind = kKindStripes;
-    else if (!has_blk && !has_str && m.nD <= kc.dcap) kind = kKindLists;
+    else if (!has_blk && !has_str && m.nD <= kDshWave) kind = kKindLists;
     else kind = kKindGeneral;
     if (kind == kKindGeneral) {
-      if (tid == 0) *scratch_slot(ix, kc, m) = kKindGeneral << kKindShift;
+      if (lane == 0) *scratch_slot(ix, kc, m) = kKindGeneral << kKindShift;
       return;
     }
   } else {
@@ -349,80 +404,70 @@ __global__ void __launch_bounds__(kThreads) k_items_lists(sa_pattern_desc d, sa_
   if (kind == kKindBlocks) {
     const int32_t bs = kc.bs;
     if (!fill) {
-      for (int32_t cb = tid; cb <= m.cb1; cb += kThreads) {
-        if (m.brow[cb]) {
-          const int32_t c0 = cb * bs, c1 = min(b1, c0 + bs - 1);
-          cnt[2] += c1 - c0 + 1;
-          cnt[3] += column_pairs(c0, c1, b0, b1);
-        }
-      }
-      store_counts(ix, kc, m, cnt, kind, red_sh);
+      cnt[2] = blk_cols;
+      cnt[3] = blk_pairs;
+      store_counts_wave(ix, kc, m, cnt, kind);
       return;
     }
-    // fill: every set block but the last is full, so block k of the row (in order) starts at k * bs;
-    // the set blocks of each chunk are listed in LDS and each wave writes whole blocks, lane by column
-    int64_t base = ix.col_ptr[m.it];
+    // fill: every set block but the last is full, so set block k of the row (in order) starts at
+    // output k * bs; the wave writes one block at a time, lane by column (coalesced)
+    const int64_t base = ix.col_ptr[m.it];
     const int64_t cap = ix.capacity.n_cols;
-    for (int32_t cbase = 0; cbase <= m.cb1; cbase += 4 * kThreads) {
-      int32_t mine = 0;
-      uint8_t f[4];
+    int64_t done = 0;  // set blocks before the current chunk of 64 block columns
+    for (int32_t cbase = 0; cbase <= m.cb1; cbase += 8 * 64) {  // eight loads in flight per lane
+      uint8_t f[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int32_t cb = cbase + 4 * tid + u;
+      for (int u = 0; u < 8; ++u) {
+        const int32_t cb = cbase + u * 64 + lane;
         f[u] = cb <= m.cb1 ? m.brow[cb] : 0;
-        mine += f[u] ? 1 : 0;
       }
-      int32_t tot;
-      int32_t r = block_exscan<int32_t>(mine, &tot, sh32);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (f[u]) list_sh[r++] = cbase + 4 * tid + u;
-      __syncthreads();
-      for (int32_t e = wave; e < tot; e += kWaves) {
-        const int32_t c0 = list_sh[e] * bs, c1 = min(b1, c0 + bs - 1);
-        const int64_t out = base + (int64_t)e * bs;
-        for (int32_t c = c0 + lane; c <= c1; c += 64) {
-          const int64_t pos = out + (c - c0);
-          if (pos < cap) ix.col_idx[pos] = c; else overflow = true;
+      for (int u = 0; u < 8; ++u) {
+        const uint64_t set0 = __ballot(f[u] != 0);
+        uint64_t set = set0;
+        while (set) {
+          const int j = __ffsll((unsigned long long)set) - 1;
+          const int64_t k = done + __popcll(set0 & ((1ull << j) - 1ull));  // set blocks before this one
+          set &= set - 1;
+          const int32_t c0 = (cbase + u * 64 + j) * bs, c1 = min(b1, c0 + bs - 1);
+          for (int32_t c = c0 + lane; c <= c1; c += 64) {
+            const int64_t pos = base + k * bs + (c - c0);
+            if (pos < cap) ix.col_idx[pos] = c; else overflow = true;
+          }
         }
+        done += __popcll(set0);
       }
-      __syncthreads();
-      base += (int64_t)tot * bs;
     }
   } else if (kind == kKindStripes) {
     if (!fill && !validate) {
       // sorted list: entries below b0 each give every row; the few in [b0, b1] are summed one by one
       const int64_t len = m.sp1 - m.sp0;
-      if (wave < 2) {
-        const int64_t n = wave_upper_bound(d.stripe_col + m.sp0, len, wave == 0 ? b1 : b0 - 1);
-        if (lane == 0) bound_sh[wave] = n;
-      }
-      __syncthreads();
-      const int64_t n_le = bound_sh[0], n_lt = bound_sh[1];
-      if (tid == 0) {
+      const int64_t n_le = wave_upper_bound(d.stripe_col + m.sp0, len, b1);
+      const int64_t n_lt = wave_upper_bound(d.stripe_col + m.sp0, n_le, b0 - 1);
+      if (lane == 0) {
         cnt[2] = n_le;
         cnt[3] = n_lt * (long long)(b1 - b0 + 1);
       }
-      for (int64_t q = n_lt + tid; q < n_le; q += kThreads) {
+      for (int64_t q = n_lt + lane; q < n_le; q += 64) {
         const int32_t c = d.stripe_col[m.sp0 + q];
         cnt[3] += b1 - max(c, b0) + 1;
       }
-      store_counts(ix, kc, m, cnt, kind, red_sh);
+      store_counts_wave(ix, kc, m, cnt, kind);
       return;
     }
     if (!fill) {
-      for (int64_t pb = m.sp0; pb < m.sp1; pb += 8 * kThreads) {
+      for (int64_t pb = m.sp0; pb < m.sp1; pb += 8 * 64) {
         int32_t c[8], prev[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int64_t p = pb + u * kThreads + tid;
+          const int64_t p = pb + u * 64 + lane;
           c[u] = p < m.sp1 ? d.stripe_col[p] : -1;
-          prev[u] = (validate && p < m.sp1 && p > m.sp0) ? d.stripe_col[p - 1] : -1;
+          prev[u] = (p < m.sp1 && p > m.sp0) ? d.stripe_col[p - 1] : -1;
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int64_t p = pb + u * kThreads + tid;
-          if (validate && p < m.sp1 && (c[u] < 0 || c[u] >= S || (p > m.sp0 && prev[u] >= c[u]))) bad = true;
+          const int64_t p = pb + u * 64 + lane;
+          if (p < m.sp1 && (c[u] < 0 || c[u] >= S || (p > m.sp0 && prev[u] >= c[u]))) bad = true;
           if (c[u] >= 0 && c[u] <= b1) {
             cnt[2] += 1;
             cnt[3] += b1 - max(c[u], b0) + 1;
@@ -430,22 +475,22 @@ __global__ void __launch_bounds__(kThreads) k_items_lists(sa_pattern_desc d, sa_
         }
       }
       if (bad) atomicOr(ix.status, SA_STATUS_DESC_INVALID);
-      store_counts(ix, kc, m, cnt, kind, red_sh);
+      store_counts_wave(ix, kc, m, cnt, kind);
       return;
     }
     // fill: the columns <= b1 of a sorted list are its first n entries
     const int64_t base = ix.col_ptr[m.it], n = ix.col_ptr[m.it + 1] - base;
     const int64_t cap = ix.capacity.n_cols;
-    for (int64_t qb = 0; qb < n; qb += 8 * kThreads) {
+    for (int64_t qb = 0; qb < n; qb += 8 * 64) {
       int32_t c[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int64_t q = qb + u * kThreads + tid;
+        const int64_t q = qb + u * 64 + lane;
         c[u] = q < n ? d.stripe_col[m.sp0 + q] : 0;
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int64_t q = qb + u * kThreads + tid;
+        const int64_t q = qb + u * 64 + lane;
         if (q < n) {
           int32_t col = c[u];
           if (col < 0 || col > b1) {  // only an unsorted list gets here; keep every column in range
@@ -458,20 +503,20 @@ __global__ void __launch_bounds__(kThreads) k_items_lists(sa_pattern_desc d, sa_
     }
   } else {  // kKindLists
     const int32_t nD = m.nD;
-    for (int32_t pb = 0; pb < nD; pb += 8 * kThreads) {
+    for (int32_t pb = 0; pb < nD; pb += 8 * 64) {
       int32_t r[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int32_t p = pb + u * kThreads + tid;
+        const int32_t p = pb + u * 64 + lane;
         r[u] = p < nD ? m.D[p] : 0;
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int32_t p = pb + u * kThreads + tid;
+        const int32_t p = pb + u * 64 + lane;
         if (p < nD) Dsh[p] = r[u];
       }
     }
-    __syncthreads();
+    wave_lds_sync();
     // A run [lo, hi] of D (lo <= b1) touches key columns I = [max(0, b0 - hi), b1 - lo] (clipped to
     // [0, b1]); runs in descending offset order give intervals in ascending column order, and U's
     // segments are the merged intervals.  The run with the next larger offsets starts at index q + 1
@@ -501,17 +546,17 @@ __global__ void __launch_bounds__(kThreads) k_items_lists(sa_pattern_desc d, sa_
     };
 
     if (!fill) {
-      for (int32_t p = tid; p < nD; p += kThreads) {
+      for (int32_t p = lane; p < nD; p += 64) {
         bool st, en;
         int32_t s0, s1;
         seg_flags(p, st, en, s0, s1);
         cnt[0] += st ? 1 : 0;
       }
-      for (int32_t pb = m.vp0; pb < m.vp1; pb += 8 * kThreads) {
+      for (int32_t pb = m.vp0; pb < m.vp1; pb += 8 * 64) {
         int32_t c[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int32_t p = pb + u * kThreads + tid;
+          const int32_t p = pb + u * 64 + lane;
           c[u] = p < m.vp1 ? d.vert_col[p] : -1;
         }
 #pragma unroll
@@ -530,33 +575,33 @@ __global__ void __launch_bounds__(kThreads) k_items_lists(sa_pattern_desc d, sa_
       }
       // diagonal pairs of each row: offsets r in D_h with r <= i
       if (nD > 0)
-        for (int32_t i = b0 + tid; i <= b1; i += kThreads) cnt[3] += upper_bound_i32(Dsh, nD, i);
-      store_counts(ix, kc, m, cnt, kind, red_sh);
+        for (int32_t i = b0 + lane; i <= b1; i += 64) cnt[3] += upper_bound_i32(Dsh, nD, i);
+      store_counts_wave(ix, kc, m, cnt, kind);
       return;
     }
     // fill: segments in ascending column order = runs in descending offset order
     int64_t bs_lo = ix.seg_ptr[m.it], bs_hi = bs_lo;
-    for (int32_t cbase = 0; cbase < nD; cbase += kThreads) {
-      const int32_t p = nD - 1 - (cbase + tid);
+    for (int32_t cbase = 0; cbase < nD; cbase += 64) {
+      const int32_t p = nD - 1 - (cbase + lane);
       bool st, en;
       int32_t s0 = 0, s1 = 0;
       seg_flags(p, st, en, s0, s1);
-      int32_t tst, ten;
-      const int32_t rst = block_exscan<int32_t>(st ? 1 : 0, &tst, sh32);
-      const int32_t ren = block_exscan<int32_t>(en ? 1 : 0, &ten, sh32);
+      const uint64_t mst = __ballot(st), men = __ballot(en);
       if (st) {
-        if (bs_lo + rst < ix.capacity.n_segs) ix.seg_lo[bs_lo + rst] = s0; else overflow = true;
+        const int64_t pos = bs_lo + lanes_below(mst);
+        if (pos < ix.capacity.n_segs) ix.seg_lo[pos] = s0; else overflow = true;
       }
       if (en) {
-        if (bs_hi + ren < ix.capacity.n_segs) ix.seg_hi[bs_hi + ren] = s1; else overflow = true;
+        const int64_t pos = bs_hi + lanes_below(men);
+        if (pos < ix.capacity.n_segs) ix.seg_hi[pos] = s1; else overflow = true;
       }
-      bs_lo += tst;
-      bs_hi += ten;
+      bs_lo += __popcll(mst);
+      bs_hi += __popcll(men);
     }
     // verticals in list order, split into in-segment and gathered columns
     int64_t b_in = ix.bcol_ptr[m.it], b_out = ix.col_ptr[m.it];
-    for (int32_t pb = m.vp0; pb < m.vp1; pb += kThreads) {
-      const int32_t p = pb + tid;
+    for (int32_t pb = m.vp0; pb < m.vp1; pb += 64) {
+      const int32_t p = pb + lane;
       const int32_t c = p < m.vp1 ? d.vert_col[p] : -1;
       bool in = false, out = false;
       if (c >= 0 && c <= b1) {
@@ -564,17 +609,17 @@ __global__ void __launch_bounds__(kThreads) k_items_lists(sa_pattern_desc d, sa_
         if (count_in(Dsh, nD, a - c, b1 - c) > 0) in = true;
         else out = true;
       }
-      int32_t tin, tout;
-      const int32_t rin = block_exscan<int32_t>(in ? 1 : 0, &tin, sh32);
-      const int32_t rout = block_exscan<int32_t>(out ? 1 : 0, &tout, sh32);
+      const uint64_t min_ = __ballot(in), mout = __ballot(out);
       if (in) {
-        if (b_in + rin < ix.capacity.n_bcols) ix.bcol_idx[b_in + rin] = c; else overflow = true;
+        const int64_t pos = b_in + lanes_below(min_);
+        if (pos < ix.capacity.n_bcols) ix.bcol_idx[pos] = c; else overflow = true;
       }
       if (out) {
-        if (b_out + rout < ix.capacity.n_cols) ix.col_idx[b_out + rout] = c; else overflow = true;
+        const int64_t pos = b_out + lanes_below(mout);
+        if (pos < ix.capacity.n_cols) ix.col_idx[pos] = c; else overflow = true;
       }
-      b_in += tin;
-      b_out += tout;
+      b_in += __popcll(min_);
+      b_out += __popcll(mout);
     }
   }
   if (bad) atomicOr(ix.status, SA_STATUS_DESC_INVALID);
@@ -1058,7 +1103,9 @@ hipError_t launch_index_items(const sa_pattern_desc& d, const sa_index& ix, int3
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k_items_lists, dim3((unsigned)items), dim3(kThreads), 0, stream, d, ix, fill, validate, kc);
+  const unsigned list_grid = (unsigned)((items + kListWaves - 1) / kListWaves);
+  hipLaunchKernelGGL(k_items_lists, dim3(list_grid), dim3(64 * kListWaves), 0, stream, d, ix, fill, validate, kc,
+                     (int32_t)items);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned gen_grid = (unsigned)((items + kGenBatch - 1) / kGenBatch);
