@@ -19,15 +19,15 @@
 // values are the transforms of the fp32 minimum and maximum of A: the min/max pass
 // runs in fp32 and each element is transformed once.
 //
-// Layout: one 256-thread workgroup per map; wave w takes rows w, w+4, ...; lanes
-// take columns.  Hits accumulate with LDS atomics; the map is read once from HBM
+// Layout: one 1024-thread workgroup per map; wave w takes rows w, w+16, ...; lanes
+// take columns, four loads in flight per lane.  Hits accumulate with LDS atomics; the map is read once from HBM
 // (the causal half) plus once more for the fp32 row min/max, which hits in cache.
 #include "sa_internal.h"
 
 namespace sa {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;  // 16 waves per map: two maps fill a CU's 32 wave slots
 
 __device__ inline double box_cox_half(float a, double eps, double lambda) {
 #pragma clang fp contract(off)
@@ -88,10 +88,21 @@ __global__ void __launch_bounds__(kThreads)
     float amin = gmin, amax = gmax;
     if (norm_scope == 0) {
       float mn = INFINITY, mx = -INFINITY;
-      for (int j = lane; j <= i; j += 64) {
-        const float a = row[j];
-        mn = fminf(mn, a);
-        mx = fmaxf(mx, a);
+      for (int jb = 0; jb <= i; jb += 4 * 64) {
+        float a[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int j = jb + u * 64 + lane;
+          a[u] = j <= i ? row[j] : INFINITY;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int j = jb + u * 64 + lane;
+          if (j <= i) {
+            mn = fminf(mn, a[u]);
+            mx = fmaxf(mx, a[u]);
+          }
+        }
       }
       amin = wave_min(mn);
       amax = wave_max(mx);
@@ -101,17 +112,28 @@ __global__ void __launch_bounds__(kThreads)
     const bool flat = (ymax == ymin);
     const double range = ymax - ymin;
     uint8_t* mrow = true_mask ? true_mask + (map * L + i) * (int64_t)L : nullptr;
-    for (int j = lane; j < L; j += 64) {
-      uint8_t keep = 0;
-      if (j <= i) {
-        const double y = box_cox_half(row[j], eps, lambda);
-        keep = flat ? 1 : (((y - ymin) / range) >= tau);
-        if (keep) {
-          atomicAdd(&hd[i - j], 1);
-          atomicAdd(&hv[j], 1);
-        }
+    for (int jb = 0; jb < L; jb += 4 * 64) {
+      float a[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = jb + u * 64 + lane;
+        a[u] = j <= i ? row[j] : 0.0f;
       }
-      if (mrow) mrow[j] = keep;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = jb + u * 64 + lane;
+        if (j >= L) continue;
+        uint8_t keep = 0;
+        if (j <= i) {
+          const double y = box_cox_half(a[u], eps, lambda);
+          keep = flat ? 1 : (((y - ymin) / range) >= tau);
+          if (keep) {
+            atomicAdd(&hd[i - j], 1);
+            atomicAdd(&hv[j], 1);
+          }
+        }
+        if (mrow) mrow[j] = keep;
+      }
     }
   }
   __syncthreads();
