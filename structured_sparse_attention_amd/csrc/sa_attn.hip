@@ -571,11 +571,8 @@ __global__ void __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(2))
 }
 
 // ============================================================================
-// bf16 kernel.  Four waves per workgroup.  BM = 128: wave w owns rows 32w..32w+31
-// and all 64 keys of a tile.  BM = 64: the two 32-row halves are split again by
-// key halves (waves 2, 3 take keys 32..63 of every tile, with their own softmax
-// state), and the two halves of each row are merged at the end -- so four waves
-// share every K/V tile either way.
+// bf16 kernel for 128-row blocks.  Four waves per workgroup: wave w owns rows
+// 32w..32w+31 and all 64 keys of a tile, so four waves share every K/V tile.
 // K and V tiles travel global -> LDS with buffer_load ... lds (no register
 // staging), double-buffered: the loads of tile t+1 are in flight while tile t is
 // computed, one barrier per tile.  Tiles are stored key-row-major with the
@@ -594,12 +591,11 @@ __global__ void __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(2))
 template <int D>
 __device__ inline int vswz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
-template <int D, int BM, int KS>
+template <int D, int BM>
 struct Cfg3 {
-  static constexpr int KSPLIT = KS;
-  static constexpr int NW = (BM / 32) * KS;
+  static constexpr int NW = BM / 32;
   static constexpr int T = 64 * NW;
-  static constexpr int NKB = (BN / KSPLIT) / 32;      // 32-key blocks per wave per tile
+  static constexpr int NKB = BN / 32;                 // 32-key blocks per tile
   static constexpr int QS = D / 16;
   static constexpr int OB = D / 32;
   static constexpr int ROWB = D * 2;                  // bytes per key row
@@ -616,16 +612,16 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
-template <int D, int BM, int KS>
-__global__ void __launch_bounds__(64 * (BM / 32) * KS) __attribute__((amdgpu_waves_per_eu(2)))
+template <int D, int BM>
+__global__ void __launch_bounds__(64 * (BM / 32)) __attribute__((amdgpu_waves_per_eu(2)))
 k_attn_bf16(Params p) {
-  using C = Cfg3<D, BM, KS>;
+  using C = Cfg3<D, BM>;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * C::STAGE];
   __shared__ __attribute__((aligned(16))) int32_t cols_sh[3][BN];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, r32 = lane & 31;
-  const int rh = wave % (BM / 32), kh = wave / (BM / 32);  // row half (32 rows), key half
+  const int rh = wave;  // this wave's 32 rows
   int b, h, rb;
   decode_item(p, b, h, rb);
   const int S = p.S;
@@ -796,7 +792,7 @@ k_attn_bf16(Params p) {
     for (int kbl = 0; kbl < C::NKB; ++kbl)
 #pragma unroll
       for (int s = 0; s < C::QS; ++s)
-        kf[kbl][s] = *reinterpret_cast<const bf16x8*>(Kst + (kh * C::NKB + kbl) * 32 * C::ROWB + koff[s & 3] +
+        kf[kbl][s] = *reinterpret_cast<const bf16x8*>(Kst + kbl * 32 * C::ROWB + koff[s & 3] +
                                                       (s >> 2) * 128);
 #pragma unroll
     for (int kbl = 0; kbl < C::NKB; ++kbl) {
@@ -813,7 +809,7 @@ k_attn_bf16(Params p) {
     for (int kbl = 0; kbl < C::NKB; ++kbl)
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm) {
-        const int kbase = ((kh * C::NKB + kbl) * 32 + 16 * mm) * C::ROWB;
+        const int kbase = (kbl * 32 + 16 * mm) * C::ROWB;
 #pragma unroll
         for (int x = 0; x < C::OB; ++x) {
           const v4i16 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(Vst + kbase + voff[x]));
@@ -822,8 +818,8 @@ k_attn_bf16(Params p) {
           vfr[kbl][mm][x] = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
         }
       }
-    // mask: value v of local block kbl is key (kh*NKB + kbl)*32 + 8*(v/4) + 4*g + v%4
-    const uint64_t mw = (m >> (kh * C::NKB * 32)) >> (4 * g);
+    // mask: value v of block kbl is key kbl*32 + 8*(v/4) + 4*g + v%4
+    const uint64_t mw = m >> (4 * g);
     if (!__all(m == ~0ull)) {
 #pragma unroll
       for (int kbl = 0; kbl < C::NKB; ++kbl)
@@ -907,31 +903,7 @@ k_attn_bf16(Params p) {
     nn = walk.next(nn);
   }
 
-  // ---- merge the key halves (BM = 64), then normalise and store
-  if constexpr (C::KSPLIT == 2) {
-    float* xch = reinterpret_cast<float*>(lds) + rh * (C::OB * 16 + 2) * 64;
-    if (kh == 1) {
-#pragma unroll
-      for (int x = 0; x < C::OB; ++x)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) xch[(x * 16 + v) * 64 + lane] = oacc[x][v];
-      xch[(C::OB * 16) * 64 + lane] = m_run;
-      xch[(C::OB * 16 + 1) * 64 + lane] = l_run;
-    }
-    __syncthreads();
-    if (kh == 1) return;
-    const float m_o = xch[(C::OB * 16) * 64 + lane];
-    const float l_o = xch[(C::OB * 16 + 1) * 64 + lane];
-    const float m_new = fmaxf(m_run, m_o);
-    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-    const float fa = __builtin_amdgcn_exp2f(m_run - m_use), fb = __builtin_amdgcn_exp2f(m_o - m_use);
-#pragma unroll
-    for (int x = 0; x < C::OB; ++x)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) oacc[x][v] = oacc[x][v] * fa + xch[(x * 16 + v) * 64 + lane] * fb;
-    l_run = l_run * fa + l_o * fb;
-    m_run = m_new;
-  }
+  // ---- normalise and store
   const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   if (row_ok) {
@@ -953,10 +925,10 @@ k_attn_bf16(Params p) {
   }
 }
 
-template <int D, int BM, int KS>
+template <int D, int BM>
 hipError_t launch_bf16(const Params& p, hipStream_t stream) {
   const int64_t blocks = (int64_t)p.B * p.hq * p.nb;
-  k_attn_bf16<D, BM, KS><<<dim3((unsigned)blocks), dim3(Cfg3<D, BM, KS>::T), 0, stream>>>(p);
+  k_attn_bf16<D, BM><<<dim3((unsigned)blocks), dim3(Cfg3<D, BM>::T), 0, stream>>>(p);
   return hipGetLastError();
 }
 
@@ -1000,7 +972,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
   // bf16: 128-row blocks run the LDS-direct kernel; 64-row blocks (two waves per block) run the
   // register-staged kernel, which keeps four blocks per CU and measured faster at that size.
   if (a.dtype == SA_DTYPE_BF16) {
-    if (p.BM == 128) return a.head_dim == 64 ? launch_bf16<64, 128, 1>(p, stream) : launch_bf16<128, 128, 1>(p, stream);
+    if (p.BM == 128) return a.head_dim == 64 ? launch_bf16<64, 128>(p, stream) : launch_bf16<128, 128>(p, stream);
     return a.head_dim == 64 ? launch_t<64, 64, true>(p, stream) : launch_t<128, 64, true>(p, stream);
   }
   return a.head_dim == 64 ? launch_bm<64, false>(p, stream) : launch_bm<128, false>(p, stream);

@@ -127,6 +127,28 @@ def test_band_edges_partial_tiles(d, BM):
     _run(desc, q, k, v, BM, all_rows(1, H, S), "band-edges")
 
 
+def _mixed_desc(S, H, seed):
+    """Every pattern kind at once in each head: diagonal runs, verticals, 128 x 128 blocks and
+    256-row stripe lists (the index builds these items with LDS bitmaps)."""
+    rng = np.random.default_rng(seed)
+    diags = [np.unique(np.concatenate([np.arange(rng.integers(1, 200)), rng.choice(S, 6, replace=False)]))
+             for _ in range(H)]
+    verts = [rng.choice(S, 9, replace=False) for _ in range(H)]
+    nbq = -(-S // 128)
+    bm = (rng.random((H, nbq, nbq)) < 0.2).astype(np.uint8)
+    stripes = [[np.sort(rng.choice(S, size=int(rng.integers(0, 60)), replace=False)) for _ in range(-(-S // 256))]
+               for _ in range(H)]
+    return W.desc_from_lists(S, diags, verts, block_mask=bm, block_size=128, stripes=stripes, stripe_rows=256)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 128), ("f32", 64)])
+@pytest.mark.parametrize("BM", [64, 128])
+def test_mixed_pattern_kinds_every_row(dtype, d, BM):
+    S, H = 1500, 4
+    q, k, v = W.qkv(18, 1, H, 2, S, d, dtype)
+    _run(_mixed_desc(S, H, 21), q, k, v, BM, all_rows(1, H, S), "mixed-kinds")
+
+
 # ------------------------------------------------------------------ workload 2 (1B-like, bf16, d=64)
 @pytest.mark.parametrize("S,BM", [(1000, 64), (1000, 128)])
 def test_llama1b_like_small_full(S, BM):
