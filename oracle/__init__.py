@@ -66,6 +66,10 @@ def _load():
                                                C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_double,
                                                C.c_void_p, C.c_int64, C.c_int, C.c_void_p, C.c_void_p,
                                                C.c_void_p]
+            lib.orc_attention_queries.argtypes = [C.POINTER(_Desc), C.c_void_p, C.c_void_p, C.c_void_p, C.c_int,
+                                                  C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_double,
+                                                  C.c_void_p, C.c_int64, C.c_int, C.c_void_p, C.c_void_p,
+                                                  C.c_void_p]
             lib.orc_capture.restype = C.c_int
             lib.orc_capture.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_double, C.c_double, C.c_double,
                                         C.c_double, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
@@ -183,6 +187,30 @@ def attention_rows(desc, q, k, v, rows, scale: Optional[float] = None, mode: int
                            float(scale), rows.ctypes.data, n, mode, o.ctypes.data, lse.ctypes.data,
                            cnt.ctypes.data)
     return (o, lse, cnt) if return_counts else (o, lse)
+
+
+def attention_queries(desc, qrows, k, v, rows, scale: Optional[float] = None, mode: int = 0):
+    """fp64 attention of explicit query vectors: row n is query qrows[n] placed at position i of head h
+    (rows[n] = (b, h, i)) against k/v [B,hkv,S,d] (the decode form).  Returns (o [n, d], lse [n])."""
+    lib = _load()
+    hd = _DescHolder(desc)
+    qrows = np.ascontiguousarray(qrows)
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    dtype = 0 if qrows.dtype == np.float32 else 1
+    assert qrows.dtype in (np.float32, np.uint16) and k.dtype == qrows.dtype and v.dtype == qrows.dtype
+    B, hkv, S, d = k.shape
+    hq = desc.H
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 3))
+    n = rows.shape[0]
+    assert qrows.shape == (n, d)
+    o = np.zeros((n, d), np.float64)
+    lse = np.zeros(n, np.float64)
+    lib.orc_attention_queries(C.byref(hd.c), qrows.ctypes.data, k.ctypes.data, v.ctypes.data, dtype, hq, hkv, S, d,
+                              float(scale), rows.ctypes.data, n, mode, o.ctypes.data, lse.ctypes.data, None)
+    return o, lse
 
 
 def capture(maps: np.ndarray, lam: float = 0.5, eps: float = 1e-8, tau: float = 0.3, mu: float = 0.8,

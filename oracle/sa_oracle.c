@@ -27,6 +27,9 @@
  *   orc_attention_rows   fp64 attention on chosen rows (dense -inf form and
  *                        sparse-enumeration form) -> textbook causal attention,
  *                        diagonal-0 identity, V==1, rows sum to one
+ *   orc_attention_queries  the same rows with explicit query vectors (decode:
+ *                        one new query at position i against the cache) ->
+ *                        equals orc_attention_rows when the vectors are Q rows
  *   orc_capture          Box-Cox / threshold / overlap score / keep -> closed form,
  *                        hand-worked example (tests/golden/capture_example.txt),
  *                        planted patterns
@@ -304,6 +307,45 @@ static double widen(const void* base, int dtype, int64_t idx) {
   return (double)f;
 }
 
+/* One row i of query head h, query vector qi (fp64, dh values) against the keys of the kv
+   head at kvbase.  keep and s are scratch of S entries. */
+static void attend_row(const orc_desc* d, const double* qi, const void* k, const void* v, int dtype,
+                       int64_t kvbase, int32_t S, int32_t dh, double scale, int32_t h, int32_t i, int mode,
+                       uint8_t* keep, double* s, double* oi, double* lse_out, int64_t* n_keys_out) {
+  orc_row_mask(d, h, i, keep);
+  if (n_keys_out) {
+    int64_t cnt = 0;
+    for (int32_t j = 0; j <= i; ++j) cnt += keep[j];
+    *n_keys_out = cnt;
+  }
+  int32_t jend = (mode == 1) ? S - 1 : i;
+  double m = -INFINITY;
+  for (int32_t j = 0; j <= jend; ++j) {
+    int retained = (j <= i) && keep[j];
+    if (mode == 0 && !retained) continue;
+    double acc = 0.0;
+    for (int32_t c = 0; c < dh; ++c) acc += qi[c] * widen(k, dtype, kvbase + (int64_t)j * dh + c);
+    s[j] = retained ? acc * scale : -INFINITY;
+    if (s[j] > m) m = s[j];
+  }
+  for (int32_t c = 0; c < dh; ++c) oi[c] = 0.0;
+  if (m == -INFINITY) { /* no retained key */
+    *lse_out = -INFINITY;
+    return;
+  }
+  double l = 0.0;
+  for (int32_t j = 0; j <= jend; ++j) {
+    int retained = (j <= i) && keep[j];
+    if (mode == 0 && !retained) continue;
+    double p = exp(s[j] - m); /* exp(-inf) = 0 for masked logits */
+    l += p;
+    if (p != 0.0)
+      for (int32_t c = 0; c < dh; ++c) oi[c] += p * widen(v, dtype, kvbase + (int64_t)j * dh + c);
+  }
+  for (int32_t c = 0; c < dh; ++c) oi[c] = oi[c] / l;
+  *lse_out = m + log(l);
+}
+
 void orc_attention_rows(const orc_desc* d, const void* q, const void* k, const void* v, int dtype,
                         int32_t B, int32_t hq, int32_t hkv, int32_t S, int32_t dh, double scale,
                         const int32_t* rows, int64_t n_rows, int mode, double* o, double* lse,
@@ -322,39 +364,34 @@ void orc_attention_rows(const orc_desc* d, const void* q, const void* k, const v
       int64_t qbase = (((int64_t)b * hq + h) * S + i) * dh;
       int64_t kvbase = ((int64_t)b * hkv + g) * (int64_t)S * dh;
       for (int32_t c = 0; c < dh; ++c) qi[c] = widen(q, dtype, qbase + c);
-      orc_row_mask(d, h, i, keep);
-      if (n_keys) {
-        int64_t cnt = 0;
-        for (int32_t j = 0; j <= i; ++j) cnt += keep[j];
-        n_keys[n] = cnt;
-      }
-      int32_t jend = (mode == 1) ? S - 1 : i;
-      double m = -INFINITY;
-      for (int32_t j = 0; j <= jend; ++j) {
-        int retained = (j <= i) && keep[j];
-        if (mode == 0 && !retained) continue;
-        double acc = 0.0;
-        for (int32_t c = 0; c < dh; ++c) acc += qi[c] * widen(k, dtype, kvbase + (int64_t)j * dh + c);
-        s[j] = retained ? acc * scale : -INFINITY;
-        if (s[j] > m) m = s[j];
-      }
-      double* oi = o + n * dh;
-      for (int32_t c = 0; c < dh; ++c) oi[c] = 0.0;
-      if (m == -INFINITY) { /* no retained key */
-        lse[n] = -INFINITY;
-        continue;
-      }
-      double l = 0.0;
-      for (int32_t j = 0; j <= jend; ++j) {
-        int retained = (j <= i) && keep[j];
-        if (mode == 0 && !retained) continue;
-        double p = exp(s[j] - m); /* exp(-inf) = 0 for masked logits */
-        l += p;
-        if (p != 0.0)
-          for (int32_t c = 0; c < dh; ++c) oi[c] += p * widen(v, dtype, kvbase + (int64_t)j * dh + c);
-      }
-      for (int32_t c = 0; c < dh; ++c) oi[c] = oi[c] / l;
-      lse[n] = m + log(l);
+      attend_row(d, qi, k, v, dtype, kvbase, S, dh, scale, h, i, mode, keep, s, o + n * dh, lse + n,
+                 n_keys ? n_keys + n : NULL);
+    }
+    free(keep);
+    free(s);
+    free(qi);
+  }
+}
+
+/* Decode form: row n of `rows` (b, h, i) takes its own query vector qrows[n][dh] (same dtype as
+   k and v) in place of Q[b][h][i]; everything else as orc_attention_rows. */
+void orc_attention_queries(const orc_desc* d, const void* qrows, const void* k, const void* v, int dtype,
+                           int32_t hq, int32_t hkv, int32_t S, int32_t dh, double scale, const int32_t* rows,
+                           int64_t n_rows, int mode, double* o, double* lse, int64_t* n_keys) {
+  int32_t group = hq / hkv;
+#pragma omp parallel
+  {
+    uint8_t* keep = (uint8_t*)malloc((size_t)S);
+    double* s = (double*)malloc(sizeof(double) * (size_t)S);
+    double* qi = (double*)malloc(sizeof(double) * (size_t)dh);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t n = 0; n < n_rows; ++n) {
+      int32_t b = rows[3 * n], h = rows[3 * n + 1], i = rows[3 * n + 2];
+      int32_t g = h / group;
+      int64_t kvbase = ((int64_t)b * hkv + g) * (int64_t)S * dh;
+      for (int32_t c = 0; c < dh; ++c) qi[c] = widen(qrows, dtype, n * (int64_t)dh + c);
+      attend_row(d, qi, k, v, dtype, kvbase, S, dh, scale, h, i, mode, keep, s, o + n * dh, lse + n,
+                 n_keys ? n_keys + n : NULL);
     }
     free(keep);
     free(s);

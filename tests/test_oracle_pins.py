@@ -306,3 +306,45 @@ def test_extension_restricted_to_capture_window_is_the_kept_union():
             j = np.arange(i + 1)
             expect = kd[i - j] | kv[j]
             np.testing.assert_array_equal(oracle.row_mask(d, h, i).astype(bool), expect)
+
+
+# ------------------------------------------------------------------ decode form (explicit query vectors)
+def test_query_form_equals_row_form_on_q_rows():
+    """Row n of attention_queries with qrows[n] = Q[b, h, i] is, bit for bit, row (b, h, i) of attention_rows."""
+    rng = np.random.default_rng(41)
+    d = _rand_desc(rng, 48, 4, ("diag", "vert", "block", "stripe"))
+    q, k, v = W.qkv(41, 2, 4, 2, 48, 16, "bf16")
+    rows = np.array([(b, h, i) for b in range(2) for h in range(4) for i in (0, 7, 31, 47)], np.int32)
+    o1, l1 = oracle.attention_rows(d, q, k, v, rows)
+    o2, l2 = oracle.attention_queries(d, np.stack([q[b, h, i] for b, h, i in rows]), k, v, rows)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_query_form_full_mask_is_textbook_single_query_attention():
+    """With every causal key retained, a query vector at position t is softmax(q K[:t+1]^T / sqrt(d)) V[:t+1]."""
+    S, dh = 80, 32
+    d = W.tiny("all_ones", S=S)
+    _, k, v = W.qkv(42, 1, 1, 1, S, dh, "f32")
+    qv = np.random.default_rng(42).standard_normal((5, dh)).astype(np.float32)
+    ts = [0, 1, 17, 50, 79]
+    o, lse = oracle.attention_queries(d, qv, k, v, np.array([(0, 0, t) for t in ts], np.int32))
+    for n, t in enumerate(ts):
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(qv[n:n + 1].astype(np.float64))[None, None],
+            torch.from_numpy(k[0, 0, :t + 1].astype(np.float64))[None, None],
+            torch.from_numpy(v[0, 0, :t + 1].astype(np.float64))[None, None])
+        np.testing.assert_allclose(o[n], ref.numpy().reshape(dh), atol=1e-12)
+        s = (k[0, 0, :t + 1].astype(np.float64) @ qv[n].astype(np.float64)) / np.sqrt(dh)
+        np.testing.assert_allclose(lse[n], np.log(np.exp(s).sum()), atol=1e-12)
+
+
+def test_query_form_diagonal_zero_returns_the_cache_row():
+    """D = {0} only: the query at position t sees key t alone, so the output is V[t] exactly."""
+    S, dh = 40, 16
+    d = W.tiny("diag0", S=S)
+    _, k, v = W.qkv(43, 1, 1, 1, S, dh, "bf16")
+    qv = W.bf16_bits(np.random.default_rng(43).standard_normal((3, dh)).astype(np.float32))
+    ts = [0, 9, 39]
+    o, _ = oracle.attention_queries(d, qv, k, v, np.array([(0, 0, t) for t in ts], np.int32))
+    for n, t in enumerate(ts):
+        assert np.array_equal(o[n], W.bf16_bits_to_f32(v[0, 0, t]).astype(np.float64))
