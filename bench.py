@@ -5,8 +5,9 @@ index build (count, scan, fill) from the pattern descriptor, then the sparse
 attention forward.  Default workload: the LLaMA-3-8B-shaped layer (S = 65536,
 32 query / 8 kv heads, d = 128, bf16; half vertical+slash heads, half 64x64
 block-sparse heads).  Also reported: the attention time at S = 131072 (stripe
-masks), the pattern-capture time on 16 x 32 maps of 512 x 512, and the CPU
-oracle timed on a bounded sample of the same workload.
+masks), the pattern-capture time on 16 x 32 maps of 512 x 512, one decode step
+(16 sequences, one new query each, against 64K caches with the same patterns),
+and the CPU oracle timed on a bounded sample of the same workload.
 
 Prints ONE JSON line.  Only one GPU is used; --gpus above 1 exits with a message.
 """
@@ -134,6 +135,60 @@ def capture_ms(sa, torch, reps=5):
     return dict(ms=ms, maps=int(maps.shape[0]), L=512, read_GBps=causal_bytes / (ms * 1e-3) / 1e9)
 
 
+def decode_row_keys(ixn, h, t, nb, BM, nwords):
+    """Retained keys of row t of head h, read off the index (segments filtered by the diagonal bitmap
+    and the in-segment columns, then the gathered columns <= t)."""
+    it = h * nb + t // BM
+    dbits = ixn["dbits"].reshape(-1, nwords)[h]
+    bcols = ixn["bcol_idx"][ixn["bcol_ptr"][it]:ixn["bcol_ptr"][it + 1]]
+    n = 0
+    for s in range(ixn["seg_ptr"][it], ixn["seg_ptr"][it + 1]):
+        lo, hi = int(ixn["seg_lo"][s]), min(int(ixn["seg_hi"][s]), t)
+        if lo > t:
+            break
+        js = np.arange(lo, hi + 1)
+        r = t - js
+        on = ((dbits[r >> 5] >> (r & 31)) & 1).astype(bool) | np.isin(js, bcols)
+        n += int(on.sum())
+    cols = ixn["col_idx"][ixn["col_ptr"][it]:ixn["col_ptr"][it + 1]]
+    return n + int((cols <= t).sum())
+
+
+def decode_bench(sa, torch, B=16, reps=20):
+    """Decode (one new query per sequence) on the 64K workload's patterns: B sequences whose
+    positions sit near the end of a 64K cache, all 32 query heads."""
+    import workloads as W
+    cfg = WORKLOADS[4]
+    S, hq, hkv, d, BM = cfg["S"], cfg["hq"], cfg["hkv"], cfg["d"], cfg["row_block"]
+    desc = W.llama8b_like(S=S)
+    ix = sa.build_index(sa.DevicePatterns.from_host(desc), BM)
+    g = torch.Generator(device="cuda").manual_seed(4)
+    k = torch.randn(B, hkv, S, d, device="cuda", generator=g).to(torch.bfloat16)
+    v = torch.randn(B, hkv, S, d, device="cuda", generator=g).to(torch.bfloat16)
+    q = torch.randn(B, hq, d, device="cuda", generator=g).to(torch.bfloat16)
+    pos_h = [S - 1 - 37 * b for b in range(B)]
+    pos = torch.tensor(pos_h, dtype=torch.int32, device="cuda")
+    o = sa.sparse_attn_decode(q, k, v, pos, ix)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        sa.sparse_attn_decode(q, k, v, pos, ix, out=o)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    ixn = ix.to_numpy()
+    nw = -(-S // 32)
+    keys = sum(decode_row_keys(ixn, h, t, ix.n_row_blocks, BM, nw) for t in pos_h for h in range(hq))
+    kv_bytes = keys * 2 * d * 2  # one K row and one V row (bf16) per retained key and query head
+    del k, v, q, o, ix
+    torch.cuda.empty_cache()
+    return dict(workload="llama8b_like patterns, %d sequences at positions %d..%d of a %d-row cache, %d/%d heads, "
+                          "head_dim %d, bf16" % (B, pos_h[-1], pos_h[0], S, hq, hkv, d),
+                ms=ms, tokens_per_s=B / (ms * 1e-3), retained_keys=keys, kv_bytes=kv_bytes,
+                kv_GBps=kv_bytes / (ms * 1e-3) / 1e9, kv_frac_of_hbm=kv_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS)
+
+
 def measured_traffic(cfg):
     """HBM bytes per launch of the attention kernel, from profiles/traffic.json (hardware counters
     FETCH_SIZE + WRITE_SIZE, scaled by a 1 GiB copy), or None when the kernel source has changed
@@ -224,6 +279,9 @@ def main():
         torch.cuda.empty_cache()
         extras["capture"] = capture_ms(sa, torch)
         log("capture: %.3f ms" % extras["capture"]["ms"])
+        extras["decode"] = decode_bench(sa, torch)
+        log("decode: %.3f ms for %d tokens (%.0f GB/s of retained K/V rows)" % (
+            extras["decode"]["ms"], 16, extras["decode"]["kv_GBps"]))
 
     cpu = None
     if not args.no_cpu_baseline:

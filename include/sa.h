@@ -192,6 +192,25 @@ sa_status sa_sparse_attn_prefill(const void* q, const void* k, const void* v, vo
                                  int32_t dtype, float softmax_scale, const sa_index* idx, void* stream);
 
 /*
+ * sa_sparse_attn_decode: one new query row per sequence against a K/V cache
+ * [DAM, Referee Report Summary; What carries the argument], i.e. row pos[b] of the
+ * prefill output when Q[b][h][pos[b]] is q[b][h]: the keys are the cache rows
+ * j <= pos[b] that the mask retains for row pos[b], masked logits get no weight.
+ *   q, o  [batch][hq][head_dim], element type `dtype`; o has q's type.
+ *   k, v  [batch][hkv][S][head_dim] (the cache; rows > pos[b] are never read).
+ *   pos   int32 [batch] (device): the query position of each sequence,
+ *         0 <= pos[b] < S; a position outside that range gives o = 0, lse = -inf.
+ *   lse   NULL or float [batch][hq] (natural log; -inf without retained keys).
+ *   softmax_scale, head_dim, GQA mapping and idx as for sa_sparse_attn_prefill
+ *   (the index is the prefill index of the same patterns and S).
+ * Arithmetic: fp32 dot products and online softmax (exp2 domain), fp32 P.V.
+ * Errors: SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_HIP.
+ */
+sa_status sa_sparse_attn_decode(const void* q, const void* k, const void* v, const int32_t* pos, void* o, float* lse,
+                                int32_t batch, int32_t hq, int32_t hkv, int32_t S, int32_t head_dim, int32_t dtype,
+                                float softmax_scale, const sa_index* idx, void* stream);
+
+/*
  * sa_pattern_capture [DAM, What carries the argument]: for each averaged attention
  * map A (float [n_maps][L][L], row-major; entries with j > i are ignored):
  *   y = (sqrt(A + eps) - 1) / lambda    Box-Cox with lambda = 0.5 (x^0.5 = sqrt x)

@@ -17,8 +17,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-__all__ = ["SAError", "DevicePatterns", "SparseIndex", "build_index", "sparse_attn_prefill", "pattern_capture",
-           "patterns_to_desc", "library_path", "version", "lib"]
+__all__ = ["SAError", "DevicePatterns", "SparseIndex", "build_index", "sparse_attn_prefill", "sparse_attn_decode",
+           "pattern_capture", "patterns_to_desc", "library_path", "version", "lib"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libsa.so")
@@ -68,6 +68,9 @@ def _load():
     lib.sa_sparse_attn_prefill.restype = C.c_int32
     lib.sa_sparse_attn_prefill.argtypes = [C.c_void_p] * 4 + [C.c_void_p] + [C.c_int32] * 6 + \
         [C.c_float, C.POINTER(_Index), C.c_void_p]
+    lib.sa_sparse_attn_decode.restype = C.c_int32
+    lib.sa_sparse_attn_decode.argtypes = [C.c_void_p] * 6 + [C.c_int32] * 6 + [C.c_float, C.POINTER(_Index),
+                                                                                 C.c_void_p]
     lib.sa_pattern_capture.restype = C.c_int32
     lib.sa_pattern_capture.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_double, C.c_double, C.c_double,
                                        C.c_double, C.c_int32] + [C.c_void_p] * 5 + [C.c_void_p]
@@ -243,6 +246,41 @@ def sparse_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index
     _check(_lib.sa_sparse_attn_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse), B, hq,
                                        k.shape[1], S, d, dt, scale, C.byref(c), _stream(stream)),
            "sa_sparse_attn_prefill")
+    return (o, lse) if return_lse else o
+
+
+def sparse_attn_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pos: torch.Tensor, index: SparseIndex,
+                       softmax_scale: Optional[float] = None, return_lse: bool = False,
+                       out: Optional[torch.Tensor] = None, stream=None):
+    """sa_sparse_attn_decode: q [B,Hq,d] at positions pos (int32 [B], on the GPU) against the cache
+    k/v [B,Hkv,S,d] (bf16 or fp32, contiguous)."""
+    if q.dtype == torch.bfloat16:
+        dt = SA_DTYPE_BF16
+    elif q.dtype == torch.float32:
+        dt = SA_DTYPE_F32
+    else:
+        raise TypeError("q must be bfloat16 or float32")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if q.dim() != 3 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q [B,Hq,d] and k, v [B,Hkv,S,d] expected")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, hq, d = q.shape
+    if k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k/v shape does not match q")
+    if pos.dtype != torch.int32 or pos.shape != (B,) or pos.device != q.device:
+        raise ValueError("pos must be an int32 [B] tensor on q's device")
+    S = k.shape[2]
+    o = torch.empty_like(q) if out is None else out
+    if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous():
+        raise ValueError("out must match q")
+    lse = torch.empty((B, hq), dtype=torch.float32, device=q.device) if return_lse else None
+    c = index.c_struct()
+    scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    _check(_lib.sa_sparse_attn_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), pos.data_ptr(), o.data_ptr(),
+                                      _ptr(lse), B, hq, k.shape[1], S, d, dt, scale, C.byref(c), _stream(stream)),
+           "sa_sparse_attn_decode")
     return (o, lse) if return_lse else o
 
 

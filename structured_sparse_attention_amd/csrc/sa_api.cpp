@@ -112,6 +112,24 @@ sa_status sa_sparse_attn_prefill(const void* q, const void* k, const void* v, vo
   return hip_status(sa::launch_attention(a, static_cast<hipStream_t>(stream)));
 }
 
+sa_status sa_sparse_attn_decode(const void* q, const void* k, const void* v, const int32_t* pos, void* o, float* lse,
+                                int32_t batch, int32_t hq, int32_t hkv, int32_t S, int32_t head_dim, int32_t dtype,
+                                float softmax_scale, const sa_index* idx, void* stream) {
+  if (!q || !k || !v || !pos || !o || !idx) return SA_ERR_INVALID_ARG;
+  if (batch < 1 || hq < 1 || hkv < 1 || S < 1 || hq % hkv != 0) return SA_ERR_INVALID_ARG;
+  if (dtype != SA_DTYPE_BF16 && dtype != SA_DTYPE_F32) return SA_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return SA_ERR_UNSUPPORTED;
+  if (idx->S != S || idx->n_heads != hq) return SA_ERR_INVALID_ARG;
+  if ((idx->row_block != 64 && idx->row_block != 128) || idx->n_row_blocks != cdiv(S, idx->row_block))
+    return SA_ERR_INVALID_ARG;
+  if (!index_arrays_ok(*idx)) return SA_ERR_INVALID_ARG;
+  if ((int64_t)batch * hq > 0x7fffffffLL) return SA_ERR_UNSUPPORTED;
+  const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf((float)head_dim);
+  if (!isfinite(scale)) return SA_ERR_INVALID_ARG;
+  sa::DecodeArgs a{q, k, v, pos, o, lse, batch, hq, hkv, S, head_dim, dtype, scale, idx};
+  return hip_status(sa::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
 sa_status sa_pattern_capture(const float* maps, int32_t n_maps, int32_t L, double lambda, double eps, double tau,
                              double mu, int32_t norm_scope, uint8_t* keep_diag, uint8_t* keep_vert,
                              int32_t* diag_hits, int32_t* vert_hits, uint8_t* true_mask, void* stream) {

@@ -33,6 +33,20 @@ struct AttnArgs {
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
 
+// Decode (sa_decode.hip): one query row per sequence at position pos[b].
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* pos;
+  void* o;
+  float* lse;
+  int32_t batch, hq, hkv, S, head_dim, dtype;
+  float scale;
+  const sa_index* idx;
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
 // Pattern capture and extension (sa_capture.hip).
 hipError_t launch_capture(const float* maps, int32_t n_maps, int32_t L, double lambda, double eps, double tau,
                           double mu, int32_t norm_scope, uint8_t* keep_diag, uint8_t* keep_vert, int32_t* diag_hits,

@@ -25,8 +25,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for f in ("sa_build_index", "sa_sparse_attn_prefill", "sa_pattern_capture", "sa_patterns_to_desc",
-              "sa_status_string", "sa_version"):
+    for f in ("sa_build_index", "sa_sparse_attn_prefill", "sa_sparse_attn_decode", "sa_pattern_capture",
+              "sa_patterns_to_desc", "sa_status_string", "sa_version"):
         assert f in names
 
 
@@ -93,6 +93,20 @@ def test_attention_validation(m):
     assert f(p, p, p, p, None, 1, 2, 1, 512, 64, 1, 0.0, C.byref(ix), None) == -1   # heads != index heads
     assert f(p, p, p, p, None, 0, 1, 1, 512, 64, 1, 0.0, C.byref(ix), None) == -1   # batch
     assert f(p, p, p, p, None, 1, 1, 1, 512, 64, 1, 0.0, C.byref(_index(m, col_idx=None)), None) == -1
+
+
+def test_decode_validation(m):
+    f = m.lib.sa_sparse_attn_decode
+    ix = _index(m)
+    p = FAKE.value
+    assert f(p, p, p, None, p, None, 1, 1, 1, 512, 64, 1, 0.0, C.byref(ix), None) == -1   # pos
+    assert f(None, p, p, p, p, None, 1, 1, 1, 512, 64, 1, 0.0, C.byref(ix), None) == -1  # q
+    assert f(p, p, p, p, p, None, 1, 3, 2, 512, 64, 1, 0.0, C.byref(ix), None) == -1     # hq % hkv
+    assert f(p, p, p, p, p, None, 1, 1, 1, 512, 64, 7, 0.0, C.byref(ix), None) == -1     # dtype
+    assert f(p, p, p, p, p, None, 1, 1, 1, 512, 96, 1, 0.0, C.byref(ix), None) == -2     # head_dim
+    assert f(p, p, p, p, p, None, 1, 1, 1, 256, 64, 1, 0.0, C.byref(ix), None) == -1     # S != index S
+    assert f(p, p, p, p, p, None, 0, 1, 1, 512, 64, 1, 0.0, C.byref(ix), None) == -1     # batch
+    assert f(p, p, p, p, p, None, 1, 1, 1, 512, 64, 1, float("inf"), C.byref(ix), None) == -1
 
 
 def test_capture_validation(m):
