@@ -16,7 +16,7 @@
 // it reads its K row (a full row per lane) and forms q . k against the query kept
 // in its registers; the group's scores update the wave's running max and sum (exp2
 // domain).  P.V then runs with the lanes over head dimensions: for each retained key
-// of the group the wave reads the V row once (coalesced, eight rows in flight) and
+// of the group the wave reads the V row once (coalesced, sixteen rows in flight) and
 // every lane accumulates its slice.  Decode moves each retained K and V row once and
 // does 4 d flops per row, so it is bound by HBM (or L2) bandwidth, not by arithmetic;
 // no MFMA.  The waves' partial (max, sum, output) are merged in LDS at the end.
@@ -154,13 +154,13 @@ __global__ void __launch_bounds__(64 * kWaves) k_decode(DecParams p) {
     const float pj = keep ? __builtin_amdgcn_exp2f(x - m_run) : 0.0f;
     l_lane += pj;
     // P.V with the lanes over head dimensions: lane owns dimensions [DPL * lane, DPL * lane + DPL);
-    // the retained keys go eight at a time so that eight V rows are in flight
+    // the retained keys go sixteen at a time so that sixteen V rows are in flight
     uint64_t mask = __ballot(keep);
     while (mask) {
-      float ps[8];
-      int32_t js[8];
+      float ps[16];
+      int32_t js[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 16; ++u) {
         const int src = mask ? __ffsll((unsigned long long)mask) - 1 : 0;
         const bool live = mask != 0ull;
         mask &= mask - 1;
@@ -168,15 +168,15 @@ __global__ void __launch_bounds__(64 * kWaves) k_decode(DecParams p) {
         js[u] = live ? __shfl(j, src, 64) : -1;
       }
       if constexpr (BF16) {
-        uint32_t w[8];
+        uint32_t w[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 16; ++u) {
           const E* vrow = Vg + (int64_t)(js[u] < 0 ? 0 : js[u]) * D + DPL * lane;
           if constexpr (DPL == 2) w[u] = js[u] < 0 ? 0u : *reinterpret_cast<const uint32_t*>(vrow);
           else w[u] = js[u] < 0 ? 0u : (uint32_t)(*reinterpret_cast<const uint16_t*>(vrow)) << 16;
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 16; ++u) {
           if constexpr (DPL == 2) {
             oacc[0] = __builtin_fmaf(ps[u], bf16_lo(w[u]), oacc[0]);
             oacc[1] = __builtin_fmaf(ps[u], bf16_hi(w[u]), oacc[1]);
@@ -185,15 +185,15 @@ __global__ void __launch_bounds__(64 * kWaves) k_decode(DecParams p) {
           }
         }
       } else {
-        float w[8][DPL];
+        float w[16][DPL];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 16; ++u) {
           const E* vrow = Vg + (int64_t)(js[u] < 0 ? 0 : js[u]) * D + DPL * lane;
 #pragma unroll
           for (int e = 0; e < DPL; ++e) w[u][e] = js[u] < 0 ? 0.0f : vrow[e];
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < 16; ++u)
 #pragma unroll
           for (int e = 0; e < DPL; ++e) oacc[e] = __builtin_fmaf(ps[u], w[u][e], oacc[e]);
       }
