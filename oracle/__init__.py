@@ -70,6 +70,8 @@ def _load():
                                                   C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_double,
                                                   C.c_void_p, C.c_int64, C.c_int, C.c_void_p, C.c_void_p,
                                                   C.c_void_p]
+            lib.orc_attention_maps.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int32, C.c_int32, C.c_int32,
+                                               C.c_int32, C.c_int32, C.c_double, C.c_void_p]
             lib.orc_capture.restype = C.c_int
             lib.orc_capture.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_double, C.c_double, C.c_double,
                                         C.c_double, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
@@ -211,6 +213,22 @@ def attention_queries(desc, qrows, k, v, rows, scale: Optional[float] = None, mo
     lib.orc_attention_queries(C.byref(hd.c), qrows.ctypes.data, k.ctypes.data, v.ctypes.data, dtype, hq, hkv, S, d,
                               float(scale), rows.ctypes.data, n, mode, o.ctypes.data, lse.ctypes.data, None)
     return o, lse
+
+
+def attention_maps(q, k, scale: Optional[float] = None) -> np.ndarray:
+    """Batch-averaged causal attention maps [hq, L, L] (float64) of q [B,hq,L,d] against k [B,hkv,L,d]."""
+    lib = _load()
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    dtype = 0 if q.dtype == np.float32 else 1
+    assert q.dtype in (np.float32, np.uint16) and k.dtype == q.dtype
+    B, hq, L, d = q.shape
+    hkv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    maps = np.zeros((hq, L, L), np.float64)
+    lib.orc_attention_maps(q.ctypes.data, k.ctypes.data, dtype, B, hq, hkv, L, d, float(scale), maps.ctypes.data)
+    return maps
 
 
 def capture(maps: np.ndarray, lam: float = 0.5, eps: float = 1e-8, tau: float = 0.3, mu: float = 0.8,

@@ -27,6 +27,9 @@
  *   orc_attention_rows   fp64 attention on chosen rows (dense -inf form and
  *                        sparse-enumeration form) -> textbook causal attention,
  *                        diagonal-0 identity, V==1, rows sum to one
+ *   orc_attention_maps   batch-averaged causal attention maps at the capture
+ *                        length -> rows sum to one, uniform rows for equal keys,
+ *                        torch softmax of the masked scores
  *   orc_attention_queries  the same rows with explicit query vectors (decode:
  *                        one new query at position i against the cache) ->
  *                        equals orc_attention_rows when the vectors are Q rows
@@ -396,6 +399,52 @@ void orc_attention_queries(const orc_desc* d, const void* qrows, const void* k, 
     free(keep);
     free(s);
     free(qi);
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Averaged attention maps, fp64.                                           */
+/* [DAM] "What carries the argument": a frozen model reads sequences cut to */
+/* the pattern capture length L and its attention maps are averaged over    */
+/* the inputs; "Assumptions & free parameters": the mean attention over     */
+/* batches stands in for each sequence's own.  For query head h (kv head    */
+/* g = h / (hq/hkv)) and each row i < L:                                     */
+/*   maps[h][i][j] = (1/B) sum_b softmax_j( (q_bhi . k_bgj) * scale ),      */
+/*                   the softmax over j <= i;  maps[h][i][j] = 0 for j > i. */
+/* q [B][hq][L][dh], k [B][hkv][L][dh] (dtype as for attention).            */
+/* ------------------------------------------------------------------------ */
+void orc_attention_maps(const void* q, const void* k, int dtype, int32_t B, int32_t hq, int32_t hkv, int32_t L,
+                        int32_t dh, double scale, double* maps /* [hq][L][L] */) {
+  int32_t group = hq / hkv;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)L);
+#pragma omp for schedule(dynamic, 1) collapse(2)
+    for (int32_t h = 0; h < hq; ++h)
+      for (int32_t i = 0; i < L; ++i) {
+        double* row = maps + ((int64_t)h * L + i) * L;
+        for (int32_t j = 0; j < L; ++j) row[j] = 0.0;
+        int32_t g = h / group;
+        for (int32_t b = 0; b < B; ++b) {
+          int64_t qb = (((int64_t)b * hq + h) * L + i) * dh;
+          int64_t kb = ((int64_t)b * hkv + g) * (int64_t)L * dh;
+          double m = -INFINITY;
+          for (int32_t j = 0; j <= i; ++j) {
+            double acc = 0.0;
+            for (int32_t c = 0; c < dh; ++c) acc += widen(q, dtype, qb + c) * widen(k, dtype, kb + (int64_t)j * dh + c);
+            s[j] = acc * scale;
+            if (s[j] > m) m = s[j];
+          }
+          double l = 0.0;
+          for (int32_t j = 0; j <= i; ++j) {
+            s[j] = exp(s[j] - m);
+            l += s[j];
+          }
+          for (int32_t j = 0; j <= i; ++j) row[j] += s[j] / l;
+        }
+        for (int32_t j = 0; j <= i; ++j) row[j] /= (double)B;
+      }
+    free(s);
   }
 }
 

@@ -348,3 +348,32 @@ def test_query_form_diagonal_zero_returns_the_cache_row():
     o, _ = oracle.attention_queries(d, qv, k, v, np.array([(0, 0, t) for t in ts], np.int32))
     for n, t in enumerate(ts):
         assert np.array_equal(o[n], W.bf16_bits_to_f32(v[0, 0, t]).astype(np.float64))
+
+
+# ------------------------------------------------------------------ averaged attention maps (capture input)
+def test_attention_maps_rows_sum_to_one_and_zero_above_diagonal():
+    q, k, _ = W.qkv(51, 3, 4, 2, 40, 16, "bf16")
+    m = oracle.attention_maps(q, k)
+    np.testing.assert_allclose(m.sum(axis=2), 1.0, atol=1e-12)
+    assert np.all(m[:, np.triu_indices(40, 1)[0], np.triu_indices(40, 1)[1]] == 0.0)
+
+
+def test_attention_maps_equal_keys_give_uniform_rows():
+    """Every key equal: each causal row is uniform, 1 / (i + 1), whatever the queries."""
+    q, _, _ = W.qkv(52, 2, 2, 1, 30, 8, "f32")
+    k = np.tile(np.random.default_rng(52).standard_normal((1, 1, 1, 8)).astype(np.float32), (2, 1, 30, 1))
+    m = oracle.attention_maps(q, k)
+    i = np.arange(30)
+    expect = np.where(i[None, :] <= i[:, None], 1.0 / (i[:, None] + 1.0), 0.0)
+    np.testing.assert_allclose(m, np.broadcast_to(expect, m.shape), atol=1e-14)
+
+
+def test_attention_maps_match_torch_softmax_average():
+    q, k, _ = W.qkv(53, 3, 4, 2, 33, 16, "f32")
+    m = oracle.attention_maps(q, k, scale=0.3)
+    qt = torch.from_numpy(q.astype(np.float64))
+    kt = torch.from_numpy(np.repeat(k, 2, axis=1).astype(np.float64))
+    s = (qt @ kt.transpose(-1, -2)) * 0.3
+    s = s.masked_fill(~torch.tril(torch.ones(33, 33, dtype=torch.bool)), float("-inf"))
+    ref = torch.softmax(s, dim=-1).mean(dim=0).numpy()
+    np.testing.assert_allclose(m, ref, atol=1e-13)
