@@ -135,6 +135,34 @@ def capture_ms(sa, torch, reps=5):
     return dict(ms=ms, maps=int(maps.shape[0]), L=512, read_GBps=causal_bytes / (ms * 1e-3) / 1e9)
 
 
+def maps_from_qk_ms(sa, torch, reps=5):
+    """Capture maps from Q/K: 16 layers x 32 query heads (8 kv heads per layer) stacked into one
+    call, batch 16, L = 512, d = 64 (bf16), then the capture of those 512 maps.  One layer's
+    structured Q/K is generated and repeated over the 16 layers (the work does not depend on values)."""
+    import workloads as W
+    q, k = W.capture_qk(47, 16, 32, 8, 512, 64, "bf16")
+    qd = torch.from_numpy(q.view(np.int16)).cuda().view(torch.bfloat16).repeat(1, 16, 1, 1).contiguous()
+    kd = torch.from_numpy(k.view(np.int16)).cuda().view(torch.bfloat16).repeat(1, 16, 1, 1).contiguous()
+    maps = torch.empty((512, 512, 512), dtype=torch.float32, device="cuda")
+    sa.attention_maps(qd, kd, out=maps)
+    sa.pattern_capture(maps)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record()
+    for _ in range(reps):
+        sa.attention_maps(qd, kd, out=maps)
+    ev[1].record()
+    for _ in range(reps):
+        sa.pattern_capture(maps)
+    ev[2].record()
+    torch.cuda.synchronize()
+    maps_ms, cap_ms = ev[0].elapsed_time(ev[1]) / reps, ev[1].elapsed_time(ev[2]) / reps
+    nrb = 512 // 64
+    flops = 2.0 * 2 * 16 * 512 * (nrb * (nrb + 1) // 2) * 64 * 64 * 64   # two score passes over the computed tiles
+    return dict(maps_ms=maps_ms, capture_ms=cap_ms, B=16, heads=512, L=512, d=64,
+                maps_tile_TFLOPs=flops / (maps_ms * 1e-3) / 1e12)
+
+
 def decode_row_keys(ixn, h, t, nb, BM, nwords):
     """Retained keys of row t of head h, read off the index (segments filtered by the diagonal bitmap
     and the in-segment columns, then the gathered columns <= t)."""
@@ -279,6 +307,9 @@ def main():
         torch.cuda.empty_cache()
         extras["capture"] = capture_ms(sa, torch)
         log("capture: %.3f ms" % extras["capture"]["ms"])
+        extras["capture_from_qk"] = maps_from_qk_ms(sa, torch)
+        log("capture from Q/K: maps %.3f ms + capture %.3f ms" % (extras["capture_from_qk"]["maps_ms"],
+                                                                extras["capture_from_qk"]["capture_ms"]))
         extras["decode"] = decode_bench(sa, torch)
         log("decode: %.3f ms for %d tokens (%.0f GB/s of retained K/V rows)" % (
             extras["decode"]["ms"], 16, extras["decode"]["kv_GBps"]))

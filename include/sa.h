@@ -24,6 +24,8 @@
  *     synchronise `stream`.
  *   - The library never allocates or frees device memory: the caller owns every
  *     buffer.  It keeps no state between calls; calls are thread-safe.
+ *   - q, k, v, o and maps base addresses are 16-byte aligned (hipMalloc's are);
+ *     a misaligned one is SA_ERR_INVALID_ARG.
  *   - Arguments are validated on the host before anything is enqueued: a negative
  *     return value means nothing was launched, except SA_ERR_HIP, which reports a
  *     failed launch.
@@ -209,6 +211,23 @@ sa_status sa_sparse_attn_prefill(const void* q, const void* k, const void* v, vo
 sa_status sa_sparse_attn_decode(const void* q, const void* k, const void* v, const int32_t* pos, void* o, float* lse,
                                 int32_t batch, int32_t hq, int32_t hkv, int32_t S, int32_t head_dim, int32_t dtype,
                                 float softmax_scale, const sa_index* idx, void* stream);
+
+/*
+ * sa_attention_maps [DAM, What carries the argument: average attention maps of the
+ * first L (pattern capture length) positions, accumulated over the inputs;
+ * Assumptions & free parameters: the batch mean stands in for each sequence]:
+ *   maps[h][i][j] = (1/batch) sum_b softmax_j( q[b][h][i] . k[b][g][j] * scale ),
+ *                   the softmax over j <= i;  maps[h][i][j] = 0 for j > i,
+ *   g = h / (hq / hkv); softmax_scale <= 0 selects 1 / sqrt(head_dim).
+ *   q [batch][hq][L][head_dim], k [batch][hkv][L][head_dim]: element type `dtype`.
+ *   maps  float [hq][L][L] (every element written): the input of sa_pattern_capture.
+ * Arithmetic: fp32 MFMA scores, fp32 softmax (exp2 domain), batch mean accumulated
+ * in element order b = 0, 1, ...
+ * Limits: 1 <= L <= 4096, head_dim 64 or 128.
+ * Errors: SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_HIP.
+ */
+sa_status sa_attention_maps(const void* q, const void* k, int32_t batch, int32_t hq, int32_t hkv, int32_t L,
+                            int32_t head_dim, int32_t dtype, float softmax_scale, float* maps, void* stream);
 
 /*
  * sa_pattern_capture [DAM, What carries the argument]: for each averaged attention

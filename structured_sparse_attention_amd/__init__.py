@@ -18,7 +18,7 @@ import numpy as np
 import torch
 
 __all__ = ["SAError", "DevicePatterns", "SparseIndex", "build_index", "sparse_attn_prefill", "sparse_attn_decode",
-           "pattern_capture", "patterns_to_desc", "library_path", "version", "lib"]
+           "attention_maps", "pattern_capture", "patterns_to_desc", "library_path", "version", "lib"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libsa.so")
@@ -71,6 +71,8 @@ def _load():
     lib.sa_sparse_attn_decode.restype = C.c_int32
     lib.sa_sparse_attn_decode.argtypes = [C.c_void_p] * 6 + [C.c_int32] * 6 + [C.c_float, C.POINTER(_Index),
                                                                                  C.c_void_p]
+    lib.sa_attention_maps.restype = C.c_int32
+    lib.sa_attention_maps.argtypes = [C.c_void_p, C.c_void_p] + [C.c_int32] * 6 + [C.c_float, C.c_void_p, C.c_void_p]
     lib.sa_pattern_capture.restype = C.c_int32
     lib.sa_pattern_capture.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_double, C.c_double, C.c_double,
                                        C.c_double, C.c_int32] + [C.c_void_p] * 5 + [C.c_void_p]
@@ -282,6 +284,32 @@ def sparse_attn_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pos: t
                                       _ptr(lse), B, hq, k.shape[1], S, d, dt, scale, C.byref(c), _stream(stream)),
            "sa_sparse_attn_decode")
     return (o, lse) if return_lse else o
+
+
+def attention_maps(q: torch.Tensor, k: torch.Tensor, softmax_scale: Optional[float] = None,
+                   out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """sa_attention_maps: batch-averaged causal attention maps [Hq, L, L] (float32) of q [B,Hq,L,d] against
+    k [B,Hkv,L,d] (bf16 or fp32, contiguous, on the GPU); the input of pattern_capture."""
+    if q.dtype == torch.bfloat16:
+        dt = SA_DTYPE_BF16
+    elif q.dtype == torch.float32:
+        dt = SA_DTYPE_F32
+    else:
+        raise TypeError("q must be bfloat16 or float32")
+    if k.dtype != q.dtype:
+        raise TypeError("q and k must share one dtype")
+    if q.dim() != 4 or k.dim() != 4 or not (q.is_contiguous() and k.is_contiguous()):
+        raise ValueError("contiguous q [B,Hq,L,d] and k [B,Hkv,L,d] expected")
+    B, hq, L, d = q.shape
+    if k.shape[0] != B or k.shape[2] != L or k.shape[3] != d:
+        raise ValueError("k shape does not match q")
+    maps = torch.empty((hq, L, L), dtype=torch.float32, device=q.device) if out is None else out
+    if maps.shape != (hq, L, L) or maps.dtype != torch.float32 or not maps.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [Hq, L, L] tensor")
+    scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    _check(_lib.sa_attention_maps(q.data_ptr(), k.data_ptr(), B, hq, k.shape[1], L, d, dt, scale, maps.data_ptr(),
+                                  _stream(stream)), "sa_attention_maps")
+    return maps
 
 
 def pattern_capture(maps: torch.Tensor, lam: float = 0.5, eps: float = 1e-8, tau: float = 0.3, mu: float = 0.8,

@@ -10,6 +10,8 @@ namespace {
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 sa_status hip_status(hipError_t e) { return e == hipSuccess ? SA_OK : SA_ERR_HIP; }
+// element rows are moved in 16-byte vectors
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool index_arrays_ok(const sa_index& ix) {
   return ix.run_ptr && ix.run_lo && ix.run_hi && ix.seg_ptr && ix.seg_lo && ix.seg_hi && ix.bcol_ptr &&
@@ -98,6 +100,7 @@ sa_status sa_sparse_attn_prefill(const void* q, const void* k, const void* v, vo
                                  int32_t hq, int32_t hkv, int32_t S, int32_t head_dim, int32_t dtype,
                                  float softmax_scale, const sa_index* idx, void* stream) {
   if (!q || !k || !v || !o || !idx) return SA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SA_ERR_INVALID_ARG;
   if (batch < 1 || hq < 1 || hkv < 1 || S < 1 || hq % hkv != 0) return SA_ERR_INVALID_ARG;
   if (dtype != SA_DTYPE_BF16 && dtype != SA_DTYPE_F32) return SA_ERR_INVALID_ARG;
   if (head_dim != 64 && head_dim != 128) return SA_ERR_UNSUPPORTED;
@@ -116,6 +119,7 @@ sa_status sa_sparse_attn_decode(const void* q, const void* k, const void* v, con
                                 int32_t batch, int32_t hq, int32_t hkv, int32_t S, int32_t head_dim, int32_t dtype,
                                 float softmax_scale, const sa_index* idx, void* stream) {
   if (!q || !k || !v || !pos || !o || !idx) return SA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SA_ERR_INVALID_ARG;
   if (batch < 1 || hq < 1 || hkv < 1 || S < 1 || hq % hkv != 0) return SA_ERR_INVALID_ARG;
   if (dtype != SA_DTYPE_BF16 && dtype != SA_DTYPE_F32) return SA_ERR_INVALID_ARG;
   if (head_dim != 64 && head_dim != 128) return SA_ERR_UNSUPPORTED;
@@ -141,6 +145,21 @@ sa_status sa_pattern_capture(const float* maps, int32_t n_maps, int32_t L, doubl
   if (L > sa::kMaxCaptureL) return SA_ERR_UNSUPPORTED;
   return hip_status(sa::launch_capture(maps, n_maps, L, lambda, eps, tau, mu, norm_scope, keep_diag, keep_vert,
                                        diag_hits, vert_hits, true_mask, static_cast<hipStream_t>(stream)));
+}
+
+sa_status sa_attention_maps(const void* q, const void* k, int32_t batch, int32_t hq, int32_t hkv, int32_t L,
+                            int32_t head_dim, int32_t dtype, float softmax_scale, float* maps, void* stream) {
+  if (!q || !k || !maps) return SA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(maps)) return SA_ERR_INVALID_ARG;
+  if (batch < 1 || hq < 1 || hkv < 1 || L < 1 || hq % hkv != 0) return SA_ERR_INVALID_ARG;
+  if (dtype != SA_DTYPE_BF16 && dtype != SA_DTYPE_F32) return SA_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return SA_ERR_UNSUPPORTED;
+  if (L > sa::kMaxCaptureL) return SA_ERR_UNSUPPORTED;
+  if ((int64_t)hq * ((L + 63) / 64) > 0x7fffffffLL) return SA_ERR_UNSUPPORTED;
+  const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf((float)head_dim);
+  if (!isfinite(scale)) return SA_ERR_INVALID_ARG;
+  return hip_status(sa::launch_attention_maps(q, k, batch, hq, hkv, L, head_dim, dtype, scale, maps,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 sa_status sa_patterns_to_desc(const uint8_t* keep_diag, const uint8_t* keep_vert, int32_t n_maps, int32_t L,

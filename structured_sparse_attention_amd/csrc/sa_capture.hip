@@ -22,6 +22,8 @@
 // Layout: one 1024-thread workgroup per map; wave w takes rows w, w+16, ...; lanes
 // take columns, four loads in flight per lane.  Hits accumulate with LDS atomics; the map is read once from HBM
 // (the causal half) plus once more for the fp32 row min/max, which hits in cache.
+#include <type_traits>
+
 #include "sa_internal.h"
 
 namespace sa {
@@ -146,6 +148,191 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
+// ---------------------------------------------------------------------------
+// Averaged attention maps at the capture length ("What carries the argument":
+// average attention maps of the first L positions, accumulated over the inputs;
+// "Assumptions & free parameters": the batch mean stands in for each sequence):
+//   maps[h][i][j] = (1/B) sum_b softmax_j(q_bhi . k_bgj * scale), j <= i; 0 above.
+// One workgroup (two waves, 64 query rows) per (head, 64-row block).  Scores are
+// S^T = K Q^T on MFMA (lane = query row, as in the attention kernels) over 64-key
+// tiles staged in LDS.  Sequences are taken kMapChunk at a time: pass 1 finds the
+// row max and 1/sum (exp2 domain) of every sequence of the chunk and keeps them in
+// LDS; pass 2 walks the key tiles once, recomputes each sequence's scores and sums
+// p_b / B in registers, so a map element is written once per chunk (added to the
+// previous chunks' sum after the first).  No other workgroup touches these rows.
+// ---------------------------------------------------------------------------
+typedef __bf16 mbf16x8 __attribute__((ext_vector_type(8)));
+typedef float mf32x16 __attribute__((ext_vector_type(16)));
+constexpr int kMapChunk = 16;
+
+template <int D, bool BF16>
+__global__ void __launch_bounds__(128) k_maps(const void* qv, const void* kv, int32_t B, int32_t hq, int32_t hkv,
+                                              int32_t L, float scale_log2, float* maps) {
+  using E = typename std::conditional<BF16, uint16_t, float>::type;
+  using QF = typename std::conditional<BF16, mbf16x8, float>::type;
+  constexpr int QS = BF16 ? D / 16 : D / 2;           // MFMA k-steps over d
+  constexpr int KSTR = BF16 ? D + 8 : D + 1;          // LDS row stride of the K tile (elements)
+  __shared__ __attribute__((aligned(16))) E Ks[64 * KSTR];
+  __shared__ float st_m[kMapChunk][128], st_il[kMapChunk][128];  // per lane: its row's max, 1/sum
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, r32 = lane & 31;
+  const int nrb = (L + 63) / 64;
+  const int h = blockIdx.x / nrb, rb = blockIdx.x % nrb;
+  const int kvh = h / (hq / hkv);
+  const int i = rb * 64 + wave * 32 + r32;  // this lane's query row
+  const bool row_ok = i < L;
+  const float invB = 1.0f / (float)B;
+  const bool vec_rows = (L & 3) == 0;  // map rows 16-byte aligned
+  float* mrow = maps + ((int64_t)h * L + (row_ok ? i : 0)) * L;
+
+  // zeros above the block diagonal (keys of the tiles past this row block)
+  for (int r = 0; r < 64 && rb * 64 + r < L; ++r) {
+    float* zrow = maps + ((int64_t)h * L + rb * 64 + r) * L;
+    for (int jj = (rb + 1) * 64 + tid; jj < L; jj += 128) zrow[jj] = 0.0f;
+  }
+
+  auto kbase = [&](int b) { return static_cast<const E*>(kv) + ((int64_t)b * hkv + kvh) * L * (int64_t)D; };
+  auto load_q = [&](int b, QF (&qf)[QS]) {
+    const E* Qb = static_cast<const E*>(qv) + ((int64_t)b * hq + h) * L * (int64_t)D;
+#pragma unroll
+    for (int s = 0; s < QS; ++s) {
+      if constexpr (BF16) {
+        uint4 u = make_uint4(0u, 0u, 0u, 0u);
+        if (row_ok) u = *reinterpret_cast<const uint4*>(Qb + (int64_t)i * D + 16 * s + 8 * g);
+        qf[s] = __builtin_bit_cast(mbf16x8, u);
+      } else {
+        qf[s] = row_ok ? Qb[(int64_t)i * D + 2 * s + g] : 0.0f;
+      }
+    }
+  };
+  auto load_tile = [&](const E* Kb, int kt) {  // keys kt*64 .. kt*64+63 of one sequence into LDS
+    __syncthreads();
+    constexpr int CH = D * (int)sizeof(E) / 16;  // 16-byte chunks per key row
+    for (int x = tid; x < 64 * CH; x += 128) {
+      const int r = x / CH, c = x % CH, j = kt * 64 + r;
+      uint4 u = make_uint4(0u, 0u, 0u, 0u);
+      if (j < L) u = *(reinterpret_cast<const uint4*>(Kb + (int64_t)j * D) + c);
+      E* dst = Ks + r * KSTR + c * (16 / (int)sizeof(E));
+      if constexpr (BF16) {
+        *reinterpret_cast<uint4*>(dst) = u;
+      } else {
+        dst[0] = __uint_as_float(u.x);
+        dst[1] = __uint_as_float(u.y);
+        dst[2] = __uint_as_float(u.z);
+        dst[3] = __uint_as_float(u.w);
+      }
+    }
+    __syncthreads();
+  };
+  // scaled logits of the LDS tile for this lane's row: value v of block kb is key
+  // kt*64 + kb*32 + 8(v/4) + 4g + v%4; keys past the row are -inf
+  auto scores = [&](const QF (&qf)[QS], int kt, float (&x)[2][16]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      mf32x16 acc;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < QS; ++s) {
+        if constexpr (BF16) {
+          const mbf16x8 kf = *reinterpret_cast<const mbf16x8*>(&Ks[(kb * 32 + r32) * KSTR + 16 * s + 8 * g]);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], acc, 0, 0, 0);
+        } else {
+          const float kf = Ks[(kb * 32 + r32) * KSTR + 2 * s + g];
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kf, qf[s], acc, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int j = kt * 64 + kb * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+        x[kb][v] = (j <= i) ? acc[v] * scale_log2 : -INFINITY;
+      }
+    }
+  };
+
+  for (int b0 = 0; b0 < B; b0 += kMapChunk) {
+    const int nb = min(kMapChunk, B - b0);
+    // pass 1: row max and 1/sum of each sequence of the chunk
+    for (int bb = 0; bb < nb; ++bb) {
+      QF qf[QS];
+      load_q(b0 + bb, qf);
+      float m = -INFINITY, l = 0.0f;
+      for (int kt = 0; kt <= rb; ++kt) {
+        load_tile(kbase(b0 + bb), kt);
+        float x[2][16];
+        scores(qf, kt, x);
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, x[kb][v]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));  // the row's other keys sit in lane ^ 32
+        const float mn = fmaxf(m, tmax);  // finite: key kt*64 <= i for every kt <= rb
+        float part = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) part += __builtin_amdgcn_exp2f(x[kb][v] - mn);
+        part += __shfl_xor(part, 32, 64);
+        l = (m == -INFINITY ? 0.0f : l * __builtin_amdgcn_exp2f(m - mn)) + part;
+        m = mn;
+      }
+      st_m[bb][tid] = m;  // read back by this lane only
+      st_il[bb][tid] = 1.0f / l;
+    }
+    // pass 2: per key tile, the chunk's probabilities summed in registers
+    for (int kt = 0; kt <= rb; ++kt) {
+      float acc[2][16];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[kb][v] = 0.0f;
+      for (int bb = 0; bb < nb; ++bb) {
+        QF qf[QS];
+        load_q(b0 + bb, qf);
+        load_tile(kbase(b0 + bb), kt);
+        float x[2][16];
+        scores(qf, kt, x);
+        const float m = st_m[bb][tid], il = st_il[bb][tid];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[kb][v] += __builtin_amdgcn_exp2f(x[kb][v] - m) * il;
+      }
+      if (row_ok) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const int j0 = kt * 64 + kb * 32 + 8 * qd + 4 * g;
+            if (vec_rows && j0 + 3 < L) {
+              float4* dst = reinterpret_cast<float4*>(mrow + j0);
+              float4 cur = b0 == 0 ? make_float4(0.0f, 0.0f, 0.0f, 0.0f) : *dst;
+              cur.x += acc[kb][4 * qd + 0] * invB;
+              cur.y += acc[kb][4 * qd + 1] * invB;
+              cur.z += acc[kb][4 * qd + 2] * invB;
+              cur.w += acc[kb][4 * qd + 3] * invB;
+              *dst = cur;
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (j0 + e < L) mrow[j0 + e] = (b0 == 0 ? 0.0f : mrow[j0 + e]) + acc[kb][4 * qd + e] * invB;
+            }
+          }
+      }
+    }
+  }
+}
+
+template <int D, bool BF16>
+hipError_t launch_maps_t(const void* q, const void* k, int32_t B, int32_t hq, int32_t hkv, int32_t L, float scale,
+                         float* maps, hipStream_t stream) {
+  const int nrb = (L + 63) / 64;
+  k_maps<D, BF16><<<dim3((unsigned)(hq * nrb)), dim3(128), 0, stream>>>(q, k, B, hq, hkv, L,
+                                                                          scale * 1.44269504088896340736f, maps);
+  return hipGetLastError();
+}
+
 // kept flags -> CSR descriptor lists at length S (entries < S).  One workgroup.
 constexpr int kDescThreads = 1024;
 __global__ void __launch_bounds__(kDescThreads)
@@ -190,6 +377,15 @@ hipError_t launch_capture(const float* maps, int32_t n_maps, int32_t L, double l
   hipLaunchKernelGGL(k_capture, dim3((unsigned)n_maps), dim3(kThreads), lds, stream, maps, L, lambda, eps, tau, mu,
                      norm_scope, keep_diag, keep_vert, diag_hits, vert_hits, true_mask);
   return hipGetLastError();
+}
+
+hipError_t launch_attention_maps(const void* q, const void* k, int32_t batch, int32_t hq, int32_t hkv, int32_t L,
+                                 int32_t head_dim, int32_t dtype, float scale, float* maps, hipStream_t stream) {
+  if (dtype == SA_DTYPE_BF16)
+    return head_dim == 64 ? launch_maps_t<64, true>(q, k, batch, hq, hkv, L, scale, maps, stream)
+                          : launch_maps_t<128, true>(q, k, batch, hq, hkv, L, scale, maps, stream);
+  return head_dim == 64 ? launch_maps_t<64, false>(q, k, batch, hq, hkv, L, scale, maps, stream)
+                        : launch_maps_t<128, false>(q, k, batch, hq, hkv, L, scale, maps, stream);
 }
 
 hipError_t launch_patterns_to_desc(const uint8_t* keep_diag, const uint8_t* keep_vert, int32_t n_maps, int32_t L,

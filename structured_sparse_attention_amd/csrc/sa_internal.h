@@ -51,6 +51,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_capture(const float* maps, int32_t n_maps, int32_t L, double lambda, double eps, double tau,
                           double mu, int32_t norm_scope, uint8_t* keep_diag, uint8_t* keep_vert, int32_t* diag_hits,
                           int32_t* vert_hits, uint8_t* true_mask, hipStream_t stream);
+hipError_t launch_attention_maps(const void* q, const void* k, int32_t batch, int32_t hq, int32_t hkv, int32_t L,
+                                 int32_t head_dim, int32_t dtype, float scale, float* maps, hipStream_t stream);
 hipError_t launch_patterns_to_desc(const uint8_t* keep_diag, const uint8_t* keep_vert, int32_t n_maps, int32_t L,
                                    int32_t S, int32_t* diag_ptr, int32_t* diag_off, int32_t* vert_ptr,
                                    int32_t* vert_col, hipStream_t stream);

@@ -25,8 +25,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for f in ("sa_build_index", "sa_sparse_attn_prefill", "sa_sparse_attn_decode", "sa_pattern_capture",
-              "sa_patterns_to_desc", "sa_status_string", "sa_version"):
+    for f in ("sa_build_index", "sa_sparse_attn_prefill", "sa_sparse_attn_decode", "sa_attention_maps",
+              "sa_pattern_capture", "sa_patterns_to_desc", "sa_status_string", "sa_version"):
         assert f in names
 
 
@@ -93,6 +93,7 @@ def test_attention_validation(m):
     assert f(p, p, p, p, None, 1, 2, 1, 512, 64, 1, 0.0, C.byref(ix), None) == -1   # heads != index heads
     assert f(p, p, p, p, None, 0, 1, 1, 512, 64, 1, 0.0, C.byref(ix), None) == -1   # batch
     assert f(p, p, p, p, None, 1, 1, 1, 512, 64, 1, 0.0, C.byref(_index(m, col_idx=None)), None) == -1
+    assert f(p, p, p, p + 8, None, 1, 1, 1, 512, 64, 1, 0.0, C.byref(ix), None) == -1  # o not 16-byte aligned
 
 
 def test_decode_validation(m):
@@ -107,6 +108,21 @@ def test_decode_validation(m):
     assert f(p, p, p, p, p, None, 1, 1, 1, 256, 64, 1, 0.0, C.byref(ix), None) == -1     # S != index S
     assert f(p, p, p, p, p, None, 0, 1, 1, 512, 64, 1, 0.0, C.byref(ix), None) == -1     # batch
     assert f(p, p, p, p, p, None, 1, 1, 1, 512, 64, 1, float("inf"), C.byref(ix), None) == -1
+    assert f(p, p, p + 2, p, p, None, 1, 1, 1, 512, 64, 1, 0.0, C.byref(ix), None) == -1  # v not 16-byte aligned
+
+
+def test_attention_maps_validation(m):
+    f = m.lib.sa_attention_maps
+    p = FAKE.value
+    assert f(None, p, 1, 1, 1, 64, 64, 1, 0.0, p, None) == -1
+    assert f(p, p, 1, 1, 1, 64, 64, 1, 0.0, None, None) == -1
+    assert f(p, p, 1, 3, 2, 64, 64, 1, 0.0, p, None) == -1      # hq % hkv
+    assert f(p, p, 0, 1, 1, 64, 64, 1, 0.0, p, None) == -1      # batch
+    assert f(p, p, 1, 1, 1, 64, 64, 9, 0.0, p, None) == -1      # dtype
+    assert f(p, p, 1, 1, 1, 64, 80, 1, 0.0, p, None) == -2      # head_dim
+    assert f(p, p, 1, 1, 1, 5000, 64, 1, 0.0, p, None) == -2    # L above the capture window
+    assert f(p + 4, p, 1, 1, 1, 64, 64, 1, 0.0, p, None) == -1  # q not 16-byte aligned
+    assert f(p, p, 1, 1, 1, 64, 64, 1, 0.0, p + 8, None) == -1  # maps not 16-byte aligned
 
 
 def test_capture_validation(m):

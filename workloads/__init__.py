@@ -206,6 +206,37 @@ def capture_maps(layers: int = 16, heads: int = 32, L: int = 512, n_avg: int = 1
     return out
 
 
+def capture_qk(config_id: int, B: int, hq: int, hkv: int, L: int, d: int, dtype: str, n_freq: int = 12,
+               local: float = 6.0, sink: float = 6.0):
+    """Q [B,hq,L,d], K [B,hkv,L,d] whose causal attention carries local-band and sink-column structure.
+
+    Dims 0..2*n_freq-1 hold a positional code: q_i and k_j carry cos/sin(w_m * pos) with
+    w_m geometric in [pi/256, pi/16], so their product depends on i - j only and peaks at
+    i = j with height `local` (in units of the 1/sqrt(d) scaled logit).  Dim 2*n_freq is a
+    shared direction: every query has a, keys j < 4 and 4 seeded columns per kv head have a,
+    with a*a/sqrt(d) = `sink`.  Remaining dims and all dims get N(0, 0.5^2) noise per sequence.
+    """
+    rt = np.sqrt(np.sqrt(d))
+    w = np.geomspace(np.pi / 256, np.pi / 16, n_freq)
+    pos = np.arange(L)[:, None] * w[None, :]
+    code = np.concatenate([np.cos(pos), np.sin(pos)], axis=1) * np.sqrt(local / n_freq) * rt   # [L, 2*n_freq]
+    a = np.sqrt(sink) * rt
+    q = np.zeros((B, hq, L, d), np.float64)
+    k = np.zeros((B, hkv, L, d), np.float64)
+    q[..., :2 * n_freq] = code
+    k[..., :2 * n_freq] = code
+    q[..., 2 * n_freq] = a
+    for g in range(hkv):
+        rng = np.random.default_rng([config_id, 3000, g])
+        cols = np.concatenate([np.arange(min(4, L)), rng.choice(np.arange(4, L), size=min(4, max(L - 4, 0)), replace=False)])
+        k[:, g, cols, 2 * n_freq] = a
+    rng = np.random.default_rng([config_id, 3001])
+    q += 0.5 * rng.standard_normal(q.shape)
+    k += 0.5 * rng.standard_normal(k.shape)
+    q, k = q.astype(np.float32), k.astype(np.float32)
+    return (q, k) if dtype == "f32" else (bf16_bits(q), bf16_bits(k))
+
+
 def llama8b_like(S: int = 65536, H: int = 32, band: int = 1024, block_p: float = 0.08,
                  block_size: int = 64) -> PatternDesc:
     """Workload 4: even heads vertical+slash, odd heads 64x64 block-sparse."""
