@@ -76,6 +76,12 @@ def _load():
             lib.orc_capture.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_double, C.c_double, C.c_double,
                                         C.c_double, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                         C.c_void_p]
+            lib.orc_capture_scores.restype = C.c_int
+            lib.orc_capture_scores.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_double, C.c_double, C.c_int32,
+                                               C.c_void_p]
+            lib.orc_coverage.restype = None
+            lib.orc_coverage.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
+                                         C.c_void_p]
             _lib = lib
     return _lib
 
@@ -245,8 +251,32 @@ def capture(maps: np.ndarray, lam: float = 0.5, eps: float = 1e-8, tau: float = 
     rc = lib.orc_capture(maps.ctypes.data, n, L, lam, eps, tau, mu, norm_scope, kd.ctypes.data, kv.ctypes.data,
                          hdg.ctypes.data, hv.ctypes.data, None if tm is None else tm.ctypes.data)
     if rc != 0:
-        raise ValueError("oracle capture supports lambda = 0.5 only")
+        raise ValueError("lambda must be finite, and eps > 0 when lambda <= 0")
     return dict(keep_diag=kd, keep_vert=kv, diag_hits=hdg, vert_hits=hv, true_mask=tm)
+
+
+def capture_scores(maps: np.ndarray, lam: float = 0.5, eps: float = 1e-8, norm_scope: int = 0) -> np.ndarray:
+    """The normalised Box-Cox value t (float64 [n, L, L]) that capture compares with tau; NaN above the diagonal."""
+    lib = _load()
+    maps = np.ascontiguousarray(maps, dtype=np.float32)
+    n, L, _ = maps.shape
+    t = np.empty((n, L, L), np.float64)
+    if lib.orc_capture_scores(maps.ctypes.data, n, L, lam, eps, norm_scope, t.ctypes.data) != 0:
+        raise ValueError("lambda must be finite, and eps > 0 when lambda <= 0")
+    return t
+
+
+def coverage(maps: np.ndarray, keep_diag: np.ndarray, keep_vert: np.ndarray):
+    """Per map: (attention mass share, cell count) of the kept patterns inside the L x L causal window."""
+    lib = _load()
+    maps = np.ascontiguousarray(maps, dtype=np.float32)
+    n, L, _ = maps.shape
+    kd = np.ascontiguousarray(keep_diag, dtype=np.uint8).reshape(n, L)
+    kv = np.ascontiguousarray(keep_vert, dtype=np.uint8).reshape(n, L)
+    mass = np.zeros(n, np.float64)
+    cells = np.zeros(n, np.int64)
+    lib.orc_coverage(maps.ctypes.data, n, L, kd.ctypes.data, kv.ctypes.data, mass.ctypes.data, cells.ctypes.data)
+    return mass, cells
 
 
 def extend(keep_diag: np.ndarray, keep_vert: np.ndarray, S: int):

@@ -36,6 +36,12 @@
  *   orc_capture          Box-Cox / threshold / overlap score / keep -> closed form,
  *                        hand-worked example (tests/golden/capture_example.txt),
  *                        planted patterns
+ *   orc_capture_scores   the normalised transform t of every causal cell, any
+ *                        lambda -> scipy.special.boxcox plus min-max, the
+ *                        linear case lambda = 1, the log case lambda = 0
+ *   orc_coverage         attention mass and cell count of the kept patterns
+ *                        inside the capture window -> brute-force numpy masks,
+ *                        all-kept and diagonal-0-only cases
  */
 #include <math.h>
 #include <stdint.h>
@@ -456,26 +462,77 @@ void orc_attention_maps(const void* q, const void* k, int dtype, int32_t B, int3
 /* i >= c; overlap score gamma_k = sum(M * P_k) / sum(P_k); keep if         */
 /* gamma_k >= mu = 0.8.  Referee Report, minor comment 1: the stabiliser    */
 /* epsilon is 1e-8 in one section and 1e-10 in an appendix (a parameter).   */
-/* Box-Cox (textbook): y = (x^lambda - 1) / lambda, x = A + eps; for        */
-/* lambda = 0.5, x^lambda = sqrt(x).  The pages do not say how y is scaled  */
-/* before comparing with tau; this oracle min-max normalises y per causal   */
-/* row (norm_scope 0) or per map (norm_scope 1).  A row or map whose        */
-/* transformed values are all equal counts as fully retained.               */
-/* Only the causal half (j <= i) of each map is read.                       */
-/* Operation order is fixed: x = A + eps; s = sqrt(x); y = (s - 1) / lambda; */
-/* t = (y - ymin) / (ymax - ymin); M = (t >= tau).                           */
-/* Returns 0, or 2 if lambda != 0.5 (only the square-root case is exact).   */
+/* Box-Cox (textbook): y = (x^lambda - 1) / lambda, x = A + eps, and       */
+/* y = log x at lambda = 0.  For lambda = 0.5, x^lambda = sqrt(x), which is */
+/* correctly rounded, so that case is exact; other lambdas use the C        */
+/* library's pow / log (the referee's sensitivity question needs them).     */
+/* The pages do not say how y is scaled before comparing with tau; this     */
+/* oracle min-max normalises y per causal row (norm_scope 0) or per map     */
+/* (norm_scope 1).  A row or map whose transformed values are all equal     */
+/* counts as fully retained (t = 1).  Only the causal half (j <= i) of each */
+/* map is read.  Operation order: x = A + eps; y as above;                  */
+/* t = (y - ymin) / (ymax - ymin); M = (t >= tau).                          */
+/* Returns 0, or 2 for a non-finite lambda, or for lambda <= 0 with eps <= 0 */
+/* (x = 0 would give an infinite y).                                        */
 /* ------------------------------------------------------------------------ */
-static double boxcox_half(float a, double eps, double lambda) {
+static double boxcox(float a, double eps, double lambda) {
   double x = (double)a + eps;
-  double s = sqrt(x);
-  return (s - 1.0) / lambda;
+  if (lambda == 0.5) {
+    double s = sqrt(x);
+    return (s - 1.0) / lambda;
+  }
+  if (lambda == 0.0) return log(x);
+  return (pow(x, lambda) - 1.0) / lambda;
+}
+
+static int lambda_ok(double lambda, double eps) { return isfinite(lambda) && (lambda > 0.0 || eps > 0.0); }
+
+/* min and max of y over the causal map (norm_scope 1) */
+static void map_range(const float* A, int32_t L, double eps, double lambda, double* gmin, double* gmax) {
+  *gmin = INFINITY;
+  *gmax = -INFINITY;
+  for (int32_t i = 0; i < L; ++i)
+    for (int32_t j = 0; j <= i; ++j) {
+      double y = boxcox(A[(int64_t)i * L + j], eps, lambda);
+      if (y < *gmin) *gmin = y;
+      if (y > *gmax) *gmax = y;
+    }
+}
+
+/* t[j], j <= i, of row i; gmin/gmax are used when norm_scope is 1 */
+static void row_scores(const float* A, int32_t L, int32_t i, double eps, double lambda, int32_t norm_scope,
+                       double gmin, double gmax, double* t) {
+  double ymin = INFINITY, ymax = -INFINITY;
+  for (int32_t j = 0; j <= i; ++j) {
+    t[j] = boxcox(A[(int64_t)i * L + j], eps, lambda);
+    if (t[j] < ymin) ymin = t[j];
+    if (t[j] > ymax) ymax = t[j];
+  }
+  if (norm_scope == 1) { ymin = gmin; ymax = gmax; }
+  for (int32_t j = 0; j <= i; ++j) t[j] = (ymax == ymin) ? 1.0 : (t[j] - ymin) / (ymax - ymin);
+}
+
+int orc_capture_scores(const float* maps, int32_t n_maps, int32_t L, double lambda, double eps, int32_t norm_scope,
+                       double* t) {
+  if (!lambda_ok(lambda, eps)) return 2;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int32_t mi = 0; mi < n_maps; ++mi) {
+    const float* A = maps + (int64_t)mi * L * L;
+    double gmin = 0.0, gmax = 0.0;
+    if (norm_scope == 1) map_range(A, L, eps, lambda, &gmin, &gmax);
+    for (int32_t i = 0; i < L; ++i) {
+      double* row = t + ((int64_t)mi * L + i) * L;
+      row_scores(A, L, i, eps, lambda, norm_scope, gmin, gmax, row);
+      for (int32_t j = i + 1; j < L; ++j) row[j] = NAN;
+    }
+  }
+  return 0;
 }
 
 int orc_capture(const float* maps, int32_t n_maps, int32_t L, double lambda, double eps, double tau,
                 double mu, int32_t norm_scope, uint8_t* keep_diag, uint8_t* keep_vert,
                 int32_t* diag_hits, int32_t* vert_hits, uint8_t* true_mask) {
-  if (lambda != 0.5) return 2;
+  if (!lambda_ok(lambda, eps)) return 2;
 #pragma omp parallel
   {
     double* y = (double*)malloc(sizeof(double) * (size_t)L);
@@ -486,29 +543,11 @@ int orc_capture(const float* maps, int32_t n_maps, int32_t L, double lambda, dou
     for (int32_t mi = 0; mi < n_maps; ++mi) {
       const float* A = maps + (int64_t)mi * L * L;
       memset(M, 0, (size_t)L * (size_t)L);
-      double gmin = INFINITY, gmax = -INFINITY;
-      if (norm_scope == 1) {
-        for (int32_t i = 0; i < L; ++i)
-          for (int32_t j = 0; j <= i; ++j) {
-            double t = boxcox_half(A[(int64_t)i * L + j], eps, lambda);
-            if (t < gmin) gmin = t;
-            if (t > gmax) gmax = t;
-          }
-      }
+      double gmin = 0.0, gmax = 0.0;
+      if (norm_scope == 1) map_range(A, L, eps, lambda, &gmin, &gmax);
       for (int32_t i = 0; i < L; ++i) {
-        double ymin = INFINITY, ymax = -INFINITY;
-        for (int32_t j = 0; j <= i; ++j) {
-          y[j] = boxcox_half(A[(int64_t)i * L + j], eps, lambda);
-          if (y[j] < ymin) ymin = y[j];
-          if (y[j] > ymax) ymax = y[j];
-        }
-        if (norm_scope == 1) { ymin = gmin; ymax = gmax; }
-        for (int32_t j = 0; j <= i; ++j) {
-          int keep;
-          if (ymax == ymin) keep = 1;
-          else keep = ((y[j] - ymin) / (ymax - ymin)) >= tau;
-          M[(int64_t)i * L + j] = (uint8_t)keep;
-        }
+        row_scores(A, L, i, eps, lambda, norm_scope, gmin, gmax, y);
+        for (int32_t j = 0; j <= i; ++j) M[(int64_t)i * L + j] = (uint8_t)(y[j] >= tau);
       }
       /* overlap scores over the pool: diagonal r has L - r cells, vertical c has L - c */
       for (int32_t r = 0; r < L; ++r) {
@@ -536,4 +575,35 @@ int orc_capture(const float* maps, int32_t n_maps, int32_t L, double lambda, dou
     free(y); free(M); free(hd); free(hv);
   }
   return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Coverage of the kept patterns inside the capture window.  The referee    */
+/* ([DAM] Referee Report, major comments 2 and 4) asks how the kept masks   */
+/* agree with the full attention and how sparse they are as the             */
+/* hyperparameters move.  Per map: the cells (i, j), j <= i < L, on a kept  */
+/* diagonal (i - j) or a kept vertical (j); cells = their number, mass =    */
+/* the sum of A over them divided by the sum of A over the causal map.      */
+/* ------------------------------------------------------------------------ */
+void orc_coverage(const float* maps, int32_t n_maps, int32_t L, const uint8_t* keep_diag, const uint8_t* keep_vert,
+                  double* mass, int64_t* cells) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int32_t mi = 0; mi < n_maps; ++mi) {
+    const float* A = maps + (int64_t)mi * L * L;
+    const uint8_t* kd = keep_diag + (int64_t)mi * L;
+    const uint8_t* kv = keep_vert + (int64_t)mi * L;
+    double kept = 0.0, total = 0.0;
+    int64_t n = 0;
+    for (int32_t i = 0; i < L; ++i)
+      for (int32_t j = 0; j <= i; ++j) {
+        double a = (double)A[(int64_t)i * L + j];
+        total += a;
+        if (kd[i - j] || kv[j]) {
+          kept += a;
+          ++n;
+        }
+      }
+    mass[mi] = total > 0.0 ? kept / total : 0.0;
+    cells[mi] = n;
+  }
 }

@@ -290,9 +290,96 @@ def test_capture_planted_patterns(scope):
     assert sorted(np.nonzero(c["keep_vert"][0])[0].tolist()) == [2, L - 1]
 
 
-def test_capture_rejects_other_lambda():
+def test_capture_rejects_bad_lambda():
     with pytest.raises(ValueError):
-        oracle.capture(np.ones((1, 4, 4), np.float32), lam=0.25)
+        oracle.capture(np.ones((1, 4, 4), np.float32), lam=float("nan"))
+    with pytest.raises(ValueError):
+        oracle.capture(np.ones((1, 4, 4), np.float32), lam=0.0, eps=0.0)   # log 0
+    with pytest.raises(ValueError):
+        oracle.capture_scores(np.ones((1, 4, 4), np.float32), lam=-1.0, eps=0.0)
+
+
+def _minmax_rows(y, scope):
+    """Min-max scaling of the causal cells of y [L, L] (NaN above the diagonal): per row or per map."""
+    L = y.shape[0]
+    t = np.full_like(y, np.nan)
+    if scope == 1:
+        lo, hi = np.nanmin(y), np.nanmax(y)
+    for i in range(L):
+        r = y[i, :i + 1]
+        if scope == 0:
+            lo, hi = r.min(), r.max()
+        t[i, :i + 1] = 1.0 if hi == lo else (r - lo) / (hi - lo)
+    return t
+
+
+@pytest.mark.parametrize("lam", [-0.5, 0.0, 0.25, 0.5, 1.0, 2.0])
+@pytest.mark.parametrize("scope", [0, 1])
+def test_capture_scores_follow_scipy_boxcox(lam, scope):
+    """t = min-max of scipy.special.boxcox(A + eps, lambda) over the causal row (or map)."""
+    from scipy.special import boxcox
+    maps = W.capture_maps(layers=1, heads=2, L=96, n_avg=2, layer_offset=5)
+    t = oracle.capture_scores(maps, lam=lam, eps=1e-8, norm_scope=scope)
+    L = 96
+    for n in range(2):
+        y = np.where(np.tri(L, dtype=bool), boxcox(maps[n].astype(np.float64) + 1e-8, lam), np.nan)
+        ref = _minmax_rows(y, scope)
+        np.testing.assert_allclose(t[n], ref, rtol=0, atol=1e-11, equal_nan=True)
+
+
+def test_capture_scores_linear_case_and_mask():
+    """lambda = 1 makes y = A + eps - 1, so t is the min-max of A itself; M = (t >= tau) cell by cell."""
+    maps = W.capture_maps(layers=1, heads=2, L=80, n_avg=3, layer_offset=9)
+    L = 80
+    t = oracle.capture_scores(maps, lam=1.0, eps=1e-10)
+    c = oracle.capture(maps, lam=1.0, eps=1e-10, tau=0.2, want_mask=True)
+    for n in range(2):
+        a = np.where(np.tri(L, dtype=bool), maps[n].astype(np.float64), np.nan)
+        np.testing.assert_allclose(t[n], _minmax_rows(a, 0), rtol=0, atol=1e-12, equal_nan=True)
+        tri = np.tri(L, dtype=bool)
+        np.testing.assert_array_equal(c["true_mask"][n][tri], (t[n][tri] >= 0.2).astype(np.uint8))
+
+
+@pytest.mark.parametrize("lam", [0.0, 0.25, 1.0])
+def test_capture_keep_sets_shrink_as_tau_and_mu_grow(lam):
+    """A higher tau removes cells from M, a higher mu asks more of each pattern: kept sets can only shrink."""
+    maps = W.capture_maps(layers=1, heads=4, L=128, n_avg=4, layer_offset=11)
+    prev = None
+    for tau in (0.1, 0.2, 0.3, 0.4, 0.5):
+        c = oracle.capture(maps, lam=lam, tau=tau)
+        if prev is not None:
+            assert not (c["keep_diag"] & ~prev["keep_diag"]).any() and not (c["keep_vert"] & ~prev["keep_vert"]).any()
+        prev = c
+    prev = None
+    for mu in (0.6, 0.7, 0.8, 0.9, 1.0):
+        c = oracle.capture(maps, lam=lam, mu=mu)
+        if prev is not None:
+            assert not (c["keep_diag"] & ~prev["keep_diag"]).any() and not (c["keep_vert"] & ~prev["keep_vert"]).any()
+        prev = c
+
+
+def test_coverage_brute_force_and_special_cases():
+    maps = W.capture_maps(layers=1, heads=3, L=70, n_avg=2, layer_offset=13)
+    L = 70
+    rng = np.random.default_rng(5)
+    kd = (rng.random((3, L)) < 0.1).astype(np.uint8)
+    kv = (rng.random((3, L)) < 0.1).astype(np.uint8)
+    mass, cells = oracle.coverage(maps, kd, kv)
+    i, j = np.tril_indices(L)
+    for n in range(3):
+        on = (kd[n][i - j] | kv[n][j]).astype(bool)
+        a = maps[n][i, j].astype(np.float64)
+        assert cells[n] == on.sum()
+        assert abs(mass[n] - a[on].sum() / a.sum()) < 1e-12
+    ones, zeros = np.ones((3, L), np.uint8), np.zeros((3, L), np.uint8)
+    m1, c1 = oracle.coverage(maps, ones, zeros)                 # every diagonal: the whole causal window
+    assert np.all(c1 == L * (L + 1) // 2) and np.allclose(m1, 1.0, rtol=0, atol=1e-12)
+    d0 = zeros.copy()
+    d0[:, 0] = 1
+    m0, c0 = oracle.coverage(maps, d0, zeros)                   # diagonal 0 only: the trace share
+    for n in range(3):
+        assert c0[n] == L
+        assert abs(m0[n] - np.trace(maps[n].astype(np.float64)) / np.tril(maps[n].astype(np.float64)).sum()) < 1e-12
 
 
 def test_extension_restricted_to_capture_window_is_the_kept_union():
