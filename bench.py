@@ -163,6 +163,60 @@ def maps_from_qk_ms(sa, torch, reps=5):
                 maps_tile_TFLOPs=flops / (maps_ms * 1e-3) / 1e12)
 
 
+SWEEP_LAMBDA = (-0.5, 0.0, 0.25, 0.5, 1.0)
+SWEEP_TAU = (0.1, 0.2, 0.3, 0.4, 0.5)
+SWEEP_MU = (0.6, 0.7, 0.8, 0.9, 1.0)
+SWEEP_PCL = (256, 512, 1024)
+
+
+def capture_sweep(sa, torch, S=16384):
+    """Sensitivity of the kept masks to the capture length (PCL), lambda, tau and mu, on two kinds of
+    synthetic maps per PCL: the pattern-capture workload's maps (32 heads, 16 averaged softmaxes) and
+    maps computed on the GPU from structured Q/K (batch 16, 32/8 heads, d 64).  For every grid point:
+    kept diagonals and verticals per head, the kept patterns' share of the attention mass and of the
+    cells inside the L x L window (sa_pattern_coverage), and the density of the mask extended to S
+    (exact retained pairs from the index over all causal pairs)."""
+    import workloads as W
+    out = []
+    causal_S = 32 * S * (S + 1) / 2.0
+    for L in SWEEP_PCL:
+        srcs = []
+        t0 = time.time()
+        srcs.append(("workload maps", torch.from_numpy(W.capture_maps(layers=1, heads=32, L=L, n_avg=16)).cuda()))
+        q, k = W.capture_qk(48, 16, 32, 8, L, 64, "bf16")
+        qd = torch.from_numpy(q.view(np.int16)).cuda().view(torch.bfloat16)
+        kd = torch.from_numpy(k.view(np.int16)).cuda().view(torch.bfloat16)
+        srcs.append(("maps from Q/K", sa.attention_maps(qd, kd)))
+        log("sweep: PCL %d maps ready in %.1fs" % (L, time.time() - t0))
+        for name, maps in srcs:
+            for lam in SWEEP_LAMBDA:
+                for tau in SWEEP_TAU:
+                    for mu in SWEEP_MU:
+                        c = sa.pattern_capture(maps, lam=lam, tau=tau, mu=mu, return_hits=False)
+                        mass, cells = sa.pattern_coverage(maps, c["keep_diag"], c["keep_vert"])
+                        ix = sa.build_index(sa.patterns_to_desc(c["keep_diag"], c["keep_vert"], S), 64)
+                        out.append(dict(maps=name, pcl=L, lam=lam, tau=tau, mu=mu,
+                                        diags=float(c["keep_diag"].float().sum(1).mean().item()),
+                                        verts=float(c["keep_vert"].float().sum(1).mean().item()),
+                                        mass=float(mass.mean().item()), mass_min=float(mass.min().item()),
+                                        cells=float(cells.double().mean().item()) / (L * (L + 1) / 2.0),
+                                        density_S=ix.total_pairs / causal_S))
+    # timing of one capture of the 512 workload maps per transform kind
+    maps = torch.from_numpy(W.capture_maps(layers=16, heads=32, n_avg=4)).cuda()
+    timing = {}
+    for lam in (0.5, 0.0, 0.25):
+        sa.pattern_capture(maps, lam=lam)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(5):
+            sa.pattern_capture(maps, lam=lam)
+        b.record()
+        torch.cuda.synchronize()
+        timing[str(lam)] = a.elapsed_time(b) / 5
+    return dict(S=S, points=out, capture_ms_512_maps=timing)
+
+
 def decode_row_keys(ixn, h, t, nb, BM, nwords):
     """Retained keys of row t of head h, read off the index (segments filtered by the diagonal bitmap
     and the in-segment columns, then the gathered columns <= t)."""
@@ -243,6 +297,8 @@ def main():
     ap.add_argument("--config", type=int, default=4, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the S=131072 and capture measurements")
+    ap.add_argument("--capture-sweep", action="store_true",
+                    help="only run the capture sensitivity sweep (PCL, lambda, tau, mu) and print it as JSON")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one device copy of 1 GiB (reference for hardware byte counters)")
     args = ap.parse_args()
@@ -253,6 +309,10 @@ def main():
 
     import torch
     import structured_sparse_attention_amd as sa
+
+    if args.capture_sweep:
+        print(json.dumps(capture_sweep(sa, torch)))
+        return
 
     cfg = WORKLOADS[args.config]
     desc, qkv_host, pat, qkv_dev, ix = setup(args.config)

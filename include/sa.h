@@ -230,26 +230,45 @@ sa_status sa_attention_maps(const void* q, const void* k, int32_t batch, int32_t
                             int32_t head_dim, int32_t dtype, float softmax_scale, float* maps, void* stream);
 
 /*
- * sa_pattern_capture [DAM, What carries the argument]: for each averaged attention
+ * sa_pattern_capture [DAM, What carries the argument; Referee Report major comment 4
+ * for lambda, tau and mu other than the pages' values]: for each averaged attention
  * map A (float [n_maps][L][L], row-major; entries with j > i are ignored):
- *   y = (sqrt(A + eps) - 1) / lambda    Box-Cox with lambda = 0.5 (x^0.5 = sqrt x)
+ *   y = Box-Cox(A + eps): (x^lambda - 1) / lambda, log x at lambda = 0; the
+ *       pages' lambda = 0.5 is computed as (sqrt(x) - 1) / 0.5
  *   t = (y - ymin) / (ymax - ymin)      min/max over the causal row (norm_scope 0)
  *                                       or over the causal map (norm_scope 1);
  *                                       a constant row/map gives t = 1
- *   M = (t >= tau)                      the binary true mask
+ *   M = (t >= tau)                      the binary true mask (t = 1 on a constant row)
  *   diag_hits[r] = sum_i M[i][i-r], vert_hits[c] = sum_i M[i][c]
  *   keep_diag[r] = hits / (L - r) >= mu, keep_vert[c] = hits / (L - c) >= mu
- * All of it in fp64 with correctly rounded sqrt and division, so the keep flags,
- * hit counts and mask are exact.  eps: 1e-8 in one section of the paper, 1e-10 in
- * its appendix [DAM, Referee Report minor comment 1] -- a parameter here.
+ * All of it in fp64.  At lambda = 0.5 sqrt and division are correctly rounded, so
+ * the keep flags, hit counts and mask are exact; other lambdas use the device pow /
+ * log (a few ulp), so a cell whose t lies within about 1e-15 of tau may differ
+ * from a correctly rounded evaluation.  eps: 1e-8 in one section of the paper,
+ * 1e-10 in its appendix [DAM, Referee Report minor comment 1] -- a parameter here.
  * Requires every causal entry finite with A + eps >= 0 (attention probabilities).
  *   keep_diag, keep_vert  uint8 [n_maps][L];  diag_hits, vert_hits NULL or int32
  *   [n_maps][L];  true_mask NULL or uint8 [n_maps][L][L] (zeros above the diagonal).
- * Limits: 1 <= L <= 4096; lambda == 0.5 (else SA_ERR_UNSUPPORTED); norm_scope 0 or 1.
+ * Limits: 1 <= L <= 4096; lambda finite, and eps > 0 when lambda <= 0 (else
+ * SA_ERR_INVALID_ARG); norm_scope 0 or 1.
  */
 sa_status sa_pattern_capture(const float* maps, int32_t n_maps, int32_t L, double lambda, double eps, double tau,
                              double mu, int32_t norm_scope, uint8_t* keep_diag, uint8_t* keep_vert,
                              int32_t* diag_hits, int32_t* vert_hits, uint8_t* true_mask, void* stream);
+
+/*
+ * sa_pattern_coverage [DAM, Referee Report major comments 2 and 4: agreement of the
+ * kept masks with the attention maps, and their sparsity]: per map m,
+ *   cells[m] = #{ (i, j) : j <= i < L, keep_diag[m][i - j] or keep_vert[m][j] }
+ *   mass[m]  = sum of A over those cells / sum of A over j <= i  (0 if that is 0)
+ *   maps  float [n_maps][L][L] as for sa_pattern_capture;  keep_* uint8 [n_maps][L]
+ *   mass  double [n_maps];  cells  NULL or int64 [n_maps]
+ * fp64 sums in a fixed order (deterministic; the order differs from a plain
+ * row-major sum, so mass agrees with one to rounding).
+ * Limits: 1 <= L <= 4096.  Errors: SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_HIP.
+ */
+sa_status sa_pattern_coverage(const float* maps, int32_t n_maps, int32_t L, const uint8_t* keep_diag,
+                              const uint8_t* keep_vert, double* mass, int64_t* cells, void* stream);
 
 /*
  * sa_patterns_to_desc [DAM, What carries the argument; Circularity Check 1]: the kept

@@ -18,7 +18,7 @@ import numpy as np
 import torch
 
 __all__ = ["SAError", "DevicePatterns", "SparseIndex", "build_index", "sparse_attn_prefill", "sparse_attn_decode",
-           "attention_maps", "pattern_capture", "patterns_to_desc", "library_path", "version", "lib"]
+           "attention_maps", "pattern_capture", "pattern_coverage", "patterns_to_desc", "library_path", "version", "lib"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libsa.so")
@@ -76,6 +76,8 @@ def _load():
     lib.sa_pattern_capture.restype = C.c_int32
     lib.sa_pattern_capture.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_double, C.c_double, C.c_double,
                                        C.c_double, C.c_int32] + [C.c_void_p] * 5 + [C.c_void_p]
+    lib.sa_pattern_coverage.restype = C.c_int32
+    lib.sa_pattern_coverage.argtypes = [C.c_void_p, C.c_int32, C.c_int32] + [C.c_void_p] * 4 + [C.c_void_p]
     lib.sa_patterns_to_desc.restype = C.c_int32
     lib.sa_patterns_to_desc.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32] + \
         [C.c_void_p] * 4 + [C.c_void_p]
@@ -328,6 +330,22 @@ def pattern_capture(maps: torch.Tensor, lam: float = 0.5, eps: float = 1e-8, tau
                                    kv.data_ptr(), _ptr(hd), _ptr(hv), _ptr(tm), _stream(stream)),
            "sa_pattern_capture")
     return dict(keep_diag=kd, keep_vert=kv, diag_hits=hd, vert_hits=hv, true_mask=tm)
+
+
+def pattern_coverage(maps: torch.Tensor, keep_diag: torch.Tensor, keep_vert: torch.Tensor, stream=None):
+    """sa_pattern_coverage: per map, (attention-mass share float64 [n], cell count int64 [n]) of the kept
+    diagonals and verticals inside the L x L causal window."""
+    if maps.dtype != torch.float32 or maps.dim() != 3 or maps.shape[1] != maps.shape[2] or not maps.is_contiguous():
+        raise ValueError("maps must be a contiguous float32 [n, L, L] tensor")
+    n, L, _ = maps.shape
+    for f in (keep_diag, keep_vert):
+        if f.dtype != torch.uint8 or tuple(f.shape) != (n, L) or not f.is_contiguous():
+            raise ValueError("keep flags must be contiguous uint8 [n, L] tensors")
+    mass = torch.empty(n, dtype=torch.float64, device=maps.device)
+    cells = torch.empty(n, dtype=torch.int64, device=maps.device)
+    _check(_lib.sa_pattern_coverage(maps.data_ptr(), n, L, keep_diag.data_ptr(), keep_vert.data_ptr(),
+                                    mass.data_ptr(), cells.data_ptr(), _stream(stream)), "sa_pattern_coverage")
+    return mass, cells
 
 
 def patterns_to_desc(keep_diag: torch.Tensor, keep_vert: torch.Tensor, S: int, stream=None) -> DevicePatterns:

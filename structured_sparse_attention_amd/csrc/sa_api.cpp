@@ -140,11 +140,20 @@ sa_status sa_pattern_capture(const float* maps, int32_t n_maps, int32_t L, doubl
   if (!maps || !keep_diag || !keep_vert) return SA_ERR_INVALID_ARG;
   if (n_maps < 1 || L < 1) return SA_ERR_INVALID_ARG;
   if (norm_scope != 0 && norm_scope != 1) return SA_ERR_INVALID_ARG;
-  if (!isfinite(eps) || !isfinite(tau) || !isfinite(mu)) return SA_ERR_INVALID_ARG;
-  if (lambda != 0.5) return SA_ERR_UNSUPPORTED;
+  if (!isfinite(eps) || !isfinite(tau) || !isfinite(mu) || !isfinite(lambda)) return SA_ERR_INVALID_ARG;
+  if (lambda <= 0.0 && !(eps > 0.0)) return SA_ERR_INVALID_ARG;  // A = 0 would give an infinite transform
   if (L > sa::kMaxCaptureL) return SA_ERR_UNSUPPORTED;
   return hip_status(sa::launch_capture(maps, n_maps, L, lambda, eps, tau, mu, norm_scope, keep_diag, keep_vert,
                                        diag_hits, vert_hits, true_mask, static_cast<hipStream_t>(stream)));
+}
+
+sa_status sa_pattern_coverage(const float* maps, int32_t n_maps, int32_t L, const uint8_t* keep_diag,
+                              const uint8_t* keep_vert, double* mass, int64_t* cells, void* stream) {
+  if (!maps || !keep_diag || !keep_vert || !mass) return SA_ERR_INVALID_ARG;
+  if (n_maps < 1 || L < 1) return SA_ERR_INVALID_ARG;
+  if (L > sa::kMaxCaptureL) return SA_ERR_UNSUPPORTED;
+  return hip_status(sa::launch_coverage(maps, n_maps, L, keep_diag, keep_vert, mass, cells,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 sa_status sa_attention_maps(const void* q, const void* k, int32_t batch, int32_t hq, int32_t hkv, int32_t L,

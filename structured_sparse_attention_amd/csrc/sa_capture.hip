@@ -12,12 +12,18 @@
 // parameter here).  The pages do not say how the transformed values are scaled
 // before the threshold; they are min-max normalised per causal row (or per map).
 //
-// Exactness: every step is fp64 with correctly rounded sqrt and division and no
-// contraction, so the mask, the hit counts and the keep flags equal those of any
-// IEEE fp64 evaluation in the same order.  The transform is monotone
-// non-decreasing in A, so the row (or map) minimum and maximum of the transformed
-// values are the transforms of the fp32 minimum and maximum of A: the min/max pass
-// runs in fp32 and each element is transformed once.
+// Other lambdas (Referee Report major comment 4 asks how the masks move with
+// lambda, tau, mu and the capture length) use the textbook Box-Cox form.
+//
+// Exactness: at lambda = 0.5 every step is fp64 with correctly rounded sqrt and
+// division and no contraction, so the mask, the hit counts and the keep flags
+// equal those of any IEEE fp64 evaluation in the same order.  Other lambdas go
+// through the device pow / log, a few ulp from the correctly rounded value: only
+// cells whose normalised score lies within about 1e-15 of tau can differ.  The
+// transform is monotone non-decreasing in A for every lambda, so the row (or map)
+// minimum and maximum of the transformed values are the transforms of the fp32
+// minimum and maximum of A: the min/max pass runs in fp32 and each element is
+// transformed once.
 //
 // Layout: one 1024-thread workgroup per map; wave w takes rows w, w+16, ...; lanes
 // take columns, four loads in flight per lane.  Hits accumulate with LDS atomics; the map is read once from HBM
@@ -31,11 +37,21 @@ namespace {
 
 constexpr int kThreads = 1024;  // 16 waves per map: two maps fill a CU's 32 wave slots
 
-__device__ inline double box_cox_half(float a, double eps, double lambda) {
+// Box-Cox of x = A + eps: (sqrt(x) - 1) / 0.5 at lambda = 0.5 (correctly rounded, exact),
+// log x at lambda = 0, (x^lambda - 1) / lambda otherwise (device pow / log: a few ulp).
+enum { kBoxCoxHalf = 0, kBoxCoxLog = 1, kBoxCoxPow = 2 };
+template <int KIND>
+__device__ inline double box_cox(float a, double eps, double lambda) {
 #pragma clang fp contract(off)
   const double x = (double)a + eps;
-  const double s = sqrt(x);
-  return (s - 1.0) / lambda;
+  if constexpr (KIND == kBoxCoxHalf) {
+    const double s = sqrt(x);
+    return (s - 1.0) / lambda;
+  } else if constexpr (KIND == kBoxCoxLog) {
+    return log(x);
+  } else {
+    return (pow(x, lambda) - 1.0) / lambda;
+  }
 }
 
 __device__ inline float wave_min(float x) {
@@ -47,6 +63,7 @@ __device__ inline float wave_max(float x) {
   return x;
 }
 
+template <int KIND>
 __global__ void __launch_bounds__(kThreads)
     k_capture(const float* maps, int32_t L, double lambda, double eps, double tau, double mu, int32_t norm_scope,
               uint8_t* keep_diag, uint8_t* keep_vert, int32_t* diag_hits, int32_t* vert_hits, uint8_t* true_mask) {
@@ -109,8 +126,8 @@ __global__ void __launch_bounds__(kThreads)
       amin = wave_min(mn);
       amax = wave_max(mx);
     }
-    const double ymin = box_cox_half(amin, eps, lambda);
-    const double ymax = box_cox_half(amax, eps, lambda);
+    const double ymin = box_cox<KIND>(amin, eps, lambda);
+    const double ymax = box_cox<KIND>(amax, eps, lambda);
     const bool flat = (ymax == ymin);
     const double range = ymax - ymin;
     uint8_t* mrow = true_mask ? true_mask + (map * L + i) * (int64_t)L : nullptr;
@@ -127,8 +144,9 @@ __global__ void __launch_bounds__(kThreads)
         if (j >= L) continue;
         uint8_t keep = 0;
         if (j <= i) {
-          const double y = box_cox_half(a[u], eps, lambda);
-          keep = flat ? 1 : (((y - ymin) / range) >= tau);
+          const double y = box_cox<KIND>(a[u], eps, lambda);
+          const double t = flat ? 1.0 : (y - ymin) / range;
+          keep = t >= tau;
           if (keep) {
             atomicAdd(&hd[i - j], 1);
             atomicAdd(&hv[j], 1);
@@ -333,6 +351,75 @@ hipError_t launch_maps_t(const void* q, const void* k, int32_t B, int32_t hq, in
   return hipGetLastError();
 }
 
+// Coverage of the kept patterns inside the capture window (Referee Report major
+// comments 2 and 4: agreement of the kept masks with the attention, and their
+// sparsity, as the hyperparameters move): per map, the cells (i, j), j <= i < L,
+// on a kept diagonal or a kept vertical, and their share of the attention mass.
+// One 1024-thread workgroup per map; wave w takes rows w, w+16, ...; fp64 sums
+// reduced in a fixed order (deterministic).
+constexpr int kCovThreads = 1024;
+__global__ void __launch_bounds__(kCovThreads)
+    k_coverage(const float* maps, int32_t L, const uint8_t* keep_diag, const uint8_t* keep_vert, double* mass,
+               int64_t* cells) {
+  extern __shared__ uint8_t kflags[];  // [L] diagonal flags, then [L] vertical flags
+  __shared__ double red_k[kCovThreads / 64], red_t[kCovThreads / 64];
+  __shared__ long long red_n[kCovThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t map = blockIdx.x;
+  const float* A = maps + map * (int64_t)L * L;
+  for (int r = tid; r < L; r += kCovThreads) {
+    kflags[r] = keep_diag[map * L + r];
+    kflags[L + r] = keep_vert[map * L + r];
+  }
+  __syncthreads();
+  double kept = 0.0, total = 0.0;
+  long long n = 0;
+  for (int i = wave; i < L; i += kCovThreads / 64) {
+    const float* row = A + (int64_t)i * L;
+    for (int jb = 0; jb <= i; jb += 4 * 64) {
+      float a[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = jb + u * 64 + lane;
+        a[u] = j <= i ? row[j] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = jb + u * 64 + lane;
+        if (j <= i) {
+          total += (double)a[u];
+          if (kflags[i - j] | kflags[L + j]) {
+            kept += (double)a[u];
+            ++n;
+          }
+        }
+      }
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    kept += __shfl_xor(kept, o, 64);
+    total += __shfl_xor(total, o, 64);
+    n += __shfl_xor(n, o, 64);
+  }
+  if (lane == 0) {
+    red_k[wave] = kept;
+    red_t[wave] = total;
+    red_n[wave] = n;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double k = 0.0, t = 0.0;
+    long long c = 0;
+    for (int w = 0; w < kCovThreads / 64; ++w) {
+      k += red_k[w];
+      t += red_t[w];
+      c += red_n[w];
+    }
+    mass[map] = t > 0.0 ? k / t : 0.0;
+    if (cells) cells[map] = c;
+  }
+}
+
 // kept flags -> CSR descriptor lists at length S (entries < S).  One workgroup.
 constexpr int kDescThreads = 1024;
 __global__ void __launch_bounds__(kDescThreads)
@@ -374,7 +461,8 @@ hipError_t launch_capture(const float* maps, int32_t n_maps, int32_t L, double l
                           double mu, int32_t norm_scope, uint8_t* keep_diag, uint8_t* keep_vert, int32_t* diag_hits,
                           int32_t* vert_hits, uint8_t* true_mask, hipStream_t stream) {
   const size_t lds = 2 * sizeof(int32_t) * (size_t)L;
-  hipLaunchKernelGGL(k_capture, dim3((unsigned)n_maps), dim3(kThreads), lds, stream, maps, L, lambda, eps, tau, mu,
+  auto kern = lambda == 0.5 ? k_capture<kBoxCoxHalf> : lambda == 0.0 ? k_capture<kBoxCoxLog> : k_capture<kBoxCoxPow>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)n_maps), dim3(kThreads), lds, stream, maps, L, lambda, eps, tau, mu,
                      norm_scope, keep_diag, keep_vert, diag_hits, vert_hits, true_mask);
   return hipGetLastError();
 }
@@ -386,6 +474,13 @@ hipError_t launch_attention_maps(const void* q, const void* k, int32_t batch, in
                           : launch_maps_t<128, true>(q, k, batch, hq, hkv, L, scale, maps, stream);
   return head_dim == 64 ? launch_maps_t<64, false>(q, k, batch, hq, hkv, L, scale, maps, stream)
                         : launch_maps_t<128, false>(q, k, batch, hq, hkv, L, scale, maps, stream);
+}
+
+hipError_t launch_coverage(const float* maps, int32_t n_maps, int32_t L, const uint8_t* keep_diag,
+                           const uint8_t* keep_vert, double* mass, int64_t* cells, hipStream_t stream) {
+  hipLaunchKernelGGL(k_coverage, dim3((unsigned)n_maps), dim3(kCovThreads), 2 * (size_t)L, stream, maps, L, keep_diag,
+                     keep_vert, mass, cells);
+  return hipGetLastError();
 }
 
 hipError_t launch_patterns_to_desc(const uint8_t* keep_diag, const uint8_t* keep_vert, int32_t n_maps, int32_t L,

@@ -53,6 +53,8 @@ hipError_t launch_capture(const float* maps, int32_t n_maps, int32_t L, double l
                           int32_t* vert_hits, uint8_t* true_mask, hipStream_t stream);
 hipError_t launch_attention_maps(const void* q, const void* k, int32_t batch, int32_t hq, int32_t hkv, int32_t L,
                                  int32_t head_dim, int32_t dtype, float scale, float* maps, hipStream_t stream);
+hipError_t launch_coverage(const float* maps, int32_t n_maps, int32_t L, const uint8_t* keep_diag,
+                           const uint8_t* keep_vert, double* mass, int64_t* cells, hipStream_t stream);
 hipError_t launch_patterns_to_desc(const uint8_t* keep_diag, const uint8_t* keep_vert, int32_t n_maps, int32_t L,
                                    int32_t S, int32_t* diag_ptr, int32_t* diag_off, int32_t* vert_ptr,
                                    int32_t* vert_col, hipStream_t stream);

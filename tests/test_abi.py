@@ -26,7 +26,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for f in ("sa_build_index", "sa_sparse_attn_prefill", "sa_sparse_attn_decode", "sa_attention_maps",
-              "sa_pattern_capture", "sa_patterns_to_desc", "sa_status_string", "sa_version"):
+              "sa_pattern_capture", "sa_pattern_coverage", "sa_patterns_to_desc", "sa_status_string", "sa_version"):
         assert f in names
 
 
@@ -131,9 +131,16 @@ def test_capture_validation(m):
     assert f(None, 1, 8, 0.5, 1e-8, 0.3, 0.8, 0, p, p, None, None, None, None) == -1
     assert f(p, 0, 8, 0.5, 1e-8, 0.3, 0.8, 0, p, p, None, None, None, None) == -1
     assert f(p, 1, 8, 0.5, 1e-8, 0.3, 0.8, 2, p, p, None, None, None, None) == -1
-    assert f(p, 1, 8, 0.25, 1e-8, 0.3, 0.8, 0, p, p, None, None, None, None) == -2
+    assert f(p, 1, 8, float("inf"), 1e-8, 0.3, 0.8, 0, p, p, None, None, None, None) == -1   # lambda
+    assert f(p, 1, 8, 0.0, 0.0, 0.3, 0.8, 0, p, p, None, None, None, None) == -1   # log 0 possible
+    assert f(p, 1, 8, -0.5, 0.0, 0.3, 0.8, 0, p, p, None, None, None, None) == -1  # 0^-0.5 possible
     assert f(p, 1, 5000, 0.5, 1e-8, 0.3, 0.8, 0, p, p, None, None, None, None) == -2
     assert f(p, 1, 8, 0.5, float("nan"), 0.3, 0.8, 0, p, p, None, None, None, None) == -1
+    c = m.lib.sa_pattern_coverage
+    assert c(None, 1, 8, p, p, p, None, None) == -1
+    assert c(p, 1, 8, p, p, None, None, None) == -1     # mass is required
+    assert c(p, 0, 8, p, p, p, None, None) == -1
+    assert c(p, 1, 5000, p, p, p, None, None) == -2
     g = m.lib.sa_patterns_to_desc
     assert g(None, p, 1, 8, 8, p, p, p, p, None) == -1
     assert g(p, p, 1, 8, 0, p, p, p, p, None) == -1

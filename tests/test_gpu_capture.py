@@ -53,11 +53,56 @@ def test_capture_thresholds_and_mu():
     _capture_both(maps, tau=0.55, mu=0.6)
 
 
-def test_capture_rejects_other_lambda():
+def test_capture_rejects_bad_lambda():
     m = sa()
-    with pytest.raises(m.SAError) as e:
-        m.pattern_capture(torch.zeros(1, 8, 8, device="cuda"), lam=0.25)
-    assert e.value.code == -2
+    for lam, eps in ((float("nan"), 1e-8), (0.0, 0.0)):
+        with pytest.raises(m.SAError) as e:
+            m.pattern_capture(torch.zeros(1, 8, 8, device="cuda"), lam=lam, eps=eps)
+        assert e.value.code == -1
+
+
+@pytest.mark.parametrize("lam", [-0.5, 0.0, 0.25, 1.0, 2.0])
+@pytest.mark.parametrize("scope", [0, 1])
+def test_capture_other_lambdas(lam, scope):
+    """Box-Cox through the device pow / log.  Those are a few ulp from the host's, so the comparison is
+    exact only where no cell's normalised score is within 1e-9 of tau: the oracle's scores show that first."""
+    note("capture lambda=%g scope=%d" % (lam, scope))
+    maps = W.capture_maps(layers=1, heads=32, n_avg=8, layer_offset=17)
+    t = oracle.capture_scores(maps, lam=lam, norm_scope=scope)
+    assert not (np.abs(t - 0.3) < 1e-9).any()
+    _capture_both(maps, lam=lam, norm_scope=scope)
+
+
+@pytest.mark.parametrize("lam,tau,mu", [(0.5, 0.3, 0.8), (0.0, 0.5, 0.7), (1.0, 0.1, 0.9)])
+def test_coverage_matches_oracle(lam, tau, mu):
+    m = sa()
+    maps = W.capture_maps(layers=1, heads=32, n_avg=8, layer_offset=19)
+    md = torch.from_numpy(maps).cuda()
+    c = m.pattern_capture(md, lam=lam, tau=tau, mu=mu)
+    mass, cells = m.pattern_coverage(md, c["keep_diag"], c["keep_vert"])
+    torch.cuda.synchronize()
+    rm, rc = oracle.coverage(maps, c["keep_diag"].cpu().numpy(), c["keep_vert"].cpu().numpy())
+    np.testing.assert_array_equal(cells.cpu().numpy(), rc)
+    np.testing.assert_allclose(mass.cpu().numpy(), rm, rtol=0, atol=1e-12)
+    assert 0.0 < rm.min() and rm.max() <= 1.0
+
+
+def test_coverage_edge_cases():
+    """Every diagonal kept: the whole window, mass 1; nothing kept: 0; L = 1."""
+    m = sa()
+    maps = W.capture_maps(layers=1, heads=4, L=200, n_avg=2)
+    md = torch.from_numpy(maps).cuda()
+    ones = torch.ones((4, 200), dtype=torch.uint8, device="cuda")
+    zeros = torch.zeros_like(ones)
+    mass, cells = m.pattern_coverage(md, ones, zeros)
+    m0, c0 = m.pattern_coverage(md, zeros, zeros)
+    one = torch.full((2, 1, 1), 0.7, device="cuda")
+    m1, c1 = m.pattern_coverage(one, torch.zeros((2, 1), dtype=torch.uint8, device="cuda"),
+                                torch.ones((2, 1), dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert (cells == 200 * 201 // 2).all() and (mass - 1).abs().max().item() < 1e-12
+    assert (c0 == 0).all() and (m0 == 0).all()
+    assert (c1 == 1).all() and (m1 == 1).all()
 
 
 @pytest.mark.parametrize("S", [300, 512, 16384])
