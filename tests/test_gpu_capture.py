@@ -75,13 +75,14 @@ def test_capture_other_lambdas(lam, scope):
 
 @pytest.mark.parametrize("lam,tau,mu", [(0.5, 0.3, 0.8), (0.0, 0.5, 0.7), (1.0, 0.1, 0.9)])
 def test_coverage_matches_oracle(lam, tau, mu):
+    """Keep flags from the oracle's capture of the same maps feed both sides."""
     m = sa()
     maps = W.capture_maps(layers=1, heads=32, n_avg=8, layer_offset=19)
-    md = torch.from_numpy(maps).cuda()
-    c = m.pattern_capture(md, lam=lam, tau=tau, mu=mu)
-    mass, cells = m.pattern_coverage(md, c["keep_diag"], c["keep_vert"])
+    c = oracle.capture(maps, lam=lam, tau=tau, mu=mu)
+    mass, cells = m.pattern_coverage(torch.from_numpy(maps).cuda(), torch.from_numpy(c["keep_diag"]).cuda(),
+                                     torch.from_numpy(c["keep_vert"]).cuda())
     torch.cuda.synchronize()
-    rm, rc = oracle.coverage(maps, c["keep_diag"].cpu().numpy(), c["keep_vert"].cpu().numpy())
+    rm, rc = oracle.coverage(maps, c["keep_diag"], c["keep_vert"])
     np.testing.assert_array_equal(cells.cpu().numpy(), rc)
     np.testing.assert_allclose(mass.cpu().numpy(), rm, rtol=0, atol=1e-12)
     assert 0.0 < rm.min() and rm.max() <= 1.0

@@ -7,6 +7,7 @@ import torch
 
 import oracle
 import workloads as W
+from capture_bounds import certain_patterns
 from gpu_util import assert_close_f32, note, sa, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -61,20 +62,25 @@ def test_maps_full_capture_length_limit():
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_capture_from_qk_pipeline(d):
-    """One layer at the capture length: 32 query heads / 8 kv heads, batch 16, L = 512.
-    GPU maps -> GPU capture equals the oracle capture of those maps bit for bit; the maps
-    themselves match the oracle's to 1e-5, and the oracle capture of the oracle's maps keeps
-    the sink columns 0..3 and diagonal 0 that the inputs were built to carry."""
+    """One layer at the capture length: 32 query heads / 8 kv heads, batch 16, L = 512.  The GPU
+    pipeline (maps -> capture) against the oracle pipeline on the same Q/K.  The maps agree within
+    |A_gpu - A| <= 1e-5 A + 1e-9 (checked); the keep flags must then agree on every pattern whose
+    decision no map within that bound can change (tests/capture_bounds.py), and those must be
+    nearly all of them.  The inputs carry sink columns 0..3 and diagonal 0, which both keep."""
     m = sa()
     q, k = W.capture_qk(46, 16, 32, 8, 512, d, "bf16")
-    maps, ref_maps = _maps(q, k, "pipeline d=%d" % d)
-    got = m.pattern_capture(maps, return_hits=True, return_mask=True)
+    note("capture pipeline from Q/K d=%d" % d)
+    maps = m.attention_maps(to_dev(q), to_dev(k))
+    got = m.pattern_capture(maps)
     torch.cuda.synchronize()
-    ref = oracle.capture(maps.cpu().numpy(), want_mask=True)
-    for key in ("keep_diag", "keep_vert", "diag_hits", "vert_hits", "true_mask"):
-        np.testing.assert_array_equal(got[key].cpu().numpy(), ref[key], err_msg=key)
+    ref_maps = oracle.attention_maps(q, k)
+    g = maps.cpu().numpy().astype(np.float64)
+    assert (np.abs(g - ref_maps) <= 1e-5 * ref_maps + 1e-9).all()
+    ref = oracle.capture(ref_maps.astype(np.float32))
+    cd, cv = certain_patterns(ref_maps.astype(np.float32), 1e-5 + 1e-7, 1e-9)
+    note("certain patterns: diag %.5f vert %.5f" % (cd.mean(), cv.mean()))
+    assert cd.mean() > 0.99 and cv.mean() > 0.99
+    gd, gv = got["keep_diag"].cpu().numpy(), got["keep_vert"].cpu().numpy()
+    np.testing.assert_array_equal(gd[cd], ref["keep_diag"][cd])
+    np.testing.assert_array_equal(gv[cv], ref["keep_vert"][cv])
     assert ref["keep_vert"][:, :4].all() and ref["keep_diag"][:, 0].all()
-    ref2 = oracle.capture(ref_maps.astype(np.float32))
-    agree = (ref2["keep_diag"] == ref["keep_diag"]).mean(), (ref2["keep_vert"] == ref["keep_vert"]).mean()
-    note("keep-flag agreement with the capture of the oracle's maps: diag %.5f vert %.5f" % agree)
-    assert min(agree) > 0.99
