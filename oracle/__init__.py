@@ -79,6 +79,12 @@ def _load():
             lib.orc_capture_scores.restype = C.c_int
             lib.orc_capture_scores.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_double, C.c_double, C.c_int32,
                                                C.c_void_p]
+            lib.orc_sample_scores.restype = None
+            lib.orc_sample_scores.argtypes = [C.c_void_p, C.c_void_p, C.c_int] + [C.c_int32] * 5 + \
+                [C.c_double, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]
+            lib.orc_select_patterns.restype = None
+            lib.orc_select_patterns.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_double, C.c_int32,
+                                                C.c_void_p, C.c_void_p]
             lib.orc_coverage.restype = None
             lib.orc_coverage.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
                                          C.c_void_p]
@@ -293,3 +299,38 @@ def extend(keep_diag: np.ndarray, keep_vert: np.ndarray, S: int):
     diags = [d[d < S] for d in diags]
     verts = [c[c < S] for c in verts]
     return diags, verts
+
+
+def sample_scores(q, k, row0: int, n_rows: int, scale: Optional[float] = None):
+    """Runtime capture: per head, the attention mass that query rows row0 .. row0+n_rows-1 of every
+    sequence put on each diagonal r and each vertical c (float64 [hq, S] each), and each sampled
+    row's natural-log LSE [B, hq, n_rows]."""
+    lib = _load()
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    assert q.dtype in (np.float32, np.uint16) and k.dtype == q.dtype
+    dtype = 0 if q.dtype == np.float32 else 1
+    B, hq, S, d = q.shape
+    assert 0 <= row0 and row0 + n_rows <= S
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    diag = np.zeros((hq, S), np.float64)
+    vert = np.zeros((hq, S), np.float64)
+    lse = np.zeros((B, hq, n_rows), np.float64)
+    lib.orc_sample_scores(q.ctypes.data, k.ctypes.data, dtype, B, hq, k.shape[1], S, d, float(scale), row0, n_rows,
+                          diag.ctypes.data, vert.ctypes.data, lse.ctypes.data)
+    return diag, vert, lse
+
+
+def select_patterns(diag: np.ndarray, vert: np.ndarray, alpha: float, band: int = 0):
+    """Keep flags (uint8 [hq, S] each) from integer scores: per head and family, the top patterns
+    whose running sum first reaches ceil(alpha * total), ties kept; diagonals r < band always."""
+    lib = _load()
+    diag = np.ascontiguousarray(diag, dtype=np.int64)
+    vert = np.ascontiguousarray(vert, dtype=np.int64)
+    hq, S = diag.shape
+    kd = np.zeros((hq, S), np.uint8)
+    kv = np.zeros((hq, S), np.uint8)
+    lib.orc_select_patterns(diag.ctypes.data, vert.ctypes.data, hq, S, float(alpha), int(band), kd.ctypes.data,
+                            kv.ctypes.data)
+    return kd, kv

@@ -42,6 +42,11 @@
  *   orc_coverage         attention mass and cell count of the kept patterns
  *                        inside the capture window -> brute-force numpy masks,
  *                        all-kept and diagonal-0-only cases
+ *   orc_sample_scores    runtime capture: attention mass of sampled query rows
+ *                        per diagonal and per vertical -> numpy softmax brute
+ *                        force, mass totals, causal support
+ *   orc_select_patterns  smallest top set reaching a mass fraction, ties kept
+ *                        -> Python sorted() brute force, alpha = 1, all-zero
  */
 #include <math.h>
 #include <stdint.h>
@@ -605,5 +610,108 @@ void orc_coverage(const float* maps, int32_t n_maps, int32_t L, const uint8_t* k
       }
     mass[mi] = total > 0.0 ? kept / total : 0.0;
     cells[mi] = n;
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Runtime capture from a sample of the input's own query rows.             */
+/* [SampleAttention] abstract: head-specific sparse patterns are captured   */
+/* at runtime, per input, at low cost.  Reading used here: the rows         */
+/* i = row0 .. row0 + n_rows - 1 of every sequence take their causal        */
+/* softmax over all keys j <= i (scores q_i . k_j * scale, GQA head          */
+/* h / (hq / hkv)); each row's probabilities are added onto the DAM pattern */
+/* pool of its head ([DAM] "What carries the argument": diagonals j = i - r */
+/* and verticals j = c):                                                    */
+/*   diag[h][r] += p_i(i - r),  vert[h][c] += p_i(c),  summed over b and i.  */
+/* lse[b][h][n] = log sum_j exp(s_ij) of sampled row row0 + n (natural log). */
+/* ------------------------------------------------------------------------ */
+void orc_sample_scores(const void* q, const void* k, int dtype, int32_t B, int32_t hq, int32_t hkv, int32_t S,
+                       int32_t dh, double scale, int32_t row0, int32_t n_rows, double* diag /* [hq][S] */,
+                       double* vert /* [hq][S] */, double* lse /* [B][hq][n_rows] */) {
+  int32_t group = hq / hkv;
+#pragma omp parallel
+  {
+    double* sc = (double*)malloc(sizeof(double) * (size_t)S);
+#pragma omp for schedule(dynamic, 1)
+    for (int32_t h = 0; h < hq; ++h) {
+      double* dg = diag + (int64_t)h * S;
+      double* vt = vert + (int64_t)h * S;
+      for (int32_t x = 0; x < S; ++x) dg[x] = vt[x] = 0.0;
+      int32_t g = h / group;
+      for (int32_t b = 0; b < B; ++b)
+        for (int32_t n = 0; n < n_rows; ++n) {
+          int32_t i = row0 + n;
+          int64_t qb = (((int64_t)b * hq + h) * S + i) * dh;
+          int64_t kb = ((int64_t)b * hkv + g) * (int64_t)S * dh;
+          double m = -INFINITY;
+          for (int32_t j = 0; j <= i; ++j) {
+            double acc = 0.0;
+            for (int32_t c = 0; c < dh; ++c) acc += widen(q, dtype, qb + c) * widen(k, dtype, kb + (int64_t)j * dh + c);
+            sc[j] = acc * scale;
+            if (sc[j] > m) m = sc[j];
+          }
+          double l = 0.0;
+          for (int32_t j = 0; j <= i; ++j) {
+            sc[j] = exp(sc[j] - m);
+            l += sc[j];
+          }
+          for (int32_t j = 0; j <= i; ++j) {
+            double p = sc[j] / l;
+            dg[i - j] += p;
+            vt[j] += p;
+          }
+          if (lse) lse[((int64_t)b * hq + h) * n_rows + n] = m + log(l);
+        }
+    }
+    free(sc);
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Pattern selection from scores (integers: fixed-point masses).  Per head  */
+/* and per family (diagonals, verticals): with T = the family's total and   */
+/* target = ceil(alpha * T) (IEEE double product), sort the scores in       */
+/* descending order, walk until the running sum first reaches target; the   */
+/* score there is theta, and every pattern with score >= theta and > 0 is   */
+/* kept (ties at theta all kept).  T = 0 keeps nothing.  Diagonals r < band */
+/* (the local window) are always kept.                                      */
+/* ------------------------------------------------------------------------ */
+static int cmp_desc_i64(const void* a, const void* b) {
+  int64_t x = *(const int64_t*)a, y = *(const int64_t*)b;
+  return (x < y) - (x > y);
+}
+
+static void select_family(const int64_t* v, int32_t S, double alpha, uint8_t* keep, int64_t* tmp) {
+  int64_t total = 0;
+  for (int32_t x = 0; x < S; ++x) total += v[x];
+  for (int32_t x = 0; x < S; ++x) keep[x] = 0;
+  if (total <= 0) return;
+  int64_t target = (int64_t)ceil(alpha * (double)total);
+  if (target < 1) target = 1;
+  memcpy(tmp, v, sizeof(int64_t) * (size_t)S);
+  qsort(tmp, (size_t)S, sizeof(int64_t), cmp_desc_i64);
+  int64_t run = 0, theta = tmp[0];
+  for (int32_t x = 0; x < S; ++x) {
+    run += tmp[x];
+    if (run >= target) {
+      theta = tmp[x];
+      break;
+    }
+  }
+  for (int32_t x = 0; x < S; ++x) keep[x] = (uint8_t)(v[x] >= theta && v[x] > 0);
+}
+
+void orc_select_patterns(const int64_t* diag, const int64_t* vert, int32_t hq, int32_t S, double alpha,
+                         int32_t band, uint8_t* keep_diag, uint8_t* keep_vert) {
+#pragma omp parallel
+  {
+    int64_t* tmp = (int64_t*)malloc(sizeof(int64_t) * (size_t)S);
+#pragma omp for schedule(dynamic, 1)
+    for (int32_t h = 0; h < hq; ++h) {
+      select_family(diag + (int64_t)h * S, S, alpha, keep_diag + (int64_t)h * S, tmp);
+      select_family(vert + (int64_t)h * S, S, alpha, keep_vert + (int64_t)h * S, tmp);
+      for (int32_t r = 0; r < band && r < S; ++r) keep_diag[(int64_t)h * S + r] = 1;
+    }
+    free(tmp);
   }
 }

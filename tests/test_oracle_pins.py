@@ -19,6 +19,11 @@ from brute import attention_brute, index_brute, mask_matrix
 from golden.load import arr, load
 
 
+def widen64(x):
+    """float32 or bf16 bit patterns -> float64 values."""
+    return W.bf16_bits_to_f32(x).astype(np.float64) if x.dtype == np.uint16 else x.astype(np.float64)
+
+
 def _rand_desc(rng, S, H, kinds):
     diags, verts = [], []
     for _ in range(H):
@@ -464,3 +469,93 @@ def test_attention_maps_match_torch_softmax_average():
     s = s.masked_fill(~torch.tril(torch.ones(33, 33, dtype=torch.bool)), float("-inf"))
     ref = torch.softmax(s, dim=-1).mean(dim=0).numpy()
     np.testing.assert_allclose(m, ref, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# runtime capture: sampled-row scores and pattern selection
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_sample_scores_brute_force(dtype):
+    """Numpy twin: softmax of the sampled rows over j <= i, mass added per diagonal i - j and per column j."""
+    B, hq, hkv, S, d, row0, n = 2, 4, 2, 40, 16, 25, 10
+    q, k, _ = W.qkv(61, B, hq, hkv, S, d, dtype)
+    diag, vert, lse = oracle.sample_scores(q, k, row0, n)
+    qf, kf = widen64(q), widen64(k)
+    rd = np.zeros((hq, S))
+    rv = np.zeros((hq, S))
+    rl = np.zeros((B, hq, n))
+    for b in range(B):
+        for h in range(hq):
+            g = h // (hq // hkv)
+            for x in range(n):
+                i = row0 + x
+                s = kf[b, g, :i + 1] @ qf[b, h, i] / np.sqrt(d)
+                rl[b, h, x] = np.log(np.exp(s - s.max()).sum()) + s.max()
+                p = np.exp(s - s.max())
+                p /= p.sum()
+                j = np.arange(i + 1)
+                np.add.at(rd[h], i - j, p)
+                np.add.at(rv[h], j, p)
+    np.testing.assert_allclose(diag, rd, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(vert, rv, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, rl, rtol=0, atol=1e-12)
+
+
+def test_sample_scores_totals_and_support():
+    B, hq, hkv, S, d, row0, n = 3, 2, 1, 64, 8, 10, 20
+    q, k, _ = W.qkv(62, B, hq, hkv, S, d, "f32")
+    diag, vert, _ = oracle.sample_scores(q, k, row0, n, scale=0.7)
+    np.testing.assert_allclose(diag.sum(1), B * n, rtol=1e-13)
+    np.testing.assert_allclose(vert.sum(1), B * n, rtol=1e-13)
+    last = row0 + n - 1
+    assert not diag[:, last + 1:].any() and not vert[:, last + 1:].any()
+    assert (diag[:, :last + 1] > 0).all() and (vert[:, :last + 1] > 0).all()
+    # a single sampled row at position 0 sees only key 0
+    d0, v0, l0 = oracle.sample_scores(q, k, 0, 1)
+    assert np.all(d0[:, 0] == B) and np.all(v0[:, 0] == B) and not d0[:, 1:].any()
+
+
+def _select_brute(v, alpha):
+    total = int(v.sum())
+    if total == 0:
+        return np.zeros(v.shape, np.uint8)
+    target = max(1, int(np.ceil(alpha * float(total))))
+    run = 0
+    for x in sorted(v.tolist(), reverse=True):
+        run += x
+        if run >= target:
+            theta = x
+            break
+    return ((v >= theta) & (v > 0)).astype(np.uint8)
+
+
+@pytest.mark.parametrize("alpha", [0.05, 0.5, 0.9, 0.97, 1.0])
+def test_select_patterns_brute_force(alpha):
+    rng = np.random.default_rng(int(alpha * 1000))
+    hq, S = 3, 50
+    diag = rng.choice([0, 1, 2, 5, 5, 40, 300, 1 << 33], size=(hq, S)).astype(np.int64)   # many ties
+    vert = rng.integers(0, 1 << 40, size=(hq, S)).astype(np.int64)
+    vert[:, ::3] = 0
+    kd, kv = oracle.select_patterns(diag, vert, alpha, band=4)
+    for h in range(hq):
+        ed = _select_brute(diag[h], alpha)
+        ed[:4] = 1
+        np.testing.assert_array_equal(kd[h], ed)
+        np.testing.assert_array_equal(kv[h], _select_brute(vert[h], alpha))
+
+
+def test_select_patterns_special_cases():
+    hq, S = 2, 30
+    rng = np.random.default_rng(3)
+    v = rng.integers(0, 1000, size=(hq, S)).astype(np.int64)
+    v[0, 5] = 0
+    kd, kv = oracle.select_patterns(v, v, 1.0)
+    np.testing.assert_array_equal(kv, (v > 0).astype(np.uint8))       # alpha = 1: every pattern with mass
+    z = np.zeros((hq, S), np.int64)
+    kd, kv = oracle.select_patterns(z, z, 0.9, band=3)
+    assert not kv.any() and kd[:, :3].all() and not kd[:, 3:].any()   # no mass: only the local band
+    one = np.zeros((hq, S), np.int64)
+    one[:, 7] = 10
+    one[:, 9] = 1
+    kd, kv = oracle.select_patterns(one, one, 0.9)                    # 10 of 11 reaches 0.9
+    assert kv[:, 7].all() and kv.sum() == hq
