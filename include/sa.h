@@ -271,6 +271,61 @@ sa_status sa_pattern_coverage(const float* maps, int32_t n_maps, int32_t L, cons
                               const uint8_t* keep_vert, double* mass, int64_t* cells, void* stream);
 
 /*
+ * sa_sample_scores [SampleAttention, abstract: head-specific sparse patterns captured
+ * at runtime, per input, at low cost; DAM, What carries the argument: the pattern
+ * pool of diagonals j = i - r and verticals j = c]: the query rows
+ * i = row0 .. row0 + n_rows - 1 of every sequence take their causal softmax over
+ * the keys j <= i (scores q_i . k_j * scale, kv head h / (hq / hkv)), and each
+ * row's probabilities on the pairs not covered yet -- outside the local window
+ * (i - j >= band) and off the columns marked in skip_cols -- are ADDED onto its
+ * head's pattern scores:
+ *   diag_score[h][r] += round(p_i(i - r) * 2^32)     (per term)
+ *   vert_score[h][c] += sum of p_i(c), rounded to units of 2^-32 per partial sum
+ * int64 fixed point, so the sums are exact integer sums whatever the order of the
+ * atomics (deterministic); the caller zeroes both arrays first and may call again
+ * with other row blocks to accumulate.  Each sampled row holds 2^32 units in all
+ * (its probabilities sum to 1), the window and skipped columns included.
+ *   q [batch][hq][S][head_dim], k [batch][hkv][S][head_dim]: element type `dtype`.
+ *   skip_cols  NULL or uint8 [hq][S] (nonzero: column already kept).
+ *   row_lse  float [batch][hq][n_rows]: natural-log LSE of each sampled row over all
+ *            its keys; written, or read when lse_given is nonzero (a second call
+ *            over the same rows skips that pass).
+ *   diag_score, vert_score  int64 [hq][S], 8-byte aligned.
+ * Arithmetic: fp32 MFMA scores, fp32 softmax (exp2 domain), as for attention.
+ * Limits: 0 <= row0, 1 <= n_rows <= 2048, row0 + n_rows <= S, batch * n_rows <= 2^20,
+ * band >= 0; head_dim 64 or 128.  softmax_scale <= 0 selects 1 / sqrt(head_dim).
+ * Errors: SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_HIP.
+ */
+sa_status sa_sample_scores(const void* q, const void* k, int32_t batch, int32_t hq, int32_t hkv, int32_t S,
+                           int32_t head_dim, int32_t dtype, float softmax_scale, int32_t row0, int32_t n_rows,
+                           int32_t band, const uint8_t* skip_cols, int32_t lse_given, float* row_lse,
+                           int64_t* diag_score, int64_t* vert_score, void* stream);
+
+/*
+ * sa_select_patterns [SampleAttention, abstract: adaptive, head-specific selection,
+ * near-lossless; the rule is this library's reading]: for one pattern family, per
+ * head h, scores v[0..S) as sa_sample_scores makes them over `rows` sampled row
+ * sequences (batch * n_rows):
+ *   T_all = rows * 2^32 (all sampled mass);  T = sum v (the mass not covered yet);
+ *   need = ceil(alpha * (double)T_all) - (T_all - T): what this family must add so
+ *          that the covered mass reaches alpha of T_all;
+ *   need <= 0: nothing is kept;  need > T: every pattern with v > 0 is kept;
+ *   else theta = the largest score value with sum of { v : v >= theta } >= need,
+ *        keep[x] = (v[x] >= theta and v[x] > 0): the fewest top-scoring patterns,
+ *        ties at theta all kept.
+ *   Patterns x < band are always kept (the local window, for the diagonal family).
+ * The two-stage use: columns first (scores with skip_cols = NULL, band = the
+ * window), then diagonals (scores with skip_cols = the kept columns); the window,
+ * the columns and the diagonals then hold at least alpha of the sampled mass.
+ * Exact integer arithmetic (the product alpha * T_all is one IEEE double rounding).
+ *   scores  int64 [n_heads][S] (>= 0, 8-byte aligned);  keep  uint8 [n_heads][S].
+ * Limits: 0 < alpha <= 1, 1 <= rows <= 2^30, band >= 0.
+ * Errors: SA_ERR_INVALID_ARG, SA_ERR_HIP.
+ */
+sa_status sa_select_patterns(const int64_t* scores, int32_t n_heads, int32_t S, double alpha, int64_t rows,
+                             int32_t band, uint8_t* keep, void* stream);
+
+/*
  * sa_patterns_to_desc [DAM, What carries the argument; Circularity Check 1]: the kept
  * patterns of each map are pasted into an S x S mask, i.e. the per-head descriptor
  * lists at length S are D_h = { r : keep_diag[h][r], r < S } and

@@ -81,10 +81,10 @@ def _load():
                                                C.c_void_p]
             lib.orc_sample_scores.restype = None
             lib.orc_sample_scores.argtypes = [C.c_void_p, C.c_void_p, C.c_int] + [C.c_int32] * 5 + \
-                [C.c_double, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]
+                [C.c_double, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
             lib.orc_select_patterns.restype = None
-            lib.orc_select_patterns.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_double, C.c_int32,
-                                                C.c_void_p, C.c_void_p]
+            lib.orc_select_patterns.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_double, C.c_int64, C.c_int32,
+                                                C.c_void_p]
             lib.orc_coverage.restype = None
             lib.orc_coverage.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
                                          C.c_void_p]
@@ -301,10 +301,12 @@ def extend(keep_diag: np.ndarray, keep_vert: np.ndarray, S: int):
     return diags, verts
 
 
-def sample_scores(q, k, row0: int, n_rows: int, scale: Optional[float] = None):
+def sample_scores(q, k, row0: int, n_rows: int, band: int = 0, skip_cols: Optional[np.ndarray] = None,
+                  scale: Optional[float] = None):
     """Runtime capture: per head, the attention mass that query rows row0 .. row0+n_rows-1 of every
-    sequence put on each diagonal r and each vertical c (float64 [hq, S] each), and each sampled
-    row's natural-log LSE [B, hq, n_rows]."""
+    sequence put on each diagonal r and each vertical c, over the pairs outside the local window
+    (i - j >= band) and off the columns in skip_cols (uint8 [hq, S]); float64 [hq, S] each, and
+    each sampled row's natural-log LSE over all its keys [B, hq, n_rows]."""
     lib = _load()
     q = np.ascontiguousarray(q)
     k = np.ascontiguousarray(k)
@@ -314,23 +316,37 @@ def sample_scores(q, k, row0: int, n_rows: int, scale: Optional[float] = None):
     assert 0 <= row0 and row0 + n_rows <= S
     if scale is None:
         scale = 1.0 / np.sqrt(d)
+    skip = None if skip_cols is None else np.ascontiguousarray(skip_cols, dtype=np.uint8).reshape(hq, S)
     diag = np.zeros((hq, S), np.float64)
     vert = np.zeros((hq, S), np.float64)
     lse = np.zeros((B, hq, n_rows), np.float64)
     lib.orc_sample_scores(q.ctypes.data, k.ctypes.data, dtype, B, hq, k.shape[1], S, d, float(scale), row0, n_rows,
-                          diag.ctypes.data, vert.ctypes.data, lse.ctypes.data)
+                          int(band), _ptr(skip), diag.ctypes.data, vert.ctypes.data, lse.ctypes.data)
     return diag, vert, lse
 
 
-def select_patterns(diag: np.ndarray, vert: np.ndarray, alpha: float, band: int = 0):
-    """Keep flags (uint8 [hq, S] each) from integer scores: per head and family, the top patterns
-    whose running sum first reaches ceil(alpha * total), ties kept; diagonals r < band always."""
+def fixed_point(x: np.ndarray) -> np.ndarray:
+    """float64 masses -> int64 in units of 2^-32 (round to nearest)."""
+    return np.rint(np.asarray(x, np.float64) * 4294967296.0).astype(np.int64)
+
+
+def select_patterns(scores: np.ndarray, alpha: float, rows: int, band: int = 0) -> np.ndarray:
+    """Keep flags (uint8 [n, S]) from integer scores of one family: the fewest top patterns that bring
+    the covered mass of `rows` sampled rows to alpha (ties kept); patterns x < band always kept."""
     lib = _load()
-    diag = np.ascontiguousarray(diag, dtype=np.int64)
-    vert = np.ascontiguousarray(vert, dtype=np.int64)
-    hq, S = diag.shape
-    kd = np.zeros((hq, S), np.uint8)
-    kv = np.zeros((hq, S), np.uint8)
-    lib.orc_select_patterns(diag.ctypes.data, vert.ctypes.data, hq, S, float(alpha), int(band), kd.ctypes.data,
-                            kv.ctypes.data)
-    return kd, kv
+    scores = np.ascontiguousarray(scores, dtype=np.int64)
+    n, S = scores.shape
+    keep = np.zeros((n, S), np.uint8)
+    lib.orc_select_patterns(scores.ctypes.data, n, S, float(alpha), int(rows), int(band), keep.ctypes.data)
+    return keep
+
+
+def runtime_capture(q, k, row0: int, n_rows: int, alpha: float, band: int, scale: Optional[float] = None):
+    """The two-stage per-input capture: columns first (window counted as covered), then diagonals on
+    the mass still uncovered.  Returns (keep_diag, keep_vert) uint8 [hq, S] and the stage scores."""
+    B = q.shape[0]
+    _, vert, _ = sample_scores(q, k, row0, n_rows, band=band, scale=scale)
+    keep_vert = select_patterns(fixed_point(vert), alpha, B * n_rows)
+    diag, _, _ = sample_scores(q, k, row0, n_rows, band=band, skip_cols=keep_vert, scale=scale)
+    keep_diag = select_patterns(fixed_point(diag), alpha, B * n_rows, band=band)
+    return keep_diag, keep_vert, vert, diag

@@ -622,11 +622,15 @@ void orc_coverage(const float* maps, int32_t n_maps, int32_t L, const uint8_t* k
 /* h / (hq / hkv)); each row's probabilities are added onto the DAM pattern */
 /* pool of its head ([DAM] "What carries the argument": diagonals j = i - r */
 /* and verticals j = c):                                                    */
-/*   diag[h][r] += p_i(i - r),  vert[h][c] += p_i(c),  summed over b and i.  */
-/* lse[b][h][n] = log sum_j exp(s_ij) of sampled row row0 + n (natural log). */
+/*   diag[h][r] += p_i(i - r),  vert[h][c] += p_i(c),  summed over b and i,  */
+/* only for the pairs not already covered: outside the local window         */
+/* (i - j >= band) and off the columns marked in skip_cols (NULL: none).    */
+/* lse[b][h][n] = log sum_j exp(s_ij) of sampled row row0 + n (natural log, */
+/* over all its keys).                                                      */
 /* ------------------------------------------------------------------------ */
 void orc_sample_scores(const void* q, const void* k, int dtype, int32_t B, int32_t hq, int32_t hkv, int32_t S,
-                       int32_t dh, double scale, int32_t row0, int32_t n_rows, double* diag /* [hq][S] */,
+                       int32_t dh, double scale, int32_t row0, int32_t n_rows, int32_t band,
+                       const uint8_t* skip_cols /* [hq][S] or NULL */, double* diag /* [hq][S] */,
                        double* vert /* [hq][S] */, double* lse /* [B][hq][n_rows] */) {
   int32_t group = hq / hkv;
 #pragma omp parallel
@@ -636,6 +640,7 @@ void orc_sample_scores(const void* q, const void* k, int dtype, int32_t B, int32
     for (int32_t h = 0; h < hq; ++h) {
       double* dg = diag + (int64_t)h * S;
       double* vt = vert + (int64_t)h * S;
+      const uint8_t* skip = skip_cols ? skip_cols + (int64_t)h * S : NULL;
       for (int32_t x = 0; x < S; ++x) dg[x] = vt[x] = 0.0;
       int32_t g = h / group;
       for (int32_t b = 0; b < B; ++b)
@@ -655,7 +660,8 @@ void orc_sample_scores(const void* q, const void* k, int dtype, int32_t B, int32
             sc[j] = exp(sc[j] - m);
             l += sc[j];
           }
-          for (int32_t j = 0; j <= i; ++j) {
+          for (int32_t j = 0; j <= i - band; ++j) {
+            if (skip && skip[j]) continue;
             double p = sc[j] / l;
             dg[i - j] += p;
             vt[j] += p;
@@ -668,49 +674,51 @@ void orc_sample_scores(const void* q, const void* k, int dtype, int32_t B, int32
 }
 
 /* ------------------------------------------------------------------------ */
-/* Pattern selection from scores (integers: fixed-point masses).  Per head  */
-/* and per family (diagonals, verticals): with T = the family's total and   */
-/* target = ceil(alpha * T) (IEEE double product), sort the scores in       */
-/* descending order, walk until the running sum first reaches target; the   */
-/* score there is theta, and every pattern with score >= theta and > 0 is   */
-/* kept (ties at theta all kept).  T = 0 keeps nothing.  Diagonals r < band */
-/* (the local window) are always kept.                                      */
+/* Pattern selection from scores (integers: fixed-point masses in units of  */
+/* 2^-32 of one row's probability).  The sampled rows hold T_all = rows *   */
+/* 2^32 of mass; the scores v of one family add up to T = the mass not yet  */
+/* covered, so T_all - T is already covered (the local window, columns kept */
+/* before).  The family must bring the covered mass to ceil(alpha * T_all): */
+/* need = ceil(alpha * T_all) - (T_all - T) (IEEE double product).  If      */
+/* need <= 0 nothing is kept.  Otherwise sort v in descending order and     */
+/* walk until the running sum first reaches need; the value there is theta */
+/* and every pattern with v >= theta and v > 0 is kept (ties at theta all   */
+/* kept).  Patterns x < band are always kept (the local window's diagonals).*/
 /* ------------------------------------------------------------------------ */
 static int cmp_desc_i64(const void* a, const void* b) {
   int64_t x = *(const int64_t*)a, y = *(const int64_t*)b;
   return (x < y) - (x > y);
 }
 
-static void select_family(const int64_t* v, int32_t S, double alpha, uint8_t* keep, int64_t* tmp) {
-  int64_t total = 0;
-  for (int32_t x = 0; x < S; ++x) total += v[x];
-  for (int32_t x = 0; x < S; ++x) keep[x] = 0;
-  if (total <= 0) return;
-  int64_t target = (int64_t)ceil(alpha * (double)total);
-  if (target < 1) target = 1;
-  memcpy(tmp, v, sizeof(int64_t) * (size_t)S);
-  qsort(tmp, (size_t)S, sizeof(int64_t), cmp_desc_i64);
-  int64_t run = 0, theta = tmp[0];
-  for (int32_t x = 0; x < S; ++x) {
-    run += tmp[x];
-    if (run >= target) {
-      theta = tmp[x];
-      break;
-    }
-  }
-  for (int32_t x = 0; x < S; ++x) keep[x] = (uint8_t)(v[x] >= theta && v[x] > 0);
-}
-
-void orc_select_patterns(const int64_t* diag, const int64_t* vert, int32_t hq, int32_t S, double alpha,
-                         int32_t band, uint8_t* keep_diag, uint8_t* keep_vert) {
+void orc_select_patterns(const int64_t* scores, int32_t n_heads, int32_t S, double alpha, int64_t rows,
+                         int32_t band, uint8_t* keep) {
+  const int64_t t_all = rows * ((int64_t)1 << 32);
 #pragma omp parallel
   {
     int64_t* tmp = (int64_t*)malloc(sizeof(int64_t) * (size_t)S);
 #pragma omp for schedule(dynamic, 1)
-    for (int32_t h = 0; h < hq; ++h) {
-      select_family(diag + (int64_t)h * S, S, alpha, keep_diag + (int64_t)h * S, tmp);
-      select_family(vert + (int64_t)h * S, S, alpha, keep_vert + (int64_t)h * S, tmp);
-      for (int32_t r = 0; r < band && r < S; ++r) keep_diag[(int64_t)h * S + r] = 1;
+    for (int32_t h = 0; h < n_heads; ++h) {
+      const int64_t* v = scores + (int64_t)h * S;
+      uint8_t* kp = keep + (int64_t)h * S;
+      int64_t total = 0;
+      for (int32_t x = 0; x < S; ++x) total += v[x];
+      int64_t need = (int64_t)ceil(alpha * (double)t_all) - (t_all - total);
+      int64_t theta = INT64_MAX;
+      if (need > 0) {
+        memcpy(tmp, v, sizeof(int64_t) * (size_t)S);
+        qsort(tmp, (size_t)S, sizeof(int64_t), cmp_desc_i64);
+        int64_t run = 0;
+        for (int32_t x = 0; x < S; ++x) {
+          run += tmp[x];
+          if (run >= need) {
+            theta = tmp[x];
+            break;
+          }
+        }
+        /* need > total: even every pattern falls short; all with mass are kept */
+        if (run < need) theta = 1;
+      }
+      for (int32_t x = 0; x < S; ++x) kp[x] = (uint8_t)((v[x] >= theta && v[x] > 0) || x < band);
     }
     free(tmp);
   }

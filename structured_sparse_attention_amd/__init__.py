@@ -18,7 +18,7 @@ import numpy as np
 import torch
 
 __all__ = ["SAError", "DevicePatterns", "SparseIndex", "build_index", "sparse_attn_prefill", "sparse_attn_decode",
-           "attention_maps", "pattern_capture", "pattern_coverage", "patterns_to_desc", "library_path", "version", "lib"]
+           "attention_maps", "pattern_capture", "pattern_coverage", "patterns_to_desc", "sample_scores", "select_patterns", "library_path", "version", "lib"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libsa.so")
@@ -76,6 +76,12 @@ def _load():
     lib.sa_pattern_capture.restype = C.c_int32
     lib.sa_pattern_capture.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_double, C.c_double, C.c_double,
                                        C.c_double, C.c_int32] + [C.c_void_p] * 5 + [C.c_void_p]
+    lib.sa_sample_scores.restype = C.c_int32
+    lib.sa_sample_scores.argtypes = [C.c_void_p, C.c_void_p] + [C.c_int32] * 6 + [C.c_float] + [C.c_int32] * 3 + \
+        [C.c_void_p, C.c_int32] + [C.c_void_p] * 3 + [C.c_void_p]
+    lib.sa_select_patterns.restype = C.c_int32
+    lib.sa_select_patterns.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_double, C.c_int64, C.c_int32,
+                                       C.c_void_p, C.c_void_p]
     lib.sa_pattern_coverage.restype = C.c_int32
     lib.sa_pattern_coverage.argtypes = [C.c_void_p, C.c_int32, C.c_int32] + [C.c_void_p] * 4 + [C.c_void_p]
     lib.sa_patterns_to_desc.restype = C.c_int32
@@ -346,6 +352,57 @@ def pattern_coverage(maps: torch.Tensor, keep_diag: torch.Tensor, keep_vert: tor
     _check(_lib.sa_pattern_coverage(maps.data_ptr(), n, L, keep_diag.data_ptr(), keep_vert.data_ptr(),
                                     mass.data_ptr(), cells.data_ptr(), _stream(stream)), "sa_pattern_coverage")
     return mass, cells
+
+
+def sample_scores(q: torch.Tensor, k: torch.Tensor, row0: int, n_rows: int, band: int = 0,
+                  skip_cols: Optional[torch.Tensor] = None, softmax_scale: Optional[float] = None, scores=None,
+                  row_lse: Optional[torch.Tensor] = None, lse_given: bool = False, stream=None):
+    """sa_sample_scores: adds the attention mass of query rows row0 .. row0+n_rows-1 on the pairs outside
+    the window (i - j >= band) and off `skip_cols` onto per-head diagonal and vertical scores (int64
+    [Hq, S] each, fixed point 2^-32).  `scores` = (diag, vert) to accumulate into, new zeroed arrays
+    otherwise; `row_lse` [B, Hq, n_rows] is written, or read when lse_given.  Returns (diag, vert, row_lse)."""
+    if q.dtype == torch.bfloat16:
+        dt = SA_DTYPE_BF16
+    elif q.dtype == torch.float32:
+        dt = SA_DTYPE_F32
+    else:
+        raise TypeError("q must be bfloat16 or float32")
+    if k.dtype != q.dtype or q.dim() != 4 or k.dim() != 4 or not (q.is_contiguous() and k.is_contiguous()):
+        raise ValueError("contiguous q [B,Hq,S,d] and k [B,Hkv,S,d] of one dtype expected")
+    B, hq, S, d = q.shape
+    if k.shape[0] != B or k.shape[2] != S or k.shape[3] != d:
+        raise ValueError("k shape does not match q")
+    if scores is None:
+        scores = (torch.zeros((hq, S), dtype=torch.int64, device=q.device),
+                  torch.zeros((hq, S), dtype=torch.int64, device=q.device))
+    diag, vert = scores
+    for t in (diag, vert):
+        if t.dtype != torch.int64 or tuple(t.shape) != (hq, S) or not t.is_contiguous():
+            raise ValueError("scores must be contiguous int64 [Hq, S] tensors")
+    if skip_cols is not None and (skip_cols.dtype != torch.uint8 or tuple(skip_cols.shape) != (hq, S)
+                                  or not skip_cols.is_contiguous()):
+        raise ValueError("skip_cols must be a contiguous uint8 [Hq, S] tensor")
+    if row_lse is None:
+        if lse_given:
+            raise ValueError("lse_given needs row_lse")
+        row_lse = torch.empty((B, hq, max(n_rows, 1)), dtype=torch.float32, device=q.device)
+    scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    _check(_lib.sa_sample_scores(q.data_ptr(), k.data_ptr(), B, hq, k.shape[1], S, d, dt, scale, row0, n_rows, band,
+                                 _ptr(skip_cols), int(bool(lse_given)), row_lse.data_ptr(), diag.data_ptr(),
+                                 vert.data_ptr(), _stream(stream)), "sa_sample_scores")
+    return diag, vert, row_lse
+
+
+def select_patterns(scores: torch.Tensor, alpha: float, rows: int, band: int = 0, stream=None) -> torch.Tensor:
+    """sa_select_patterns for one family: keep flags (uint8 [Hq, S]) of the fewest top patterns that bring
+    the covered mass of `rows` sampled rows to `alpha`; patterns x < band always kept."""
+    if scores.dtype != torch.int64 or scores.dim() != 2 or not scores.is_contiguous():
+        raise ValueError("scores must be a contiguous int64 [Hq, S] tensor")
+    n, S = scores.shape
+    keep = torch.empty((n, S), dtype=torch.uint8, device=scores.device)
+    _check(_lib.sa_select_patterns(scores.data_ptr(), n, S, float(alpha), int(rows), int(band), keep.data_ptr(),
+                                   _stream(stream)), "sa_select_patterns")
+    return keep
 
 
 def patterns_to_desc(keep_diag: torch.Tensor, keep_vert: torch.Tensor, S: int, stream=None) -> DevicePatterns:

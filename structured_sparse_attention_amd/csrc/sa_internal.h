@@ -11,6 +11,8 @@ namespace sa {
 constexpr int32_t kMaxIndexS = 262144;
 // Largest capture window (two int32 hit arrays of L entries live in LDS).
 constexpr int32_t kMaxCaptureL = 4096;
+constexpr int32_t kMaxSampleRows = 2048;       // sampled rows per call
+constexpr int64_t kMaxSampleRowSeqs = 1 << 20; // batch * rows per call: fixed-point totals < 2^52
 
 // Index builder (sa_index.hip).  All launches go on `stream`.  Order of a build: heads, items (count),
 // scan, [size query], items (fill), heads (fill).
@@ -53,6 +55,12 @@ hipError_t launch_capture(const float* maps, int32_t n_maps, int32_t L, double l
                           int32_t* vert_hits, uint8_t* true_mask, hipStream_t stream);
 hipError_t launch_attention_maps(const void* q, const void* k, int32_t batch, int32_t hq, int32_t hkv, int32_t L,
                                  int32_t head_dim, int32_t dtype, float scale, float* maps, hipStream_t stream);
+hipError_t launch_sample_scores(const void* q, const void* k, int32_t batch, int32_t hq, int32_t hkv, int32_t S,
+                                int32_t head_dim, int32_t dtype, float scale, int32_t row0, int32_t n_rows,
+                                int32_t band, const uint8_t* skip_cols, bool lse_given, float* row_lse, int64_t* diag,
+                                int64_t* vert, hipStream_t stream);
+hipError_t launch_select(const int64_t* scores, int32_t n_heads, int32_t S, double alpha, int64_t t_all, int32_t band,
+                         uint8_t* keep, hipStream_t stream);
 hipError_t launch_coverage(const float* maps, int32_t n_maps, int32_t L, const uint8_t* keep_diag,
                            const uint8_t* keep_vert, double* mass, int64_t* cells, hipStream_t stream);
 hipError_t launch_patterns_to_desc(const uint8_t* keep_diag, const uint8_t* keep_vert, int32_t n_maps, int32_t L,

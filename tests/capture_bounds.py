@@ -51,3 +51,35 @@ def certain_patterns(A, rel, ab, eps=1e-8, tau=0.3, mu=0.8):
             hi = np.bincount(idx, weights=maybe, minlength=L)
             out[m] = (lo / length >= mu) | (hi / length < mu)
     return cd, cv
+
+
+def certain_selection(x, rel, ab, alpha, rows, band=0):
+    """Scores x (float64 [n, S], mass units) and a bound |x' - x| <= rel * x + ab on another computation
+    of them: per pattern, whether sa_select_patterns decides it the same way for every such x'.
+
+    With U = T_all - ceil(alpha * T_all) (the mass allowed to stay uncovered; T_all = rows), a
+    pattern is dropped exactly when the mass of all patterns scoring at or below it, itself
+    included, fits in U (and always when its score is 0).  The interval bounds of that sum decide
+    which patterns are sure either way.  Patterns x < band are kept for every x'."""
+    x = np.asarray(x, dtype=np.float64)
+    n, S = x.shape
+    t_all = float(rows)
+    U = t_all - np.ceil(alpha * t_all * 4294967296.0) / 4294967296.0
+    sure = np.zeros((n, S), bool)
+    for h in range(n):
+        v = x[h]
+        lo = np.maximum(v * (1 - rel) - ab, 0.0)
+        hi = v * (1 + rel) + ab
+        # largest possible bottom sum of p: every y whose low end can be <= p's high end, at its high end
+        o_lo = np.sort(lo)
+        c_hi = np.concatenate([[0.0], np.cumsum(hi[np.argsort(lo)])])
+        bmax = c_hi[np.searchsorted(o_lo, hi, side="right")]
+        # smallest possible bottom sum: p itself plus every y whose high end is <= p's low end, at its low end
+        o_hi = np.sort(hi)
+        c_lo = np.concatenate([[0.0], np.cumsum(lo[np.argsort(hi)])])
+        bmin = c_lo[np.searchsorted(o_hi, lo, side="right")]
+        bmin = np.maximum(bmin, lo)   # p's own low end is always in its bottom sum
+        zero = hi <= 0.0
+        sure[h] = zero | (bmax <= U) | ((bmin > U) & (lo > 0.0))
+        sure[h, :band] = True
+    return sure

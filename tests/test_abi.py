@@ -26,7 +26,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for f in ("sa_build_index", "sa_sparse_attn_prefill", "sa_sparse_attn_decode", "sa_attention_maps",
-              "sa_pattern_capture", "sa_pattern_coverage", "sa_patterns_to_desc", "sa_status_string", "sa_version"):
+              "sa_pattern_capture", "sa_pattern_coverage", "sa_patterns_to_desc", "sa_sample_scores",
+              "sa_select_patterns", "sa_status_string", "sa_version"):
         assert f in names
 
 
@@ -123,6 +124,41 @@ def test_attention_maps_validation(m):
     assert f(p, p, 1, 1, 1, 5000, 64, 1, 0.0, p, None) == -2    # L above the capture window
     assert f(p + 4, p, 1, 1, 1, 64, 64, 1, 0.0, p, None) == -1  # q not 16-byte aligned
     assert f(p, p, 1, 1, 1, 64, 64, 1, 0.0, p + 8, None) == -1  # maps not 16-byte aligned
+
+
+def test_sample_and_select_validation(m):
+    f = m.lib.sa_sample_scores
+    p = FAKE.value
+    # q, k, batch, hq, hkv, S, d, dtype, scale, row0, n_rows, band, skip, lse_given, lse, diag, vert, stream
+    args = [p, p, 1, 4, 2, 512, 64, 1, 0.0, 448, 64, 16, None, 0, p, p, p, None]   # valid but for the field changed
+
+    def bad(changes, code):
+        a = list(args)
+        for i, val in changes:
+            a[i] = val
+        assert f(*a) == code, changes
+    bad([(0, None)], -1)            # q
+    bad([(16, None)], -1)           # vert
+    bad([(15, p + 4)], -1)          # diag not 8-byte aligned
+    bad([(3, 3)], -1)               # hq % hkv
+    bad([(7, 5)], -1)               # dtype
+    bad([(6, 96)], -2)              # head_dim
+    bad([(9, -1)], -1)              # row0
+    bad([(10, 0)], -1)              # n_rows
+    bad([(10, 65)], -1)             # row0 + n_rows > S
+    bad([(11, -1)], -1)             # band
+    bad([(5, 8192), (9, 0), (10, 4096)], -2)              # more rows than one call takes
+    bad([(2, 1024), (5, 8192), (9, 0), (10, 2048)], -2)   # batch * rows above 2^20
+    g = m.lib.sa_select_patterns
+    assert g(None, 1, 8, 0.9, 4, 0, p, None) == -1
+    assert g(p, 1, 8, 0.0, 4, 0, p, None) == -1       # alpha
+    assert g(p, 1, 8, 1.5, 4, 0, p, None) == -1
+    assert g(p, 1, 8, float("nan"), 4, 0, p, None) == -1
+    assert g(p, 1, 8, 0.9, 0, 0, p, None) == -1       # rows
+    assert g(p, 1, 8, 0.9, 1 << 31, 0, p, None) == -1
+    assert g(p, 1, 8, 0.9, 4, -1, p, None) == -1      # band
+    assert g(p, 0, 8, 0.9, 4, 0, p, None) == -1
+    assert g(p + 4, 1, 8, 0.9, 4, 0, p, None) == -1   # scores not 8-byte aligned
 
 
 def test_capture_validation(m):

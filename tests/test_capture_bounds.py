@@ -4,7 +4,7 @@ import numpy as np
 
 import oracle
 import workloads as W
-from capture_bounds import certain_patterns
+from capture_bounds import certain_patterns, certain_selection
 
 
 def test_certain_patterns_survive_every_perturbation_within_the_bound():
@@ -23,3 +23,24 @@ def test_certain_patterns_survive_every_perturbation_within_the_bound():
             assert not (dd & cd).any() and not (dv & cv).any()
             flips_outside += int(dd.sum() + dv.sum())
     assert flips_outside > 0   # the bound is not vacuous: uncertain patterns do flip
+
+
+def test_certain_selection_survives_every_perturbation_within_the_bound():
+    rng = np.random.default_rng(8)
+    n, S, rows = 6, 400, 8
+    x = rng.pareto(1.2, size=(n, S))
+    x *= 0.7 * rows / x.sum(axis=1, keepdims=True)    # 70 % of the sampled mass not covered yet
+    x[:, ::17] = 0.0
+    flips_outside = 0
+    for rel, ab in ((1e-3, 1e-6), (2e-2, 1e-5)):
+        for alpha in (0.5, 0.9, 0.97):
+            sure = certain_selection(x, rel, ab, alpha, rows, band=3)
+            ref = oracle.select_patterns(oracle.fixed_point(x), alpha, rows, band=3)
+            assert sure.mean() > 0.8
+            for trial in range(10):
+                e = rng.uniform(-1, 1, x.shape) if trial % 2 else rng.choice([-1, 1], x.shape)
+                xp = np.maximum(x + e * (rel * x + ab), 0.0)
+                got = oracle.select_patterns(oracle.fixed_point(xp), alpha, rows, band=3)
+                assert not ((got != ref) & sure).any()
+                flips_outside += int((got != ref).sum())
+    assert flips_outside > 0

@@ -1,0 +1,153 @@
+"""GPU parity: runtime capture from sampled query rows (sa_sample_scores) and pattern selection
+(sa_select_patterns) against the fp64 oracle, and the two-stage per-input pipeline end to end.
+
+Scores are int64 fixed point (2^-32 of one row's mass); against the oracle's fp64 sums they agree
+within 1e-5 relative plus 1e-7 absolute (fp32 scores and softmax; per-term rounding of the fixed
+point).  The selection is exact integer arithmetic, so on the same integer scores it is bit-exact.
+The pipeline's keep flags are compared on every pattern whose decision no score within that bound
+can change (tests/capture_bounds.py)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from capture_bounds import certain_selection
+from gpu_util import assert_close_bf16, note, sa, to_dev
+
+pytestmark = pytest.mark.gpu
+
+UNIT = 4294967296.0
+REL, ABS = 1e-5, 1e-7
+
+
+def _scores_close(got, ref, what):
+    g = got.cpu().numpy().astype(np.float64) / UNIT
+    err = np.abs(g - ref)
+    bad = err > REL * ref + ABS
+    assert not bad.any(), "%s: %d scores off, worst %.3g at %.3g" % (what, bad.sum(), err.max(), ref.flat[err.argmax()])
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 128), ("f32", 64), ("f32", 128)])
+@pytest.mark.parametrize("band,skip", [(0, False), (16, True)])
+def test_sample_scores_vs_oracle(dtype, d, band, skip):
+    """S = 700 (ragged), 100 sampled rows from 600 (four chunks, the last one partial), GQA 4:2, batch 2."""
+    m = sa()
+    B, hq, hkv, S, row0, n = 2, 4, 2, 700, 600, 100
+    q, k, _ = W.qkv(81, B, hq, hkv, S, d, dtype)
+    skip_cols = (np.random.default_rng(9).random((hq, S)) < 0.2).astype(np.uint8) if skip else None
+    note("sample scores %s d=%d band=%d skip=%s" % (dtype, d, band, skip))
+    dg, vt, lse = m.sample_scores(to_dev(q), to_dev(k), row0, n, band=band,
+                                  skip_cols=None if skip_cols is None else torch.from_numpy(skip_cols).cuda())
+    torch.cuda.synchronize()
+    rd, rv, rl = oracle.sample_scores(q, k, row0, n, band=band, skip_cols=skip_cols)
+    _scores_close(dg, rd, "diag")
+    _scores_close(vt, rv, "vert")
+    np.testing.assert_allclose(lse.cpu().numpy().astype(np.float64), rl, rtol=0, atol=1e-5)
+
+
+def test_sample_scores_totals_accumulation_and_lse_reuse():
+    m = sa()
+    B, hq, hkv, S, d = 1, 2, 1, 1000, 128
+    q, k, _ = W.qkv(82, B, hq, hkv, S, d, "bf16")
+    qd, kd = to_dev(q), to_dev(k)
+    note("sample scores totals / accumulation")
+    d1, v1, l1 = m.sample_scores(qd, kd, 900, 100)
+    d2, v2, _ = m.sample_scores(qd, kd, 300, 64)
+    da, va, _ = m.sample_scores(qd, kd, 900, 100)
+    m.sample_scores(qd, kd, 300, 64, scores=(da, va))              # accumulate a second block
+    dr, vr, _ = m.sample_scores(qd, kd, 900, 100, row_lse=l1, lse_given=True)
+    torch.cuda.synchronize()
+    assert torch.equal(da, d1 + d2) and torch.equal(va, v1 + v2)  # integer sums: exact
+    assert torch.equal(dr, d1) and torch.equal(vr, v1)            # the given LSE is the one computed
+    for t in (d1, v1):                                            # 100 rows of mass one each
+        tot = t.sum(dim=1).double().cpu().numpy() / UNIT
+        assert np.all(np.abs(tot - 100.0) < 1e-4), tot
+
+
+def _rand_scores(rng, n, S, rows, uncovered):
+    x = rng.pareto(1.1, size=(n, S))
+    x[:, rng.random(S) < 0.1] = 0.0
+    x *= uncovered * rows / x.sum(axis=1, keepdims=True)
+    v = oracle.fixed_point(x)
+    v[:, 5:40:7] = v[:, 5:6]          # ties
+    return v
+
+
+@pytest.mark.parametrize("alpha", [0.3, 0.8, 0.95, 0.999, 1.0])
+@pytest.mark.parametrize("S", [1, 777, 131072])
+def test_select_matches_oracle_bit_exact(alpha, S):
+    m = sa()
+    rng = np.random.default_rng(int(alpha * 1000) + S)
+    rows = 64
+    v = _rand_scores(rng, 5, S, rows, uncovered=0.6)
+    note("select alpha=%g S=%d" % (alpha, S))
+    for band in (0, 16):
+        got = m.select_patterns(torch.from_numpy(v).cuda(), alpha, rows, band=band)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(got.cpu().numpy(), oracle.select_patterns(v, alpha, rows, band=band))
+
+
+def test_select_edge_cases():
+    m = sa()
+    rng = np.random.default_rng(4)
+    rows = 8
+    v = _rand_scores(rng, 3, 500, rows, uncovered=0.05)   # 95 % already covered
+    for alpha in (0.9, 0.95, 0.96, 1.0):                   # need <= 0, about 0, > 0, and need > all scores
+        got = m.select_patterns(torch.from_numpy(v).cuda(), alpha, rows)
+        np.testing.assert_array_equal(got.cpu().numpy(), oracle.select_patterns(v, alpha, rows))
+    z = np.zeros((2, 300), np.int64)
+    got = m.select_patterns(torch.from_numpy(z).cuda(), 0.9, rows, band=5)
+    np.testing.assert_array_equal(got.cpu().numpy(), oracle.select_patterns(z, 0.9, rows, band=5))
+    big = np.full((2, 4096), (1 << 40) + 12345, np.int64)   # all equal, many bits
+    got = m.select_patterns(torch.from_numpy(big).cuda(), 0.5, 1 << 20)
+    np.testing.assert_array_equal(got.cpu().numpy(), oracle.select_patterns(big, 0.5, 1 << 20))
+
+
+@pytest.mark.parametrize("alpha", [0.9, 0.97])
+def test_runtime_capture_pipeline(alpha):
+    """Two-stage per-input capture on the GPU (columns, then diagonals on what the columns leave),
+    then extension, index and attention; against the oracle's two stages and attention."""
+    m = sa()
+    B, hq, hkv, S, d, n, band = 1, 8, 2, 4096, 128, 64, 64
+    q, k = W.runtime_qk(83, B, hq, hkv, S, d, "bf16")
+    _, _, v = W.qkv(83, B, hq, hkv, S, d, "bf16")
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    row0 = S - n
+    note("runtime capture pipeline alpha=%g" % alpha)
+    _, vs, lse = m.sample_scores(qd, kd, row0, n, band=band)
+    keep_v = m.select_patterns(vs, alpha, B * n)
+    ds, _, _ = m.sample_scores(qd, kd, row0, n, band=band, skip_cols=keep_v, row_lse=lse, lse_given=True)
+    keep_d = m.select_patterns(ds, alpha, B * n, band=band)
+    pat = m.patterns_to_desc(keep_d, keep_v, S)
+    ix = m.build_index(pat, 64)
+    o = m.sparse_attn_prefill(qd, kd, vd, ix)
+    torch.cuda.synchronize()
+
+    rkd, rkv, rv, rd = oracle.runtime_capture(q, k, row0, n, alpha, band)
+    gv, gd = keep_v.cpu().numpy(), keep_d.cpu().numpy()
+    sure_v = certain_selection(rv, REL, ABS, alpha, B * n)
+    np.testing.assert_array_equal(gv[sure_v], rkv[sure_v])
+    assert sure_v.mean() > 0.99
+    # stage 2 runs on the same uncovered mass where the column flags came out equal (the unsure
+    # decisions usually fall the same way); compare it on those heads
+    heads = [h for h in range(hq) if np.array_equal(gv[h], rkv[h])]
+    assert len(heads) >= hq - 2, heads
+    sure_d = certain_selection(rd, REL, ABS, alpha, B * n, band=band)
+    for h in heads:
+        np.testing.assert_array_equal(gd[h][sure_d[h]], rkd[h][sure_d[h]])
+    heads = [h for h in heads if np.array_equal(gd[h], rkd[h])]
+    assert len(heads) >= hq - 2, heads
+    note("heads with equal masks: %s; unsure column decisions %d, diagonal %d"
+         % (heads, int((~sure_v).sum()), int((~sure_d).sum())))
+    # on those heads the masks are equal: attention on the oracle's mask, sampled rows
+    desc = W.desc_from_lists(S, [np.nonzero(x)[0] for x in rkd], [np.nonzero(x)[0] for x in rkv])
+    pc = ix.pair_count.cpu().numpy()
+    rpc = oracle.pair_count(desc)
+    assert all(pc[h] == rpc[h] for h in heads)
+    rng = np.random.default_rng(5)
+    rows = np.array([(0, h, i) for h in heads for i in np.concatenate([[0, S - 1], rng.choice(S, 24)])], np.int32)
+    ref, _ = oracle.attention_rows(desc, q, k, v, rows)
+    idx = torch.from_numpy(rows.astype(np.int64)).cuda()
+    got = o[idx[:, 0], idx[:, 1], idx[:, 2]].float().cpu().numpy().astype(np.float64)
+    assert_close_bf16(got, ref, "runtime pipeline attention")

@@ -474,12 +474,14 @@ def test_attention_maps_match_torch_softmax_average():
 # ---------------------------------------------------------------------------
 # runtime capture: sampled-row scores and pattern selection
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_sample_scores_brute_force(dtype):
-    """Numpy twin: softmax of the sampled rows over j <= i, mass added per diagonal i - j and per column j."""
+@pytest.mark.parametrize("dtype,band,skip", [("f32", 0, False), ("bf16", 0, False), ("f32", 7, True)])
+def test_sample_scores_brute_force(dtype, band, skip):
+    """Numpy twin: softmax of the sampled rows over j <= i, mass added per diagonal i - j and per
+    column j for the pairs with i - j >= band whose column is not skipped."""
     B, hq, hkv, S, d, row0, n = 2, 4, 2, 40, 16, 25, 10
     q, k, _ = W.qkv(61, B, hq, hkv, S, d, dtype)
-    diag, vert, lse = oracle.sample_scores(q, k, row0, n)
+    skip_cols = (np.random.default_rng(6).random((hq, S)) < 0.3).astype(np.uint8) if skip else None
+    diag, vert, lse = oracle.sample_scores(q, k, row0, n, band=band, skip_cols=skip_cols)
     qf, kf = widen64(q), widen64(k)
     rd = np.zeros((hq, S))
     rv = np.zeros((hq, S))
@@ -494,8 +496,11 @@ def test_sample_scores_brute_force(dtype):
                 p = np.exp(s - s.max())
                 p /= p.sum()
                 j = np.arange(i + 1)
-                np.add.at(rd[h], i - j, p)
-                np.add.at(rv[h], j, p)
+                out = i - j >= band
+                if skip:
+                    out &= skip_cols[h][j] == 0
+                np.add.at(rd[h], (i - j)[out], p[out])
+                np.add.at(rv[h], j[out], p[out])
     np.testing.assert_allclose(diag, rd, rtol=0, atol=1e-12)
     np.testing.assert_allclose(vert, rv, rtol=0, atol=1e-12)
     np.testing.assert_allclose(lse, rl, rtol=0, atol=1e-12)
@@ -510,52 +515,84 @@ def test_sample_scores_totals_and_support():
     last = row0 + n - 1
     assert not diag[:, last + 1:].any() and not vert[:, last + 1:].any()
     assert (diag[:, :last + 1] > 0).all() and (vert[:, :last + 1] > 0).all()
-    # a single sampled row at position 0 sees only key 0
-    d0, v0, l0 = oracle.sample_scores(q, k, 0, 1)
+    d0, v0, l0 = oracle.sample_scores(q, k, 0, 1)          # row 0 sees key 0 only
     assert np.all(d0[:, 0] == B) and np.all(v0[:, 0] == B) and not d0[:, 1:].any()
+    # the window's mass leaves both families; skipped columns leave both too
+    db, vb, _ = oracle.sample_scores(q, k, row0, n, band=5, scale=0.7)
+    assert not db[:, :5].any()
+    np.testing.assert_allclose(db.sum(1), diag[:, 5:].sum(1), rtol=1e-13)
+    np.testing.assert_allclose(vb.sum(1), db.sum(1), rtol=1e-13)
+    sk = np.zeros((hq, S), np.uint8)
+    sk[:, 3] = 1
+    ds, vs, _ = oracle.sample_scores(q, k, row0, n, skip_cols=sk, scale=0.7)
+    assert not vs[:, 3].any()
+    np.testing.assert_allclose(vs.sum(1), vert.sum(1) - vert[:, 3], rtol=1e-13)
 
 
-def _select_brute(v, alpha):
-    total = int(v.sum())
-    if total == 0:
-        return np.zeros(v.shape, np.uint8)
-    target = max(1, int(np.ceil(alpha * float(total))))
-    run = 0
-    for x in sorted(v.tolist(), reverse=True):
-        run += x
-        if run >= target:
-            theta = x
-            break
-    return ((v >= theta) & (v > 0)).astype(np.uint8)
+def _select_brute(v, alpha, rows, band=0):
+    t_all = rows * (1 << 32)
+    need = int(np.ceil(alpha * float(t_all))) - (t_all - int(v.sum()))
+    keep = np.zeros(v.shape, np.uint8)
+    if need > 0:
+        run, theta = 0, 1
+        for x in sorted(v.tolist(), reverse=True):
+            run += x
+            if run >= need:
+                theta = x
+                break
+        keep = ((v >= theta) & (v > 0)).astype(np.uint8)
+    keep[:band] = 1
+    return keep
 
 
 @pytest.mark.parametrize("alpha", [0.05, 0.5, 0.9, 0.97, 1.0])
 def test_select_patterns_brute_force(alpha):
     rng = np.random.default_rng(int(alpha * 1000))
-    hq, S = 3, 50
-    diag = rng.choice([0, 1, 2, 5, 5, 40, 300, 1 << 33], size=(hq, S)).astype(np.int64)   # many ties
-    vert = rng.integers(0, 1 << 40, size=(hq, S)).astype(np.int64)
-    vert[:, ::3] = 0
-    kd, kv = oracle.select_patterns(diag, vert, alpha, band=4)
-    for h in range(hq):
-        ed = _select_brute(diag[h], alpha)
-        ed[:4] = 1
-        np.testing.assert_array_equal(kd[h], ed)
-        np.testing.assert_array_equal(kv[h], _select_brute(vert[h], alpha))
+    n, S, rows = 3, 50, 4
+    unit = 1 << 32
+    a = rng.choice([0, 1, 2, 5, 5, 40, 300, unit // 8, unit // 8], size=(n, S)).astype(np.int64)   # many ties
+    b = rng.integers(0, unit // 16, size=(n, S)).astype(np.int64)
+    b[:, ::3] = 0
+    for v, band in ((a, 4), (b, 0)):
+        got = oracle.select_patterns(v, alpha, rows, band=band)
+        for h in range(n):
+            np.testing.assert_array_equal(got[h], _select_brute(v[h], alpha, rows, band), err_msg=str(h))
 
 
 def test_select_patterns_special_cases():
-    hq, S = 2, 30
-    rng = np.random.default_rng(3)
-    v = rng.integers(0, 1000, size=(hq, S)).astype(np.int64)
-    v[0, 5] = 0
-    kd, kv = oracle.select_patterns(v, v, 1.0)
-    np.testing.assert_array_equal(kv, (v > 0).astype(np.uint8))       # alpha = 1: every pattern with mass
-    z = np.zeros((hq, S), np.int64)
-    kd, kv = oracle.select_patterns(z, z, 0.9, band=3)
-    assert not kv.any() and kd[:, :3].all() and not kd[:, 3:].any()   # no mass: only the local band
-    one = np.zeros((hq, S), np.int64)
-    one[:, 7] = 10
-    one[:, 9] = 1
-    kd, kv = oracle.select_patterns(one, one, 0.9)                    # 10 of 11 reaches 0.9
-    assert kv[:, 7].all() and kv.sum() == hq
+    n, S = 2, 30
+    unit = 1 << 32
+    v = np.zeros((n, S), np.int64)
+    v[:, 7] = unit // 2
+    v[:, 9] = unit // 4
+    v[:, 11] = unit // 4            # uncovered mass = 1 row: nothing covered yet
+    k = oracle.select_patterns(v, 0.5, 1)
+    assert k[:, 7].all() and k.sum() == n                       # the top pattern alone reaches half
+    k = oracle.select_patterns(v, 0.6, 1)
+    assert k[:, [7, 9, 11]].all() and k.sum() == 3 * n          # a tie at the threshold keeps both
+    k = oracle.select_patterns(v, 0.2, 4, band=3)               # 3 of 4 rows already covered: need < 0
+    assert k[:, :3].all() and k.sum() == 3 * n
+    k = oracle.select_patterns(v, 1.0, 2)                       # more than the scores hold: all with mass
+    np.testing.assert_array_equal(k, (v > 0).astype(np.uint8))
+    np.testing.assert_array_equal(oracle.select_patterns(np.zeros((n, S), np.int64), 0.9, 1), 0)
+
+
+def test_runtime_capture_covers_alpha_of_the_sampled_mass():
+    """After both stages the window, kept columns and kept diagonals hold at least alpha of every
+    head's sampled mass (to the fixed-point rounding), measured by a numpy softmax of the rows."""
+    B, hq, hkv, S, d, n, band = 1, 4, 2, 512, 64, 32, 16
+    q, k = W.runtime_qk(63, B, hq, hkv, S, d, "f32")
+    for alpha in (0.8, 0.95):
+        kd, kv, _, _ = oracle.runtime_capture(q, k, S - n, n, alpha, band)
+        qf, kf = widen64(q), widen64(k)
+        for h in range(hq):
+            g = h // (hq // hkv)
+            cov = 0.0
+            for i in range(S - n, S):
+                s = kf[0, g, :i + 1] @ qf[0, h, i] / np.sqrt(d)
+                p = np.exp(s - s.max())
+                p /= p.sum()
+                j = np.arange(i + 1)
+                cov += p[(i - j < band) | (kd[h][i - j] == 1) | (kv[h][j] == 1)].sum()
+            assert cov / n >= alpha - 1e-6, (alpha, h, cov / n)
+        assert kd.sum() < hq * S and kv.sum() < hq * S

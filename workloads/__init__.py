@@ -237,6 +237,43 @@ def capture_qk(config_id: int, B: int, hq: int, hkv: int, L: int, d: int, dtype:
     return (q, k) if dtype == "f32" else (bf16_bits(q), bf16_bits(k))
 
 
+def runtime_qk(config_id: int, B: int, hq: int, hkv: int, S: int, d: int, dtype: str, n_cols: int = 16):
+    """Q [B,hq,S,d], K [B,hkv,S,d] for per-input capture at long S (float32 math, bf16 or f32 out).
+
+    Dims 0..15 carry a positional code (cos/sin of 8 frequencies geometric in [pi/256, pi/8]), so
+    the logits peak at i = j with height 8 and fall off over tens of positions (a local band);
+    dim 16 is a shared direction: every query has d^(1/4) * f (f seeded per query head in
+    [0.8, 1.2]), sink keys 0..3 have 9 d^(1/4) and `n_cols` seeded columns per kv head have
+    8 d^(1/4), i.e. logit boosts of 9 f and 8 f; every dim gets N(0, 0.3^2) noise.  Generated
+    one head at a time.
+    """
+    rt = np.float32(np.sqrt(np.sqrt(d)))
+    w = np.geomspace(np.pi / 256, np.pi / 8, 8).astype(np.float32)
+    pos = np.arange(S, dtype=np.float32)[:, None] * w[None, :]
+    code = (np.concatenate([np.cos(pos), np.sin(pos)], axis=1) * np.float32(np.sqrt(8.0 / 8)) * rt).astype(np.float32)
+    out_q = np.empty((B, hq, S, d), np.uint16 if dtype != "f32" else np.float32)
+    out_k = np.empty((B, hkv, S, d), out_q.dtype)
+    conv = (lambda x: x) if dtype == "f32" else bf16_bits
+    for g in range(hkv):
+        rng = np.random.default_rng([config_id, 4000, g])
+        cols = rng.choice(np.arange(4, S), size=min(n_cols, max(S - 4, 0)), replace=False) if S > 4 else np.zeros(0, int)
+        for b in range(B):
+            x = 0.3 * rng.standard_normal((S, d), dtype=np.float32)
+            x[:, :16] += code
+            x[:min(4, S), 16] += 9.0 * rt
+            x[cols, 16] += 8.0 * rt
+            out_k[b, g] = conv(x)
+    for h in range(hq):
+        rng = np.random.default_rng([config_id, 4001, h])
+        f = np.float32(rng.uniform(0.8, 1.2))
+        for b in range(B):
+            x = 0.3 * rng.standard_normal((S, d), dtype=np.float32)
+            x[:, :16] += code
+            x[:, 16] += rt * f
+            out_q[b, h] = conv(x)
+    return out_q, out_k
+
+
 def llama8b_like(S: int = 65536, H: int = 32, band: int = 1024, block_p: float = 0.08,
                  block_size: int = 64) -> PatternDesc:
     """Workload 4: even heads vertical+slash, odd heads 64x64 block-sparse."""
