@@ -236,6 +236,62 @@ def decode_row_keys(ixn, h, t, nb, BM, nwords):
     return n + int((cols <= t).sum())
 
 
+def runtime_capture_bench(sa, torch, S=65536, n_rows=128, band=1024, alpha_cols=0.8, alpha=0.9, reps=3):
+    """Per-input capture then attention at the 64K layer shape (batch 1, 32/8 heads, head_dim 128,
+    bf16): the last `n_rows` query rows are sampled; columns to alpha_cols of the sampled mass, then
+    diagonals on the mass the columns leave, to alpha; window of `band` diagonals; the kept patterns
+    are extended to S, indexed and run.
+    Q/K carry sinks, seeded columns and a positional band (workloads.runtime_qk); V is N(0,1)."""
+    import workloads as W
+    t0 = time.time()
+    q, k = W.runtime_qk(84, 1, 32, 8, S, 128, "bf16")
+    qd = torch.from_numpy(q.view(np.int16)).cuda().view(torch.bfloat16)
+    kd = torch.from_numpy(k.view(np.int16)).cuda().view(torch.bfloat16)
+    del q, k
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(84)
+    vd = torch.randn(kd.shape, generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    log("runtime capture: inputs ready in %.1fs" % (time.time() - t0))
+    row0 = S - n_rows
+
+    def capture():
+        _, vs, lse = sa.sample_scores(qd, kd, row0, n_rows, band=band, families=(False, True))
+        keep_v = sa.select_patterns(vs, alpha_cols, n_rows)
+        ds, _, _ = sa.sample_scores(qd, kd, row0, n_rows, band=band, skip_cols=keep_v, row_lse=lse, lse_given=True,
+                                    families=(True, False))
+        keep_d = sa.select_patterns(ds, alpha, n_rows, band=band)
+        return keep_d, keep_v
+
+    keep_d, keep_v = capture()
+    ix = sa.build_index(sa.patterns_to_desc(keep_d, keep_v, S), 64)
+    o = sa.sparse_attn_prefill(qd, kd, vd, ix)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    cap_ms, full_ms, attn_ms = [], [], []
+    for _ in range(reps):
+        ev[0].record()
+        keep_d, keep_v = capture()
+        ev[1].record()
+        ix = sa.build_index(sa.patterns_to_desc(keep_d, keep_v, S), 64)   # size query: one host sync
+        a0 = torch.cuda.Event(enable_timing=True)
+        a0.record()
+        sa.sparse_attn_prefill(qd, kd, vd, ix, out=o)
+        ev[2].record()
+        torch.cuda.synchronize()
+        cap_ms.append(ev[0].elapsed_time(ev[1]))
+        full_ms.append(ev[0].elapsed_time(ev[2]))
+        attn_ms.append(a0.elapsed_time(ev[2]))
+    pairs = ix.total_pairs
+    cap, full, att = min(cap_ms), min(full_ms), min(attn_ms)
+    return dict(workload="runtime capture: last %d rows sampled, window %d, columns to %g, diagonals to %g, 64K layer "
+                         "shape" % (n_rows, band, alpha_cols, alpha),
+                S=S, capture_ms=cap, index_and_attention_ms=full - cap, attention_ms=att, total_ms=full,
+                kept_columns_per_head=float(keep_v.float().sum(1).mean().item()),
+                kept_diagonals_beyond_window_per_head=float(keep_d.float().sum(1).mean().item()) - band,
+                retained_pairs=pairs, density=pairs / (32 * S * (S + 1) / 2.0),
+                effective_tflops=4.0 * 128 * pairs / (att * 1e-3) / 1e12)
+
+
 def decode_bench(sa, torch, B=16, reps=20):
     """Decode (one new query per sequence) on the 64K workload's patterns: B sequences whose
     positions sit near the end of a 64K cache, all 32 query heads."""
@@ -370,6 +426,10 @@ def main():
         extras["capture_from_qk"] = maps_from_qk_ms(sa, torch)
         log("capture from Q/K: maps %.3f ms + capture %.3f ms" % (extras["capture_from_qk"]["maps_ms"],
                                                                 extras["capture_from_qk"]["capture_ms"]))
+        extras["runtime_capture"] = runtime_capture_bench(sa, torch)
+        rc = extras["runtime_capture"]
+        log("runtime capture at 64K: capture %.3f ms, index + attention %.3f ms (attention %.3f ms), density %.4f"
+            % (rc["capture_ms"], rc["index_and_attention_ms"], rc["attention_ms"], rc["density"]))
         extras["decode"] = decode_bench(sa, torch)
         log("decode: %.3f ms for %d tokens (%.0f GB/s of retained K/V rows)" % (
             extras["decode"]["ms"], 16, extras["decode"]["kv_GBps"]))

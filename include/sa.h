@@ -290,16 +290,26 @@ sa_status sa_pattern_coverage(const float* maps, int32_t n_maps, int32_t L, cons
  *   row_lse  float [batch][hq][n_rows]: natural-log LSE of each sampled row over all
  *            its keys; written, or read when lse_given is nonzero (a second call
  *            over the same rows skips that pass).
- *   diag_score, vert_score  int64 [hq][S], 8-byte aligned.
+ *   workspace  device scratch of at least sa_sample_scores_workspace(...) bytes,
+ *            8-byte aligned, used when lse_given is 0 (partial row statistics per
+ *            256-key split); may be NULL when lse_given is nonzero.
+ *   diag_score, vert_score  int64 [hq][S], 8-byte aligned; either may be NULL to skip
+ *            that family (not both), e.g. verticals only for the first stage.
  * Arithmetic: fp32 MFMA scores, fp32 softmax (exp2 domain), as for attention.
  * Limits: 0 <= row0, 1 <= n_rows <= 2048, row0 + n_rows <= S, batch * n_rows <= 2^20,
  * band >= 0; head_dim 64 or 128.  softmax_scale <= 0 selects 1 / sqrt(head_dim).
- * Errors: SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_HIP.
+ * Errors: SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_CAPACITY (workspace too
+ * small), SA_ERR_HIP.
  */
 sa_status sa_sample_scores(const void* q, const void* k, int32_t batch, int32_t hq, int32_t hkv, int32_t S,
                            int32_t head_dim, int32_t dtype, float softmax_scale, int32_t row0, int32_t n_rows,
                            int32_t band, const uint8_t* skip_cols, int32_t lse_given, float* row_lse,
-                           int64_t* diag_score, int64_t* vert_score, void* stream);
+                           void* workspace, size_t workspace_bytes, int64_t* diag_score, int64_t* vert_score,
+                           void* stream);
+
+/* Bytes of workspace sa_sample_scores needs (host; 0 for invalid sizes):
+ * batch * hq * n_rows * ceil((row0 + n_rows) / 256) * 8. */
+size_t sa_sample_scores_workspace(int32_t batch, int32_t hq, int32_t row0, int32_t n_rows);
 
 /*
  * sa_select_patterns [SampleAttention, abstract: adaptive, head-specific selection,

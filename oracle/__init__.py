@@ -341,12 +341,14 @@ def select_patterns(scores: np.ndarray, alpha: float, rows: int, band: int = 0) 
     return keep
 
 
-def runtime_capture(q, k, row0: int, n_rows: int, alpha: float, band: int, scale: Optional[float] = None):
-    """The two-stage per-input capture: columns first (window counted as covered), then diagonals on
-    the mass still uncovered.  Returns (keep_diag, keep_vert) uint8 [hq, S] and the stage scores."""
+def runtime_capture(q, k, row0: int, n_rows: int, alpha_cols: float, alpha: float, band: int,
+                    scale: Optional[float] = None):
+    """The two-stage per-input capture: the fewest columns that bring the covered mass (window
+    counted) to alpha_cols, then the fewest diagonals, scored on the mass still uncovered, that bring
+    it to alpha.  Returns keep_diag, keep_vert (uint8 [hq, S]) and the two stages' float64 scores."""
     B = q.shape[0]
     _, vert, _ = sample_scores(q, k, row0, n_rows, band=band, scale=scale)
-    keep_vert = select_patterns(fixed_point(vert), alpha, B * n_rows)
+    keep_vert = select_patterns(fixed_point(vert), alpha_cols, B * n_rows)
     diag, _, _ = sample_scores(q, k, row0, n_rows, band=band, skip_cols=keep_vert, scale=scale)
     keep_diag = select_patterns(fixed_point(diag), alpha, B * n_rows, band=band)
     return keep_diag, keep_vert, vert, diag

@@ -78,7 +78,9 @@ def _load():
                                        C.c_double, C.c_int32] + [C.c_void_p] * 5 + [C.c_void_p]
     lib.sa_sample_scores.restype = C.c_int32
     lib.sa_sample_scores.argtypes = [C.c_void_p, C.c_void_p] + [C.c_int32] * 6 + [C.c_float] + [C.c_int32] * 3 + \
-        [C.c_void_p, C.c_int32] + [C.c_void_p] * 3 + [C.c_void_p]
+        [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_size_t] + [C.c_void_p] * 2 + [C.c_void_p]
+    lib.sa_sample_scores_workspace.restype = C.c_size_t
+    lib.sa_sample_scores_workspace.argtypes = [C.c_int32] * 4
     lib.sa_select_patterns.restype = C.c_int32
     lib.sa_select_patterns.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_double, C.c_int64, C.c_int32,
                                        C.c_void_p, C.c_void_p]
@@ -356,11 +358,13 @@ def pattern_coverage(maps: torch.Tensor, keep_diag: torch.Tensor, keep_vert: tor
 
 def sample_scores(q: torch.Tensor, k: torch.Tensor, row0: int, n_rows: int, band: int = 0,
                   skip_cols: Optional[torch.Tensor] = None, softmax_scale: Optional[float] = None, scores=None,
-                  row_lse: Optional[torch.Tensor] = None, lse_given: bool = False, stream=None):
+                  row_lse: Optional[torch.Tensor] = None, lse_given: bool = False, families=(True, True),
+                  stream=None):
     """sa_sample_scores: adds the attention mass of query rows row0 .. row0+n_rows-1 on the pairs outside
     the window (i - j >= band) and off `skip_cols` onto per-head diagonal and vertical scores (int64
     [Hq, S] each, fixed point 2^-32).  `scores` = (diag, vert) to accumulate into, new zeroed arrays
-    otherwise; `row_lse` [B, Hq, n_rows] is written, or read when lse_given.  Returns (diag, vert, row_lse)."""
+    otherwise (only the families flagged in `families` = (diagonals, verticals); None for the other);
+    `row_lse` [B, Hq, n_rows] is written, or read when lse_given.  Returns (diag, vert, row_lse)."""
     if q.dtype == torch.bfloat16:
         dt = SA_DTYPE_BF16
     elif q.dtype == torch.float32:
@@ -373,11 +377,13 @@ def sample_scores(q: torch.Tensor, k: torch.Tensor, row0: int, n_rows: int, band
     if k.shape[0] != B or k.shape[2] != S or k.shape[3] != d:
         raise ValueError("k shape does not match q")
     if scores is None:
-        scores = (torch.zeros((hq, S), dtype=torch.int64, device=q.device),
-                  torch.zeros((hq, S), dtype=torch.int64, device=q.device))
+        scores = tuple(torch.zeros((hq, S), dtype=torch.int64, device=q.device) if want else None
+                       for want in families)
     diag, vert = scores
+    if diag is None and vert is None:
+        raise ValueError("at least one family of scores is needed")
     for t in (diag, vert):
-        if t.dtype != torch.int64 or tuple(t.shape) != (hq, S) or not t.is_contiguous():
+        if t is not None and (t.dtype != torch.int64 or tuple(t.shape) != (hq, S) or not t.is_contiguous()):
             raise ValueError("scores must be contiguous int64 [Hq, S] tensors")
     if skip_cols is not None and (skip_cols.dtype != torch.uint8 or tuple(skip_cols.shape) != (hq, S)
                                   or not skip_cols.is_contiguous()):
@@ -387,9 +393,11 @@ def sample_scores(q: torch.Tensor, k: torch.Tensor, row0: int, n_rows: int, band
             raise ValueError("lse_given needs row_lse")
         row_lse = torch.empty((B, hq, max(n_rows, 1)), dtype=torch.float32, device=q.device)
     scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    ws_bytes = 0 if lse_given else int(_lib.sa_sample_scores_workspace(B, hq, row0, n_rows))
+    ws = torch.empty(max(ws_bytes, 8), dtype=torch.uint8, device=q.device) if not lse_given else None
     _check(_lib.sa_sample_scores(q.data_ptr(), k.data_ptr(), B, hq, k.shape[1], S, d, dt, scale, row0, n_rows, band,
-                                 _ptr(skip_cols), int(bool(lse_given)), row_lse.data_ptr(), diag.data_ptr(),
-                                 vert.data_ptr(), _stream(stream)), "sa_sample_scores")
+                                 _ptr(skip_cols), int(bool(lse_given)), row_lse.data_ptr(), _ptr(ws), ws_bytes,
+                                 _ptr(diag), _ptr(vert), _stream(stream)), "sa_sample_scores")
     return diag, vert, row_lse
 
 

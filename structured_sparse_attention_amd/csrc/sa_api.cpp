@@ -156,11 +156,17 @@ sa_status sa_pattern_coverage(const float* maps, int32_t n_maps, int32_t L, cons
                                         static_cast<hipStream_t>(stream)));
 }
 
+size_t sa_sample_scores_workspace(int32_t batch, int32_t hq, int32_t row0, int32_t n_rows) {
+  if (batch < 1 || hq < 1 || row0 < 0 || n_rows < 1) return 0;
+  return sa::sample_workspace_bytes(batch, hq, row0, n_rows);
+}
+
 sa_status sa_sample_scores(const void* q, const void* k, int32_t batch, int32_t hq, int32_t hkv, int32_t S,
                            int32_t head_dim, int32_t dtype, float softmax_scale, int32_t row0, int32_t n_rows,
                            int32_t band, const uint8_t* skip_cols, int32_t lse_given, float* row_lse,
-                           int64_t* diag_score, int64_t* vert_score, void* stream) {
-  if (!q || !k || !row_lse || !diag_score || !vert_score) return SA_ERR_INVALID_ARG;
+                           void* workspace, size_t workspace_bytes, int64_t* diag_score, int64_t* vert_score,
+                           void* stream) {
+  if (!q || !k || !row_lse || (!diag_score && !vert_score)) return SA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k)) return SA_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(diag_score) | reinterpret_cast<uintptr_t>(vert_score)) & 7u) return SA_ERR_INVALID_ARG;
   if (batch < 1 || hq < 1 || hkv < 1 || S < 1 || hq % hkv != 0 || band < 0) return SA_ERR_INVALID_ARG;
@@ -168,13 +174,19 @@ sa_status sa_sample_scores(const void* q, const void* k, int32_t batch, int32_t 
   if (head_dim != 64 && head_dim != 128) return SA_ERR_UNSUPPORTED;
   if (row0 < 0 || n_rows < 1 || (int64_t)row0 + n_rows > S) return SA_ERR_INVALID_ARG;
   if (n_rows > sa::kMaxSampleRows || (int64_t)batch * n_rows > sa::kMaxSampleRowSeqs) return SA_ERR_UNSUPPORTED;
+  if (!lse_given) {
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 7u)) return SA_ERR_INVALID_ARG;
+    if (workspace_bytes < sa::sample_workspace_bytes(batch, hq, row0, n_rows)) return SA_ERR_CAPACITY;
+  }
   const int64_t ntile = ((int64_t)row0 + n_rows - 1) / 64 + 1;
-  if ((int64_t)batch * hq * ((n_rows + 31) / 32) > 0x7fffffffLL || (int64_t)hq * ntile > 0x7fffffffLL)
+  const int64_t nsplit = ((int64_t)row0 + n_rows - 1) / 256 + 1;
+  if ((int64_t)batch * hq * nsplit > 0x7fffffffLL || (int64_t)hq * ntile > 0x7fffffffLL ||
+      (int64_t)batch * hq * n_rows > 0x7fffffffLL)
     return SA_ERR_UNSUPPORTED;
   const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf((float)head_dim);
   if (!isfinite(scale)) return SA_ERR_INVALID_ARG;
   return hip_status(sa::launch_sample_scores(q, k, batch, hq, hkv, S, head_dim, dtype, scale, row0, n_rows, band,
-                                             skip_cols, lse_given != 0, row_lse, diag_score, vert_score,
+                                             skip_cols, lse_given != 0, row_lse, workspace, diag_score, vert_score,
                                              static_cast<hipStream_t>(stream)));
 }
 

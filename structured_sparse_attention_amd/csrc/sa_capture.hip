@@ -420,38 +420,60 @@ __global__ void __launch_bounds__(kCovThreads)
   }
 }
 
-// kept flags -> CSR descriptor lists at length S (entries < S).  One workgroup.
-constexpr int kDescThreads = 1024;
+// kept flags -> CSR descriptor lists at length S (entries < S).  One workgroup per
+// (map, family) counts, one scans the counts over the maps, then one workgroup per
+// (map, family) writes the kept indices in order: per 256-flag chunk a ballot gives
+// each kept flag its rank among the kept flags before it.
+constexpr int kDescThreads = 256;
 __global__ void __launch_bounds__(kDescThreads)
-    k_to_desc(const uint8_t* keep_diag, const uint8_t* keep_vert, int32_t n_maps, int32_t L, int32_t S,
-              int32_t* diag_ptr, int32_t* diag_off, int32_t* vert_ptr, int32_t* vert_col) {
-  const int tid = threadIdx.x;
+    k_desc_count(const uint8_t* keep_diag, const uint8_t* keep_vert, int32_t L, int32_t S, int32_t* diag_ptr,
+                 int32_t* vert_ptr) {
+  __shared__ int32_t red[kDescThreads / 64];
+  const int m = blockIdx.x >> 1, fam = blockIdx.x & 1;
+  const uint8_t* f = (fam == 0 ? keep_diag : keep_vert) + (int64_t)m * L;
   const int32_t Lc = min(L, S);
-  for (int m = tid; m < n_maps; m += kDescThreads) {
-    int32_t cd = 0, cv = 0;
-    for (int r = 0; r < Lc; ++r) {
-      cd += keep_diag[(int64_t)m * L + r] != 0;
-      cv += keep_vert[(int64_t)m * L + r] != 0;
-    }
-    diag_ptr[m + 1] = cd;
-    vert_ptr[m + 1] = cv;
-  }
+  int32_t c = 0;
+  for (int x = threadIdx.x; x < Lc; x += kDescThreads) c += f[x] != 0;
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
   __syncthreads();
-  if (tid == 0) {
-    diag_ptr[0] = 0;
-    vert_ptr[0] = 0;
-    for (int m = 0; m < n_maps; ++m) {
-      diag_ptr[m + 1] += diag_ptr[m];
-      vert_ptr[m + 1] += vert_ptr[m];
-    }
+  if (threadIdx.x == 0) {
+    int32_t t = 0;
+    for (int w = 0; w < kDescThreads / 64; ++w) t += red[w];
+    (fam == 0 ? diag_ptr : vert_ptr)[m + 1] = t;
   }
-  __syncthreads();
-  for (int m = tid; m < n_maps; m += kDescThreads) {
-    int32_t pd = diag_ptr[m], pv = vert_ptr[m];
-    for (int r = 0; r < Lc; ++r) {
-      if (keep_diag[(int64_t)m * L + r]) diag_off[pd++] = r;
-      if (keep_vert[(int64_t)m * L + r]) vert_col[pv++] = r;
+}
+
+__global__ void k_desc_scan(int32_t n_maps, int32_t* diag_ptr, int32_t* vert_ptr) {
+  int32_t* p = threadIdx.x == 0 ? diag_ptr : vert_ptr;
+  p[0] = 0;
+  for (int m = 0; m < n_maps; ++m) p[m + 1] += p[m];
+}
+
+__global__ void __launch_bounds__(kDescThreads)
+    k_desc_fill(const uint8_t* keep_diag, const uint8_t* keep_vert, int32_t L, int32_t S, const int32_t* diag_ptr,
+                int32_t* diag_off, const int32_t* vert_ptr, int32_t* vert_col) {
+  __shared__ int32_t wcount[kDescThreads / 64];
+  const int m = blockIdx.x >> 1, fam = blockIdx.x & 1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint8_t* f = (fam == 0 ? keep_diag : keep_vert) + (int64_t)m * L;
+  int32_t* out = fam == 0 ? diag_off : vert_col;
+  int32_t base = (fam == 0 ? diag_ptr : vert_ptr)[m];
+  const int32_t Lc = min(L, S);
+  for (int32_t c0 = 0; c0 < Lc; c0 += kDescThreads) {
+    const int32_t x = c0 + tid;
+    const bool on = x < Lc && f[x] != 0;
+    const unsigned long long bal = __ballot(on);
+    if (lane == 0) wcount[wave] = __popcll(bal);
+    __syncthreads();
+    int32_t before = 0, total = 0;
+    for (int w = 0; w < kDescThreads / 64; ++w) {
+      before += w < wave ? wcount[w] : 0;
+      total += wcount[w];
     }
+    if (on) out[base + before + __popcll(bal & ((1ull << lane) - 1ull))] = x;
+    base += total;
+    __syncthreads();
   }
 }
 
@@ -486,8 +508,11 @@ hipError_t launch_coverage(const float* maps, int32_t n_maps, int32_t L, const u
 hipError_t launch_patterns_to_desc(const uint8_t* keep_diag, const uint8_t* keep_vert, int32_t n_maps, int32_t L,
                                    int32_t S, int32_t* diag_ptr, int32_t* diag_off, int32_t* vert_ptr,
                                    int32_t* vert_col, hipStream_t stream) {
-  hipLaunchKernelGGL(k_to_desc, dim3(1), dim3(kDescThreads), 0, stream, keep_diag, keep_vert, n_maps, L, S, diag_ptr,
-                     diag_off, vert_ptr, vert_col);
+  hipLaunchKernelGGL(k_desc_count, dim3((unsigned)(2 * n_maps)), dim3(kDescThreads), 0, stream, keep_diag, keep_vert, L,
+                     S, diag_ptr, vert_ptr);
+  hipLaunchKernelGGL(k_desc_scan, dim3(1), dim3(2), 0, stream, n_maps, diag_ptr, vert_ptr);
+  hipLaunchKernelGGL(k_desc_fill, dim3((unsigned)(2 * n_maps)), dim3(kDescThreads), 0, stream, keep_diag, keep_vert, L,
+                     S, diag_ptr, diag_off, vert_ptr, vert_col);
   return hipGetLastError();
 }
 

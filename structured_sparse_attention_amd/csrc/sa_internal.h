@@ -55,10 +55,11 @@ hipError_t launch_capture(const float* maps, int32_t n_maps, int32_t L, double l
                           int32_t* vert_hits, uint8_t* true_mask, hipStream_t stream);
 hipError_t launch_attention_maps(const void* q, const void* k, int32_t batch, int32_t hq, int32_t hkv, int32_t L,
                                  int32_t head_dim, int32_t dtype, float scale, float* maps, hipStream_t stream);
+size_t sample_workspace_bytes(int32_t batch, int32_t hq, int32_t row0, int32_t n_rows);
 hipError_t launch_sample_scores(const void* q, const void* k, int32_t batch, int32_t hq, int32_t hkv, int32_t S,
                                 int32_t head_dim, int32_t dtype, float scale, int32_t row0, int32_t n_rows,
-                                int32_t band, const uint8_t* skip_cols, bool lse_given, float* row_lse, int64_t* diag,
-                                int64_t* vert, hipStream_t stream);
+                                int32_t band, const uint8_t* skip_cols, bool lse_given, float* row_lse, void* workspace,
+                                int64_t* diag, int64_t* vert, hipStream_t stream);
 hipError_t launch_select(const int64_t* scores, int32_t n_heads, int32_t S, double alpha, int64_t t_all, int32_t band,
                          uint8_t* keep, hipStream_t stream);
 hipError_t launch_coverage(const float* maps, int32_t n_maps, int32_t L, const uint8_t* keep_diag,

@@ -27,7 +27,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for f in ("sa_build_index", "sa_sparse_attn_prefill", "sa_sparse_attn_decode", "sa_attention_maps",
               "sa_pattern_capture", "sa_pattern_coverage", "sa_patterns_to_desc", "sa_sample_scores",
-              "sa_select_patterns", "sa_status_string", "sa_version"):
+              "sa_sample_scores_workspace", "sa_select_patterns", "sa_status_string", "sa_version"):
         assert f in names
 
 
@@ -129,8 +129,11 @@ def test_attention_maps_validation(m):
 def test_sample_and_select_validation(m):
     f = m.lib.sa_sample_scores
     p = FAKE.value
-    # q, k, batch, hq, hkv, S, d, dtype, scale, row0, n_rows, band, skip, lse_given, lse, diag, vert, stream
-    args = [p, p, 1, 4, 2, 512, 64, 1, 0.0, 448, 64, 16, None, 0, p, p, p, None]   # valid but for the field changed
+    # q, k, batch, hq, hkv, S, d, dtype, scale, row0, n_rows, band, skip, lse_given, lse, ws, ws_bytes, diag, vert,
+    # stream; valid but for the field changed
+    ws = m.lib.sa_sample_scores_workspace(1, 4, 448, 64)
+    assert ws == 4 * 64 * 2 * 8                                   # 512 keys: two 256-key splits
+    args = [p, p, 1, 4, 2, 512, 64, 1, 0.0, 448, 64, 16, None, 0, p, p, ws, p, p, None]
 
     def bad(changes, code):
         a = list(args)
@@ -138,8 +141,11 @@ def test_sample_and_select_validation(m):
             a[i] = val
         assert f(*a) == code, changes
     bad([(0, None)], -1)            # q
-    bad([(16, None)], -1)           # vert
-    bad([(15, p + 4)], -1)          # diag not 8-byte aligned
+    bad([(17, None), (18, None)], -1)   # neither family
+    bad([(18, p + 4)], -1)          # vert not 8-byte aligned
+    bad([(17, p + 4)], -1)          # diag not 8-byte aligned
+    bad([(15, None)], -1)           # workspace needed to compute the LSE
+    bad([(16, ws - 8)], -4)         # workspace too small
     bad([(3, 3)], -1)               # hq % hkv
     bad([(7, 5)], -1)               # dtype
     bad([(6, 96)], -2)              # head_dim

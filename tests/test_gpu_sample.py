@@ -57,9 +57,13 @@ def test_sample_scores_totals_accumulation_and_lse_reuse():
     da, va, _ = m.sample_scores(qd, kd, 900, 100)
     m.sample_scores(qd, kd, 300, 64, scores=(da, va))              # accumulate a second block
     dr, vr, _ = m.sample_scores(qd, kd, 900, 100, row_lse=l1, lse_given=True)
+    d_only, none_v, _ = m.sample_scores(qd, kd, 900, 100, families=(True, False))
+    none_d, v_only, _ = m.sample_scores(qd, kd, 900, 100, families=(False, True))
     torch.cuda.synchronize()
     assert torch.equal(da, d1 + d2) and torch.equal(va, v1 + v2)  # integer sums: exact
     assert torch.equal(dr, d1) and torch.equal(vr, v1)            # the given LSE is the one computed
+    assert none_v is None and none_d is None
+    assert torch.equal(d_only, d1) and torch.equal(v_only, v1)    # one family alone: the same sums
     for t in (d1, v1):                                            # 100 rows of mass one each
         tot = t.sum(dim=1).double().cpu().numpy() / UNIT
         assert np.all(np.abs(tot - 100.0) < 1e-4), tot
@@ -104,29 +108,32 @@ def test_select_edge_cases():
     np.testing.assert_array_equal(got.cpu().numpy(), oracle.select_patterns(big, 0.5, 1 << 20))
 
 
-@pytest.mark.parametrize("alpha", [0.9, 0.97])
-def test_runtime_capture_pipeline(alpha):
-    """Two-stage per-input capture on the GPU (columns, then diagonals on what the columns leave),
-    then extension, index and attention; against the oracle's two stages and attention."""
+@pytest.mark.parametrize("alpha_cols,alpha", [(0.8, 0.9), (0.9, 0.97)])
+def test_runtime_capture_pipeline(alpha_cols, alpha):
+    """Two-stage per-input capture on the GPU (columns to alpha_cols, then diagonals on what the
+    columns leave, to alpha), then extension, index and attention; against the oracle's two stages
+    and attention."""
     m = sa()
     B, hq, hkv, S, d, n, band = 1, 8, 2, 4096, 128, 64, 64
     q, k = W.runtime_qk(83, B, hq, hkv, S, d, "bf16")
     _, _, v = W.qkv(83, B, hq, hkv, S, d, "bf16")
     qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
     row0 = S - n
-    note("runtime capture pipeline alpha=%g" % alpha)
-    _, vs, lse = m.sample_scores(qd, kd, row0, n, band=band)
-    keep_v = m.select_patterns(vs, alpha, B * n)
-    ds, _, _ = m.sample_scores(qd, kd, row0, n, band=band, skip_cols=keep_v, row_lse=lse, lse_given=True)
+    note("runtime capture pipeline alpha_cols=%g alpha=%g" % (alpha_cols, alpha))
+    _, vs, lse = m.sample_scores(qd, kd, row0, n, band=band, families=(False, True))
+    keep_v = m.select_patterns(vs, alpha_cols, B * n)
+    ds, _, _ = m.sample_scores(qd, kd, row0, n, band=band, skip_cols=keep_v, row_lse=lse, lse_given=True,
+                               families=(True, False))
     keep_d = m.select_patterns(ds, alpha, B * n, band=band)
     pat = m.patterns_to_desc(keep_d, keep_v, S)
     ix = m.build_index(pat, 64)
     o = m.sparse_attn_prefill(qd, kd, vd, ix)
     torch.cuda.synchronize()
 
-    rkd, rkv, rv, rd = oracle.runtime_capture(q, k, row0, n, alpha, band)
+    rkd, rkv, rv, rd = oracle.runtime_capture(q, k, row0, n, alpha_cols, alpha, band)
     gv, gd = keep_v.cpu().numpy(), keep_d.cpu().numpy()
-    sure_v = certain_selection(rv, REL, ABS, alpha, B * n)
+    assert (rkd.sum(1) > band).all() and (rkv.sum(1) > 0).all()    # both stages keep patterns
+    sure_v = certain_selection(rv, REL, ABS, alpha_cols, B * n)
     np.testing.assert_array_equal(gv[sure_v], rkv[sure_v])
     assert sure_v.mean() > 0.99
     # stage 2 runs on the same uncovered mass where the column flags came out equal (the unsure

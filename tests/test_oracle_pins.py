@@ -580,10 +580,10 @@ def test_select_patterns_special_cases():
 def test_runtime_capture_covers_alpha_of_the_sampled_mass():
     """After both stages the window, kept columns and kept diagonals hold at least alpha of every
     head's sampled mass (to the fixed-point rounding), measured by a numpy softmax of the rows."""
-    B, hq, hkv, S, d, n, band = 1, 4, 2, 512, 64, 32, 16
+    B, hq, hkv, S, d, n, band = 1, 4, 2, 512, 128, 32, 16
     q, k = W.runtime_qk(63, B, hq, hkv, S, d, "f32")
-    for alpha in (0.8, 0.95):
-        kd, kv, _, _ = oracle.runtime_capture(q, k, S - n, n, alpha, band)
+    for alpha_cols, alpha in ((0.5, 0.8), (0.8, 0.95), (0.95, 0.95)):
+        kd, kv, _, _ = oracle.runtime_capture(q, k, S - n, n, alpha_cols, alpha, band)
         qf, kf = widen64(q), widen64(k)
         for h in range(hq):
             g = h // (hq // hkv)
@@ -596,3 +596,5 @@ def test_runtime_capture_covers_alpha_of_the_sampled_mass():
                 cov += p[(i - j < band) | (kd[h][i - j] == 1) | (kv[h][j] == 1)].sum()
             assert cov / n >= alpha - 1e-6, (alpha, h, cov / n)
         assert kd.sum() < hq * S and kv.sum() < hq * S
+        if alpha_cols < alpha:
+            assert (kd.sum(1) > band).any()          # the diagonals close the gap

@@ -240,17 +240,20 @@ def capture_qk(config_id: int, B: int, hq: int, hkv: int, L: int, d: int, dtype:
 def runtime_qk(config_id: int, B: int, hq: int, hkv: int, S: int, d: int, dtype: str, n_cols: int = 16):
     """Q [B,hq,S,d], K [B,hkv,S,d] for per-input capture at long S (float32 math, bf16 or f32 out).
 
-    Dims 0..15 carry a positional code (cos/sin of 8 frequencies geometric in [pi/256, pi/8]), so
-    the logits peak at i = j with height 8 and fall off over tens of positions (a local band);
-    dim 16 is a shared direction: every query has d^(1/4) * f (f seeded per query head in
-    [0.8, 1.2]), sink keys 0..3 have 9 d^(1/4) and `n_cols` seeded columns per kv head have
-    8 d^(1/4), i.e. logit boosts of 9 f and 8 f; every dim gets N(0, 0.3^2) noise.  Generated
-    one head at a time.
+    Dims 0..63 carry a positional code (cos/sin of 32 frequencies geometric in [pi/4096, pi/4]),
+    so the logits peak at i = j with height 8 and fall off over tens of positions (a local band),
+    with a texture of about one logit far from the diagonal; dim 64 is a shared direction: every
+    query has d^(1/4) * f (f seeded per query head in [0.9, 1.1]), sink keys 0..3 have
+    13 d^(1/4) and `n_cols` seeded columns per kv head have 11 d^(1/4), i.e. logit boosts of 13 f
+    and 11 f (sinks that hold most of a long row's mass); every dim gets N(0, 0.3^2) noise.
+    Needs d >= 65.  Generated one head at a time.
     """
+    nf = 32
+    assert d > 2 * nf
     rt = np.float32(np.sqrt(np.sqrt(d)))
-    w = np.geomspace(np.pi / 256, np.pi / 8, 8).astype(np.float32)
+    w = np.geomspace(np.pi / 4096, np.pi / 4, nf).astype(np.float32)
     pos = np.arange(S, dtype=np.float32)[:, None] * w[None, :]
-    code = (np.concatenate([np.cos(pos), np.sin(pos)], axis=1) * np.float32(np.sqrt(8.0 / 8)) * rt).astype(np.float32)
+    code = (np.concatenate([np.cos(pos), np.sin(pos)], axis=1) * np.float32(np.sqrt(8.0 / nf)) * rt).astype(np.float32)
     out_q = np.empty((B, hq, S, d), np.uint16 if dtype != "f32" else np.float32)
     out_k = np.empty((B, hkv, S, d), out_q.dtype)
     conv = (lambda x: x) if dtype == "f32" else bf16_bits
@@ -259,17 +262,17 @@ def runtime_qk(config_id: int, B: int, hq: int, hkv: int, S: int, d: int, dtype:
         cols = rng.choice(np.arange(4, S), size=min(n_cols, max(S - 4, 0)), replace=False) if S > 4 else np.zeros(0, int)
         for b in range(B):
             x = 0.3 * rng.standard_normal((S, d), dtype=np.float32)
-            x[:, :16] += code
-            x[:min(4, S), 16] += 9.0 * rt
-            x[cols, 16] += 8.0 * rt
+            x[:, :2 * nf] += code
+            x[:min(4, S), 2 * nf] += 13.0 * rt
+            x[cols, 2 * nf] += 11.0 * rt
             out_k[b, g] = conv(x)
     for h in range(hq):
         rng = np.random.default_rng([config_id, 4001, h])
-        f = np.float32(rng.uniform(0.8, 1.2))
+        f = np.float32(rng.uniform(0.9, 1.1))
         for b in range(B):
             x = 0.3 * rng.standard_normal((S, d), dtype=np.float32)
-            x[:, :16] += code
-            x[:, 16] += rt * f
+            x[:, :2 * nf] += code
+            x[:, 2 * nf] += rt * f
             out_q[b, h] = conv(x)
     return out_q, out_k
 
