@@ -1,7 +1,8 @@
 """structured_sparse_attention_amd -- Python binding of libsa.so (gfx950).
 
 Argument marshalling only: every step of the path (index build, sparse attention,
-pattern capture, pattern extension) runs in the HIP kernels of ``libsa.so``;
+decode, attention maps, pattern capture and coverage, pattern extension, runtime
+capture from sampled rows) runs in the HIP kernels of ``libsa.so``;
 PyTorch supplies device memory and the current HIP stream.  The C ABI is declared
 in ``include/sa.h``.  Importing this package loads ``libsa.so`` and raises if it
 has not been built (``python structured_sparse_attention_amd/build.py``); there is
@@ -18,7 +19,8 @@ import numpy as np
 import torch
 
 __all__ = ["SAError", "DevicePatterns", "SparseIndex", "build_index", "sparse_attn_prefill", "sparse_attn_decode",
-           "attention_maps", "pattern_capture", "pattern_coverage", "patterns_to_desc", "sample_scores", "select_patterns", "library_path", "version", "lib"]
+           "attention_maps", "pattern_capture", "pattern_coverage", "patterns_to_desc", "sample_scores",
+           "select_patterns", "library_path", "version", "lib"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libsa.so")
@@ -108,6 +110,14 @@ def _stream(stream) -> Optional[int]:
     if stream is None:
         stream = torch.cuda.current_stream()
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _hold(t: Optional[torch.Tensor], stream) -> None:
+    """A temporary that a call on `stream` reads is not handed to another allocation before that stream
+    has used it (torch's allocator otherwise only tracks the current stream).  Raw stream handles
+    cannot be tracked: with one, temporaries are made on the current stream and the caller orders it."""
+    if t is not None and stream is not None and isinstance(stream, torch.cuda.Stream):
+        t.record_stream(stream)
 
 
 def _check(code: int, where: str):
@@ -398,6 +408,7 @@ def sample_scores(q: torch.Tensor, k: torch.Tensor, row0: int, n_rows: int, band
     _check(_lib.sa_sample_scores(q.data_ptr(), k.data_ptr(), B, hq, k.shape[1], S, d, dt, scale, row0, n_rows, band,
                                  _ptr(skip_cols), int(bool(lse_given)), row_lse.data_ptr(), _ptr(ws), ws_bytes,
                                  _ptr(diag), _ptr(vert), _stream(stream)), "sa_sample_scores")
+    _hold(ws, stream)
     return diag, vert, row_lse
 
 
@@ -422,7 +433,9 @@ def patterns_to_desc(keep_diag: torch.Tensor, keep_vert: torch.Tensor, S: int, s
     vp = torch.empty(n + 1, dtype=torch.int32, device=dev)
     do = torch.empty(cap, dtype=torch.int32, device=dev)
     vc = torch.empty(cap, dtype=torch.int32, device=dev)
-    _check(_lib.sa_patterns_to_desc(keep_diag.contiguous().data_ptr(), keep_vert.contiguous().data_ptr(), n, L, S,
-                                    dp.data_ptr(), do.data_ptr(), vp.data_ptr(), vc.data_ptr(), _stream(stream)),
-           "sa_patterns_to_desc")
+    kd, kv = keep_diag.contiguous(), keep_vert.contiguous()
+    _check(_lib.sa_patterns_to_desc(kd.data_ptr(), kv.data_ptr(), n, L, S, dp.data_ptr(), do.data_ptr(), vp.data_ptr(),
+                                    vc.data_ptr(), _stream(stream)), "sa_patterns_to_desc")
+    _hold(kd, stream)
+    _hold(kv, stream)
     return DevicePatterns(S, n, dp, do, vp, vc, device=dev)
