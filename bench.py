@@ -217,6 +217,34 @@ def capture_sweep(sa, torch, S=16384):
     return dict(S=S, points=out, capture_ms_512_maps=timing)
 
 
+def machine_calibration(sa, torch, reps=5):
+    """Measured counterparts of the vendor figures used for the rooflines: dense bf16 MFMA throughput
+    (sa_calib_mfma_bf16: 2048 workgroups x 4 waves x 2048 rounds x 4 MFMAs of 32x32x16) and random 16 KiB
+    chunk reads (sa_calib_gather: 8192 workgroups x 16 chunks = 2 GiB requested) from regions of 2 MiB
+    (L2), 32 MiB, 256 MiB (the MALL's size) and 2 GiB (HBM)."""
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+    n_wg, iters = 2048, 2048
+    ms = timed(lambda: sa.calib_mfma_bf16(n_wg, iters))
+    out = dict(mfma_bf16_dense_TFLOPs=n_wg * 4 * iters * 4 * 32768 / (ms * 1e-3) / 1e12)
+    buf = torch.empty(1 << 31, dtype=torch.uint8, device="cuda")
+    gather = {}
+    for name, region in (("2MiB", 2 << 20), ("32MiB", 32 << 20), ("256MiB", 256 << 20), ("2GiB", 1 << 31)):
+        ms = timed(lambda: sa.calib_gather(buf, region, 16384, 8192, 16))
+        gather[name] = 8192 * 16 * 16384 / (ms * 1e-3) / 1e12
+    del buf
+    out["random_16KiB_read_TBps"] = gather
+    return out
+
+
 def decode_row_keys(ixn, h, t, nb, BM, nwords):
     """Retained keys of row t of head h, read off the index (segments filtered by the diagonal bitmap
     and the in-segment columns, then the gathered columns <= t)."""
@@ -431,6 +459,10 @@ def main():
         log("runtime capture at 64K: capture %.3f ms, index + attention %.3f ms (attention %.3f ms), density %.4f"
             % (rc["capture_ms"], rc["index_and_attention_ms"], rc["attention_ms"], rc["density"]))
         extras["decode"] = decode_bench(sa, torch)
+        extras["machine"] = machine_calibration(sa, torch)
+        log("machine: dense bf16 MFMA %.0f TFLOP/s; random 16 KiB reads %s TB/s" % (
+            extras["machine"]["mfma_bf16_dense_TFLOPs"],
+            ", ".join("%s %.1f" % kv for kv in extras["machine"]["random_16KiB_read_TBps"].items())))
         log("decode: %.3f ms for %d tokens (%.0f GB/s of retained K/V rows)" % (
             extras["decode"]["ms"], 16, extras["decode"]["kv_GBps"]))
 

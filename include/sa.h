@@ -348,6 +348,24 @@ sa_status sa_patterns_to_desc(const uint8_t* keep_diag, const uint8_t* keep_vert
                               int32_t S, int32_t* diag_ptr, int32_t* diag_off, int32_t* vert_ptr,
                               int32_t* vert_col, void* stream);
 
+/*
+ * Calibration (measurement support; computes nothing of the method).
+ *
+ * sa_calib_mfma_bf16: n_workgroups workgroups of 256 threads each run `iters` rounds of
+ *   four independent 32x32x16 bf16 MFMAs per wave from registers, i.e.
+ *   n_workgroups * 4 waves * iters * 4 * 32768 flops; the caller times the launch.
+ *   sink float [n_workgroups * 256] receives one value per thread.
+ * sa_calib_gather: n_workgroups workgroups of 256 threads each read reads_per_workgroup
+ *   chunks of chunk_bytes at pseudo-random chunk-aligned offsets (splitmix64 of seed,
+ *   workgroup and read index) of buf[0 .. region_bytes), with 16-byte loads:
+ *   n_workgroups * reads_per_workgroup * chunk_bytes bytes requested.  buf 16-byte
+ *   aligned; chunk_bytes a multiple of 16, at most region_bytes; sink as above.
+ * Errors: SA_ERR_INVALID_ARG, SA_ERR_HIP.
+ */
+sa_status sa_calib_mfma_bf16(int32_t n_workgroups, int32_t iters, float* sink, void* stream);
+sa_status sa_calib_gather(const void* buf, int64_t region_bytes, int32_t chunk_bytes, int32_t n_workgroups,
+                          int32_t reads_per_workgroup, uint64_t seed, float* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,7 +20,7 @@ import torch
 
 __all__ = ["SAError", "DevicePatterns", "SparseIndex", "build_index", "sparse_attn_prefill", "sparse_attn_decode",
            "attention_maps", "pattern_capture", "pattern_coverage", "patterns_to_desc", "sample_scores",
-           "select_patterns", "library_path", "version", "lib"]
+           "select_patterns", "calib_mfma_bf16", "calib_gather", "library_path", "version", "lib"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libsa.so")
@@ -88,6 +88,11 @@ def _load():
                                        C.c_void_p, C.c_void_p]
     lib.sa_pattern_coverage.restype = C.c_int32
     lib.sa_pattern_coverage.argtypes = [C.c_void_p, C.c_int32, C.c_int32] + [C.c_void_p] * 4 + [C.c_void_p]
+    lib.sa_calib_mfma_bf16.restype = C.c_int32
+    lib.sa_calib_mfma_bf16.argtypes = [C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]
+    lib.sa_calib_gather.restype = C.c_int32
+    lib.sa_calib_gather.argtypes = [C.c_void_p, C.c_int64, C.c_int32, C.c_int32, C.c_int32, C.c_uint64, C.c_void_p,
+                                    C.c_void_p]
     lib.sa_patterns_to_desc.restype = C.c_int32
     lib.sa_patterns_to_desc.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32] + \
         [C.c_void_p] * 4 + [C.c_void_p]
@@ -96,6 +101,24 @@ def _load():
 
 _lib = _load()
 lib = _lib
+
+
+def calib_mfma_bf16(n_workgroups: int, iters: int, stream=None) -> torch.Tensor:
+    """sa_calib_mfma_bf16 (measurement support): launches the dense bf16 MFMA loop; returns its sink."""
+    sink = torch.empty(n_workgroups * 256, dtype=torch.float32, device="cuda")
+    _check(_lib.sa_calib_mfma_bf16(n_workgroups, iters, sink.data_ptr(), _stream(stream)), "sa_calib_mfma_bf16")
+    return sink
+
+
+def calib_gather(buf: torch.Tensor, region_bytes: int, chunk_bytes: int, n_workgroups: int, reads: int, seed: int = 1,
+                 stream=None) -> torch.Tensor:
+    """sa_calib_gather (measurement support): random chunk reads from buf[0 .. region_bytes); returns its sink."""
+    if buf.numel() * buf.element_size() < region_bytes:
+        raise ValueError("buf is smaller than region_bytes")
+    sink = torch.empty(n_workgroups * 256, dtype=torch.float32, device=buf.device)
+    _check(_lib.sa_calib_gather(buf.data_ptr(), region_bytes, chunk_bytes, n_workgroups, reads, seed, sink.data_ptr(),
+                                _stream(stream)), "sa_calib_gather")
+    return sink
 
 
 def library_path() -> str:

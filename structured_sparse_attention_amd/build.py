@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsa.so")
-SOURCES = ["sa_api.cpp", "sa_index.hip", "sa_attn.hip", "sa_decode.hip", "sa_capture.hip", "sa_sample.hip"]
+SOURCES = ["sa_api.cpp", "sa_index.hip", "sa_attn.hip", "sa_decode.hip", "sa_capture.hip", "sa_sample.hip", "sa_calib.hip"]
 ARCH = "gfx950"
 
 

@@ -201,6 +201,20 @@ sa_status sa_select_patterns(const int64_t* scores, int32_t n_heads, int32_t S, 
                                       static_cast<hipStream_t>(stream)));
 }
 
+sa_status sa_calib_mfma_bf16(int32_t n_workgroups, int32_t iters, float* sink, void* stream) {
+  if (!sink || n_workgroups < 1 || iters < 1) return SA_ERR_INVALID_ARG;
+  return hip_status(sa::launch_calib_mfma(n_workgroups, iters, sink, static_cast<hipStream_t>(stream)));
+}
+
+sa_status sa_calib_gather(const void* buf, int64_t region_bytes, int32_t chunk_bytes, int32_t n_workgroups,
+                          int32_t reads_per_workgroup, uint64_t seed, float* sink, void* stream) {
+  if (!buf || !sink || n_workgroups < 1 || reads_per_workgroup < 1) return SA_ERR_INVALID_ARG;
+  if (!aligned16(buf) || chunk_bytes < 16 || chunk_bytes % 16 != 0 || region_bytes < chunk_bytes)
+    return SA_ERR_INVALID_ARG;
+  return hip_status(sa::launch_calib_gather(buf, region_bytes, chunk_bytes, n_workgroups, reads_per_workgroup, seed,
+                                            sink, static_cast<hipStream_t>(stream)));
+}
+
 sa_status sa_attention_maps(const void* q, const void* k, int32_t batch, int32_t hq, int32_t hkv, int32_t L,
                             int32_t head_dim, int32_t dtype, float softmax_scale, float* maps, void* stream) {
   if (!q || !k || !maps) return SA_ERR_INVALID_ARG;

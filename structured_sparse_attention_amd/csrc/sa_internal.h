@@ -62,6 +62,9 @@ hipError_t launch_sample_scores(const void* q, const void* k, int32_t batch, int
                                 int64_t* diag, int64_t* vert, hipStream_t stream);
 hipError_t launch_select(const int64_t* scores, int32_t n_heads, int32_t S, double alpha, int64_t t_all, int32_t band,
                          uint8_t* keep, hipStream_t stream);
+hipError_t launch_calib_mfma(int32_t n_wg, int32_t iters, float* sink, hipStream_t stream);
+hipError_t launch_calib_gather(const void* buf, int64_t region_bytes, int32_t chunk_bytes, int32_t n_wg, int32_t reads,
+                               uint64_t seed, float* sink, hipStream_t stream);
 hipError_t launch_coverage(const float* maps, int32_t n_maps, int32_t L, const uint8_t* keep_diag,
                            const uint8_t* keep_vert, double* mass, int64_t* cells, hipStream_t stream);
 hipError_t launch_patterns_to_desc(const uint8_t* keep_diag, const uint8_t* keep_vert, int32_t n_maps, int32_t L,

@@ -27,7 +27,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for f in ("sa_build_index", "sa_sparse_attn_prefill", "sa_sparse_attn_decode", "sa_attention_maps",
               "sa_pattern_capture", "sa_pattern_coverage", "sa_patterns_to_desc", "sa_sample_scores",
-              "sa_sample_scores_workspace", "sa_select_patterns", "sa_status_string", "sa_version"):
+              "sa_sample_scores_workspace", "sa_select_patterns", "sa_calib_mfma_bf16", "sa_calib_gather", "sa_status_string", "sa_version"):
         assert f in names
 
 
@@ -165,6 +165,17 @@ def test_sample_and_select_validation(m):
     assert g(p, 1, 8, 0.9, 4, -1, p, None) == -1      # band
     assert g(p, 0, 8, 0.9, 4, 0, p, None) == -1
     assert g(p + 4, 1, 8, 0.9, 4, 0, p, None) == -1   # scores not 8-byte aligned
+
+
+def test_calibration_validation(m):
+    p = FAKE.value
+    assert m.lib.sa_calib_mfma_bf16(0, 10, p, None) == -1
+    assert m.lib.sa_calib_mfma_bf16(4, 10, None, None) == -1
+    g = m.lib.sa_calib_gather
+    assert g(p, 1 << 20, 16384, 8, 4, 1, None, None) == -1          # sink
+    assert g(p, 1 << 20, 100, 8, 4, 1, p, None) == -1               # chunk not a multiple of 16
+    assert g(p, 4096, 16384, 8, 4, 1, p, None) == -1                # chunk larger than the region
+    assert g(p + 8, 1 << 20, 16384, 8, 4, 1, p, None) == -1         # buffer not 16-byte aligned
 
 
 def test_capture_validation(m):

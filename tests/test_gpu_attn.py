@@ -185,9 +185,10 @@ def test_llama8b_like_small_full():
 
 
 def test_llama8b_like_full_size_sampled():
+    """Every row of the first, the last and 32 seeded row blocks of every head."""
     desc = W.llama8b_like()
     q, k, v = W.qkv(4, 1, 32, 8, 65536, 128, "bf16")
-    rows = rows_of_blocks(1, 32, 65536, 64, 2, np.random.default_rng(4))
+    rows = rows_of_blocks(1, 32, 65536, 64, 32, np.random.default_rng(4))
     _run(desc, q, k, v, 64, rows, "8b-like")
 
 
@@ -201,9 +202,10 @@ def test_long_stripes_small_full(BM):
 
 
 def test_long_stripes_full_size_sampled():
+    """Every row of the first, the last and 16 seeded 128-row blocks of every head."""
     desc = W.long_stripes()
     q, k, v = W.qkv(5, 1, 32, 8, 131072, 128, "bf16")
-    rows = rows_of_blocks(1, 32, 131072, 128, 1, np.random.default_rng(5))
+    rows = rows_of_blocks(1, 32, 131072, 128, 16, np.random.default_rng(5))
     _run(desc, q, k, v, 128, rows, "stripes-131k")
 
 
