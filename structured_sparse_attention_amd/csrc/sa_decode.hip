@@ -12,14 +12,17 @@
 // Work: one workgroup of eight waves per (sequence, query head).  Candidate keys are
 // the segment columns <= t (retained iff (t - j) is a diagonal offset of the head or
 // j is an in-segment column of the item) and the gathered columns <= t.  The waves
-// take interleaved groups of 64 candidates; within a group each lane holds one key:
-// it reads its K row (a full row per lane) and forms q . k against the query kept
-// in its registers; the group's scores update the wave's running max and sum (exp2
-// domain).  P.V then runs with the lanes over head dimensions: for each retained key
-// of the group the wave reads the V row once (coalesced, sixteen rows in flight) and
-// every lane accumulates its slice.  Decode moves each retained K and V row once and
-// does 4 d flops per row, so it is bound by HBM (or L2) bandwidth, not by arithmetic;
-// no MFMA.  The waves' partial (max, sum, output) are merged in LDS at the end.
+// take interleaved batches of 64 candidates; each lane tests one candidate, and the
+// retained keys are compacted into a per-wave queue in LDS, so that the work below
+// always runs on full groups of 64 retained keys (a far diagonal leaves one key in
+// its 64-wide segment).  For a group each lane holds one key: it reads its K row (a
+// full row per lane) and forms q . k against the query kept in its registers; the
+// group's scores update the wave's running max and sum (exp2 domain).  P.V then runs
+// with the lanes over head dimensions: the group's (key, p) pairs are read back from
+// LDS and 32 V rows are loaded at once (coalesced rows), every lane accumulating its
+// slice.  Decode moves each retained K and V row once and does 4 d flops per row, so
+// it is bound by memory latency and bandwidth, not by arithmetic; no MFMA.  The
+// waves' partial (max, sum, output) are merged in LDS at the end.
 #include <type_traits>
 
 #include "sa_internal.h"
@@ -78,8 +81,11 @@ __global__ void __launch_bounds__(64 * kWaves) k_decode(DecParams p) {
   using E = typename std::conditional<BF16, uint16_t, float>::type;
   constexpr int QW = BF16 ? D / 2 : D;  // query registers: bf16 pairs or fp32 values
   constexpr int DPL = D / 64;           // head dimensions per lane in P.V
+  constexpr int VB = 32;                // V rows loaded at once
   __shared__ float m_sh[kWaves], l_sh[kWaves];
   __shared__ float o_sh[kWaves][D];
+  __shared__ int32_t kq[kWaves][128];  // per-wave queue of retained keys
+  __shared__ float kp[kWaves][64];     // probabilities of the group being processed
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b = blockIdx.x / p.hq, h = blockIdx.x % p.hq;
@@ -119,9 +125,12 @@ __global__ void __launch_bounds__(64 * kWaves) k_decode(DecParams p) {
   float oacc[DPL];
 #pragma unroll
   for (int x = 0; x < DPL; ++x) oacc[x] = 0.0f;
+  int qn = 0;  // keys waiting in kq[wave] (wave-uniform)
 
-  // one group of up to 64 candidate keys, lane = key j (keep: retained for row t)
-  auto group = [&](int32_t j, bool keep) {
+  // the first n (1..64) keys of the queue: lane l takes key kq[wave][l]
+  auto group = [&](int n) {
+    const bool keep = lane < n;
+    const int32_t j = keep ? kq[wave][lane] : 0;
     float x = -INFINITY;
     if (keep) {
       const uint4* krow = reinterpret_cast<const uint4*>(Kg + (int64_t)j * D);
@@ -142,8 +151,7 @@ __global__ void __launch_bounds__(64 * kWaves) k_decode(DecParams p) {
       }
       x = acc * p.scale_log2;
     }
-    const float gmax = dec_wave_max(x);
-    if (gmax == -INFINITY) return;  // no retained key in the group (wave-uniform)
+    const float gmax = dec_wave_max(x);  // finite: lane 0 holds a key
     if (gmax > m_run) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - gmax);  // exp2(-inf) = 0 on the first group
       l_lane *= alpha;
@@ -153,30 +161,24 @@ __global__ void __launch_bounds__(64 * kWaves) k_decode(DecParams p) {
     }
     const float pj = keep ? __builtin_amdgcn_exp2f(x - m_run) : 0.0f;
     l_lane += pj;
-    // P.V with the lanes over head dimensions: lane owns dimensions [DPL * lane, DPL * lane + DPL);
-    // the retained keys go sixteen at a time so that sixteen V rows are in flight
-    uint64_t mask = __ballot(keep);
-    while (mask) {
-      float ps[16];
-      int32_t js[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int src = mask ? __ffsll((unsigned long long)mask) - 1 : 0;
-        const bool live = mask != 0ull;
-        mask &= mask - 1;
-        ps[u] = live ? __shfl(pj, src, 64) : 0.0f;
-        js[u] = live ? __shfl(j, src, 64) : -1;
-      }
+    kp[wave][lane] = pj;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's LDS writes are done before it reads them
+    // P.V with the lanes over head dimensions: lane owns dimensions [DPL * lane, DPL * lane + DPL)
+    for (int u0 = 0; u0 < n; u0 += VB) {
+      float ps[VB];
       if constexpr (BF16) {
-        uint32_t w[16];
+        uint32_t w[VB];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const E* vrow = Vg + (int64_t)(js[u] < 0 ? 0 : js[u]) * D + DPL * lane;
-          if constexpr (DPL == 2) w[u] = js[u] < 0 ? 0u : *reinterpret_cast<const uint32_t*>(vrow);
-          else w[u] = js[u] < 0 ? 0u : (uint32_t)(*reinterpret_cast<const uint16_t*>(vrow)) << 16;
+        for (int u = 0; u < VB; ++u) {
+          const bool live = u0 + u < n;
+          const int32_t jj = live ? kq[wave][u0 + u] : 0;
+          ps[u] = live ? kp[wave][u0 + u] : 0.0f;
+          const E* vrow = Vg + (int64_t)jj * D + DPL * lane;
+          if constexpr (DPL == 2) w[u] = live ? *reinterpret_cast<const uint32_t*>(vrow) : 0u;
+          else w[u] = live ? (uint32_t)(*reinterpret_cast<const uint16_t*>(vrow)) << 16 : 0u;
         }
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
+        for (int u = 0; u < VB; ++u) {
           if constexpr (DPL == 2) {
             oacc[0] = __builtin_fmaf(ps[u], bf16_lo(w[u]), oacc[0]);
             oacc[1] = __builtin_fmaf(ps[u], bf16_hi(w[u]), oacc[1]);
@@ -185,49 +187,91 @@ __global__ void __launch_bounds__(64 * kWaves) k_decode(DecParams p) {
           }
         }
       } else {
-        float w[16][DPL];
+        float w[VB][DPL];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const E* vrow = Vg + (int64_t)(js[u] < 0 ? 0 : js[u]) * D + DPL * lane;
+        for (int u = 0; u < VB; ++u) {
+          const bool live = u0 + u < n;
+          const int32_t jj = live ? kq[wave][u0 + u] : 0;
+          ps[u] = live ? kp[wave][u0 + u] : 0.0f;
+          const E* vrow = Vg + (int64_t)jj * D + DPL * lane;
 #pragma unroll
-          for (int e = 0; e < DPL; ++e) w[u][e] = js[u] < 0 ? 0.0f : vrow[e];
+          for (int e = 0; e < DPL; ++e) w[u][e] = live ? vrow[e] : 0.0f;
         }
 #pragma unroll
-        for (int u = 0; u < 16; ++u)
+        for (int u = 0; u < VB; ++u)
 #pragma unroll
           for (int e = 0; e < DPL; ++e) oacc[e] = __builtin_fmaf(ps[u], w[u][e], oacc[e]);
       }
     }
   };
 
-  // segment columns <= t: retained iff (t - j) is a diagonal offset or j is an in-segment column
+  // Candidates in batches of 64 (lane = candidate j, keep = retained for row t): first the
+  // segment columns <= t (retained iff (t - j) is a diagonal offset or j is an in-segment
+  // column), then the gathered columns <= t (the list ascends, so they are a prefix).  The
+  // retained ones join the queue in order; each full group (and at the end the rest) is
+  // processed, the keys beyond it move to the front.  One loop, so that the group code is
+  // emitted once.
   const int64_t s0 = p.seg_ptr[item], s1 = p.seg_ptr[item + 1];
-  for (int64_t s = s0; s < s1; ++s) {
-    const int32_t lo = p.seg_lo[s];
-    if (lo > t) break;  // segments ascend
-    const int32_t hi = min(p.seg_hi[s], t);
-    for (int32_t jb = lo + 64 * wave; jb <= hi; jb += 64 * kWaves) {
-      const int32_t j = jb + lane;
-      bool keep = false;
-      if (j <= hi) {
+  const int64_t c0 = p.col_ptr[item], c1 = p.col_ptr[item + 1];
+  int64_t seg = s0;
+  int32_t jb = 0, shi = -1;  // current segment's next batch start and end (clipped to t)
+  auto open_segment = [&]() {
+    while (seg < s1) {
+      const int32_t lo = p.seg_lo[seg];
+      if (lo > t) {  // segments ascend: none left at or below t
+        seg = s1;
+        break;
+      }
+      jb = lo + 64 * wave;
+      shi = min(p.seg_hi[seg], t);
+      if (jb <= shi) return;
+      ++seg;
+    }
+  };
+  open_segment();
+  int64_t cb = c0 + 64 * wave;
+  bool cols_done = false;
+  for (;;) {
+    int32_t j = 0;
+    bool keep = false, last = false;
+    if (seg < s1) {
+      j = jb + lane;
+      if (j <= shi) {
         const int32_t r = t - j;
         keep = (dbh[r >> 5] >> (r & 31)) & 1u;
         if (!keep && bc1 > bc0) keep = in_sorted(p.bcol_idx, bc0, bc1, j);
       }
-      group(j, keep);
+      jb += 64 * kWaves;
+      if (jb > shi) {
+        ++seg;
+        open_segment();
+      }
+    } else if (!cols_done && cb < c1) {
+      const int64_t ci = cb + lane;
+      j = ci < c1 ? p.col_idx[ci] : S;
+      keep = j <= t;
+      cb += 64 * kWaves;
+      if (__ballot(keep) == 0ull || cb >= c1) cols_done = true;
+    } else {
+      last = true;
     }
-  }
-  // gathered columns <= t (the list ascends, so they are a prefix)
-  const int64_t c0 = p.col_ptr[item], c1 = p.col_ptr[item + 1];
-  for (int64_t cb = c0 + 64 * wave; cb < c1; cb += 64 * kWaves) {
-    const int64_t ci = cb + lane;
-    const int32_t j = ci < c1 ? p.col_idx[ci] : S;
-    const bool keep = j <= t;
-    if (__ballot(keep) == 0ull) break;
-    group(keep ? j : 0, keep);
+    const uint64_t mask = __ballot(keep);
+    if (keep) kq[wave][qn + __popcll(mask & ((1ull << lane) - 1ull))] = j;
+    qn += __popcll(mask);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the queue is written before it is read
+    if (qn >= 64 || (last && qn > 0)) {
+      const int n = min(qn, 64);
+      group(n);
+      const int32_t rest = lane < qn - n ? kq[wave][n + lane] : 0;
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      if (lane < qn - n) kq[wave][lane] = rest;
+      qn -= n;
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+    }
+    if (last) break;
   }
 
-  // merge the four waves
+  // merge the waves
   const float l_w = dec_wave_sum(l_lane);
   if (lane == 0) {
     m_sh[wave] = m_run;
