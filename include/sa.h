@@ -15,6 +15,9 @@
  *            abstract: block-level (64 x 64) attention sparsity.
  *   [Anchor] "AnchorAttention: Difference-Aware Sparse Attention with Stripe
  *            Granularity", abstract: stripe-granularity sparsity for prefill.
+ *   [SampleAttention] "SampleAttention: Near-Lossless Acceleration of Long Context
+ *            LLM Inference with Adaptive Structured Sparse Attention", abstract:
+ *            head-specific sparse patterns captured at runtime, per input.
  *
  * Conventions for every call:
  *   - Pointers are DEVICE pointers unless marked (host).  Structs are passed by
