@@ -209,6 +209,30 @@ def test_long_stripes_full_size_sampled():
     _run(desc, q, k, v, 128, rows, "stripes-131k")
 
 
+@pytest.mark.parametrize("kind,BM", [("blocks", 64), ("stripes", 128)])
+def test_repeatable_on_a_side_stream_into_a_dirty_buffer(kind, BM):
+    """No atomics or order-dependent sums: a second launch, on another stream and into an output buffer
+    holding garbage, gives the same bits; refilling the index in place does not change them either."""
+    m = sa()
+    S = 3000
+    desc = W.llama8b_like(S=S, H=8) if kind == "blocks" else W.long_stripes(S=S, H=8, band=512)
+    q, k, v = W.qkv(19, 1, 8, 2, S, 128, "bf16")
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    pat = m.DevicePatterns.from_host(desc)
+    ix = m.build_index(pat, BM)
+    note("repeatability BM=%d" % BM)
+    o1, l1 = m.sparse_attn_prefill(qd, kd, vd, ix, return_lse=True)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        o2 = torch.full_like(o1, float("nan"))
+        m.refill_index(pat, ix, stream=side)
+        _, l2 = m.sparse_attn_prefill(qd, kd, vd, ix, return_lse=True, out=o2, stream=side)
+    side.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
 def test_rejects_bad_arguments():
     m = sa()
     desc = W.tiny("base")
