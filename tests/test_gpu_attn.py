@@ -209,6 +209,17 @@ def test_long_stripes_full_size_sampled():
     _run(desc, q, k, v, 128, rows, "stripes-131k")
 
 
+# ------------------------------------------------------------------ the longest accepted sequence
+@pytest.mark.parametrize("dtype,d,BM", [("bf16", 128, 64), ("bf16", 128, 128), ("f32", 64, 128)])
+def test_max_length_sampled(dtype, d, BM):
+    """S = 262144 with every pattern kind: every row of the first, the last and 6 seeded row blocks
+    of each head (K/V offsets up to the end of the slab, diagonals and columns up to S - 1)."""
+    desc = W.max_length()
+    q, k, v = W.qkv(22, 1, 2, 1, W.MAX_S, d, dtype)
+    rows = rows_of_blocks(1, 2, W.MAX_S, BM, 6, np.random.default_rng(22))
+    _run(desc, q, k, v, BM, rows, "max-length")
+
+
 @pytest.mark.parametrize("kind,BM", [("blocks", 64), ("stripes", 128)])
 def test_repeatable_on_a_side_stream_into_a_dirty_buffer(kind, BM):
     """No atomics or order-dependent sums: a second launch, on another stream and into an output buffer

@@ -119,3 +119,11 @@ def test_decode_long_stripes_full_size():
     desc = W.long_stripes(H=4)
     _, k, v = W.qkv(38, 1, 4, 1, S, 128, "bf16")
     _decode(desc, _queries(7, 1, 4, 128, "bf16"), k, v, [S - 1], 128, "stripes-131k")
+
+
+def test_decode_max_length():
+    """S = 262144, every pattern kind; the last position, the first and one in the middle."""
+    S = W.MAX_S
+    desc = W.max_length()
+    _, k, v = W.qkv(39, 3, 2, 1, S, 128, "bf16")
+    _decode(desc, _queries(8, 3, 2, 128, "bf16"), k, v, [S - 1, 0, 131071], 128, "max-length")

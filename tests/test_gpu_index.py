@@ -69,6 +69,12 @@ def test_index_edge_lengths(S):
         _compare(W.desc_from_lists(S, diags, verts), BM, "edge")
 
 
+@pytest.mark.parametrize("BM", [64, 128])
+def test_index_max_length(BM):
+    """The longest accepted sequence, every pattern kind, offsets and columns up to S - 1."""
+    _compare(W.max_length(), BM, "max-length")
+
+
 def test_index_mixed_all_kinds():
     rng = np.random.default_rng(21)
     S, H = 1500, 4

@@ -42,7 +42,7 @@ import numpy as np
 __all__ = [
     "PatternDesc", "bf16_bits", "bf16_bits_to_f32", "qkv",
     "tiny", "llama1b_like", "capture_maps", "llama8b_like", "long_stripes",
-    "desc_from_lists", "CONFIG_SHAPES",
+    "desc_from_lists", "CONFIG_SHAPES", "MAX_S", "max_length",
 ]
 
 # (B, Hq, Hkv, d, S, dtype) of the five workloads
@@ -332,3 +332,29 @@ def long_stripes(S: int = 131072, H: int = 32, stripe_rows: int = 128, band: int
         stripes.append(per)
     return desc_from_lists(S, [np.zeros(0)] * H, [np.zeros(0)] * H, stripes=stripes,
                            stripe_rows=stripe_rows, meta=dict(workload="long_stripes"))
+
+
+MAX_S = 262144   # the longest sequence the index accepts
+
+
+def max_length(S: int = MAX_S, H: int = 2, seed: int = 9) -> PatternDesc:
+    """Every pattern kind at the longest accepted sequence: a 256-wide band plus far diagonals up
+    to S - 1, sinks plus verticals up to S - 1, 128 x 128 blocks at density 0.002 plus block
+    column 0 and the last block row, and 128-row stripe lists of up to 8 random columns."""
+    rng = np.random.default_rng([10, seed])
+    nbq = -(-S // 128)
+    bm = (rng.random((H, nbq, nbq)) < 0.002).astype(np.uint8)
+    bm[:, :, 0] = 1
+    bm[:, nbq - 1, :] = 1
+    bm = np.tril(bm)
+    diags, verts, stripes = [], [], []
+    for h in range(H):
+        diags.append(np.concatenate([np.arange(256), rng.choice(np.arange(256, S), 12, replace=False), [S - 1]]))
+        verts.append(np.concatenate([np.arange(16), rng.choice(np.arange(16, S), 20, replace=False), [S - 1]]))
+        per = []
+        for t in range(-(-S // 128)):
+            top = min(S, (t + 1) * 128) - 1
+            per.append(np.sort(rng.choice(top + 1, size=min(top + 1, int(rng.integers(0, 9))), replace=False)))
+        stripes.append(per)
+    return desc_from_lists(S, diags, verts, block_mask=bm, block_size=128, stripes=stripes, stripe_rows=128,
+                           meta=dict(workload="max_length"))
