@@ -387,8 +387,8 @@ def main():
                     help="also run one device copy of 1 GiB (reference for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (see DESIGN.md for how the "
-              "work would shard across GPUs); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (the work would shard by "
+              "query heads, one kv group per GPU); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

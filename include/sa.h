@@ -46,7 +46,7 @@ extern "C" {
 typedef int32_t sa_status;
 #define SA_OK 0
 #define SA_ERR_INVALID_ARG (-1)  /* null pointer, bad shape or size, inconsistent sizes */
-#define SA_ERR_UNSUPPORTED (-2)  /* valid request outside what this build implements */
+#define SA_ERR_UNSUPPORTED (-2)  /* valid request outside what the library implements */
 #define SA_ERR_DESC_INVALID (-3) /* descriptor contents not sorted/unique/in range */
 #define SA_ERR_CAPACITY (-4)     /* an output array is smaller than the result */
 #define SA_ERR_HIP (-5)          /* a HIP runtime call or kernel launch failed */
