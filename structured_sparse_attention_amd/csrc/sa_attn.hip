@@ -58,6 +58,15 @@ struct Params {
   int32_t nwords;
 };
 
+// Values the whole wave shares, loaded through the vector memory path, moved to scalar registers so
+// that the tile walk runs on the scalar unit and holds no vector registers.
+__device__ inline int32_t uni(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ inline int64_t uni64(int64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)x);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ inline uint64_t prefix_mask(int n) {  // bits [0, n), n clamped to [0, 64]
   return n <= 0 ? 0ull : (n >= 64 ? ~0ull : ((1ull << n) - 1ull));
 }
@@ -167,8 +176,8 @@ struct TileWalk {
     t.pc = c0;
     if (s0 < s1) {
       t.kind = 1;
-      t.j0 = seg_lo[s0];
-      t.shi = seg_hi[s0];
+      t.j0 = uni(seg_lo[s0]);
+      t.shi = uni(seg_hi[s0]);
       t.nvalid = min(BN, t.shi - t.j0 + 1);
     } else {
       start_gather(t);
@@ -192,8 +201,8 @@ struct TileWalk {
       if (t.j0 + BN <= t.shi) {
         t.j0 += BN;
       } else if (++t.seg < s1) {
-        t.j0 = seg_lo[t.seg];
-        t.shi = seg_hi[t.seg];
+        t.j0 = uni(seg_lo[t.seg]);
+        t.shi = uni(seg_hi[t.seg]);
       } else {
         start_gather(t);
         return t;
@@ -259,12 +268,12 @@ __global__ void __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(2))
   float m_run = -INFINITY, l_run = 0.0f;
 
   const int64_t item = (int64_t)h * p.nb + rb;
-  int64_t bp = p.bcol_ptr[item];
-  const int64_t bp_end = p.bcol_ptr[item + 1];
+  int64_t bp = uni64(p.bcol_ptr[item]);
+  const int64_t bp_end = uni64(p.bcol_ptr[item + 1]);
   TileWalk walk;
-  walk.s1 = p.seg_ptr[item + 1];
-  walk.c0 = p.col_ptr[item];
-  walk.c1 = p.col_ptr[item + 1];
+  walk.s1 = uni64(p.seg_ptr[item + 1]);
+  walk.c0 = uni64(p.col_ptr[item]);
+  walk.c1 = uni64(p.col_ptr[item + 1]);
   walk.seg_lo = p.seg_lo;
   walk.seg_hi = p.seg_hi;
 
@@ -506,7 +515,7 @@ __global__ void __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(2))
   auto load_cols = [&](const Tile& t, int32_t* dst) {
     if (t.kind == 2 && tid < BN) dst[tid] = tid < t.nvalid ? p.col_idx[t.pc + tid] : 0;
   };
-  Tile cur = walk.first(p.seg_ptr[item]);
+  Tile cur = walk.first(uni64(p.seg_ptr[item]));
   Tile nxt = walk.next(cur);
   Tile nn = walk.next(nxt);
   load_cols(cur, cols_sh[0]);
@@ -651,12 +660,12 @@ k_attn_bf16(Params p) {
   float m_run = -INFINITY, l_run = 0.0f;
 
   const int64_t item = (int64_t)h * p.nb + rb;
-  int64_t bp = p.bcol_ptr[item];
-  const int64_t bp_end = p.bcol_ptr[item + 1];
+  int64_t bp = uni64(p.bcol_ptr[item]);
+  const int64_t bp_end = uni64(p.bcol_ptr[item + 1]);
   TileWalk walk;
-  walk.s1 = p.seg_ptr[item + 1];
-  walk.c0 = p.col_ptr[item];
-  walk.c1 = p.col_ptr[item + 1];
+  walk.s1 = uni64(p.seg_ptr[item + 1]);
+  walk.c0 = uni64(p.col_ptr[item]);
+  walk.c1 = uni64(p.col_ptr[item + 1]);
   walk.seg_lo = p.seg_lo;
   walk.seg_hi = p.seg_hi;
 
@@ -869,7 +878,7 @@ k_attn_bf16(Params p) {
   auto load_cols = [&](const Tile& t, int32_t* dst) {
     if (t.kind == 2 && tid < BN) dst[tid] = tid < t.nvalid ? p.col_idx[t.pc + tid] : 0;
   };
-  Tile cur = walk.first(p.seg_ptr[item]);
+  Tile cur = walk.first(uni64(p.seg_ptr[item]));
   Tile nxt = walk.next(cur);
   Tile nn = walk.next(nxt);
   load_cols(cur, cols_sh[0]);
