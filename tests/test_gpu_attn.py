@@ -97,6 +97,31 @@ def test_empty_rows_zero_output_minus_inf_lse():
         assert o[0, 0, :70].float().abs().max().item() == 0.0
 
 
+def _short_desc(S, H):
+    """Diagonals {0, 1, 5}, columns {0, S - 1}, 128 x 128 blocks and 128-row stripes, clipped to S; the last
+    head holds no pattern at all (every row empty)."""
+    rng = np.random.default_rng(S)
+    nbq = -(-S // 128)
+    bm = (rng.random((H, nbq, nbq)) < 0.5).astype(np.uint8)
+    bm[H - 1] = 0
+    diags = [np.array([r for r in (0, 1, 5) if r < S]) for _ in range(H - 1)] + [np.zeros(0)]
+    verts = [np.unique([0, S - 1]) for _ in range(H - 1)] + [np.zeros(0)]
+    stripes = [[np.sort(rng.choice(min(S, (t + 1) * 128), size=min(3, min(S, (t + 1) * 128)), replace=False))
+                if h < H - 1 else np.zeros(0) for t in range(nbq)] for h in range(H)]
+    return W.desc_from_lists(S, diags, verts, block_mask=bm, block_size=128, stripes=stripes, stripe_rows=128)
+
+
+@pytest.mark.parametrize("S", [1, 2, 31, 63, 64, 65, 127, 129])
+@pytest.mark.parametrize("dtype,d,BM", [("bf16", 128, 64), ("bf16", 128, 128), ("f32", 64, 64)])
+def test_short_sequences_and_an_empty_head(S, dtype, d, BM):
+    """Sequences shorter than one tile or a tile plus one row, every pattern kind, and a head with no pattern
+    (zero output, lse -inf)."""
+    H = 3
+    q, k, v = W.qkv(23, 1, H, 1, S, d, dtype)
+    o, _ = _run(_short_desc(S, H), q, k, v, BM, all_rows(1, H, S), "short-S")
+    assert o[0, H - 1].float().abs().max().item() == 0.0
+
+
 def test_batch_and_gqa_and_custom_scale():
     S, d = 333, 64
     desc = W.llama1b_like(S=S, H=6)

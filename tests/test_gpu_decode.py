@@ -127,3 +127,15 @@ def test_decode_max_length():
     desc = W.max_length()
     _, k, v = W.qkv(39, 3, 2, 1, S, 128, "bf16")
     _decode(desc, _queries(8, 3, 2, 128, "bf16"), k, v, [S - 1, 0, 131071], 128, "max-length")
+
+
+@pytest.mark.parametrize("S", [1, 2, 65, 129])
+@pytest.mark.parametrize("BM", [64, 128])
+def test_decode_short_sequences_and_an_empty_head(S, BM):
+    """Caches shorter than one tile or a tile plus one row, every pattern kind, a head with no pattern."""
+    from test_gpu_attn import _short_desc
+    pos = sorted({0, S - 1, S // 2, max(0, S - 2)})
+    B, H = len(pos), 3
+    _, k, v = W.qkv(40, B, H, 1, S, 128, "bf16")
+    o = _decode(_short_desc(S, H), _queries(9, B, H, 128, "bf16"), k, v, pos, BM, "short-S")
+    assert o[:, H - 1].float().abs().max().item() == 0.0
