@@ -25,9 +25,14 @@
 // minimum and maximum of A: the min/max pass runs in fp32 and each element is
 // transformed once.
 //
-// Layout: one 1024-thread workgroup per map; wave w takes rows w, w+16, ...; lanes
-// take columns, four loads in flight per lane.  Hits accumulate with LDS atomics; the map is read once from HBM
-// (the causal half) plus once more for the fp32 row min/max, which hits in cache.
+// At lambda = 0.5 the keep test is also monotone in A (every step rounds monotonically), so each
+// row's kept elements are those at or above one fp32 threshold, found per row by bisection with the
+// same fp64 steps; the element pass then compares in fp32 and needs no fp64 at all.
+//
+// Layout: one 1024-thread workgroup per map.  Pass 1: the fp32 min/max of every row (wave w takes rows
+// w, w+16, ..., four rows at a time, lanes over columns); pass 2: one thread per row transforms the
+// extremes and finds the threshold; pass 3: the element pass (lanes over columns, four loads in
+// flight per lane), hits accumulating with LDS atomics.  The causal half of the map is read twice.
 #include <type_traits>
 
 #include "sa_internal.h"
@@ -63,15 +68,23 @@ __device__ inline float wave_max(float x) {
   return x;
 }
 
+// How a row's keep flags are decided in the element pass.
+enum { kRowThreshold = 0, kRowAll = 1, kRowNone = 2, kRowEach = 3 };
+
 template <int KIND>
 __global__ void __launch_bounds__(kThreads)
     k_capture(const float* maps, int32_t L, double lambda, double eps, double tau, double mu, int32_t norm_scope,
               uint8_t* keep_diag, uint8_t* keep_vert, int32_t* diag_hits, int32_t* vert_hits, uint8_t* true_mask) {
 #pragma clang fp contract(off)
-  extern __shared__ int32_t hits[];  // [L] diagonal hits, then [L] vertical hits
+  // LDS: [L] diagonal hits, [L] vertical hits, then per row: A min, A max, threshold, mode
+  extern __shared__ int32_t lds[];
   __shared__ float red[2 * (kThreads / 64)];
-  int32_t* hd = hits;
-  int32_t* hv = hits + L;
+  int32_t* hd = lds;
+  int32_t* hv = lds + L;
+  float* rmin = reinterpret_cast<float*>(lds + 2 * L);
+  float* rmax = reinterpret_cast<float*>(lds + 3 * L);
+  float* rthr = reinterpret_cast<float*>(lds + 4 * L);
+  int32_t* rmode = lds + 5 * L;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t map = blockIdx.x;
   const float* A = maps + map * (int64_t)L * L;
@@ -79,7 +92,8 @@ __global__ void __launch_bounds__(kThreads)
     hd[r] = 0;
     hv[r] = 0;
   }
-  float gmin = INFINITY, gmax = -INFINITY;
+
+  // 1. the fp32 minimum and maximum of every causal row (norm_scope 0) or of the map (1)
   if (norm_scope == 1) {
     float mn = INFINITY, mx = -INFINITY;
     for (int i = wave; i < L; i += kThreads / 64)
@@ -95,41 +109,102 @@ __global__ void __launch_bounds__(kThreads)
       red[kThreads / 64 + wave] = mx;
     }
     __syncthreads();
+    float gmin = INFINITY, gmax = -INFINITY;
     for (int w = 0; w < kThreads / 64; ++w) {
       gmin = fminf(gmin, red[w]);
       gmax = fmaxf(gmax, red[kThreads / 64 + w]);
     }
-  }
-  __syncthreads();
-
-  for (int i = wave; i < L; i += kThreads / 64) {
-    const float* row = A + (int64_t)i * L;
-    float amin = gmin, amax = gmax;
-    if (norm_scope == 0) {
-      float mn = INFINITY, mx = -INFINITY;
-      for (int jb = 0; jb <= i; jb += 4 * 64) {
-        float a[4];
+    for (int r = tid; r < L; r += kThreads) {
+      rmin[r] = gmin;
+      rmax[r] = gmax;
+    }
+  } else {
+    // four rows per wave at a time (rows w, w + 16, w + 32, w + 48 of each block of 64), so that four
+    // independent loads and reductions are in flight
+    constexpr int kRows = 4, kStride = kThreads / 64;
+    for (int i0 = wave; i0 < L; i0 += kRows * kStride) {
+      float mn[kRows], mx[kRows];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int j = jb + u * 64 + lane;
-          a[u] = j <= i ? row[j] : INFINITY;
+      for (int q = 0; q < kRows; ++q) {
+        mn[q] = INFINITY;
+        mx[q] = -INFINITY;
+      }
+      const int ilast = min(L - 1, i0 + (kRows - 1) * kStride);
+      for (int j = lane; j <= ilast; j += 64) {
+        float a[kRows];
+#pragma unroll
+        for (int q = 0; q < kRows; ++q) {
+          const int i = i0 + q * kStride;
+          a[q] = (i < L && j <= i) ? A[(int64_t)i * L + j] : 0.0f;
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int j = jb + u * 64 + lane;
-          if (j <= i) {
-            mn = fminf(mn, a[u]);
-            mx = fmaxf(mx, a[u]);
+        for (int q = 0; q < kRows; ++q) {
+          const int i = i0 + q * kStride;
+          if (i < L && j <= i) {
+            mn[q] = fminf(mn[q], a[q]);
+            mx[q] = fmaxf(mx[q], a[q]);
           }
         }
       }
-      amin = wave_min(mn);
-      amax = wave_max(mx);
+#pragma unroll
+      for (int q = 0; q < kRows; ++q) {
+        const int i = i0 + q * kStride;
+        const float lo = wave_min(mn[q]), hi = wave_max(mx[q]);
+        if (lane == 0 && i < L) {
+          rmin[i] = lo;
+          rmax[i] = hi;
+        }
+      }
     }
+  }
+  __syncthreads();
+
+  // 2. one thread per row: the transform of the extremes and, at lambda = 0.5, the keep threshold.
+  // There the test t >= tau, t = (y(a) - ymin) / (ymax - ymin), is monotone non-decreasing in a: each
+  // step (a + eps, the correctly rounded sqrt, - 1, * 2, - ymin, / range) rounds monotonically.  So
+  // for finite a >= 0 the kept elements of a row are those at or above the smallest float that
+  // passes, found by bisection over the ordered bit patterns of [min, max] with the same fp64 steps.
+  // Rows with a negative or non-finite extreme, and the other lambdas (device log / pow), test each
+  // element.
+  for (int r = tid; r < L; r += kThreads) {
+    const float amin = rmin[r], amax = rmax[r];
     const double ymin = box_cox<KIND>(amin, eps, lambda);
     const double ymax = box_cox<KIND>(amax, eps, lambda);
-    const bool flat = (ymax == ymin);
-    const double range = ymax - ymin;
+    int mode = kRowEach;
+    float thr = 0.0f;
+    if (ymax == ymin) {
+      mode = 1.0 >= tau ? kRowAll : kRowNone;  // flat: t = 1 for every element
+    } else if (KIND == kBoxCoxHalf && amin >= 0.0f && amax < INFINITY) {
+      const double range = ymax - ymin;
+      auto pass = [&](float a) { return (box_cox<KIND>(a, eps, lambda) - ymin) / range >= tau; };
+      if (!pass(amax)) {
+        mode = kRowNone;
+      } else {
+        uint32_t lo = __float_as_uint(amin) & 0x7fffffffu, hi = __float_as_uint(amax);
+        while (lo < hi) {
+          const uint32_t mid = lo + ((hi - lo) >> 1);
+          if (pass(__uint_as_float(mid))) hi = mid;
+          else lo = mid + 1;
+        }
+        mode = kRowThreshold;
+        thr = __uint_as_float(lo);
+      }
+    }
+    rmode[r] = mode;
+    rthr[r] = thr;
+  }
+  __syncthreads();
+
+  // 3. element pass: keep flags, hits, optional true mask
+  for (int i = wave; i < L; i += kThreads / 64) {
+    const float* row = A + (int64_t)i * L;
+    const int mode = rmode[i];
+    const float thr = rthr[i];
+    double ymin = 0.0, range = 1.0;
+    if (mode == kRowEach) {
+      ymin = box_cox<KIND>(rmin[i], eps, lambda);
+      range = box_cox<KIND>(rmax[i], eps, lambda) - ymin;
+    }
     uint8_t* mrow = true_mask ? true_mask + (map * L + i) * (int64_t)L : nullptr;
     for (int jb = 0; jb < L; jb += 4 * 64) {
       float a[4];
@@ -144,9 +219,9 @@ __global__ void __launch_bounds__(kThreads)
         if (j >= L) continue;
         uint8_t keep = 0;
         if (j <= i) {
-          const double y = box_cox<KIND>(a[u], eps, lambda);
-          const double t = flat ? 1.0 : (y - ymin) / range;
-          keep = t >= tau;
+          if (mode == kRowThreshold) keep = a[u] >= thr;
+          else if (mode == kRowAll) keep = 1;
+          else if (mode == kRowEach) keep = (box_cox<KIND>(a[u], eps, lambda) - ymin) / range >= tau;
           if (keep) {
             atomicAdd(&hd[i - j], 1);
             atomicAdd(&hv[j], 1);
@@ -482,8 +557,13 @@ __global__ void __launch_bounds__(kDescThreads)
 hipError_t launch_capture(const float* maps, int32_t n_maps, int32_t L, double lambda, double eps, double tau,
                           double mu, int32_t norm_scope, uint8_t* keep_diag, uint8_t* keep_vert, int32_t* diag_hits,
                           int32_t* vert_hits, uint8_t* true_mask, hipStream_t stream) {
-  const size_t lds = 2 * sizeof(int32_t) * (size_t)L;
+  const size_t lds = 6 * sizeof(int32_t) * (size_t)L;  // hits, then per-row min, max, threshold, mode
   auto kern = lambda == 0.5 ? k_capture<kBoxCoxHalf> : lambda == 0.0 ? k_capture<kBoxCoxLog> : k_capture<kBoxCoxPow>;
+  if (lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(kern, dim3((unsigned)n_maps), dim3(kThreads), lds, stream, maps, L, lambda, eps, tau, mu,
                      norm_scope, keep_diag, keep_vert, diag_hits, vert_hits, true_mask);
   return hipGetLastError();

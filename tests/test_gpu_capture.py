@@ -48,6 +48,35 @@ def test_capture_odd_sizes(L):
     _capture_both(A.astype(np.float32))
 
 
+def _edge_maps(L=96):
+    """Rows that take each decision path of the capture kernel: ordinary rows, zeros and -0.0, entries in
+    [-eps, 0) (per-element path), constant rows, rows of two values, rows whose values differ by one ulp,
+    and values from 1e-30 to 1."""
+    rng = np.random.default_rng(97)
+    A = np.tril(rng.random((4, L, L))).astype(np.float32)
+    A[0, 10, :11] = 0.25                                      # constant row
+    A[0, 11, :12] = np.where(np.arange(12) % 2, 0.5, 0.0)     # two values
+    A[0, 20, :21] = -0.0                                      # constant -0.0
+    A[0, 21, :22] = 0.0
+    A[0, 21, 5] = -0.0
+    A[0, 30, :31] = np.nextafter(np.float32(0.3), np.float32(1.0))
+    A[0, 30, 7] = np.float32(0.3)                             # one ulp apart
+    A[1] = np.tril(np.float32(10.0) ** rng.uniform(-30, 0, (L, L)).astype(np.float32))
+    A[2, 40, :41] = rng.uniform(-5e-9, 1e-9, 41).astype(np.float32)   # A + eps >= 0 with eps = 1e-8
+    A[2, 41, :42] = np.float32(-5e-9)
+    A[3] = np.tril(np.round(rng.random((L, L)) * 3) / 3).astype(np.float32)   # few distinct values
+    return A
+
+
+@pytest.mark.parametrize("tau", [-0.5, 0.0, 0.3, 1.0, 1.5])
+@pytest.mark.parametrize("scope", [0, 1])
+def test_capture_edge_rows(tau, scope):
+    """Bit-exact against the oracle on rows that take every path (per-row thresholds at lambda = 0.5, the
+    per-element path, constant rows) and on thresholds that keep all or nothing."""
+    note("capture edge rows tau=%g scope=%d" % (tau, scope))
+    _capture_both(_edge_maps(), tau=tau, norm_scope=scope)
+
+
 def test_capture_thresholds_and_mu():
     maps = W.capture_maps(layers=1, heads=4, n_avg=4, layer_offset=7)
     _capture_both(maps, tau=0.55, mu=0.6)
