@@ -159,13 +159,15 @@ __global__ void __launch_bounds__(kThreads)
   }
   __syncthreads();
 
-  // 2. one thread per row: the transform of the extremes and, at lambda = 0.5, the keep threshold.
-  // There the test t >= tau, t = (y(a) - ymin) / (ymax - ymin), is monotone non-decreasing in a: each
-  // step (a + eps, the correctly rounded sqrt, - 1, * 2, - ymin, / range) rounds monotonically.  So
-  // for finite a >= 0 the kept elements of a row are those at or above the smallest float that
-  // passes, found by bisection over the ordered bit patterns of [min, max] with the same fp64 steps.
-  // Rows with a negative or non-finite extreme, and the other lambdas (device log / pow), test each
-  // element.
+  // 2. one thread per row: the transform of the extremes and the keep threshold.  At lambda = 0.5 the
+  // test t >= tau, t = (y(a) - ymin) / (ymax - ymin), is monotone non-decreasing in a: each step
+  // (a + eps, the correctly rounded sqrt, - 1, * 2, - ymin, / range) rounds monotonically.  So for
+  // finite a >= 0 the kept elements of a row are those at or above the smallest float that passes,
+  // found by bisection over the ordered bit patterns of [min, max] with the same fp64 steps.  Box-Cox
+  // is increasing for every lambda; with the device log / pow (a few ulp, not guaranteed monotone at
+  // that scale) the threshold decides like a per-element test except for cells whose t lies within a
+  // few ulp of tau, the cells that may differ from a correctly rounded evaluation anyway.  Rows with
+  // a negative or non-finite extreme test each element.
   for (int r = tid; r < L; r += kThreads) {
     const float amin = rmin[r], amax = rmax[r];
     const double ymin = box_cox<KIND>(amin, eps, lambda);
@@ -174,7 +176,7 @@ __global__ void __launch_bounds__(kThreads)
     float thr = 0.0f;
     if (ymax == ymin) {
       mode = 1.0 >= tau ? kRowAll : kRowNone;  // flat: t = 1 for every element
-    } else if (KIND == kBoxCoxHalf && amin >= 0.0f && amax < INFINITY) {
+    } else if (amin >= 0.0f && amax < INFINITY) {
       const double range = ymax - ymin;
       auto pass = [&](float a) { return (box_cox<KIND>(a, eps, lambda) - ymin) / range >= tau; };
       if (!pass(amax)) {
