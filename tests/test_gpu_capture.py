@@ -77,6 +77,18 @@ def test_capture_edge_rows(tau, scope):
     _capture_both(_edge_maps(), tau=tau, norm_scope=scope)
 
 
+def test_capture_longest_window():
+    """L = 4096, the longest capture window (its per-row tables need more than 64 KiB of LDS)."""
+    L = 4096
+    rng = np.random.default_rng(4096)
+    A = rng.random((2, L, L), dtype=np.float32) ** 4
+    A = np.tril(A)
+    A /= np.maximum(1e-30, A.sum(axis=2, keepdims=True))
+    note("capture L=%d" % L)
+    for scope in (0, 1):
+        _capture_both(A.astype(np.float32), norm_scope=scope)
+
+
 def test_capture_thresholds_and_mu():
     maps = W.capture_maps(layers=1, heads=4, n_avg=4, layer_offset=7)
     _capture_both(maps, tau=0.55, mu=0.6)
