@@ -282,8 +282,10 @@ sa_status sa_pattern_coverage(const float* maps, int32_t n_maps, int32_t L, cons
  * row's probabilities on the pairs not covered yet -- outside the local window
  * (i - j >= band) and off the columns marked in skip_cols -- are ADDED onto its
  * head's pattern scores:
- *   diag_score[h][r] += round(p_i(i - r) * 2^32)     (per term)
+ *   diag_score[h][r] += sum of p_i(i - r), rounded to units of 2^-32 per partial sum
  *   vert_score[h][c] += sum of p_i(c), rounded to units of 2^-32 per partial sum
+ * (partial sums: fp32, in a fixed order, over the rows of a 32-row chunk and the
+ * sequences of the batch for a column, over a 32-row, 32-key block for a diagonal);
  * int64 fixed point, so the sums are exact integer sums whatever the order of the
  * atomics (deterministic); the caller zeroes both arrays first and may call again
  * with other row blocks to accumulate.  Each sampled row holds 2^32 units in all

@@ -24,9 +24,11 @@
 //   and split goes to the caller's workspace and is merged per row in split order.
 // k_sample_acc: one workgroup of 4 waves per (64-key tile, head), heads of a kv group
 //   adjacent; the tile is staged in LDS per sequence, the waves take 32-row chunks,
-//   recompute the scores and add p = exp2(s - lse): diagonals with int64 LDS atomics,
-//   verticals in registers, reduced across the lanes by a butterfly and across the
-//   waves in a fixed order; one global int64 atomic per touched pattern.
+//   recompute the scores and add p = exp2(s - lse): diagonals summed per 32-row, 32-key
+//   block through LDS (lane = diagonal, rows in order) and added with one int64 LDS
+//   atomic per block and diagonal; verticals in registers, reduced across the lanes by a
+//   butterfly and across the waves in a fixed order; one global int64 atomic per touched
+//   pattern.
 // k_select: one 1024-thread workgroup per head; the threshold is found by
 //   a most-significant-digit radix search over the score bits (8-bit digits), each
 //   pass a mass histogram of the scores inside the current bucket.
@@ -213,6 +215,8 @@ __global__ void __launch_bounds__(256) k_sample_acc(const void* qv, const void* 
   E* Ks = reinterpret_cast<E*>(smem);
   float* vpart = reinterpret_cast<float*>(smem + 64 * KSTR * sizeof(E));  // [4 waves][64 keys]
   unsigned long long* dacc = reinterpret_cast<unsigned long long*>(vpart + 4 * 64);  // diagonals r_base + x
+  // per wave: the probabilities of one 32-row chunk against one 32-key half of the tile, [row][key]
+  constexpr int kPS = 33;  // row stride (floats)
   __shared__ uint8_t skip_lds[kAccTiles * 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, r32 = lane & 31;
@@ -225,6 +229,7 @@ __global__ void __launch_bounds__(256) k_sample_acc(const void* qv, const void* 
   if (last - band < c_first) return;
   const int r_base = row0 - (c_first + kAccTiles * 64 - 1);  // diagonal of dacc[0]
   const int span = n_rows + kAccTiles * 64 - 1;
+  float* pdiag = reinterpret_cast<float*>(dacc + (DIAG ? span : 0)) + wave * 32 * kPS;
   const int nch = (n_rows + 31) / 32;
   if constexpr (DIAG)
     for (int x = tid; x < span; x += 256) dacc[x] = 0ull;
@@ -272,10 +277,20 @@ __global__ void __launch_bounds__(256) k_sample_acc(const void* qv, const void* 
             const bool ok = row_ok && j <= i - band && !skip_lds[t * 64 + jt];
             const float p = ok ? __builtin_amdgcn_exp2f(acc[v] * scale_log2 - lse2) : 0.0f;
             if constexpr (VERT) vacc[kb * 16 + v] += p;
-            if constexpr (DIAG) {
-              const unsigned long long fx = (unsigned long long)__double2ll_rn((double)p * kFixUnit);
-              if (fx) atomicAdd(&dacc[i - j - r_base], fx);
+            if constexpr (DIAG) pdiag[r32 * kPS + (jt - kb * 32)] = p;
+          }
+          if constexpr (DIAG) {
+            // diagonal sums of the 32 x 32 block: lane x takes diagonal (row - key) = x - 31, its rows
+            // in ascending order, then one fixed-point value and one LDS atomic per diagonal
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's block is in LDS
+            if (lane < 63) {
+              const int dl = lane - 31;
+              float sum = 0.0f;
+              for (int r = max(0, dl); r <= min(31, 31 + dl); ++r) sum += pdiag[r * kPS + (r - dl)];
+              const unsigned long long fx = (unsigned long long)__double2ll_rn((double)sum * kFixUnit);
+              if (fx) atomicAdd(&dacc[(row0 + ch * 32 - c0 - kb * 32) + dl - r_base], fx);
             }
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next block overwrites it
           }
         }
       }
@@ -430,7 +445,9 @@ hipError_t launch_sample_t(const void* q, const void* k, int32_t B, int32_t hq, 
   }
   const int ngrp = (row0 + n_rows - 1) / (kAccTiles * 64) + 1;
   const size_t lds = 64 * KSTR * sizeof(E) + 4 * 64 * sizeof(float) +
-                     (diag ? ((size_t)n_rows + kAccTiles * 64 - 1) * sizeof(unsigned long long) : 0);
+                     (diag ? ((size_t)n_rows + kAccTiles * 64 - 1) * sizeof(unsigned long long) +
+                                 4 * 32 * 33 * sizeof(float)
+                           : 0);
   auto kern = diag ? (vert ? k_sample_acc<D, BF16, true, true> : k_sample_acc<D, BF16, true, false>)
                    : k_sample_acc<D, BF16, false, true>;
   if (lds > 65536) {

@@ -2,8 +2,8 @@
 (sa_select_patterns) against the fp64 oracle, and the two-stage per-input pipeline end to end.
 
 Scores are int64 fixed point (2^-32 of one row's mass); against the oracle's fp64 sums they agree
-within 1e-5 relative plus 1e-7 absolute (fp32 scores and softmax; per-term rounding of the fixed
-point).  The selection is exact integer arithmetic, so on the same integer scores it is bit-exact.
+within 1e-5 relative plus 1e-7 absolute (fp32 scores, softmax and partial sums; rounding of each
+partial sum to the fixed point).  The selection is exact integer arithmetic, so on the same integer scores it is bit-exact.
 The pipeline's keep flags are compared on every pattern whose decision no score within that bound
 can change (tests/capture_bounds.py)."""
 import numpy as np
