@@ -204,7 +204,9 @@ __device__ inline void half_wave_sum(float (&v)[32]) {
 constexpr int kAccTiles = 16;  // 64-key tiles per workgroup of the accumulation pass
 
 template <int D, bool BF16, bool DIAG, bool VERT>
-__global__ void __launch_bounds__(256) k_sample_acc(const void* qv, const void* kv, int32_t B, int32_t hq, int32_t hkv,
+// three waves per SIMD: the register budget that keeps the column pass free of spills (measured
+// 10 % faster than the unconstrained two)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k_sample_acc(const void* qv, const void* kv, int32_t B, int32_t hq, int32_t hkv,
                                                     int32_t S, int32_t row0, int32_t n_rows, int32_t band,
                                                     const uint8_t* skip_cols, float scale_log2, const float* row_lse,
                                                     unsigned long long* diag_score, unsigned long long* vert_score) {
