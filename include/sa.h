@@ -177,6 +177,16 @@ sa_status sa_build_index(const sa_pattern_desc* desc, sa_index* idx, sa_index_si
                          void* stream);
 
 /*
+ * sa_build_index_workspace_bytes (host): bytes of device scratch a build of `desc` at
+ * row block `row_block` needs beyond the index arrays.  Always 0 here: the counting
+ * pass keeps its per-item counts in the index's own pointer arrays and scans them in
+ * place, and the per-item kinds ride in the dbits array until the fill writes it, so
+ * sa_build_index takes no workspace argument.  Provided so that a caller written
+ * against a workspace-taking build can size (and skip) its allocation.  desc may be NULL.
+ */
+size_t sa_build_index_workspace_bytes(const sa_pattern_desc* desc, int32_t row_block);
+
+/*
  * sa_sparse_attn_prefill: O = softmax(mask(Q K^T * scale)) V over retained pairs
  * only [DAM, Referee Report Summary; What carries the argument: masked pairs get
  * zero weight, read as logit -inf].

@@ -81,6 +81,8 @@ def _load():
     lib.sa_sample_scores.restype = C.c_int32
     lib.sa_sample_scores.argtypes = [C.c_void_p, C.c_void_p] + [C.c_int32] * 6 + [C.c_float] + [C.c_int32] * 3 + \
         [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_size_t] + [C.c_void_p] * 2 + [C.c_void_p]
+    lib.sa_build_index_workspace_bytes.restype = C.c_size_t
+    lib.sa_build_index_workspace_bytes.argtypes = [C.c_void_p, C.c_int32]
     lib.sa_sample_scores_workspace.restype = C.c_size_t
     lib.sa_sample_scores_workspace.argtypes = [C.c_int32] * 4
     lib.sa_select_patterns.restype = C.c_int32
@@ -133,6 +135,15 @@ def _stream(stream) -> Optional[int]:
     if stream is None:
         stream = torch.cuda.current_stream()
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _torch_stream(stream) -> torch.cuda.Stream:
+    """The launch stream as a torch stream object (a raw hipStream_t handle is wrapped, not owned)."""
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream))
 
 
 def _hold(t: Optional[torch.Tensor], stream) -> None:
@@ -409,7 +420,10 @@ def sample_scores(q: torch.Tensor, k: torch.Tensor, row0: int, n_rows: int, band
     B, hq, S, d = q.shape
     if k.shape[0] != B or k.shape[2] != S or k.shape[3] != d:
         raise ValueError("k shape does not match q")
+    ts = _torch_stream(stream)
+    cur = torch.cuda.current_stream(q.device)
     if scores is None:
+        # zeroed on the current stream; the launch stream waits for it below
         scores = tuple(torch.zeros((hq, S), dtype=torch.int64, device=q.device) if want else None
                        for want in families)
     diag, vert = scores
@@ -425,13 +439,26 @@ def sample_scores(q: torch.Tensor, k: torch.Tensor, row0: int, n_rows: int, band
         if lse_given:
             raise ValueError("lse_given needs row_lse")
         row_lse = torch.empty((B, hq, max(n_rows, 1)), dtype=torch.float32, device=q.device)
+    elif (row_lse.dtype != torch.float32 or tuple(row_lse.shape) != (B, hq, n_rows)
+          or not row_lse.is_contiguous() or row_lse.device != q.device):
+        raise ValueError("row_lse must be a contiguous float32 [B, Hq, n_rows] tensor on q's device")
+    for t in (diag, vert, skip_cols):
+        if t is not None and t.device != q.device:
+            raise ValueError("scores and skip_cols must be on q's device")
     scale = 0.0 if softmax_scale is None else float(softmax_scale)
     ws_bytes = 0 if lse_given else int(_lib.sa_sample_scores_workspace(B, hq, row0, n_rows))
-    ws = torch.empty(max(ws_bytes, 8), dtype=torch.uint8, device=q.device) if not lse_given else None
-    _check(_lib.sa_sample_scores(q.data_ptr(), k.data_ptr(), B, hq, k.shape[1], S, d, dt, scale, row0, n_rows, band,
-                                 _ptr(skip_cols), int(bool(lse_given)), row_lse.data_ptr(), _ptr(ws), ws_bytes,
-                                 _ptr(diag), _ptr(vert), _stream(stream)), "sa_sample_scores")
-    _hold(ws, stream)
+    ws = torch.empty(max(ws_bytes, 8), dtype=torch.uint8, device=q.device) if ws_bytes else None
+    if ts != cur:
+        # the zeroed scores and the fresh buffers were made on the current stream: order the launch after them,
+        # and keep them from being reused before the launch stream is done with them
+        ts.wait_stream(cur)
+    _check(_lib.sa_sample_scores(q.data_ptr(), k.data_ptr(), B, hq, k.shape[1], S, d, dt, scale, row0, n_rows,
+                                 band, _ptr(skip_cols), int(bool(lse_given)), row_lse.data_ptr(), _ptr(ws),
+                                 ws_bytes, _ptr(diag), _ptr(vert), ts.cuda_stream), "sa_sample_scores")
+    if ts != cur:
+        for t in (ws, diag, vert, row_lse):
+            if t is not None:
+                t.record_stream(ts)
     return diag, vert, row_lse
 
 

@@ -96,6 +96,12 @@ sa_status sa_build_index(const sa_pattern_desc* desc, sa_index* idx, sa_index_si
   return hip_status(e);
 }
 
+size_t sa_build_index_workspace_bytes(const sa_pattern_desc* desc, int32_t row_block) {
+  (void)desc;
+  (void)row_block;
+  return 0;  // counts and kinds live in the index's own arrays; the scans run in place
+}
+
 sa_status sa_sparse_attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int32_t batch,
                                  int32_t hq, int32_t hkv, int32_t S, int32_t head_dim, int32_t dtype,
                                  float softmax_scale, const sa_index* idx, void* stream) {

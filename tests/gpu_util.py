@@ -89,3 +89,15 @@ def assert_lse(got, ref, tol, what=""):
     if fin.any():
         mx = float(np.abs(got[fin] - ref[fin]).max())
         assert mx <= tol, "%s lse max-abs %.3g" % (what, mx)
+
+
+_MAPS = {}
+
+
+def workload3_maps(layers=16, heads=32, n_avg=16):
+    """The capture workload's maps (16 layers x 32 heads of 512 x 512 at n_avg = 16 by default), drawn once
+    per process and shared by the tests that use them."""
+    key = (layers, heads, n_avg)
+    if key not in _MAPS:
+        _MAPS[key] = W.capture_maps(layers=layers, heads=heads, n_avg=n_avg)
+    return _MAPS[key]

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for f in ("sa_build_index", "sa_sparse_attn_prefill", "sa_sparse_attn_decode", "sa_attention_maps",
+    for f in ("sa_build_index", "sa_build_index_workspace_bytes", "sa_sparse_attn_prefill", "sa_sparse_attn_decode", "sa_attention_maps",
               "sa_pattern_capture", "sa_pattern_coverage", "sa_patterns_to_desc", "sa_sample_scores",
               "sa_sample_scores_workspace", "sa_select_patterns", "sa_calib_mfma_bf16", "sa_calib_gather", "sa_status_string", "sa_version"):
         assert f in names
@@ -35,6 +35,13 @@ def test_library_exports_every_declared_symbol(m):
     lib = C.CDLL(m.library_path())
     missing = [f for f in declared_functions() if not hasattr(lib, f)]
     assert not missing, missing
+
+
+def test_build_index_needs_no_workspace(m):
+    f = m.lib.sa_build_index_workspace_bytes
+    f.restype = C.c_size_t
+    f.argtypes = [C.c_void_p, C.c_int32]
+    assert f(None, 64) == 0 and f(None, 128) == 0
 
 
 def test_status_strings_and_version(m):

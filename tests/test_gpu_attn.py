@@ -13,12 +13,12 @@ import torch
 import oracle
 import workloads as W
 from gpu_util import (all_rows, assert_close_bf16, assert_close_f32, assert_lse, gather_lse, gather_rows, note,
-                      rows_of_blocks, sa, to_dev, widen)
+                      rows_of_blocks, sa, to_dev, widen, workload3_maps)
 
 pytestmark = pytest.mark.gpu
 
 
-def _run(desc, q, k, v, BM, rows, what, scale=None):
+def _run(desc, q, k, v, BM, rows, what, scale=None, want_lse=False):
     m = sa()
     B, hq, S, d = q.shape
     note("attn %s S=%d hq=%d hkv=%d d=%d BM=%d dtype=%s rows=%d" % (what, S, hq, k.shape[1], d, BM, q.dtype,
@@ -38,7 +38,7 @@ def _run(desc, q, k, v, BM, rows, what, scale=None):
         # bf16: the row sum is the sum of the bf16-rounded probabilities that also weight V, each
         # within 2^-9 relative of its exact value, so |lse - lse_exact| <= ln(1 + 2^-9) < 2^-8
         assert_lse(got_lse, ref_lse, 2.0 ** -8, what)
-    return o, ix
+    return (o, ix, lse) if want_lse else (o, ix)
 
 
 # ------------------------------------------------------------------ workload 1 (fp32) and its variants
@@ -183,22 +183,45 @@ def test_llama1b_like_small_full(S, BM):
 
 
 @pytest.mark.parametrize("BM", [64, 128])
-def test_llama1b_like_full_size_sampled(BM):
+def test_llama1b_like_full_size_every_row(BM):
+    """The 1B-like workload at its full size (S = 8192, 32/8 heads, d = 64): every row of every head."""
     desc = W.llama1b_like()
     q, k, v = W.qkv(2, 1, 32, 8, 8192, 64, "bf16")
-    rows = rows_of_blocks(1, 32, 8192, BM, 4, np.random.default_rng(2))
-    _run(desc, q, k, v, BM, rows, "1b-like")
+    _run(desc, q, k, v, BM, all_rows(1, 32, 8192), "1b-like")
 
 
 # ------------------------------------------------------------------ workload 3 (capture -> S=16384)
-def test_capture_extended_attention_sampled():
-    maps = W.capture_maps(layers=1, heads=32, n_avg=16)
+def _layer_desc(layer, S=16384):
+    """The kept sets of one layer of the capture workload (oracle capture of its 32 maps), extended to S."""
+    maps = workload3_maps()[32 * layer:32 * (layer + 1)]
     c = oracle.capture(maps)
-    diags, verts = oracle.extend(c["keep_diag"], c["keep_vert"], 16384)
-    desc = W.desc_from_lists(16384, diags, verts)
-    q, k, v = W.qkv(3, 1, 32, 8, 16384, 64, "bf16")
-    rows = rows_of_blocks(1, 32, 16384, 64, 3, np.random.default_rng(3))
-    _run(desc, q, k, v, 64, rows, "capture-16k")
+    diags, verts = oracle.extend(c["keep_diag"], c["keep_vert"], S)
+    return W.desc_from_lists(S, diags, verts)
+
+
+@pytest.mark.parametrize("layer", list(range(16)))
+def test_capture_extended_attention_layer(layer):
+    """The capture workload's attention run: one call per layer (32/8 heads, d = 64, S = 16384) with that
+    layer's 32 kept sets; every row of the first, the last and 3 seeded row blocks of every head, and
+    every row of every head for layer 0."""
+    S = 16384
+    desc = _layer_desc(layer, S)
+    q, k, v = W.qkv(3, 1, 32, 8, S, 64, "bf16", seed_extra=layer)
+    rows = all_rows(1, 32, S) if layer == 0 else rows_of_blocks(1, 32, S, 64, 3, np.random.default_rng([3, layer]))
+    _run(desc, q, k, v, 64, rows, "capture-16k layer %d" % layer)
+
+
+def _dense_cross_check(desc, q, k, v, o, lse, per_head, seed, what):
+    """The dense form of the oracle (every key of the row, masked logits -inf) on `per_head` seeded rows of
+    every head, against the same output: it shares no enumeration of retained keys with the sparse form."""
+    B, hq, S, _ = q.shape
+    rng = np.random.default_rng(seed)
+    rows = np.array([(0, h, i) for h in range(hq) for i in np.concatenate([[S - 1], rng.choice(S, per_head - 1,
+                                                                                                 replace=False)])],
+                    dtype=np.int32)
+    ref, ref_lse = oracle.attention_rows(desc, q, k, v, rows, mode=1)
+    assert_close_bf16(gather_rows(o, rows), ref, what + " (dense -inf oracle)")
+    assert_lse(gather_lse(lse, rows), ref_lse, 2.0 ** -8, what + " (dense -inf oracle)")
 
 
 # ------------------------------------------------------------------ workload 4 (8B-like, d=128)
@@ -210,11 +233,13 @@ def test_llama8b_like_small_full():
 
 
 def test_llama8b_like_full_size_sampled():
-    """Every row of the first, the last and 32 seeded row blocks of every head."""
+    """Every row of the first, the last and 32 seeded row blocks of every head; then the dense (-inf) form
+    of the oracle on 64 seeded rows of every head of the same output."""
     desc = W.llama8b_like()
     q, k, v = W.qkv(4, 1, 32, 8, 65536, 128, "bf16")
     rows = rows_of_blocks(1, 32, 65536, 64, 32, np.random.default_rng(4))
-    _run(desc, q, k, v, 64, rows, "8b-like")
+    o, _, lse = _run(desc, q, k, v, 64, rows, "8b-like", want_lse=True)
+    _dense_cross_check(desc, q, k, v, o, lse, 64, 44, "8b-like")
 
 
 # ------------------------------------------------------------------ workload 5 (stripes, S=131072)
@@ -227,11 +252,13 @@ def test_long_stripes_small_full(BM):
 
 
 def test_long_stripes_full_size_sampled():
-    """Every row of the first, the last and 16 seeded 128-row blocks of every head."""
+    """Every row of the first, the last and 32 seeded 128-row blocks of every head; then the dense (-inf)
+    form of the oracle on 64 seeded rows of every head of the same output."""
     desc = W.long_stripes()
     q, k, v = W.qkv(5, 1, 32, 8, 131072, 128, "bf16")
-    rows = rows_of_blocks(1, 32, 131072, 128, 16, np.random.default_rng(5))
-    _run(desc, q, k, v, 128, rows, "stripes-131k")
+    rows = rows_of_blocks(1, 32, 131072, 128, 32, np.random.default_rng(5))
+    o, _, lse = _run(desc, q, k, v, 128, rows, "stripes-131k", want_lse=True)
+    _dense_cross_check(desc, q, k, v, o, lse, 64, 55, "stripes-131k")
 
 
 # ------------------------------------------------------------------ the longest accepted sequence

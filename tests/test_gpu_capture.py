@@ -7,7 +7,7 @@ import torch
 import oracle
 import workloads as W
 from golden.load import arr, load
-from gpu_util import assert_close_bf16, note, rows_of_blocks, sa, to_dev
+from gpu_util import assert_close_bf16, note, rows_of_blocks, sa, to_dev, workload3_maps
 
 pytestmark = pytest.mark.gpu
 
@@ -33,7 +33,19 @@ def test_capture_golden_example():
 
 
 @pytest.mark.parametrize("scope", [0, 1])
-@pytest.mark.parametrize("eps", [1e-8, 1e-10])
+def test_capture_workload_all_512_maps(scope):
+    """The whole capture workload: 16 layers x 32 heads of 512 x 512 maps at n_avg = 16, in one call,
+    keep flags, hit counts and the true mask bit for bit."""
+    note("capture all 512 workload maps scope=%d" % scope)
+    got, ref = _capture_both(workload3_maps(), norm_scope=scope)
+    kept = ref["keep_diag"].sum() + ref["keep_vert"].sum()
+    assert kept > 0
+    note("kept patterns: %d diagonals, %d verticals over 512 maps"
+         % (int(ref["keep_diag"].sum()), int(ref["keep_vert"].sum())))
+
+
+@pytest.mark.parametrize("scope", [0, 1])
+@pytest.mark.parametrize("eps", [1e-10])
 def test_capture_workload_maps(scope, eps):
     note("capture scope=%d eps=%g" % (scope, eps))
     maps = W.capture_maps(layers=2, heads=32, n_avg=16)

@@ -110,9 +110,16 @@ def test_select_edge_cases():
 
 @pytest.mark.parametrize("alpha_cols,alpha", [(0.8, 0.9), (0.9, 0.97)])
 def test_runtime_capture_pipeline(alpha_cols, alpha):
-    """Two-stage per-input capture on the GPU (columns to alpha_cols, then diagonals on what the
-    columns leave, to alpha), then extension, index and attention; against the oracle's two stages
-    and attention."""
+    """Two-stage per-input capture (columns to alpha_cols, then diagonals on what the columns leave, to
+    alpha), then extension, index and attention, against the oracle on EVERY head:
+      stage 1  GPU column scores and keep flags vs the oracle's (flags on every decision that no score
+               within the error bound can flip);
+      stage 2  run on the oracle's stage-1 flags on both sides, so that every head is scored on the same
+               uncovered mass: GPU diagonal scores and flags vs the oracle's;
+      GPU-only pipeline  its column flags may differ from the oracle's only on decisions the bound calls
+               unsure; where they are equal its diagonal flags are compared as in stage 2;
+      attention  the index and attention of the oracle's final mask on every head, every row of the first
+               and the last row block and 24 seeded rows per head."""
     m = sa()
     B, hq, hkv, S, d, n, band = 1, 8, 2, 4096, 128, 64, 64
     q, k = W.runtime_qk(83, B, hq, hkv, S, d, "bf16")
@@ -120,41 +127,66 @@ def test_runtime_capture_pipeline(alpha_cols, alpha):
     qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
     row0 = S - n
     note("runtime capture pipeline alpha_cols=%g alpha=%g" % (alpha_cols, alpha))
+    rkd, rkv, rv, rd = oracle.runtime_capture(q, k, row0, n, alpha_cols, alpha, band)
+    assert (rkd.sum(1) > band).all() and (rkv.sum(1) > 0).all()    # both stages keep patterns
+
+    # stage 1 on the GPU
     _, vs, lse = m.sample_scores(qd, kd, row0, n, band=band, families=(False, True))
     keep_v = m.select_patterns(vs, alpha_cols, B * n)
+    # stage 2 on the oracle's column flags (both sides score the same uncovered mass on every head)
+    ds_o, _, _ = m.sample_scores(qd, kd, row0, n, band=band, skip_cols=torch.from_numpy(rkv).cuda(), row_lse=lse,
+                                 lse_given=True, families=(True, False))
+    keep_d_o = m.select_patterns(ds_o, alpha, B * n, band=band)
+    # the GPU-only pipeline: stage 2 on the GPU's own column flags
     ds, _, _ = m.sample_scores(qd, kd, row0, n, band=band, skip_cols=keep_v, row_lse=lse, lse_given=True,
                                families=(True, False))
     keep_d = m.select_patterns(ds, alpha, B * n, band=band)
-    pat = m.patterns_to_desc(keep_d, keep_v, S)
-    ix = m.build_index(pat, 64)
-    o = m.sparse_attn_prefill(qd, kd, vd, ix)
     torch.cuda.synchronize()
 
-    rkd, rkv, rv, rd = oracle.runtime_capture(q, k, row0, n, alpha_cols, alpha, band)
-    gv, gd = keep_v.cpu().numpy(), keep_d.cpu().numpy()
-    assert (rkd.sum(1) > band).all() and (rkv.sum(1) > 0).all()    # both stages keep patterns
+    _scores_close(vs, rv, "stage-1 column scores")
+    _scores_close(ds_o, rd, "stage-2 diagonal scores")
+    gv, gd_o, gd = keep_v.cpu().numpy(), keep_d_o.cpu().numpy(), keep_d.cpu().numpy()
     sure_v = certain_selection(rv, REL, ABS, alpha_cols, B * n)
-    np.testing.assert_array_equal(gv[sure_v], rkv[sure_v])
-    assert sure_v.mean() > 0.99
-    # stage 2 runs on the same uncovered mass where the column flags came out equal (the unsure
-    # decisions usually fall the same way); compare it on those heads
-    heads = [h for h in range(hq) if np.array_equal(gv[h], rkv[h])]
-    assert len(heads) >= hq - 2, heads
     sure_d = certain_selection(rd, REL, ABS, alpha, B * n, band=band)
-    for h in heads:
+    assert sure_v.mean() > 0.99 and sure_d.mean() > 0.95
+    np.testing.assert_array_equal(gv[sure_v], rkv[sure_v])          # every head
+    np.testing.assert_array_equal(gd_o[sure_d], rkd[sure_d])        # every head
+    same_v = [h for h in range(hq) if np.array_equal(gv[h], rkv[h])]
+    for h in same_v:
         np.testing.assert_array_equal(gd[h][sure_d[h]], rkd[h][sure_d[h]])
-    heads = [h for h in heads if np.array_equal(gd[h], rkd[h])]
-    assert len(heads) >= hq - 2, heads
-    note("heads with equal masks: %s; unsure column decisions %d, diagonal %d"
-         % (heads, int((~sure_v).sum()), int((~sure_d).sum())))
-    # on those heads the masks are equal: attention on the oracle's mask, sampled rows
+    note("unsure decisions: columns %d, diagonals %d; heads with equal column flags %s"
+         % (int((~sure_v).sum()), int((~sure_d).sum()), same_v))
+
+    # attention on the oracle's mask, every head
     desc = W.desc_from_lists(S, [np.nonzero(x)[0] for x in rkd], [np.nonzero(x)[0] for x in rkv])
-    pc = ix.pair_count.cpu().numpy()
-    rpc = oracle.pair_count(desc)
-    assert all(pc[h] == rpc[h] for h in heads)
+    ix = m.build_index(m.DevicePatterns.from_host(desc), 64)
+    o = m.sparse_attn_prefill(qd, kd, vd, ix)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ix.pair_count.cpu().numpy(), oracle.pair_count(desc))
     rng = np.random.default_rng(5)
-    rows = np.array([(0, h, i) for h in heads for i in np.concatenate([[0, S - 1], rng.choice(S, 24)])], np.int32)
+    rows = np.array([(0, h, i) for h in range(hq)
+                     for i in np.concatenate([np.arange(64), np.arange(S - 64, S), rng.choice(S, 24)])], np.int32)
     ref, _ = oracle.attention_rows(desc, q, k, v, rows)
     idx = torch.from_numpy(rows.astype(np.int64)).cuda()
     got = o[idx[:, 0], idx[:, 1], idx[:, 2]].float().cpu().numpy().astype(np.float64)
     assert_close_bf16(got, ref, "runtime pipeline attention")
+
+
+def test_sample_scores_on_a_side_stream():
+    """Scores made on another stream than the current one (the zeroed outputs are ordered before the
+    accumulating kernel) equal those made on the current stream."""
+    m = sa()
+    B, hq, hkv, S, d = 1, 4, 2, 1500, 64
+    q, k, _ = W.qkv(84, B, hq, hkv, S, d, "bf16")
+    qd, kd = to_dev(q), to_dev(k)
+    note("sample scores side stream")
+    d1, v1, l1 = m.sample_scores(qd, kd, 1400, 100, band=8)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    torch.cuda._sleep(20000000)          # the current stream is still busy when the side launch is queued
+    d2, v2, l2 = m.sample_scores(qd, kd, 1400, 100, band=8, stream=side)
+    side.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(d1, d2) and torch.equal(v1, v2) and torch.equal(l1, l2)
+    with pytest.raises(ValueError):
+        m.sample_scores(qd, kd, 1400, 100, row_lse=torch.zeros(1, hq, 99, device="cuda"), lse_given=True)

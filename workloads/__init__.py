@@ -34,6 +34,7 @@ draw the same structure at small or ragged sizes.
 """
 from __future__ import annotations
 
+import os
 from dataclasses import dataclass, field
 from typing import List, Optional, Sequence
 
@@ -179,30 +180,43 @@ def llama1b_like(S: int = 8192, H: int = 32) -> PatternDesc:
 
 
 def capture_maps(layers: int = 16, heads: int = 32, L: int = 512, n_avg: int = 16,
-                 layer_offset: int = 0) -> np.ndarray:
+                 layer_offset: int = 0, threads: Optional[int] = None) -> np.ndarray:
     """Workload 3 maps: float32 [layers*heads, L, L] averaged causal row-softmaxes.
 
     Logits = N(0,1) + 3.0*[i-j < 32] + 3.0*[j < 4] + 2.0*[j in 4 seeded columns];
-    positions j > i carry no weight.  Computed in float64, stored float32.
+    positions j > i carry no weight.  Computed in float64, stored float32.  Each
+    map has its own seed, so the maps are drawn on a thread pool (numpy releases
+    the interpreter lock in its array loops) with the same values as in series.
     """
     i = np.arange(L)[:, None]
     j = np.arange(L)[None, :]
     causal = j <= i
     base = 3.0 * ((i - j) < 32) + 3.0 * (j < 4)
     out = np.empty((layers * heads, L, L), dtype=np.float32)
-    for l in range(layers):
-        for h in range(heads):
-            rng = np.random.default_rng([3, layer_offset + l, h])
-            cols = rng.choice(np.arange(4, L), size=4, replace=False)
-            boost = base + 2.0 * np.isin(j, cols)
-            acc = np.zeros((L, L))
-            for _ in range(n_avg):
-                z = rng.standard_normal((L, L)) + boost
-                z = np.where(causal, z, -np.inf)
-                z = z - z.max(axis=1, keepdims=True)
-                e = np.exp(z)
-                acc += e / e.sum(axis=1, keepdims=True)
-            out[l * heads + h] = (acc / n_avg).astype(np.float32)
+
+    def one(m):
+        l, h = divmod(m, heads)
+        rng = np.random.default_rng([3, layer_offset + l, h])
+        cols = rng.choice(np.arange(4, L), size=4, replace=False)
+        boost = base + 2.0 * np.isin(j, cols)
+        acc = np.zeros((L, L))
+        for _ in range(n_avg):
+            z = rng.standard_normal((L, L)) + boost
+            z = np.where(causal, z, -np.inf)
+            z = z - z.max(axis=1, keepdims=True)
+            e = np.exp(z)
+            acc += e / e.sum(axis=1, keepdims=True)
+        out[m] = (acc / n_avg).astype(np.float32)
+
+    n = layers * heads
+    workers = threads or min(16, os.cpu_count() or 1, n)
+    if workers <= 1:
+        for m in range(n):
+            one(m)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(one, range(n)))
     return out
 
 
