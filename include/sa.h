@@ -327,6 +327,30 @@ sa_status sa_sample_scores(const void* q, const void* k, int32_t batch, int32_t 
 size_t sa_sample_scores_workspace(int32_t batch, int32_t hq, int32_t row0, int32_t n_rows);
 
 /*
+ * sa_sample_scores_noalloc: for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Computes
+ * exactly what sa_sample_scores computes, with the same arguments minus the workspace,
+ * and the same kernels: the LSE pass keeps its per-split row statistics in a static
+ * device array of the library, 16 MiB (16777216 bytes) per GPU, which each GPU the
+ * library runs on holds until the process ends.  The call allocates nothing and calls
+ * no allocating routine; the caller still owns q, k, skip_cols, row_lse and the scores.
+ * Its first call on a device (with that device current) looks up the array's address
+ * on that device once.
+ *   The scratch need, batch * hq * n_rows * ceil((row0 + n_rows) / 256) * 8 bytes (as
+ *   sa_sample_scores_workspace reports), must not exceed 16 MiB: else SA_ERR_CAPACITY
+ *   and nothing is launched (e.g. 32 heads, 128 sampled rows, S up to 131072 fit).
+ *   With lse_given nonzero no scratch is used.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU (on two
+ * streams, or from two host threads) race and may corrupt each other's row LSE; order
+ * them.  The array needs no clearing (every slot a call reads, that call writes first).
+ * Errors: as sa_sample_scores (SA_ERR_CAPACITY: the scratch need is above 16 MiB).
+ */
+sa_status sa_sample_scores_noalloc(const void* q, const void* k, int32_t batch, int32_t hq, int32_t hkv, int32_t S,
+                                   int32_t head_dim, int32_t dtype, float softmax_scale, int32_t row0, int32_t n_rows,
+                                   int32_t band, const uint8_t* skip_cols, int32_t lse_given, float* row_lse,
+                                   int64_t* diag_score, int64_t* vert_score, void* stream);
+
+/*
  * sa_select_patterns [SampleAttention, abstract: adaptive, head-specific selection,
  * near-lossless; the rule is this library's reading]: for one pattern family, per
  * head h, scores v[0..S) as sa_sample_scores makes them over `rows` sampled row

@@ -81,6 +81,9 @@ def _load():
     lib.sa_sample_scores.restype = C.c_int32
     lib.sa_sample_scores.argtypes = [C.c_void_p, C.c_void_p] + [C.c_int32] * 6 + [C.c_float] + [C.c_int32] * 3 + \
         [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_size_t] + [C.c_void_p] * 2 + [C.c_void_p]
+    lib.sa_sample_scores_noalloc.restype = C.c_int32
+    lib.sa_sample_scores_noalloc.argtypes = [C.c_void_p, C.c_void_p] + [C.c_int32] * 6 + [C.c_float] + \
+        [C.c_int32] * 3 + [C.c_void_p, C.c_int32, C.c_void_p] + [C.c_void_p] * 2 + [C.c_void_p]
     lib.sa_build_index_workspace_bytes.restype = C.c_size_t
     lib.sa_build_index_workspace_bytes.argtypes = [C.c_void_p, C.c_int32]
     lib.sa_sample_scores_workspace.restype = C.c_size_t
@@ -403,12 +406,14 @@ def pattern_coverage(maps: torch.Tensor, keep_diag: torch.Tensor, keep_vert: tor
 def sample_scores(q: torch.Tensor, k: torch.Tensor, row0: int, n_rows: int, band: int = 0,
                   skip_cols: Optional[torch.Tensor] = None, softmax_scale: Optional[float] = None, scores=None,
                   row_lse: Optional[torch.Tensor] = None, lse_given: bool = False, families=(True, True),
-                  stream=None):
+                  no_alloc: bool = False, stream=None):
     """sa_sample_scores: adds the attention mass of query rows row0 .. row0+n_rows-1 on the pairs outside
     the window (i - j >= band) and off `skip_cols` onto per-head diagonal and vertical scores (int64
     [Hq, S] each, fixed point 2^-32).  `scores` = (diag, vert) to accumulate into, new zeroed arrays
     otherwise (only the families flagged in `families` = (diagonals, verticals); None for the other);
-    `row_lse` [B, Hq, n_rows] is written, or read when lse_given.  Returns (diag, vert, row_lse)."""
+    `row_lse` [B, Hq, n_rows] is written, or read when lse_given.  no_alloc: the library's
+    allocation-free entry point (its scratch is a static 16 MiB device array; the outputs are still
+    made here unless passed in).  Returns (diag, vert, row_lse)."""
     if q.dtype == torch.bfloat16:
         dt = SA_DTYPE_BF16
     elif q.dtype == torch.float32:
@@ -446,15 +451,20 @@ def sample_scores(q: torch.Tensor, k: torch.Tensor, row0: int, n_rows: int, band
         if t is not None and t.device != q.device:
             raise ValueError("scores and skip_cols must be on q's device")
     scale = 0.0 if softmax_scale is None else float(softmax_scale)
-    ws_bytes = 0 if lse_given else int(_lib.sa_sample_scores_workspace(B, hq, row0, n_rows))
+    ws_bytes = 0 if (lse_given or no_alloc) else int(_lib.sa_sample_scores_workspace(B, hq, row0, n_rows))
     ws = torch.empty(max(ws_bytes, 8), dtype=torch.uint8, device=q.device) if ws_bytes else None
     if ts != cur:
         # the zeroed scores and the fresh buffers were made on the current stream: order the launch after them,
         # and keep them from being reused before the launch stream is done with them
         ts.wait_stream(cur)
-    _check(_lib.sa_sample_scores(q.data_ptr(), k.data_ptr(), B, hq, k.shape[1], S, d, dt, scale, row0, n_rows,
-                                 band, _ptr(skip_cols), int(bool(lse_given)), row_lse.data_ptr(), _ptr(ws),
-                                 ws_bytes, _ptr(diag), _ptr(vert), ts.cuda_stream), "sa_sample_scores")
+    if no_alloc:
+        _check(_lib.sa_sample_scores_noalloc(q.data_ptr(), k.data_ptr(), B, hq, k.shape[1], S, d, dt, scale, row0,
+                                             n_rows, band, _ptr(skip_cols), int(bool(lse_given)), row_lse.data_ptr(),
+                                             _ptr(diag), _ptr(vert), ts.cuda_stream), "sa_sample_scores_noalloc")
+    else:
+        _check(_lib.sa_sample_scores(q.data_ptr(), k.data_ptr(), B, hq, k.shape[1], S, d, dt, scale, row0, n_rows,
+                                     band, _ptr(skip_cols), int(bool(lse_given)), row_lse.data_ptr(), _ptr(ws),
+                                     ws_bytes, _ptr(diag), _ptr(vert), ts.cuda_stream), "sa_sample_scores")
     if ts != cur:
         for t in (ws, diag, vert, row_lse):
             if t is not None:

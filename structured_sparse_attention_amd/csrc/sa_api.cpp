@@ -167,11 +167,15 @@ size_t sa_sample_scores_workspace(int32_t batch, int32_t hq, int32_t row0, int32
   return sa::sample_workspace_bytes(batch, hq, row0, n_rows);
 }
 
-sa_status sa_sample_scores(const void* q, const void* k, int32_t batch, int32_t hq, int32_t hkv, int32_t S,
-                           int32_t head_dim, int32_t dtype, float softmax_scale, int32_t row0, int32_t n_rows,
-                           int32_t band, const uint8_t* skip_cols, int32_t lse_given, float* row_lse,
-                           void* workspace, size_t workspace_bytes, int64_t* diag_score, int64_t* vert_score,
-                           void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the two sample-scores entry points (everything but the workspace).
+sa_status sample_args_ok(const void* q, const void* k, int32_t batch, int32_t hq, int32_t hkv, int32_t S,
+                         int32_t head_dim, int32_t dtype, float softmax_scale, int32_t row0, int32_t n_rows,
+                         int32_t band, const float* row_lse, const int64_t* diag_score, const int64_t* vert_score,
+                         float* scale_out) {
   if (!q || !k || !row_lse || (!diag_score && !vert_score)) return SA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k)) return SA_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(diag_score) | reinterpret_cast<uintptr_t>(vert_score)) & 7u) return SA_ERR_INVALID_ARG;
@@ -180,10 +184,6 @@ sa_status sa_sample_scores(const void* q, const void* k, int32_t batch, int32_t 
   if (head_dim != 64 && head_dim != 128) return SA_ERR_UNSUPPORTED;
   if (row0 < 0 || n_rows < 1 || (int64_t)row0 + n_rows > S) return SA_ERR_INVALID_ARG;
   if (n_rows > sa::kMaxSampleRows || (int64_t)batch * n_rows > sa::kMaxSampleRowSeqs) return SA_ERR_UNSUPPORTED;
-  if (!lse_given) {
-    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 7u)) return SA_ERR_INVALID_ARG;
-    if (workspace_bytes < sa::sample_workspace_bytes(batch, hq, row0, n_rows)) return SA_ERR_CAPACITY;
-  }
   const int64_t ntile = ((int64_t)row0 + n_rows - 1) / 64 + 1;
   const int64_t nsplit = ((int64_t)row0 + n_rows - 1) / 256 + 1;
   if ((int64_t)batch * hq * nsplit > 0x7fffffffLL || (int64_t)hq * ntile > 0x7fffffffLL ||
@@ -191,8 +191,47 @@ sa_status sa_sample_scores(const void* q, const void* k, int32_t batch, int32_t 
     return SA_ERR_UNSUPPORTED;
   const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf((float)head_dim);
   if (!isfinite(scale)) return SA_ERR_INVALID_ARG;
+  *scale_out = scale;
+  return SA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sa_status sa_sample_scores(const void* q, const void* k, int32_t batch, int32_t hq, int32_t hkv, int32_t S,
+                           int32_t head_dim, int32_t dtype, float softmax_scale, int32_t row0, int32_t n_rows,
+                           int32_t band, const uint8_t* skip_cols, int32_t lse_given, float* row_lse,
+                           void* workspace, size_t workspace_bytes, int64_t* diag_score, int64_t* vert_score,
+                           void* stream) {
+  float scale = 0.0f;
+  const sa_status st = sample_args_ok(q, k, batch, hq, hkv, S, head_dim, dtype, softmax_scale, row0, n_rows, band,
+                                      row_lse, diag_score, vert_score, &scale);
+  if (st != SA_OK) return st;
+  if (!lse_given) {
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 7u)) return SA_ERR_INVALID_ARG;
+    if (workspace_bytes < sa::sample_workspace_bytes(batch, hq, row0, n_rows)) return SA_ERR_CAPACITY;
+  }
   return hip_status(sa::launch_sample_scores(q, k, batch, hq, hkv, S, head_dim, dtype, scale, row0, n_rows, band,
                                              skip_cols, lse_given != 0, row_lse, workspace, diag_score, vert_score,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+sa_status sa_sample_scores_noalloc(const void* q, const void* k, int32_t batch, int32_t hq, int32_t hkv, int32_t S,
+                                   int32_t head_dim, int32_t dtype, float softmax_scale, int32_t row0, int32_t n_rows,
+                                   int32_t band, const uint8_t* skip_cols, int32_t lse_given, float* row_lse,
+                                   int64_t* diag_score, int64_t* vert_score, void* stream) {
+  float scale = 0.0f;
+  const sa_status st = sample_args_ok(q, k, batch, hq, hkv, S, head_dim, dtype, softmax_scale, row0, n_rows, band,
+                                      row_lse, diag_score, vert_score, &scale);
+  if (st != SA_OK) return st;
+  void* ws = nullptr;
+  if (!lse_given) {
+    if (sa::sample_workspace_bytes(batch, hq, row0, n_rows) > sa::kSampleStaticScratchBytes) return SA_ERR_CAPACITY;
+    if (sa::sample_static_scratch(&ws) != hipSuccess) return SA_ERR_HIP;
+  }
+  return hip_status(sa::launch_sample_scores(q, k, batch, hq, hkv, S, head_dim, dtype, scale, row0, n_rows, band,
+                                             skip_cols, lse_given != 0, row_lse, ws, diag_score, vert_score,
                                              static_cast<hipStream_t>(stream)));
 }
 

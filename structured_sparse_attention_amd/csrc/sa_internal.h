@@ -56,6 +56,10 @@ hipError_t launch_capture(const float* maps, int32_t n_maps, int32_t L, double l
 hipError_t launch_attention_maps(const void* q, const void* k, int32_t batch, int32_t hq, int32_t hkv, int32_t L,
                                  int32_t head_dim, int32_t dtype, float scale, float* maps, hipStream_t stream);
 size_t sample_workspace_bytes(int32_t batch, int32_t hq, int32_t row0, int32_t n_rows);
+// Static scratch of the allocation-free sample-scores entry point (one per GPU), and its device
+// address on the current device (looked up once per device).
+constexpr size_t kSampleStaticScratchBytes = (size_t)16 << 20;
+hipError_t sample_static_scratch(void** out);
 hipError_t launch_sample_scores(const void* q, const void* k, int32_t batch, int32_t hq, int32_t hkv, int32_t S,
                                 int32_t head_dim, int32_t dtype, float scale, int32_t row0, int32_t n_rows,
                                 int32_t band, const uint8_t* skip_cols, bool lse_given, float* row_lse, void* workspace,

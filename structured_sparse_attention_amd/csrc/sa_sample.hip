@@ -34,6 +34,8 @@
 //   pass a mass histogram of the scores inside the current bucket.
 #include <type_traits>
 
+#include <mutex>
+
 #include "sa_internal.h"
 
 namespace sa {
@@ -465,6 +467,37 @@ hipError_t launch_sample_t(const void* q, const void* k, int32_t B, int32_t hq, 
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// Scratch for callers that cannot allocate: the per-split row statistics of the LSE
+// pass in a static device array, one copy per GPU, held until the process ends.  Its
+// device address is taken once per device (hipGetSymbolAddress with that device
+// current) and passed to the kernels like a caller's workspace; the array's name is a
+// host-side stand-in and is never handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[kSampleStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t sample_static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 size_t sample_workspace_bytes(int32_t batch, int32_t hq, int32_t row0, int32_t n_rows) {
   return (size_t)batch * hq * n_rows * sample_splits(row0, n_rows) * sizeof(float2);
