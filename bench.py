@@ -71,15 +71,15 @@ def setup(cfg_id, B=1):
     return desc, (q, k, v), pat, (qd, kd, vd), ix
 
 
-def time_attention_only(sa, torch, qkv_dev, ix, reps, ws=None):
+def time_attention_only(sa, torch, qkv_dev, ix, reps):
     qd, kd, vd = qkv_dev
     o = torch.empty_like(qd)
-    sa.sparse_attn_prefill(qd, kd, vd, ix, out=o, workspace=ws)
+    sa.sparse_attn_prefill(qd, kd, vd, ix, out=o)
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for a, b in evs:
         a.record()
-        sa.sparse_attn_prefill(qd, kd, vd, ix, out=o, workspace=ws)
+        sa.sparse_attn_prefill(qd, kd, vd, ix, out=o)
         b.record()
     torch.cuda.synchronize()
     return float(np.mean([a.elapsed_time(b) for a, b in evs]))
@@ -385,8 +385,6 @@ def main():
                     help="only run the capture sensitivity sweep (PCL, lambda, tau, mu) and print it as JSON")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one device copy of 1 GiB (reference for hardware byte counters)")
-    ap.add_argument("--slice", action="store_true",
-                    help="run the attention with a workspace (key-sliced schedule) instead of one workgroup per item")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path (the work would shard by "
@@ -407,8 +405,6 @@ def main():
     pairs = ix.total_pairs
     B = qd.shape[0]
     flops = 4.0 * cfg["d"] * pairs * B
-    # the key-sliced schedule's workspace (work plan + partial states), allocated once, outside the timing
-    ws = sa.prefill_workspace(qd, kd, ix) if args.slice else None
 
     def step(ev=None):
         if ev is not None:
@@ -416,7 +412,7 @@ def main():
         sa.refill_index(pat, ix)
         if ev is not None:
             ev[1].record()
-        sa.sparse_attn_prefill(qd, kd, vd, ix, out=o, workspace=ws)
+        sa.sparse_attn_prefill(qd, kd, vd, ix, out=o)
         if ev is not None:
             ev[2].record()
 
@@ -436,22 +432,16 @@ def main():
     assert int(ix.status.item()) == 0
     log("step %.3f ms (index %.3f ms, attention %.3f ms), %d retained pairs" % (ms_per_step, index_ms, attn_ms,
                                                                               pairs))
-    sliced_units = None
-    if ws is not None:
-        sliced_units = int(ws[:96].view(torch.int32)[16:24].sum().item())
-        log("key-sliced schedule: %d units for %d items, workspace %.2f GB" % (
-            sliced_units, B * cfg["hq"] * ix.n_row_blocks, ws.numel() / 1e9))
 
     prefill_ms = {str(cfg["S"]): attn_ms}
     extras = {}
     if not args.no_extras:
-        del o, qd, kd, vd, qkv_dev, ws
+        del o, qd, kd, vd, qkv_dev
         torch.cuda.empty_cache()
         other = 5 if args.config != 5 else 4
         ocfg = WORKLOADS[other]
         _, _, opat, oqkv, oix = setup(other)
-        ows = sa.prefill_workspace(oqkv[0], oqkv[1], oix) if args.slice else None
-        oms = time_attention_only(sa, torch, oqkv, oix, reps=5, ws=ows)
+        oms = time_attention_only(sa, torch, oqkv, oix, reps=5)
         prefill_ms[str(ocfg["S"])] = oms
         extras["other_workload"] = dict(workload=ocfg["name"], S=ocfg["S"], attn_ms=oms,
                                         effective_tflops=4.0 * ocfg["d"] * oix.total_pairs / (oms * 1e-3) / 1e12,
@@ -511,8 +501,6 @@ def main():
         "cpu_baseline": None if cpu is None else {k2: cpu[k2] for k2 in ("value", "unit", "cores", "kind", "sample")},
         "prefill_attn_ms": prefill_ms,
         "index_build_ms": index_ms,
-        "schedule": "one workgroup per item" if sliced_units is None else
-                    "key-sliced (%d units for %d items)" % (sliced_units, B * cfg["hq"] * ix.n_row_blocks),
         "retained_pairs": pairs,
         "effective_flops_per_step": flops,
     }

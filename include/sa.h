@@ -197,44 +197,14 @@ size_t sa_build_index_workspace_bytes(const sa_pattern_desc* desc, int32_t row_b
  *   query head h reads kv head h / (hq / hkv) (hq % hkv == 0).
  *   softmax_scale <= 0 selects 1 / sqrt(head_dim).
  *   head_dim in {64, 128}.  idx: built for this S with n_heads == hq.
- *   workspace  NULL, or device scratch of workspace_bytes bytes, 256-byte aligned,
- *         owned by the caller, not shared with a concurrent call.  With bf16 and
- *         row block 64, a workspace of at least
- *         sa_sparse_attn_prefill_workspace_bytes(...) bytes selects the key-sliced
- *         schedule: the key axis is cut into 8 slices (one per XCD, ceil(S/8)
- *         rounded up to 64 keys each); a (batch, head, row block) item with at
- *         least 512 gathered columns spread over two or more slices runs as one
- *         unit per slice holding its keys, each unit on the XCD whose L2 holds that
- *         slice of the kv head, and the units' partial (max, sum, accumulator)
- *         states are merged by the last unit of the item to finish, in slice order,
- *         so the result is deterministic.  Other configurations ignore it (their
- *         size is 0); a NULL workspace runs one workgroup per item.  The result
- *         agrees with the one-workgroup-per-item schedule to rounding (the sums
- *         are split at slice boundaries).  Between calls the workspace needs no
- *         clearing (each call clears what it counts with).
  * bf16: bf16 MFMA products with fp32 accumulation, fp32 online softmax, probabilities
- * rounded to bf16 for the P.V product, output rounded to bf16 (nearest even); merged
- * partial states are fp32.
+ * rounded to bf16 for the P.V product, output rounded to bf16 (nearest even).
  * f32: fp32 MFMA throughout.
- * Errors: SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_CAPACITY (a workspace smaller
- * than the size query), SA_ERR_HIP.
+ * Errors: SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_HIP.
  */
 sa_status sa_sparse_attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
                                  int32_t batch, int32_t hq, int32_t hkv, int32_t S, int32_t head_dim,
-                                 int32_t dtype, float softmax_scale, const sa_index* idx, void* workspace,
-                                 size_t workspace_bytes, void* stream);
-
-/*
- * sa_sparse_attn_prefill_workspace_bytes (host): bytes of workspace that select the
- * key-sliced schedule of sa_sparse_attn_prefill for these sizes; 0 when that
- * configuration has no such schedule (fp32, row block 128) or the sizes are invalid.
- * It holds the work plan (per-XCD unit queues, about 80 bytes per item and slice)
- * and one partial state per (item, slice up to the item's last row):
- * 64 * (head_dim + 8) * 4 bytes each (about 4.9 GB at batch 1, 32 heads, S = 65536,
- * head_dim 128).
- */
-size_t sa_sparse_attn_prefill_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv, int32_t S, int32_t head_dim,
-                                              int32_t dtype, int32_t row_block);
+                                 int32_t dtype, float softmax_scale, const sa_index* idx, void* stream);
 
 /*
  * sa_sparse_attn_decode: one new query row per sequence against a K/V cache

@@ -18,8 +18,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-__all__ = ["SAError", "DevicePatterns", "SparseIndex", "build_index", "sparse_attn_prefill", "prefill_workspace",
-           "prefill_workspace_bytes", "sparse_attn_decode",
+__all__ = ["SAError", "DevicePatterns", "SparseIndex", "build_index", "sparse_attn_prefill", "sparse_attn_decode",
            "attention_maps", "pattern_capture", "pattern_coverage", "patterns_to_desc", "sample_scores",
            "select_patterns", "calib_mfma_bf16", "calib_gather", "library_path", "version", "lib"]
 
@@ -70,9 +69,7 @@ def _load():
     lib.sa_build_index.argtypes = [C.POINTER(_Desc), C.POINTER(_Index), C.POINTER(_Sizes), C.c_int32, C.c_void_p]
     lib.sa_sparse_attn_prefill.restype = C.c_int32
     lib.sa_sparse_attn_prefill.argtypes = [C.c_void_p] * 4 + [C.c_void_p] + [C.c_int32] * 6 + \
-        [C.c_float, C.POINTER(_Index), C.c_void_p, C.c_size_t, C.c_void_p]
-    lib.sa_sparse_attn_prefill_workspace_bytes.restype = C.c_size_t
-    lib.sa_sparse_attn_prefill_workspace_bytes.argtypes = [C.c_int32] * 7
+        [C.c_float, C.POINTER(_Index), C.c_void_p]
     lib.sa_sparse_attn_decode.restype = C.c_int32
     lib.sa_sparse_attn_decode.argtypes = [C.c_void_p] * 6 + [C.c_int32] * 6 + [C.c_float, C.POINTER(_Index),
                                                                                  C.c_void_p]
@@ -280,28 +277,10 @@ def refill_index(patterns: DevicePatterns, ix: SparseIndex, stream=None):
     _check(_lib.sa_build_index(C.byref(d), C.byref(c), None, 0, _stream(stream)), "sa_build_index")
 
 
-def prefill_workspace_bytes(batch: int, hq: int, hkv: int, S: int, head_dim: int, dtype: torch.dtype,
-                            row_block: int) -> int:
-    """sa_sparse_attn_prefill_workspace_bytes: bytes of workspace that select the key-sliced schedule (0: the
-    configuration has none)."""
-    dt = SA_DTYPE_BF16 if dtype == torch.bfloat16 else SA_DTYPE_F32
-    return int(_lib.sa_sparse_attn_prefill_workspace_bytes(batch, hq, hkv, S, head_dim, dt, row_block))
-
-
-def prefill_workspace(q: torch.Tensor, k: torch.Tensor, index: "SparseIndex") -> Optional[torch.Tensor]:
-    """A workspace tensor (uint8, on q's device) for the key-sliced schedule of these shapes, or None when the
-    configuration has no such schedule.  Reusable across calls of the same shapes on one stream."""
-    B, hq, S, d = q.shape
-    n = prefill_workspace_bytes(B, hq, k.shape[1], S, d, q.dtype, index.row_block)
-    return torch.empty(n, dtype=torch.uint8, device=q.device) if n > 0 else None
-
-
 def sparse_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: SparseIndex,
                         softmax_scale: Optional[float] = None, return_lse: bool = False,
-                        out: Optional[torch.Tensor] = None, workspace=None, stream=None):
-    """sa_sparse_attn_prefill: q [B,Hq,S,d], k/v [B,Hkv,S,d] (bf16 or fp32, contiguous, on the GPU).
-    workspace: None (one workgroup per item), a uint8 device tensor from prefill_workspace (key-sliced
-    schedule), or True (such a tensor made for this call)."""
+                        out: Optional[torch.Tensor] = None, stream=None):
+    """sa_sparse_attn_prefill: q [B,Hq,S,d], k/v [B,Hkv,S,d] (bf16 or fp32, contiguous, on the GPU)."""
     if q.dtype == torch.bfloat16:
         dt = SA_DTYPE_BF16
     elif q.dtype == torch.float32:
@@ -323,16 +302,9 @@ def sparse_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index
     lse = torch.empty((B, hq, S), dtype=torch.float32, device=q.device) if return_lse else None
     c = index.c_struct()
     scale = 0.0 if softmax_scale is None else float(softmax_scale)
-    if workspace is True:
-        workspace = prefill_workspace(q, k, index)
-    if workspace is not None:
-        if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.device != q.device:
-            raise ValueError("workspace must be a contiguous uint8 tensor on q's device")
-    ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel())
     _check(_lib.sa_sparse_attn_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse), B, hq,
-                                       k.shape[1], S, d, dt, scale, C.byref(c), ws_ptr, ws_bytes, _stream(stream)),
+                                       k.shape[1], S, d, dt, scale, C.byref(c), _stream(stream)),
            "sa_sparse_attn_prefill")
-    _hold(workspace, stream)
     return (o, lse) if return_lse else o
 
 

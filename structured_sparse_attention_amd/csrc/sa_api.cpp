@@ -102,18 +102,9 @@ size_t sa_build_index_workspace_bytes(const sa_pattern_desc* desc, int32_t row_b
   return 0;  // counts and kinds live in the index's own arrays; the scans run in place
 }
 
-size_t sa_sparse_attn_prefill_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv, int32_t S, int32_t head_dim,
-                                              int32_t dtype, int32_t row_block) {
-  if (batch < 1 || hq < 1 || hkv < 1 || S < 1 || hq % hkv != 0) return 0;
-  if ((head_dim != 64 && head_dim != 128) || (row_block != 64 && row_block != 128)) return 0;
-  if ((int64_t)batch * hq * cdiv(S, row_block) > 0x7fffffffLL) return 0;
-  return sa::attention_workspace_bytes(batch, hq, hkv, S, head_dim, dtype, row_block);
-}
-
 sa_status sa_sparse_attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int32_t batch,
                                  int32_t hq, int32_t hkv, int32_t S, int32_t head_dim, int32_t dtype,
-                                 float softmax_scale, const sa_index* idx, void* workspace, size_t workspace_bytes,
-                                 void* stream) {
+                                 float softmax_scale, const sa_index* idx, void* stream) {
   if (!q || !k || !v || !o || !idx) return SA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SA_ERR_INVALID_ARG;
   if (batch < 1 || hq < 1 || hkv < 1 || S < 1 || hq % hkv != 0) return SA_ERR_INVALID_ARG;
@@ -126,10 +117,7 @@ sa_status sa_sparse_attn_prefill(const void* q, const void* k, const void* v, vo
   if ((int64_t)batch * hq * idx->n_row_blocks > 0x7fffffffLL) return SA_ERR_UNSUPPORTED;
   const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf((float)head_dim);
   if (!isfinite(scale)) return SA_ERR_INVALID_ARG;
-  if (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) & 255u)) return SA_ERR_INVALID_ARG;
-  const size_t need = sa::attention_workspace_bytes(batch, hq, hkv, S, head_dim, dtype, idx->row_block);
-  if (workspace != nullptr && need > 0 && workspace_bytes < need) return SA_ERR_CAPACITY;
-  sa::AttnArgs a{q, k, v, o, lse, batch, hq, hkv, S, head_dim, dtype, scale, idx, workspace, workspace_bytes};
+  sa::AttnArgs a{q, k, v, o, lse, batch, hq, hkv, S, head_dim, dtype, scale, idx};
   return hip_status(sa::launch_attention(a, static_cast<hipStream_t>(stream)));
 }
 

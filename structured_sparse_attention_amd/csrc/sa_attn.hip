@@ -27,7 +27,6 @@
 // log2(e) scale; the O rescale is skipped when no row max moved.
 // Block order (decode_item): kv groups one after another across the whole chip,
 // neighbouring row blocks of a group on one XCD, heaviest row blocks first.
-#include <mutex>
 #include <type_traits>
 
 #include "sa_internal.h"
@@ -57,24 +56,6 @@ struct Params {
   const int32_t* col_idx;
   const uint32_t* dbits;  // [hq][nwords] diagonal offsets as bits
   int32_t nwords;
-  // key-sliced schedule (sa_plan.hip); unused when one workgroup runs one item
-  int32_t* plan_head;        // pop[8], qbase[8], qlen[8]
-  const AttnUnit* units;
-  int32_t* cnt;              // [B][hq * nb] merge counters (zero between launches)
-  unsigned char* partials;   // partial slots
-  int64_t slots_per_head;
-  int32_t q_per_slice;       // row blocks per slice (KR / 64)
-  int32_t slot_bytes;
-};
-
-// One unit of work: an item (b, h, rb), or the part of it whose keys lie in [klo, khi].
-struct UnitRange {
-  int b, h, rb;
-  int klo, khi;
-  int64_t s0, s1;   // segments
-  int64_t c0, c1;   // gathered columns
-  int64_t bp0;      // first in-segment column
-  int part, nparts; // nparts == 1: the unit owns the whole item and writes O
 };
 
 // Values the whole wave shares, loaded through the vector memory path, moved to scalar registers so
@@ -188,7 +169,6 @@ struct TileWalk {
   int64_t s1, c0, c1;
   const int32_t* seg_lo;
   const int32_t* seg_hi;
-  int klo = 0, khi = 0x7fffffff;  // segments are clipped to the unit's key range
 
   __device__ Tile first(int64_t s0) const {
     Tile t;
@@ -196,8 +176,8 @@ struct TileWalk {
     t.pc = c0;
     if (s0 < s1) {
       t.kind = 1;
-      t.j0 = max(uni(seg_lo[s0]), klo);
-      t.shi = min(uni(seg_hi[s0]), khi);
+      t.j0 = uni(seg_lo[s0]);
+      t.shi = uni(seg_hi[s0]);
       t.nvalid = min(BN, t.shi - t.j0 + 1);
     } else {
       start_gather(t);
@@ -221,8 +201,8 @@ struct TileWalk {
       if (t.j0 + BN <= t.shi) {
         t.j0 += BN;
       } else if (++t.seg < s1) {
-        t.j0 = max(uni(seg_lo[t.seg]), klo);
-        t.shi = min(uni(seg_hi[t.seg]), khi);
+        t.j0 = uni(seg_lo[t.seg]);
+        t.shi = uni(seg_hi[t.seg]);
       } else {
         start_gather(t);
         return t;
@@ -241,26 +221,18 @@ struct TileWalk {
   }
 };
 
-// Buffer loads and stores that bypass the L2 (system coherent: sc0 sc1).  The partial results of a
-// sliced item are written on one XCD and read on another; their L2s are not coherent with each
-// other, and a device-scope fence would write back or invalidate the whole L2 (the K/V slice it
-// is there to keep), so the partials travel through memory and only they pay for it.
-constexpr int kSysCoherent = 17;  // sc0 | sc1
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
-// Body of the register-staged kernel (fp32, and bf16 without a workspace): one item, from Q load to
-// output.  LDS comes from the caller.
 template <int D, int BM, bool BF16>
-__device__ __forceinline__ void attn_run(const Params& p, const UnitRange& u,
-                                         typename Cfg<D, BM, BF16>::elem* Ks, typename Cfg<D, BM, BF16>::elem* Vs,
-                                         int32_t (*cols_sh)[BN], int32_t* flag) {
+__global__ void __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(2))) k_attn(Params p) {  // 2*BM threads = BM/32 waves
   using C = Cfg<D, BM, BF16>;
   using E = typename C::elem;
+  __shared__ __attribute__((aligned(16))) E Ks[C::K_ELEMS];
+  __shared__ __attribute__((aligned(16))) E Vs[C::V_ELEMS];
+  __shared__ __attribute__((aligned(16))) int32_t cols_sh[3][BN];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, r32 = lane & 31;
-  const int b = u.b, h = u.h, rb = u.rb;
+  int b, h, rb;
+  decode_item(p, b, h, rb);
   const int S = p.S;
   const int b0 = rb * BM, b1 = min(S, b0 + BM) - 1;
   const int i = b0 + wave * 32 + r32;  // this lane's query row
@@ -296,16 +268,14 @@ __device__ __forceinline__ void attn_run(const Params& p, const UnitRange& u,
   float m_run = -INFINITY, l_run = 0.0f;
 
   const int64_t item = (int64_t)h * p.nb + rb;
-  int64_t bp = u.bp0;
+  int64_t bp = uni64(p.bcol_ptr[item]);
   const int64_t bp_end = uni64(p.bcol_ptr[item + 1]);
   TileWalk walk;
-  walk.s1 = u.s1;
-  walk.c0 = u.c0;
-  walk.c1 = u.c1;
+  walk.s1 = uni64(p.seg_ptr[item + 1]);
+  walk.c0 = uni64(p.col_ptr[item]);
+  walk.c1 = uni64(p.col_ptr[item + 1]);
   walk.seg_lo = p.seg_lo;
   walk.seg_hi = p.seg_hi;
-  walk.klo = u.klo;
-  walk.khi = u.khi;
 
   // ---- tile fetch: global -> registers (issued one tile ahead), registers -> LDS.
   // Buffer loads: an offset past the end of the kv head's slab reads as zero, so padding keys
@@ -545,7 +515,7 @@ __device__ __forceinline__ void attn_run(const Params& p, const UnitRange& u,
   auto load_cols = [&](const Tile& t, int32_t* dst) {
     if (t.kind == 2 && tid < BN) dst[tid] = tid < t.nvalid ? p.col_idx[t.pc + tid] : 0;
   };
-  Tile cur = walk.first(u.s0);
+  Tile cur = walk.first(uni64(p.seg_ptr[item]));
   Tile nxt = walk.next(cur);
   Tile nn = walk.next(nxt);
   load_cols(cur, cols_sh[0]);
@@ -609,29 +579,6 @@ __device__ __forceinline__ void attn_run(const Params& p, const UnitRange& u,
   }
 }
 
-// One workgroup per item (b, h, rb) in decode_item's order.
-template <int D, int BM, bool BF16>
-__global__ void __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(2))) k_attn(Params p) {  // 2*BM threads = BM/32 waves
-  using C = Cfg<D, BM, BF16>;
-  __shared__ __attribute__((aligned(16))) typename C::elem Ks[C::K_ELEMS];
-  __shared__ __attribute__((aligned(16))) typename C::elem Vs[C::V_ELEMS];
-  __shared__ __attribute__((aligned(16))) int32_t cols_sh[3][BN];
-  __shared__ int32_t flag;
-  UnitRange u;
-  decode_item(p, u.b, u.h, u.rb);
-  const int64_t item = (int64_t)u.h * p.nb + u.rb;
-  u.klo = 0;
-  u.khi = p.S - 1;
-  u.s0 = uni64(p.seg_ptr[item]);
-  u.s1 = uni64(p.seg_ptr[item + 1]);
-  u.c0 = uni64(p.col_ptr[item]);
-  u.c1 = uni64(p.col_ptr[item + 1]);
-  u.bp0 = uni64(p.bcol_ptr[item]);
-  u.part = 0;
-  u.nparts = 1;
-  attn_run<D, BM, BF16>(p, u, Ks, Vs, cols_sh, &flag);
-}
-
 // ============================================================================
 // bf16 kernel for 128-row blocks.  Four waves per workgroup: wave w owns rows
 // 32w..32w+31 and all 64 keys of a tile, so four waves share every K/V tile.
@@ -655,13 +602,9 @@ __device__ inline int vswz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1
 
 template <int D, int BM>
 struct Cfg3 {
-  static constexpr int NW = 4;                        // waves per workgroup
-  static constexpr int RH = BM / 32;                  // 32-row halves of the block (4 or 2)
-  static constexpr int KS = NW / RH;                  // key groups a tile is split into (1 or 2)
+  static constexpr int NW = BM / 32;
   static constexpr int T = 64 * NW;
   static constexpr int NKB = BN / 32;                 // 32-key blocks per tile
-  static constexpr int NKW = NKB / KS;                // 32-key blocks per wave
-  static constexpr int OBW = (D / 32) / KS;           // output d blocks each wave writes after the merge
   static constexpr int QS = D / 16;
   static constexpr int OB = D / 32;
   static constexpr int ROWB = D * 2;                  // bytes per key row
@@ -678,17 +621,18 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
-// Body of the LDS-direct kernels: one unit.  With 64-row blocks the four waves split each tile's keys
-// in two halves (wave w: rows 32 (w % 2) .., keys 32 (w / 2) ..), each with its own online softmax,
-// and the halves are merged through LDS at the end.
-template <int D, int BM, bool kSliced = false>
-__device__ __forceinline__ void attn_run_lds(const Params& p, const UnitRange& u, unsigned char* lds,
-                                             int32_t (*cols_sh)[BN], int32_t* flag) {
+template <int D, int BM>
+__global__ void __launch_bounds__(64 * (BM / 32)) __attribute__((amdgpu_waves_per_eu(2)))
+k_attn_bf16(Params p) {
   using C = Cfg3<D, BM>;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * C::STAGE];
+  __shared__ __attribute__((aligned(16))) int32_t cols_sh[3][BN];
+
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, r32 = lane & 31;
-  const int rh = wave % C::RH, kh = wave / C::RH;  // this wave's 32 rows, its key group
-  const int b = u.b, h = u.h, rb = u.rb;
+  const int rh = wave;  // this wave's 32 rows
+  int b, h, rb;
+  decode_item(p, b, h, rb);
   const int S = p.S;
   const int b0 = rb * BM, b1 = min(S, b0 + BM) - 1;
   const int i = b0 + rh * 32 + r32;
@@ -702,9 +646,9 @@ __device__ __forceinline__ void attn_run_lds(const Params& p, const UnitRange& u
   bf16x8 qf[C::QS];
 #pragma unroll
   for (int s = 0; s < C::QS; ++s) {
-    uint4 uq = make_uint4(0, 0, 0, 0);
-    if (row_ok) uq = *reinterpret_cast<const uint4*>(Qg + (int64_t)i * D + 16 * s + 8 * g);
-    qf[s] = *reinterpret_cast<bf16x8*>(&uq);
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (row_ok) u = *reinterpret_cast<const uint4*>(Qg + (int64_t)i * D + 16 * s + 8 * g);
+    qf[s] = *reinterpret_cast<bf16x8*>(&u);
   }
   __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): Q is in registers before the pipelined loop
 
@@ -716,16 +660,14 @@ __device__ __forceinline__ void attn_run_lds(const Params& p, const UnitRange& u
   float m_run = -INFINITY, l_run = 0.0f;
 
   const int64_t item = (int64_t)h * p.nb + rb;
-  int64_t bp = u.bp0;
+  int64_t bp = uni64(p.bcol_ptr[item]);
   const int64_t bp_end = uni64(p.bcol_ptr[item + 1]);
   TileWalk walk;
-  walk.s1 = u.s1;
-  walk.c0 = u.c0;
-  walk.c1 = u.c1;
+  walk.s1 = uni64(p.seg_ptr[item + 1]);
+  walk.c0 = uni64(p.col_ptr[item]);
+  walk.c1 = uni64(p.col_ptr[item + 1]);
   walk.seg_lo = p.seg_lo;
   walk.seg_hi = p.seg_hi;
-  walk.klo = u.klo;
-  walk.khi = u.khi;
 
   constexpr uint32_t kBufFlags = 0x00020000u;
   const uint32_t slab_bytes = (uint32_t)S * D * 2u;
@@ -850,19 +792,19 @@ __device__ __forceinline__ void attn_run_lds(const Params& p, const UnitRange& u
   }
 
   auto compute_tile = [&](int st, uint64_t m) {
-    const unsigned char* Kst = lds + st * C::STAGE + kh * C::NKW * 32 * C::ROWB;  // this wave's key blocks
-    const unsigned char* Vst = lds + st * C::STAGE + C::MAT + kh * C::NKW * 32 * C::ROWB;
-    f32x16 sacc[C::NKW];
+    const unsigned char* Kst = lds + st * C::STAGE;
+    const unsigned char* Vst = Kst + C::MAT;
+    f32x16 sacc[C::NKB];
     // all K fragments of the tile first, so that the MFMA burst below waits for LDS only once
-    bf16x8 kf[C::NKW][C::QS];
+    bf16x8 kf[C::NKB][C::QS];
 #pragma unroll
-    for (int kbl = 0; kbl < C::NKW; ++kbl)
+    for (int kbl = 0; kbl < C::NKB; ++kbl)
 #pragma unroll
       for (int s = 0; s < C::QS; ++s)
         kf[kbl][s] = *reinterpret_cast<const bf16x8*>(Kst + kbl * 32 * C::ROWB + koff[s & 3] +
                                                       (s >> 2) * 128);
 #pragma unroll
-    for (int kbl = 0; kbl < C::NKW; ++kbl) {
+    for (int kbl = 0; kbl < C::NKB; ++kbl) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) sacc[kbl][v] = 0.0f;
 #pragma unroll
@@ -871,9 +813,9 @@ __device__ __forceinline__ void attn_run_lds(const Params& p, const UnitRange& u
     }
     // all V fragments (transposed reads) next; they do not depend on the softmax and their
     // latency hides behind it
-    v8i16 vfr[C::NKW][2][C::OB];
+    v8i16 vfr[C::NKB][2][C::OB];
 #pragma unroll
-    for (int kbl = 0; kbl < C::NKW; ++kbl)
+    for (int kbl = 0; kbl < C::NKB; ++kbl)
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm) {
         const int kbase = (kbl * 32 + 16 * mm) * C::ROWB;
@@ -885,11 +827,11 @@ __device__ __forceinline__ void attn_run_lds(const Params& p, const UnitRange& u
           vfr[kbl][mm][x] = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
         }
       }
-    // mask: value v of (tile-wide) block kh*NKW + kbl is key (kh*NKW + kbl)*32 + 8*(v/4) + 4*g + v%4
-    const uint64_t mw = m >> (4 * g + 32 * C::NKW * kh);
+    // mask: value v of block kbl is key kbl*32 + 8*(v/4) + 4*g + v%4
+    const uint64_t mw = m >> (4 * g);
     if (!__all(m == ~0ull)) {
 #pragma unroll
-      for (int kbl = 0; kbl < C::NKW; ++kbl)
+      for (int kbl = 0; kbl < C::NKB; ++kbl)
 #pragma unroll
         for (int v = 0; v < 16; ++v)
           if (!((mw >> (kbl * 32 + 8 * (v >> 2) + (v & 3))) & 1ull)) sacc[kbl][v] = -INFINITY;
@@ -897,7 +839,7 @@ __device__ __forceinline__ void attn_run_lds(const Params& p, const UnitRange& u
     constexpr float kLazy = 8.0f;
     float mx = -INFINITY;
 #pragma unroll
-    for (int kbl = 0; kbl < C::NKW; ++kbl)
+    for (int kbl = 0; kbl < C::NKB; ++kbl)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kbl][v]);
     mx = pair_max(mx) * p.scale_log2;
@@ -915,7 +857,7 @@ __device__ __forceinline__ void attn_run_lds(const Params& p, const UnitRange& u
     const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-    for (int kbl = 0; kbl < C::NKW; ++kbl) {
+    for (int kbl = 0; kbl < C::NKB; ++kbl) {
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm) {
         bf16x8 pf;
@@ -936,7 +878,7 @@ __device__ __forceinline__ void attn_run_lds(const Params& p, const UnitRange& u
   auto load_cols = [&](const Tile& t, int32_t* dst) {
     if (t.kind == 2 && tid < BN) dst[tid] = tid < t.nvalid ? p.col_idx[t.pc + tid] : 0;
   };
-  Tile cur = walk.first(u.s0);
+  Tile cur = walk.first(uni64(p.seg_ptr[item]));
   Tile nxt = walk.next(cur);
   Tile nn = walk.next(nxt);
   load_cols(cur, cols_sh[0]);
@@ -970,232 +912,25 @@ __device__ __forceinline__ void attn_run_lds(const Params& p, const UnitRange& u
     nn = walk.next(nn);
   }
 
-  // ---- key groups (64-row blocks): merge the two halves of each row through LDS (the stage buffers are
-  // free now); afterwards each wave owns the output d blocks [dk, dk + OBW) of its 32 rows, and the
-  // sums run in one fixed order in both waves of a pair (key group 0 first), so they agree bit for bit.
-  constexpr int OBW = C::OBW;
-  if constexpr (C::KS == 2) {
-    constexpr int NE = OBW * 16 + 2;  // values per lane: the partner's d blocks, then m and l
-    float* xs = reinterpret_cast<float*>(lds);
-    float* mine = xs + wave * NE * 64;
-    const float* theirs = xs + (wave ^ C::RH) * NE * 64;
-    auto give = [&](auto give_c) {
-      constexpr int gb = decltype(give_c)::value;
-#pragma unroll
-      for (int x = 0; x < OBW; ++x)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mine[(x * 16 + v) * 64 + lane] = oacc[gb + x][v];
-    };
-    if (kh == 0) give(std::integral_constant<int, OBW>{});
-    else give(std::integral_constant<int, 0>{});
-    mine[(OBW * 16) * 64 + lane] = m_run;
-    mine[(OBW * 16 + 1) * 64 + lane] = l_run;
-    __syncthreads();
-    const float mo = theirs[(OBW * 16) * 64 + lane], lo = theirs[(OBW * 16 + 1) * 64 + lane];
-    const float m0 = kh == 0 ? m_run : mo, m1 = kh == 0 ? mo : m_run;
-    const float l0 = kh == 0 ? l_run : lo, l1 = kh == 0 ? lo : l_run;
-    const float M = fmaxf(m0, m1);
-    const float a0 = m0 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m0 - M);
-    const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - M);
-    auto keep = [&](auto keep_c) {
-#pragma clang fp contract(off)
-      constexpr int kb = decltype(keep_c)::value;
-#pragma unroll
-      for (int x = 0; x < OBW; ++x)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float t = theirs[(x * 16 + v) * 64 + lane];
-          const float v0 = kh == 0 ? oacc[kb + x][v] : t, v1 = kh == 0 ? t : oacc[kb + x][v];
-          oacc[kb + x][v] = v0 * a0 + v1 * a1;
-        }
-    };
-    if (kh == 0) keep(std::integral_constant<int, 0>{});
-    else keep(std::integral_constant<int, OBW>{});
-    {
-#pragma clang fp contract(off)
-      l_run = l0 * a0 + l1 * a1;
-    }
-    m_run = M;
-  }
-
-  if constexpr (kSliced) {
-    static_assert(BM == 64, "the key-sliced schedule runs 64-row units");
-    if (u.nparts > 1) {
-      // One slice of a sliced item: write this unit's partial state (running max, partial row sum and
-      // the unnormalised accumulator, in the registers' own layout) through to memory, count it in, and
-      // let the last unit of the item to arrive merge all parts in slice order (so the result does not
-      // depend on which unit came last).  Nothing waits on another workgroup.
-      const int k_sl = rb / p.q_per_slice, r_sl = rb - k_sl * p.q_per_slice;
-      const int64_t slot0 = (int64_t)(b * p.hq + h) * p.slots_per_head +
-                            (int64_t)p.q_per_slice * k_sl * (k_sl + 1) / 2 + (int64_t)r_sl * (k_sl + 1);
-      auto slot_rsrc = [&](int part) {
-        return __builtin_amdgcn_make_buffer_rsrc(p.partials + (slot0 + part) * (int64_t)p.slot_bytes, 0,
-                                                 p.slot_bytes, 0x00020000u);
-      };
-      auto acc_off = [&](int xl, int qd) { return (((wave * OBW + xl) * 4 + qd) * 64 + lane) * 16; };
-      const int ml_off = (C::NW * OBW * 4 * 64 + rh * 64 + lane) * 16;
-      int32_t* cnt = p.cnt + (int64_t)b * p.hq * p.nb + item;
-      // `kb`: the first of this wave's d blocks (a compile-time index, so the accumulators stay in registers)
-      auto store_part = [&](auto kb_c) {
-        constexpr int kb = decltype(kb_c)::value;
-        const __amdgpu_buffer_rsrc_t rs = slot_rsrc(u.part);
-#pragma unroll
-        for (int xl = 0; xl < OBW; ++xl)
-#pragma unroll
-          for (int qd = 0; qd < 4; ++qd) {
-            u32x4 v;
-            v.x = __float_as_uint(oacc[kb + xl][4 * qd]);
-            v.y = __float_as_uint(oacc[kb + xl][4 * qd + 1]);
-            v.z = __float_as_uint(oacc[kb + xl][4 * qd + 2]);
-            v.w = __float_as_uint(oacc[kb + xl][4 * qd + 3]);
-            __builtin_amdgcn_raw_buffer_store_b128(v, rs, acc_off(xl, qd), 0, kSysCoherent);
-          }
-      };
-      if (kh == 0) store_part(std::integral_constant<int, 0>{});
-      else store_part(std::integral_constant<int, OBW>{});
-      if (kh == 0) {
-        u32x4 ml;
-        ml.x = __float_as_uint(m_run);
-        ml.y = __float_as_uint(l_run);
-        ml.z = 0u;
-        ml.w = 0u;
-        __builtin_amdgcn_raw_buffer_store_b128(ml, slot_rsrc(u.part), ml_off, 0, kSysCoherent);
-      }
-      __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this thread's partial stores are complete
-      __syncthreads();                   // ... and every thread's
-      if (tid == 0) *flag = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-      __syncthreads();
-      if (*flag != u.nparts - 1) return;  // not the last unit of the item
-      // the merge reads every part back (this unit's too): the largest reference maximum, then the sums
-      // in part order
-      float mq[kMaxSlices], lq[kMaxSlices];
-#pragma unroll
-      for (int q = 0; q < kMaxSlices; ++q) {
-        mq[q] = -INFINITY;
-        lq[q] = 0.0f;
-        if (q < u.nparts) {
-          const u32x4 ml = __builtin_bit_cast(
-              u32x4, __builtin_amdgcn_raw_buffer_load_b128(slot_rsrc(q), ml_off, 0, kSysCoherent));
-          mq[q] = __uint_as_float(ml.x);
-          lq[q] = __uint_as_float(ml.y);
-        }
-      }
-      float m_all = -INFINITY;
-#pragma unroll
-      for (int q = 0; q < kMaxSlices; ++q) m_all = fmaxf(m_all, mq[q]);
-      float l_sum = 0.0f;
-      auto merge_parts = [&](auto kb_c) {
-        constexpr int kb = decltype(kb_c)::value;
-#pragma unroll
-        for (int xl = 0; xl < OBW; ++xl)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) oacc[kb + xl][v] = 0.0f;
-#pragma unroll
-        for (int q = 0; q < kMaxSlices; ++q) {
-          if (q >= u.nparts) break;
-          const float w = (mq[q] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mq[q] - m_all);
-          l_sum += lq[q] * w;
-          const __amdgpu_buffer_rsrc_t rs = slot_rsrc(q);
-#pragma unroll
-          for (int xl = 0; xl < OBW; ++xl)
-#pragma unroll
-            for (int qd = 0; qd < 4; ++qd) {
-              const u32x4 v = __builtin_bit_cast(
-                  u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, acc_off(xl, qd), 0, kSysCoherent));
-              oacc[kb + xl][4 * qd] += __uint_as_float(v.x) * w;
-              oacc[kb + xl][4 * qd + 1] += __uint_as_float(v.y) * w;
-              oacc[kb + xl][4 * qd + 2] += __uint_as_float(v.z) * w;
-              oacc[kb + xl][4 * qd + 3] += __uint_as_float(v.w) * w;
-            }
-        }
-      };
-      if (kh == 0) merge_parts(std::integral_constant<int, 0>{});
-      else merge_parts(std::integral_constant<int, OBW>{});
-      m_run = m_all;
-      l_run = l_sum;
-      if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);  // for the next launch
-    }
-  }
-
-  // ---- normalise and store this wave's d blocks
+  // ---- normalise and store
   const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   if (row_ok) {
     E* Og = static_cast<E*>(p.o) + ((int64_t)(b * p.hq + h) * S + i) * D;
-    auto store_blocks = [&](auto first_c) {
-      constexpr int first = decltype(first_c)::value;
 #pragma unroll
-      for (int x = first; x < first + OBW; ++x)
+    for (int x = 0; x < C::OB; ++x)
 #pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-          const int d0 = 32 * x + 8 * qd + 4 * g;
-          __bf16 t4[4];
+      for (int qd = 0; qd < 4; ++qd) {
+        const int d0 = 32 * x + 8 * qd + 4 * g;
+        __bf16 t4[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) t4[e] = (__bf16)(oacc[x][4 * qd + e] * inv);
-          *reinterpret_cast<uint2*>(Og + d0) = *reinterpret_cast<uint2*>(t4);
-        }
-    };
-    if (kh == 0) store_blocks(std::integral_constant<int, 0>{});
-    else store_blocks(std::integral_constant<int, OBW>{});
-    if (p.lse != nullptr && g == 0 && kh == 0) {
+        for (int e = 0; e < 4; ++e) t4[e] = (__bf16)(oacc[x][4 * qd + e] * inv);
+        *reinterpret_cast<uint2*>(Og + d0) = *reinterpret_cast<uint2*>(t4);
+      }
+    if (p.lse != nullptr && g == 0) {
       p.lse[(int64_t)(b * p.hq + h) * S + i] =
           l_tot > 0.0f ? m_run * 0.69314718055994530942f + logf(l_tot) : -INFINITY;
     }
-  }
-}
-
-// One workgroup per item (b, h, rb) in decode_item's order.
-template <int D, int BM>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k_attn_bf16(Params p) {
-  using C = Cfg3<D, BM>;
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * C::STAGE];
-  __shared__ __attribute__((aligned(16))) int32_t cols_sh[3][BN];
-  __shared__ int32_t flag;
-  UnitRange u;
-  decode_item(p, u.b, u.h, u.rb);
-  const int64_t item = (int64_t)u.h * p.nb + u.rb;
-  u.klo = 0;
-  u.khi = p.S - 1;
-  u.s0 = uni64(p.seg_ptr[item]);
-  u.s1 = uni64(p.seg_ptr[item + 1]);
-  u.c0 = uni64(p.col_ptr[item]);
-  u.c1 = uni64(p.col_ptr[item + 1]);
-  u.bp0 = uni64(p.bcol_ptr[item]);
-  u.part = 0;
-  u.nparts = 1;
-  attn_run_lds<D, BM>(p, u, lds, cols_sh, &flag);
-}
-
-// Persistent workgroups over the key-sliced plan.  Workgroup k runs on XCD k % 8 (the dispatcher deals
-// workgroups round-robin over the XCDs) and takes every (grid / 8)-th unit of queue k % 8, starting at
-// k / 8: each queue is covered by its workgroups whatever XCD they actually land on, so the placement
-// only decides L2 locality, never correctness.  No atomics, no waiting.
-template <int D>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k_attn_units(Params p) {
-  using C = Cfg3<D, 64>;
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * C::STAGE];
-  __shared__ __attribute__((aligned(16))) int32_t cols_sh[3][BN];
-  __shared__ int32_t flag;
-  const int x = blockIdx.x % kMaxSlices;
-  const int P = gridDim.x / kMaxSlices;
-  const int32_t base = p.plan_head[kMaxSlices + x], n = p.plan_head[2 * kMaxSlices + x];
-  for (int32_t pos = blockIdx.x / kMaxSlices; pos < n; pos += P) {
-    __syncthreads();  // the previous unit is done with LDS
-    const AttnUnit au = p.units[base + pos];
-    UnitRange u;
-    u.b = uni(au.b);
-    u.h = uni(au.item) / p.nb;
-    u.rb = uni(au.item) - u.h * p.nb;
-    u.klo = uni(au.klo);
-    u.khi = uni(au.khi);
-    u.s0 = uni64(au.sa);
-    u.s1 = uni64(au.sb);
-    u.c0 = uni64(au.ca);
-    u.c1 = uni64(au.cb);
-    u.bp0 = uni64(au.bp);
-    u.part = uni(au.part);
-    u.nparts = uni(au.nparts);
-    attn_run_lds<D, 64, true>(p, u, lds, cols_sh, &flag);
   }
 }
 
@@ -1218,53 +953,7 @@ hipError_t launch_bm(const Params& p, hipStream_t stream) {
   return p.BM == 64 ? launch_t<D, 64, BF16>(p, stream) : launch_t<D, 128, BF16>(p, stream);
 }
 
-// Persistent grid of the unit kernel: every workgroup slot of the device, looked up once per device.
-template <int D>
-hipError_t units_grid(int* grid) {
-  static std::mutex mu;
-  static int cached[64] = {};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  std::lock_guard<std::mutex> lock(mu);
-  if (cached[dev] == 0) {
-    int cus = 0, per_cu = 0;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&k_attn_units<D>), 256, 0);
-    if (e != hipSuccess) return e;
-    cached[dev] = kMaxSlices * ((std::max(1, cus) * std::max(1, per_cu) + kMaxSlices - 1) / kMaxSlices);
-  }
-  *grid = cached[dev];
-  return hipSuccess;
-}
-
-template <int D>
-hipError_t launch_units(Params p, const AttnArgs& a, const PlanLayout& L, hipStream_t stream) {
-  hipError_t e = launch_plan(a, L, stream);
-  if (e != hipSuccess) return e;
-  unsigned char* ws = static_cast<unsigned char*>(a.workspace);
-  p.plan_head = reinterpret_cast<int32_t*>(ws + L.head);
-  p.units = reinterpret_cast<const AttnUnit*>(ws + L.units);
-  p.cnt = reinterpret_cast<int32_t*>(ws + L.cnt);
-  p.partials = ws + L.partials;
-  p.slots_per_head = L.slots_per_head;
-  p.q_per_slice = L.KR / 64;
-  p.slot_bytes = (int32_t)L.slot_bytes;
-  int grid = 0;
-  e = units_grid<D>(&grid);
-  if (e != hipSuccess) return e;
-  k_attn_units<D><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(p);
-  return hipGetLastError();
-}
-
 }  // namespace
-
-size_t attention_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv, int32_t S, int32_t head_dim, int32_t dtype,
-                                 int32_t row_block) {
-  return plan_layout(batch, hq, hkv, S, head_dim, dtype, row_block).total;
-}
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
   Params p;
@@ -1291,19 +980,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
   p.nwords = ((a.S - 1) >> 5) + 1;
   // bf16: 128-row blocks run the LDS-direct kernel; 64-row blocks (two waves per block) run the
   // register-staged kernel, which keeps four blocks per CU and measured faster at that size.
-  p.plan_head = nullptr;
-  p.units = nullptr;
-  p.cnt = nullptr;
-  p.partials = nullptr;
-  p.slots_per_head = 0;
-  p.q_per_slice = 1;
-  p.slot_bytes = 0;
   if (a.dtype == SA_DTYPE_BF16) {
-    if (p.BM == 64 && a.workspace != nullptr) {
-      const PlanLayout L = plan_layout(a.batch, a.hq, a.hkv, a.S, a.head_dim, a.dtype, p.BM);
-      if (L.total > 0 && a.workspace_bytes >= L.total)
-        return a.head_dim == 64 ? launch_units<64>(p, a, L, stream) : launch_units<128>(p, a, L, stream);
-    }
     if (p.BM == 128) return a.head_dim == 64 ? launch_bf16<64, 128>(p, stream) : launch_bf16<128, 128>(p, stream);
     return a.head_dim == 64 ? launch_t<64, 64, true>(p, stream) : launch_t<128, 64, true>(p, stream);
   }

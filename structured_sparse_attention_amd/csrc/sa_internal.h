@@ -3,8 +3,6 @@
 
 #include <hip/hip_runtime.h>
 
-#include <algorithm>
-
 #include "sa.h"
 
 namespace sa {
@@ -34,47 +32,8 @@ struct AttnArgs {
   int32_t batch, hq, hkv, S, head_dim, dtype;
   float scale;
   const sa_index* idx;
-  void* workspace;  // NULL: one workgroup per item; else the key-sliced schedule (sa_plan.hip)
-  size_t workspace_bytes;
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
-// Workspace bytes of the key-sliced schedule for this call (0: the call never uses a workspace).
-size_t attention_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv, int32_t S, int32_t head_dim, int32_t dtype,
-                                 int32_t row_block);
-
-// ---- Key-sliced schedule (sa_plan.hip builds it, sa_attn.hip runs it).
-// The key range [0, S) is cut into kMaxSlices slices of KR keys (KR a multiple of 64); an item
-// (batch, query head, row block) with many gathered columns spread over several slices runs as one
-// unit per slice that holds some of its keys, and the units' partial results are merged by the
-// last one to finish.  Other items run as one unit.  Units are queued per XCD so that each XCD
-// reads one slice of one kv head at a time.
-constexpr int kMaxSlices = 8;           // one per XCD
-constexpr int kSliceMinCols = 512;      // gathered columns (8 tiles) before an item is sliced
-
-struct AttnUnit {  // 80 bytes
-  int32_t b, item;        // batch element; item = h * nb + rb
-  int32_t klo, khi;       // key range of the unit (segments are clipped to it)
-  int32_t part, nparts;   // index among the item's units, their count (1: the unit writes O itself)
-  int32_t slice, pad;
-  int64_t ca, cb;         // gathered columns col_idx[ca, cb)
-  int64_t sa, sb;         // segments [sa, sb)
-  int64_t bp;             // first in-segment column of the range
-};
-
-// Workspace layout of the sliced schedule (byte offsets, 256-byte aligned pieces).
-struct PlanLayout {
-  int32_t KR, ns, G;                  // slice width, slice count, kv groups (batch * hkv)
-  int64_t items, slots_per_head;      // items per batch element (hq * nb); partial slots per head
-  size_t head, counts, fills, bbase, cnt, stage, units, partials;  // offsets
-  size_t slot_bytes;                  // bytes of one partial (one unit of 64 rows)
-  size_t total;
-  int64_t max_units;
-};
-// Layout for this call; total == 0 when the configuration takes the one-workgroup-per-item path.
-PlanLayout plan_layout(int32_t batch, int32_t hq, int32_t hkv, int32_t S, int32_t head_dim, int32_t dtype,
-                       int32_t row_block);
-// Planner launches (K0..K3) for the sliced schedule.
-hipError_t launch_plan(const AttnArgs& a, const PlanLayout& L, hipStream_t stream);
 
 // Decode (sa_decode.hip): one query row per sequence at position pos[b].
 struct DecodeArgs {

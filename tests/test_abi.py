@@ -93,34 +93,15 @@ def test_attention_validation(m):
     f = m.lib.sa_sparse_attn_prefill
     ix = _index(m)
     p = FAKE.value
-    assert f(None, p, p, p, None, 1, 1, 1, 512, 64, 1, 0.0, C.byref(ix), None, 0, None) == -1
-    assert f(p, p, p, p, None, 1, 3, 2, 512, 64, 1, 0.0, C.byref(ix), None, 0, None) == -1   # hq % hkv
-    assert f(p, p, p, p, None, 1, 1, 1, 512, 64, 7, 0.0, C.byref(ix), None, 0, None) == -1   # dtype
-    assert f(p, p, p, p, None, 1, 1, 1, 512, 96, 1, 0.0, C.byref(ix), None, 0, None) == -2   # head_dim
-    assert f(p, p, p, p, None, 1, 1, 1, 256, 64, 1, 0.0, C.byref(ix), None, 0, None) == -1   # S != index S
-    assert f(p, p, p, p, None, 1, 2, 1, 512, 64, 1, 0.0, C.byref(ix), None, 0, None) == -1   # heads != index heads
-    assert f(p, p, p, p, None, 0, 1, 1, 512, 64, 1, 0.0, C.byref(ix), None, 0, None) == -1   # batch
-    assert f(p, p, p, p, None, 1, 1, 1, 512, 64, 1, 0.0, C.byref(_index(m, col_idx=None)), None, 0, None) == -1
-    assert f(p, p, p, p + 8, None, 1, 1, 1, 512, 64, 1, 0.0, C.byref(ix), None, 0, None) == -1  # o not aligned
-    # a workspace must be 256-byte aligned and at least the size query's bytes
-    need = m.lib.sa_sparse_attn_prefill_workspace_bytes(1, 1, 1, 512, 64, 1, 64)
-    assert need > 0
-    assert f(p, p, p, p, None, 1, 1, 1, 512, 64, 1, 0.0, C.byref(ix), p + 16, need, None) == -1
-    assert f(p, p, p, p, None, 1, 1, 1, 512, 64, 1, 0.0, C.byref(ix), p, need - 1, None) == -4
-
-
-def test_prefill_workspace_sizes(m):
-    f = m.lib.sa_sparse_attn_prefill_workspace_bytes
-    assert f(1, 32, 8, 65536, 128, 1, 64) > 0          # bf16, row block 64: the key-sliced schedule
-    assert f(1, 32, 8, 65536, 128, 0, 64) == 0         # fp32: none
-    assert f(1, 32, 8, 131072, 128, 1, 128) == 0       # row block 128: none
-    assert f(1, 3, 2, 512, 64, 1, 64) == 0             # hq % hkv != 0
-    assert f(0, 1, 1, 512, 64, 1, 64) == 0             # batch
-    # grows with the batch and the head count, not below the partial states alone
-    one = f(1, 32, 8, 65536, 128, 1, 64)
-    assert f(2, 32, 8, 65536, 128, 1, 64) > one
-    slots = 32 * 128 * 36                               # 32 heads x sum over row blocks of (slice + 1)
-    assert one >= slots * 64 * (128 + 8) * 4
+    assert f(None, p, p, p, None, 1, 1, 1, 512, 64, 1, 0.0, C.byref(ix), None) == -1
+    assert f(p, p, p, p, None, 1, 3, 2, 512, 64, 1, 0.0, C.byref(ix), None) == -1   # hq % hkv
+    assert f(p, p, p, p, None, 1, 1, 1, 512, 64, 7, 0.0, C.byref(ix), None) == -1   # dtype
+    assert f(p, p, p, p, None, 1, 1, 1, 512, 96, 1, 0.0, C.byref(ix), None) == -2   # head_dim
+    assert f(p, p, p, p, None, 1, 1, 1, 256, 64, 1, 0.0, C.byref(ix), None) == -1   # S != index S
+    assert f(p, p, p, p, None, 1, 2, 1, 512, 64, 1, 0.0, C.byref(ix), None) == -1   # heads != index heads
+    assert f(p, p, p, p, None, 0, 1, 1, 512, 64, 1, 0.0, C.byref(ix), None) == -1   # batch
+    assert f(p, p, p, p, None, 1, 1, 1, 512, 64, 1, 0.0, C.byref(_index(m, col_idx=None)), None) == -1
+    assert f(p, p, p, p + 8, None, 1, 1, 1, 512, 64, 1, 0.0, C.byref(ix), None) == -1  # o not 16-byte aligned
 
 
 def test_decode_validation(m):

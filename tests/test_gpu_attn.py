@@ -18,7 +18,18 @@ from gpu_util import (all_rows, assert_close_bf16, assert_close_f32, assert_lse,
 pytestmark = pytest.mark.gpu
 
 
-def _check(q, got, got_lse, ref, ref_lse, what):
+def _run(desc, q, k, v, BM, rows, what, scale=None, want_lse=False):
+    m = sa()
+    B, hq, S, d = q.shape
+    note("attn %s S=%d hq=%d hkv=%d d=%d BM=%d dtype=%s rows=%d" % (what, S, hq, k.shape[1], d, BM, q.dtype,
+                                                                     len(rows)))
+    pat = m.DevicePatterns.from_host(desc)
+    ix = m.build_index(pat, BM)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    o, lse = m.sparse_attn_prefill(qd, kd, vd, ix, softmax_scale=scale, return_lse=True)
+    torch.cuda.synchronize()
+    got, got_lse = gather_rows(o, rows), gather_lse(lse, rows)
+    ref, ref_lse = oracle.attention_rows(desc, q, k, v, rows, scale=scale)
     if q.dtype == np.float32:
         assert_close_f32(got, ref, what)
         assert_lse(got_lse, ref_lse, 1e-5, what)
@@ -27,33 +38,6 @@ def _check(q, got, got_lse, ref, ref_lse, what):
         # bf16: the row sum is the sum of the bf16-rounded probabilities that also weight V, each
         # within 2^-9 relative of its exact value, so |lse - lse_exact| <= ln(1 + 2^-9) < 2^-8
         assert_lse(got_lse, ref_lse, 2.0 ** -8, what)
-
-
-def _units(ws):
-    """Units the key-sliced plan of the last call queued (the workspace starts with the per-XCD queue heads,
-    starts and lengths, int32 [3][8])."""
-    return int(ws[:96].view(torch.int32)[16:24].sum().item())
-
-
-def _run(desc, q, k, v, BM, rows, what, scale=None, want_lse=False, schedules=("item",)):
-    """Index, attention and the oracle on `rows`; schedules: "item" (one workgroup per item, no workspace)
-    and/or "sliced" (the key-sliced schedule of a workspace call), each checked against the same oracle
-    rows.  Returns the output of the last schedule."""
-    m = sa()
-    B, hq, S, d = q.shape
-    note("attn %s S=%d hq=%d hkv=%d d=%d BM=%d dtype=%s rows=%d %s" % (what, S, hq, k.shape[1], d, BM, q.dtype,
-                                                                        len(rows), "+".join(schedules)))
-    pat = m.DevicePatterns.from_host(desc)
-    ix = m.build_index(pat, BM)
-    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
-    ref, ref_lse = oracle.attention_rows(desc, q, k, v, rows, scale=scale)
-    for sched in schedules:
-        ws = m.prefill_workspace(qd, kd, ix) if sched == "sliced" else None
-        o, lse = m.sparse_attn_prefill(qd, kd, vd, ix, softmax_scale=scale, return_lse=True, workspace=ws)
-        torch.cuda.synchronize()
-        _check(q, gather_rows(o, rows), gather_lse(lse, rows), ref, ref_lse, what + " " + sched)
-        if ws is not None:
-            note("  sliced plan: %d units for %d items" % (_units(ws), B * hq * ix.n_row_blocks))
     return (o, ix, lse) if want_lse else (o, ix)
 
 
@@ -254,62 +238,8 @@ def test_llama8b_like_full_size_sampled():
     desc = W.llama8b_like()
     q, k, v = W.qkv(4, 1, 32, 8, 65536, 128, "bf16")
     rows = rows_of_blocks(1, 32, 65536, 64, 32, np.random.default_rng(4))
-    o, _, lse = _run(desc, q, k, v, 64, rows, "8b-like", want_lse=True, schedules=("item", "sliced"))
-    _dense_cross_check(desc, q, k, v, o, lse, 64, 44, "8b-like sliced")
-
-
-# ------------------------------------------------------------------ the key-sliced schedule
-@pytest.mark.parametrize("S,d,B,hkv", [(4096, 128, 1, 2), (3000, 128, 2, 1), (4096, 64, 1, 8), (5000, 128, 3, 4)])
-def test_sliced_schedule_every_row(S, d, B, hkv):
-    """Dense block heads (p = 0.5) so that most row blocks hold >= 512 gathered columns over several key
-    slices: every row of both schedules against the oracle; ragged S, batch > 1, and kv-group counts that
-    leave XCD queues empty (their workgroups take units from the others)."""
-    H = 8
-    desc = W.llama8b_like(S=S, H=H, band=256, block_p=0.5)
-    q, k, v = W.qkv(31, B, H, hkv, S, d, "bf16")
-    _run(desc, q, k, v, 64, all_rows(B, H, S), "sliced", schedules=("item", "sliced"))
-
-
-def test_sliced_schedule_mixed_kinds_and_empty_head():
-    """Every pattern kind (diagonal runs, verticals, 128-blocks, 256-row stripes) through the sliced schedule,
-    where segments straddle slice boundaries; plus a head without any pattern."""
-    S, H = 3000, 4
-    rng = np.random.default_rng(41)
-    diags = [np.unique(np.concatenate([np.arange(300), rng.choice(S, 40, replace=False)])) for _ in range(H - 1)]
-    verts = [rng.choice(S, 200, replace=False) for _ in range(H - 1)]
-    nbq = -(-S // 128)
-    bm = (rng.random((H, nbq, nbq)) < 0.4).astype(np.uint8)
-    bm[H - 1] = 0
-    stripes = [[np.sort(rng.choice(S, size=int(rng.integers(0, 600)), replace=False)) if h < H - 1
-                else np.zeros(0, np.int64) for _ in range(-(-S // 256))] for h in range(H)]
-    desc = W.desc_from_lists(S, diags + [np.zeros(0)], verts + [np.zeros(0)], block_mask=bm, block_size=128,
-                             stripes=stripes, stripe_rows=256)
-    q, k, v = W.qkv(42, 1, H, 2, S, 128, "bf16")
-    o, _ = _run(desc, q, k, v, 64, all_rows(1, H, S), "sliced-mixed", schedules=("sliced",))
-    assert o[0, H - 1].float().abs().max().item() == 0.0
-
-
-def test_sliced_schedule_is_repeatable():
-    """The merge adds the slices' partial states in slice order, whichever unit comes last: two calls with
-    the same workspace, and a third with a workspace full of garbage, give the same bits; the merge
-    counters are left at zero."""
-    m = sa()
-    S, H = 4096, 8
-    desc = W.llama8b_like(S=S, H=H, band=256, block_p=0.5)
-    q, k, v = W.qkv(43, 1, H, 2, S, 128, "bf16")
-    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
-    ix = m.build_index(m.DevicePatterns.from_host(desc), 64)
-    note("sliced repeatability")
-    ws = m.prefill_workspace(qd, kd, ix)
-    o1, l1 = m.sparse_attn_prefill(qd, kd, vd, ix, return_lse=True, workspace=ws)
-    o2 = torch.full_like(o1, float("nan"))
-    _, l2 = m.sparse_attn_prefill(qd, kd, vd, ix, return_lse=True, workspace=ws, out=o2)
-    ws3 = torch.randint(0, 255, ws.shape, dtype=torch.uint8, device=ws.device)
-    o3, l3 = m.sparse_attn_prefill(qd, kd, vd, ix, return_lse=True, workspace=ws3)
-    torch.cuda.synchronize()
-    assert _units(ws) > ix.n_row_blocks * H     # some items did run sliced
-    for o, l in ((o2, l2), (o3, l3)):
-        assert torch.equal(o1.view(torch.int16), o.view(torch.int16)) and torch.equal(l1, l)
+    o, _, lse = _run(desc, q, k, v, 64, rows, "8b-like", want_lse=True)
+    _dense_cross_check(desc, q, k, v, o, lse, 64, 44, "8b-like")
 
 
 # ------------------------------------------------------------------ workload 5 (stripes, S=131072)
