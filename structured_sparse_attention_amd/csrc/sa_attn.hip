@@ -35,6 +35,7 @@ namespace sa {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int BN = 64;
@@ -431,14 +432,20 @@ __global__ void __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(2))
         }
       }
     }
-    // mask: value v of block kb is key kb*32 + 8*(v/4) + 4*g + v%4
+    // mask: value v of block kb is key kb*32 + 8*(v/4) + 4*g + v%4; the key's bit, sign-extended to a
+    // whole word, keeps the score or inserts -inf (bit-field extract, bit-field insert)
     if (!__all(m == ~0ull)) {
       const uint64_t mg = m >> (4 * g);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint32_t word = (uint32_t)(mg >> (32 * kb));
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if (!((mg >> (kb * 32 + 8 * (v >> 2) + (v & 3))) & 1ull)) sacc[kb][v] = -INFINITY;
+        for (int v = 0; v < 16; ++v) {
+          const int bit = 8 * (v >> 2) + (v & 3);
+          const uint32_t keep = (uint32_t)((int32_t)(word << (31 - bit)) >> 31);
+          sacc[kb][v] = __uint_as_float((__float_as_uint(sacc[kb][v]) & keep) | (0xff800000u & ~keep));
+        }
+      }
     }
     // online softmax in the log2 domain.  The reference maximum moves only when the tile maximum
     // exceeds it by more than kLazy (probabilities up to 2^kLazy are exact enough in fp32 and keep
@@ -473,9 +480,9 @@ __global__ void __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(2))
                                : mul_then_sub(sacc[kb][v], p.scale_log2, m_use);
         const float e = __builtin_amdgcn_exp2f(arg);
         sacc[kb][v] = e;
-        lsum += e;
+        if constexpr (!BF16) lsum += e;
       }
-    l_run += lsum;
+    if constexpr (!BF16) l_run += lsum;
     // O^T += V^T P^T
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -485,6 +492,11 @@ __global__ void __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(2))
           bf16x8 pf, pf_sw;
 #pragma unroll
           for (int t = 0; t < 8; ++t) pf[t] = (__bf16)sacc[kb][8 * mm + t];
+          // the row sum of the same bf16 probabilities that weight V, two per instruction
+          const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+          for (int t = 0; t < 8; t += 2)
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[t], pf[t + 1]}, ones, l_run, false);
 #pragma unroll
           for (int t = 0; t < 8; ++t) pf_sw[t] = pf[t ^ 4];
 #pragma unroll
@@ -615,9 +627,9 @@ struct Cfg3 {
   static constexpr int STAGE = 2 * MAT;
 };
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
@@ -827,14 +839,21 @@ k_attn_bf16(Params p) {
           vfr[kbl][mm][x] = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
         }
       }
-    // mask: value v of block kbl is key kbl*32 + 8*(v/4) + 4*g + v%4
+    // mask: value v of block kbl is key kbl*32 + 8*(v/4) + 4*g + v%4.  Per value, the key's bit is
+    // sign-extended into an all-ones / all-zeros word, which keeps the score or inserts -inf (two
+    // instructions: bit-field extract, bit-field insert).
     const uint64_t mw = m >> (4 * g);
     if (!__all(m == ~0ull)) {
 #pragma unroll
-      for (int kbl = 0; kbl < C::NKB; ++kbl)
+      for (int kbl = 0; kbl < C::NKB; ++kbl) {
+        const uint32_t word = (uint32_t)(mw >> (32 * kbl));
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if (!((mw >> (kbl * 32 + 8 * (v >> 2) + (v & 3))) & 1ull)) sacc[kbl][v] = -INFINITY;
+        for (int v = 0; v < 16; ++v) {
+          const int bit = 8 * (v >> 2) + (v & 3);
+          const uint32_t keep = (uint32_t)((int32_t)(word << (31 - bit)) >> 31);
+          sacc[kbl][v] = __uint_as_float((__float_as_uint(sacc[kbl][v]) & keep) | (0xff800000u & ~keep));
+        }
+      }
     }
     constexpr float kLazy = 8.0f;
     float mx = -INFINITY;
