@@ -112,10 +112,85 @@ def cpu_baseline(desc, qkv_host, cfg, target_s=15.0):
         dt = time.time() - t
     flops = 4.0 * d * float(cnt.sum())
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=cores, kind="oracle",
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=cores, kind="oracle", cpu=cpu_model(),
                 sample="%d whole row blocks per head (%d rows, %d retained pairs, seeded), fp64 sparse "
                        "enumeration, %.1f s" % (n, len(rows), int(cnt.sum()), dt),
                 seconds=dt)
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo; lscpu is not always installed)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def time_call(torch, fn, reps=10):
+    """Mean HIP-event time (ms) of fn() on the current stream, after one untimed call."""
+    fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+def small_workloads(sa, torch):
+    """The three smaller workloads' attention (and index refill) times: the tiny fp32 case (S = 512, one
+    head, d = 64, diagonals 0..63 + verticals), the 1B-shaped layer (S = 8192, 32/8 heads, d = 64) and the
+    capture workload's attention run (16 layers, each one call at S = 16384, 32/8 heads, d = 64, on the
+    layer's kept sets from the GPU capture of its 32 maps, extended to S)."""
+    import workloads as W
+    out = {}
+    # workload 1
+    desc = W.tiny("base")
+    q, k, v = W.qkv(1, 1, 1, 1, 512, 64, "f32")
+    pat = sa.DevicePatterns.from_host(desc)
+    ix = sa.build_index(pat, 64)
+    qd, kd, vd = to_dev(torch, q), to_dev(torch, k), to_dev(torch, v)
+    o = torch.empty_like(qd)
+    ms = time_call(torch, lambda: sa.sparse_attn_prefill(qd, kd, vd, ix, out=o), reps=50)
+    ims = time_call(torch, lambda: sa.refill_index(pat, ix), reps=50)
+    out["tiny_fp32"] = dict(S=512, heads="1/1", d=64, attn_ms=ms, index_ms=ims, retained_pairs=ix.total_pairs,
+                            effective_tflops=4.0 * 64 * ix.total_pairs / (ms * 1e-3) / 1e12,
+                            frac_of_fp32_peak=4.0 * 64 * ix.total_pairs / (ms * 1e-3) / 1e12 / PEAK_F32_TFLOPS)
+    # workload 2
+    desc = W.llama1b_like()
+    q, k, v = W.qkv(2, 1, 32, 8, 8192, 64, "bf16")
+    pat = sa.DevicePatterns.from_host(desc)
+    ix = sa.build_index(pat, 64)
+    qd, kd, vd = to_dev(torch, q), to_dev(torch, k), to_dev(torch, v)
+    o = torch.empty_like(qd)
+    ms = time_call(torch, lambda: sa.sparse_attn_prefill(qd, kd, vd, ix, out=o))
+    ims = time_call(torch, lambda: sa.refill_index(pat, ix))
+    out["llama1b_like"] = dict(S=8192, heads="32/8", d=64, attn_ms=ms, index_ms=ims, retained_pairs=ix.total_pairs,
+                               effective_tflops=4.0 * 64 * ix.total_pairs / (ms * 1e-3) / 1e12)
+    del qd, kd, vd, o
+    # workload 3: capture of the 512 maps on the GPU, then one attention call per layer at S = 16384
+    maps = torch.from_numpy(W.capture_maps(layers=16, heads=32, n_avg=16)).cuda()
+    cap = sa.pattern_capture(maps)
+    S = 16384
+    total_ms, pairs = 0.0, 0
+    for layer in range(16):
+        kd_ = cap["keep_diag"][32 * layer:32 * (layer + 1)].contiguous()
+        kv_ = cap["keep_vert"][32 * layer:32 * (layer + 1)].contiguous()
+        ix = sa.build_index(sa.patterns_to_desc(kd_, kv_, S), 64)
+        q, k, v = W.qkv(3, 1, 32, 8, S, 64, "bf16", seed_extra=layer)
+        qd, kd, vd = to_dev(torch, q), to_dev(torch, k), to_dev(torch, v)
+        o = torch.empty_like(qd)
+        total_ms += time_call(torch, lambda: sa.sparse_attn_prefill(qd, kd, vd, ix, out=o), reps=5)
+        pairs += ix.total_pairs
+    del maps
+    out["capture_16_layers_S16384"] = dict(S=S, heads="32/8", d=64, layers=16, attn_ms=total_ms, retained_pairs=pairs,
+                                           effective_tflops=4.0 * 64 * pairs / (total_ms * 1e-3) / 1e12)
+    return out
 
 
 def capture_ms(sa, torch, reps=5):
@@ -459,6 +534,12 @@ def main():
         log("runtime capture at 64K: capture %.3f ms, index + attention %.3f ms (attention %.3f ms), density %.4f"
             % (rc["capture_ms"], rc["index_and_attention_ms"], rc["attention_ms"], rc["density"]))
         extras["decode"] = decode_bench(sa, torch)
+        extras["small_workloads"] = small_workloads(sa, torch)
+        sw = extras["small_workloads"]
+        log("tiny fp32: %.4f ms; 1B-like S=8192: %.3f ms (%.0f TFLOP/s); capture run, 16 layers at S=16384: %.3f ms "
+            "(%.0f TFLOP/s)" % (sw["tiny_fp32"]["attn_ms"], sw["llama1b_like"]["attn_ms"],
+                                sw["llama1b_like"]["effective_tflops"], sw["capture_16_layers_S16384"]["attn_ms"],
+                                sw["capture_16_layers_S16384"]["effective_tflops"]))
         extras["machine"] = machine_calibration(sa, torch)
         log("machine: dense bf16 MFMA %.0f TFLOP/s; random 16 KiB reads %s TB/s" % (
             extras["machine"]["mfma_bf16_dense_TFLOPs"],
@@ -479,6 +560,20 @@ def main():
         del src, dst
 
     achieved = flops / (attn_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(cfg),
+                "kernel": "attention forward, bf16, head_dim %d, row block %d" % (cfg["d"], cfg["row_block"])}
+    if "machine" in extras:
+        # the same launch against what this chip measurably sustains: dense bf16 MFMA from registers, and
+        # random 16 KiB reads from a region the size of one kv head's K/V (the fabric ceiling of the gathers)
+        mfma = extras["machine"]["mfma_bf16_dense_TFLOPs"]
+        roofline["measured_peak"] = mfma
+        roofline["frac_of_measured_peak"] = achieved / mfma
+        tr = roofline["traffic"]
+        if tr:
+            gb = extras["machine"]["random_16KiB_read_TBps"]["32MiB"]
+            roofline["traffic_TBps"] = tr / (attn_ms * 1e-3) / 1e12
+            roofline["traffic_frac_of_measured_gather"] = roofline["traffic_TBps"] / gb
     out = {
         "metric": "effective TFLOP/s (retained pairs) + prefill attn ms at S=64K/131K, 1 GPU",
         "value": flops / (ms_per_step * 1e-3) / 1e12,
@@ -495,10 +590,9 @@ def main():
         "config": {"workload": "%s: batch 1, S=%d, %d q / %d kv heads, head_dim %d, row block %d"
                                % (cfg["name"], cfg["S"], cfg["hq"], cfg["hkv"], cfg["d"], cfg["row_block"]),
                    "batch": B, "seq_len": cfg["S"], "hq": cfg["hq"], "hkv": cfg["hkv"], "head_dim": cfg["d"]},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(cfg),
-                     "kernel": "attention forward, bf16, head_dim %d, row block %d" % (cfg["d"], cfg["row_block"])},
-        "cpu_baseline": None if cpu is None else {k2: cpu[k2] for k2 in ("value", "unit", "cores", "kind", "sample")},
+        "roofline": roofline,
+        "cpu_baseline": None if cpu is None else {k2: cpu[k2] for k2 in ("value", "unit", "cores", "kind", "sample",
+                                                                         "cpu")},
         "prefill_attn_ms": prefill_ms,
         "index_build_ms": index_ms,
         "retained_pairs": pairs,
