@@ -118,6 +118,32 @@ def cpu_baseline(desc, qkv_host, cfg, target_s=15.0):
                 seconds=dt)
 
 
+def cpu_small_workloads():
+    """The oracle on the three smaller workloads, whole problems: the tiny fp32 case and the 1B-shaped
+    layer (every row of every head, sparse enumeration), and the capture of the 512 maps."""
+    import oracle
+    import workloads as W
+    out = {}
+    desc = W.tiny("base")
+    q, k, v = W.qkv(1, 1, 1, 1, 512, 64, "f32")
+    rows = np.array([(0, 0, i) for i in range(512)], dtype=np.int32)
+    t = time.time()
+    oracle.attention_rows(desc, q, k, v, rows)
+    out["tiny_fp32_s"] = time.time() - t
+    desc = W.llama1b_like()
+    q, k, v = W.qkv(2, 1, 32, 8, 8192, 64, "bf16")
+    rows = np.array([(0, h, i) for h in range(32) for i in range(8192)], dtype=np.int32)
+    t = time.time()
+    _, _, cnt = oracle.attention_rows(desc, q, k, v, rows, return_counts=True)
+    out["llama1b_like_s"] = time.time() - t
+    out["llama1b_like_tflops"] = 4.0 * 64 * float(cnt.sum()) / out["llama1b_like_s"] / 1e12
+    maps = W.capture_maps(layers=16, heads=32, n_avg=16)
+    t = time.time()
+    oracle.capture(maps)
+    out["capture_512_maps_s"] = time.time() - t
+    return out
+
+
 def cpu_model() -> str:
     """The host CPU's model name (from /proc/cpuinfo; lscpu is not always installed)."""
     try:
@@ -551,6 +577,9 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(desc, qkv_host, cfg)
         log("cpu oracle: %.4f TFLOP/s on %d threads (%s)" % (cpu["value"], cpu["cores"], cpu["sample"]))
+        if not args.no_extras:
+            cpu["small_workloads"] = cpu_small_workloads()
+            log("cpu oracle, smaller workloads: %s" % json.dumps(cpu["small_workloads"]))
 
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
@@ -592,7 +621,7 @@ def main():
                    "batch": B, "seq_len": cfg["S"], "hq": cfg["hq"], "hkv": cfg["hkv"], "head_dim": cfg["d"]},
         "roofline": roofline,
         "cpu_baseline": None if cpu is None else {k2: cpu[k2] for k2 in ("value", "unit", "cores", "kind", "sample",
-                                                                         "cpu")},
+                                                                         "cpu", "small_workloads") if k2 in cpu},
         "prefill_attn_ms": prefill_ms,
         "index_build_ms": index_ms,
         "retained_pairs": pairs,
