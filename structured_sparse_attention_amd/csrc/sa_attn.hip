@@ -91,15 +91,30 @@ __device__ inline float mul_then_sub(float a, float b, float c) {
   return a * b - c;
 }
 
-// position of key kk inside the transposed V tile: bits 2 and 3 swapped, so that the 8 keys a
-// lane feeds to one P.V MFMA are 16 contiguous bytes
-__device__ inline int vt_pos(int kk) { return (kk & ~12) | ((kk & 4) << 1) | ((kk & 8) >> 1); }
+// LDS banks on gfx950: 64 banks of 4 bytes (256 bytes per cycle).  A 16-byte access is served 16
+// lanes at a time, so a conflict-free 16-byte access spreads each group of 16 lanes over 16
+// different 16-byte bank groups.
+//
+// bf16 K and V tiles are stored key-row-major (d values contiguous, 2 * D bytes per row), with
+// the 16-byte chunks of row R XOR-swizzled: K chunk c at c ^ kswz(R), V chunk c at c ^ vswz(R).
+// - K is read as the A operand of S^T = K Q^T, 16 bytes per lane, lane r (0..31) from key row r:
+//   16 consecutive rows must land on 16 different bank groups.  With 256-byte rows (16 chunks)
+//   that is chunk ^ (R % 16); with 128-byte rows two rows share the 256 bytes of the banks, so
+//   chunk ^ ((R / 2) % 8).
+// - V is read with ds_read_b64_tr_b16 (the A operand of O^T = V^T P^T): the 16 lanes of one
+//   transposed read take 32 bytes from each of 4 consecutive key rows, and chunk ^ 4 (R % 4)
+//   (256-byte rows) or chunk ^ 4 ((R / 2) % 2) (128-byte rows) puts the 8 segments of a half-wave
+//   on 8 different 32-byte bank groups.
+// Both swizzles depend on R % 16 only, and for R = a + b with a a multiple of 16 and b below it,
+// kswz(a + b) = kswz(a) ^ kswz(b) (likewise vswz).
+template <int D>
+__device__ inline int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__device__ inline int vswz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
-// Row d of the transposed V tile is 16 units of 8 bytes (4 keys).  Unit u is stored at unit
-// u ^ swz(d), swz(d) = ((d/8) % 8) * 2 + (d/64) % 2: the 16 lanes of one write (rows d = 8c + e,
-// c = 0..15) then hit 16 different units, i.e. all 32 banks once, and 16-byte reads stay
-// aligned pairs of units (swapped when bit 0 of swz(d) is set, i.e. d >= 64 within 128).
-__device__ inline int vt_unit(int u, int d) { return u ^ ((((d >> 3) & 7) << 1) | ((d >> 6) & 1)); }
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
 
 template <int D, int BM, bool BF16>
 struct Cfg {
@@ -107,12 +122,18 @@ struct Cfg {
   static constexpr int T = 64 * NW;
   static constexpr int QS = BF16 ? D / 16 : D / 2;  // MFMA k-steps over d
   static constexpr int OB = D / 32;                  // 32-wide d blocks of the output
-  // LDS strides in elements
-  static constexpr int KS = BF16 ? D + 8 : D + 1;    // K tile [BN][KS]
-  static constexpr int VS = BF16 ? BN + 8 : D + 4;   // bf16: V^T [D][VS]; f32: V [BN][VS]
+  // LDS tiles [BN][KS] (K) and [BN][VS] (V), strides in elements.  bf16 V, and K at d = 64:
+  // unpadded, chunks swizzled (vswz, kswz); bf16 K at d = 128: rows padded to 272 bytes (16
+  // consecutive rows then start on 16 consecutive 16-byte bank groups, and the reads keep
+  // immediate offsets); f32: padded rows
+  static constexpr bool KPAD = !BF16 || D == 128;
+  static constexpr int KS = BF16 ? (KPAD ? D + 8 : D) : D + 1;
+  static constexpr int VS = BF16 ? D : D + 4;
+  static constexpr int ROWB = BF16 ? 2 * D : 0;      // bytes per bf16 key row
   static constexpr int K_ELEMS = BN * KS;
-  static constexpr int V_ELEMS = BF16 ? D * VS : BN * VS;
-  // tile fetch: a task is 4 consecutive keys x one 16-byte chunk of K and of V
+  static constexpr int V_ELEMS = BN * VS;
+  // tile fetch: a task is 4 keys (bf16: kq + 16u, f32: 4 kq + u, u = 0..3) x one 16-byte chunk
+  // of K and of V
   static constexpr int EPC = BF16 ? 8 : 4;            // elements per 16-byte chunk
   static constexpr int CPR = D / EPC;                 // chunks per key row
   static constexpr int TASKS = (BN / 4) * CPR;
@@ -286,26 +307,34 @@ __global__ void __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(2))
   const __amdgpu_buffer_rsrc_t rsK = __builtin_amdgcn_make_buffer_rsrc((void*)Kg, 0, slab_bytes, kBufFlags);
   const __amdgpu_buffer_rsrc_t rsV = __builtin_amdgcn_make_buffer_rsrc((void*)Vg, 0, slab_bytes, kBufFlags);
   uint4 kreg[C::NT][4], vreg[C::NT][4];
+  // key row of key u of task group kq: bf16 kq + 16u (the 16 lanes of one LDS write then cover
+  // one 256-byte row, or two adjacent 128-byte rows), f32 4 kq + u
+  auto krow = [](int kq, int u) { return BF16 ? kq + 16 * u : 4 * kq + u; };
   auto fetch = [&](const Tile& t, const int32_t* cols) {
 #pragma unroll
     for (int it = 0; it < C::NT; ++it) {
       const int x = tid + it * C::T;
-      const int c = x % C::CPR, q4 = x / C::CPR;
+      const int c = x % C::CPR, kq = x / C::CPR;
       const bool task = (C::TASKS % C::T == 0) || x < C::TASKS;
       int key[4];
       if (t.kind == 2 && task) {
-        const int4 kc = *reinterpret_cast<const int4*>(&cols[4 * q4]);
-        key[0] = kc.x;
-        key[1] = kc.y;
-        key[2] = kc.z;
-        key[3] = kc.w;
+        if constexpr (BF16) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) key[u] = cols[kq + 16 * u];
+        } else {
+          const int4 kc = *reinterpret_cast<const int4*>(&cols[4 * kq]);
+          key[0] = kc.x;
+          key[1] = kc.y;
+          key[2] = kc.z;
+          key[3] = kc.w;
+        }
       } else {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) key[u] = t.j0 + 4 * q4 + u;
+        for (int u = 0; u < 4; ++u) key[u] = t.j0 + krow(kq, u);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const bool ok = task & (4 * q4 + u < t.nvalid) & (key[u] < S);
+        const bool ok = task & (krow(kq, u) < t.nvalid) & (key[u] < S);
         const int off = ok ? key[u] * (D * (int)sizeof(E)) + 16 * c : (int)slab_bytes;
         auto kv = __builtin_amdgcn_raw_buffer_load_b128(rsK, off, 0, 0);
         auto vv = __builtin_amdgcn_raw_buffer_load_b128(rsV, off, 0, 0);
@@ -319,25 +348,23 @@ __global__ void __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(2))
     for (int it = 0; it < C::NT; ++it) {
       const int x = tid + it * C::T;
       if (x < C::TASKS) {
-        const int c = x % C::CPR, q4 = x / C::CPR;
+        const int c = x % C::CPR, kq = x / C::CPR;
         if constexpr (BF16) {
+          // rows kq + 16u: the swizzles depend on the row mod 16 only, i.e. on kq
+          unsigned char* Kb = reinterpret_cast<unsigned char*>(Ks);
+          unsigned char* Vb = reinterpret_cast<unsigned char*>(Vs);
+          constexpr int KROWB = 2 * C::KS;
+          const int kp = kq * KROWB + 16 * (C::KPAD ? c : (c ^ kswz<D>(kq)));
+          const int vp = kq * C::ROWB + 16 * (c ^ vswz<D>(kq));
 #pragma unroll
-          for (int u = 0; u < 4; ++u) *reinterpret_cast<uint4*>(&Ks[(4 * q4 + u) * C::KS + 8 * c]) = kreg[it][u];
-          // V^T: element e of the 4 rows -> 4 consecutive keys of row d = 8c + e, at the swizzled
-          // 8-byte unit of that row (see vt_unit)
-          const int unit = vt_pos(4 * q4) >> 2;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int w = e >> 1;
-            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-            const uint32_t lo = __builtin_amdgcn_perm((&vreg[it][1].x)[w], (&vreg[it][0].x)[w], sel);
-            const uint32_t hi = __builtin_amdgcn_perm((&vreg[it][3].x)[w], (&vreg[it][2].x)[w], sel);
-            *reinterpret_cast<uint2*>(&Vs[(8 * c + e) * C::VS + 4 * vt_unit(unit, 8 * c + e)]) = make_uint2(lo, hi);
+          for (int u = 0; u < 4; ++u) {
+            *reinterpret_cast<uint4*>(Kb + kp + 16 * u * KROWB) = kreg[it][u];
+            *reinterpret_cast<uint4*>(Vb + vp + 16 * u * C::ROWB) = vreg[it][u];
           }
         } else {
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            const int kk = 4 * q4 + u;
+            const int kk = krow(kq, u);
             const float* kf = reinterpret_cast<const float*>(&kreg[it][u]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) Ks[kk * C::KS + 4 * c + e] = kf[e];
@@ -412,6 +439,17 @@ __global__ void __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(2))
     return row_ok ? m : 0ull;
   };
 
+  // per-lane LDS offsets of the bf16 operand reads.  K (swizzled rows), row r32, logical chunk
+  // 2s + g: koff0 ^ 32s.  V, transposed read of d block x (key row 4 (q16 / 2) + es of each 16):
+  // voff0 ^ 64x.  Both XORs stay inside the swizzled chunk bits of one row.
+  int koff0 = 0, voff0 = 0;
+  if constexpr (BF16) {
+    koff0 = C::KPAD ? (r32 * C::KS + 8 * g) * 2 : r32 * C::ROWB + 16 * (g ^ kswz<D>(r32));
+    const int q16 = lane >> 4, t16 = lane & 15, es = t16 >> 2, as = t16 & 3;
+    const int d = 16 * (q16 & 1) + 4 * as;
+    voff0 = (4 * (q16 >> 1) + es) * C::ROWB + 16 * ((d >> 3) ^ vswz<D>(es)) + 8 * ((d >> 2) & 1);
+  }
+
   auto compute_tile = [&](uint64_t m) {
     f32x16 sacc[2];
 #pragma unroll
@@ -421,7 +459,8 @@ __global__ void __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(2))
       if constexpr (BF16) {
 #pragma unroll
         for (int s = 0; s < C::QS; ++s) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&Ks[(kb * 32 + r32) * C::KS + 16 * s + 8 * g]);
+          const int ko = C::KPAD ? kb * 32 * C::KS * 2 + koff0 + 32 * s : kb * 32 * C::ROWB + (koff0 ^ (32 * s));
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const unsigned char*>(Ks) + ko);
           sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[kb], 0, 0, 0);
         }
       } else {
@@ -489,7 +528,7 @@ __global__ void __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(2))
       if constexpr (BF16) {
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
-          bf16x8 pf, pf_sw;
+          bf16x8 pf;
 #pragma unroll
           for (int t = 0; t < 8; ++t) pf[t] = (__bf16)sacc[kb][8 * mm + t];
           // the row sum of the same bf16 probabilities that weight V, two per instruction
@@ -497,15 +536,14 @@ __global__ void __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
           for (int t = 0; t < 8; t += 2)
             l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[t], pf[t + 1]}, ones, l_run, false);
-#pragma unroll
-          for (int t = 0; t < 8; ++t) pf_sw[t] = pf[t ^ 4];
+          const unsigned char* Vb = reinterpret_cast<const unsigned char*>(Vs) + (kb * 32 + 16 * mm) * C::ROWB;
 #pragma unroll
           for (int x = 0; x < C::OB; ++x) {
-            const int d = 32 * x + r32;
-            const int unit = 2 * (4 * kb + 2 * mm + g);  // first 8-byte unit of this lane's 8 keys
-            const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&Vs[d * C::VS + 4 * (vt_unit(unit, d) & ~1)]);
-            // rows with bit 3 of d/8 set hold the two 4-key halves swapped (see vt_unit)
-            oacc[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, (x & 2) ? pf_sw : pf, oacc[x], 0, 0, 0);
+            const int vo = voff0 ^ (64 * x);
+            const v4i16 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(Vb + vo));
+            const v4i16 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(Vb + 8 * C::ROWB + vo));
+            const v8i16 vf = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+            oacc[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf), pf, oacc[x], 0, 0, 0);
           }
         }
       } else {
@@ -597,21 +635,13 @@ __global__ void __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(2))
 // K and V tiles travel global -> LDS with buffer_load ... lds (no register
 // staging), double-buffered: the loads of tile t+1 are in flight while tile t is
 // computed, one barrier per tile.  Tiles are stored key-row-major with the
-// 16-byte chunks of row R XOR-swizzled (K: chunk ^ (R % 8); V: chunk ^ 2(R % 4))
-// so that the MFMA operand reads are free of bank conflicts.  The V operand of
-// O^T = V^T P^T is read with ds_read_b64_tr_b16, which transposes 4x4 blocks of
+// 16-byte chunks of row R XOR-swizzled (K: chunk ^ kswz(R); V: chunk ^ 2(R % 4))
+// (see kswz and vswz).  The V operand of O^T = V^T P^T is read with ds_read_b64_tr_b16, which transposes 4x4 blocks of
 // 16-bit values across each group of 16 lanes: source lane a + 4e supplies 4
 // consecutive d values of key row key0 + e, and lane 4a + b receives column b of
 // those rows, i.e. 4 consecutive keys of one d -- the layout the MFMA A operand
 // needs.  Row sums come from v_dot2_f32_bf16 on the packed probabilities.
 // ============================================================================
-// Chunk swizzle of row R of a V tile (16-byte chunks XOR'ed with vswz(R % 4)): the 16 lanes of one
-// transposed read take 32 bytes from each of 4 consecutive key rows, and with this swizzle the
-// 8 such segments of a half-wave land on 8 different 32-byte bank groups (measured free of bank
-// conflicts on gfx950 for 256-byte rows; 128-byte rows pair up two rows per 256 bytes).
-template <int D>
-__device__ inline int vswz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
-
 template <int D, int BM>
 struct Cfg3 {
   static constexpr int NW = BM / 32;
@@ -628,9 +658,6 @@ struct Cfg3 {
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef short v8i16 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 template <int D, int BM>
@@ -688,10 +715,11 @@ k_attn_bf16(Params p) {
 
   // ---- tile loads straight into LDS stage `st`: wave w fills key rows [w*LPW*RPL, (w+1)*LPW*RPL)
   // lane constants of the tile loads: key row R = R0 + lane / CPR, chunk slot P = lane % CPR.
-  // R0 is a multiple of RPL (4 or 8) and the wave's first row a multiple of 16, so R % 8 is
-  // (k * RPL) % 8 + lane / CPR with no carry, and R % 4 == (lane / CPR) % 4.
+  // R0 is a multiple of RPL (4 or 8) and the wave's first row a multiple of 16, so
+  // kswz(R) = kswz(k * RPL) ^ kswz(lane / CPR), and R % 4 == (lane / CPR) % 4.
   const int ld_r = lane / C::CPR, ld_p = lane % C::CPR;
-  const int ld_ck = 16 * (ld_p ^ ld_r), ld_cv = 16 * (ld_p ^ vswz<D>(ld_r));
+  static_assert((C::LPW * C::RPL) % 16 == 0, "each wave's first tile row must be a multiple of 16");
+  const int ld_ck = 16 * (ld_p ^ kswz<D>(ld_r)), ld_cv = 16 * (ld_p ^ vswz<D>(ld_r));
   auto issue_tile = [&](const Tile& t, int st, const int32_t* cols) {
     unsigned char* Kst = lds + st * C::STAGE;
     unsigned char* Vst = Kst + C::MAT;
@@ -708,7 +736,7 @@ k_attn_bf16(Params p) {
     for (int k = 0; k < C::LPW; ++k) {
       const int R0 = (wave * C::LPW + k) * C::RPL;
       const int base = R0 + ld_r < lim ? key[k] * C::ROWB : (int)slab_bytes;  // past the slab: zeros
-      const int ck = ld_ck ^ (16 * ((k * C::RPL) & 7));
+      const int ck = ld_ck ^ (16 * kswz<D>(k * C::RPL));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsK, (lds_void_ptr)(Kst + R0 * C::ROWB), 16, base + ck, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsV, (lds_void_ptr)(Vst + R0 * C::ROWB), 16, base + ld_cv, 0, 0, 0);
     }
@@ -792,9 +820,9 @@ k_attn_bf16(Params p) {
   };
 
   // per-lane LDS offsets that do not change from tile to tile
-  int koff[4];  // K row r32, logical chunk 2s + g for s = 0..3 (s + 4 adds 128 bytes)
+  int koff[4];  // K row r32, logical chunk 2s + g for s = 0..3 (s + 4: chunk + 8, offset ^ 128)
 #pragma unroll
-  for (int s = 0; s < 4; ++s) koff[s] = r32 * C::ROWB + 16 * ((2 * s + g) ^ (r32 & 7));
+  for (int s = 0; s < 4; ++s) koff[s] = r32 * C::ROWB + 16 * ((2 * s + g) ^ kswz<D>(r32));
   const int q16 = lane >> 4, t16 = lane & 15, es = t16 >> 2, as = t16 & 3;
   int voff[C::OB];  // transposed-read source address for d block x (key row key0 + es)
 #pragma unroll
@@ -813,8 +841,7 @@ k_attn_bf16(Params p) {
     for (int kbl = 0; kbl < C::NKB; ++kbl)
 #pragma unroll
       for (int s = 0; s < C::QS; ++s)
-        kf[kbl][s] = *reinterpret_cast<const bf16x8*>(Kst + kbl * 32 * C::ROWB + koff[s & 3] +
-                                                      (s >> 2) * 128);
+        kf[kbl][s] = *reinterpret_cast<const bf16x8*>(Kst + kbl * 32 * C::ROWB + (koff[s & 3] ^ ((s >> 2) * 128)));
 #pragma unroll
     for (int kbl = 0; kbl < C::NKB; ++kbl) {
 #pragma unroll
