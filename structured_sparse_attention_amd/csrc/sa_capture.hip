@@ -255,6 +255,9 @@ __global__ void __launch_bounds__(kThreads)
 // LDS; pass 2 walks the key tiles once, recomputes each sequence's scores and sums
 // p_b / B in registers, so a map element is written once per chunk (added to the
 // previous chunks' sum after the first).  No other workgroup touches these rows.
+// Each pass is one software-pipelined loop over its (sequence, key tile) steps: the
+// K tile and the Q fragment of step n + 1 are loaded into registers while step n is
+// computed from the other LDS buffer, with one barrier per step.
 // ---------------------------------------------------------------------------
 typedef __bf16 mbf16x8 __attribute__((ext_vector_type(8)));
 typedef float mf32x16 __attribute__((ext_vector_type(16)));
@@ -267,18 +270,36 @@ __global__ void __launch_bounds__(128) k_maps(const void* qv, const void* kv, in
   using QF = typename std::conditional<BF16, mbf16x8, float>::type;
   constexpr int QS = BF16 ? D / 16 : D / 2;           // MFMA k-steps over d
   constexpr int KSTR = BF16 ? D + 8 : D + 1;          // LDS row stride of the K tile (elements)
-  __shared__ __attribute__((aligned(16))) E Ks[64 * KSTR];
+  constexpr int KW = 64, NKB = 2;                     // keys and 32-key blocks per key tile
+  constexpr int CH = D * (int)sizeof(E) / 16;         // 16-byte chunks per key row
+  constexpr int NL = KW * CH / 128;                   // chunks of a tile per thread
+  __shared__ __attribute__((aligned(16))) E Ks[2][KW * KSTR];
   __shared__ float st_m[kMapChunk][128], st_il[kMapChunk][128];  // per lane: its row's max, 1/sum
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, r32 = lane & 31;
   const int nrb = (L + 63) / 64;
-  const int h = blockIdx.x / nrb, rb = blockIdx.x % nrb;
+  // Workgroup k runs on XCD k % 8.  When the kv heads split evenly over the 8 XCDs, XCD x takes
+  // the row blocks of kv heads x, x + 8, ... (one group at a time, heaviest row blocks first), so
+  // the K tiles of a group, shared by its query heads and row blocks, stay in that XCD's L2.
+  int h, rb;
+  if (hkv % 8 == 0) {
+    const int hpg = hq / hkv, per_group = hpg * nrb;
+    const int x = (int)(blockIdx.x % 8u), slot = (int)(blockIdx.x / 8u);
+    const int gl = slot / per_group, rem = slot % per_group;
+    rb = nrb - 1 - rem / hpg;
+    h = (x + 8 * gl) * hpg + rem % hpg;
+  } else {
+    h = blockIdx.x / nrb;
+    rb = blockIdx.x % nrb;
+  }
   const int kvh = h / (hq / hkv);
   const int i = rb * 64 + wave * 32 + r32;  // this lane's query row
   const bool row_ok = i < L;
   const float invB = 1.0f / (float)B;
   const bool vec_rows = (L & 3) == 0;  // map rows 16-byte aligned
   float* mrow = maps + ((int64_t)h * L + (row_ok ? i : 0)) * L;
+  const int last = min(L, rb * 64 + 64) - 1;  // last query row (and last key) of the row block
+  const int nkt = last / KW + 1;               // key tiles of this row block
 
   // zeros above the block diagonal (keys of the tiles past this row block)
   for (int r = 0; r < 64 && rb * 64 + r < L; ++r) {
@@ -286,8 +307,7 @@ __global__ void __launch_bounds__(128) k_maps(const void* qv, const void* kv, in
     for (int jj = (rb + 1) * 64 + tid; jj < L; jj += 128) zrow[jj] = 0.0f;
   }
 
-  auto kbase = [&](int b) { return static_cast<const E*>(kv) + ((int64_t)b * hkv + kvh) * L * (int64_t)D; };
-  auto load_q = [&](int b, QF (&qf)[QS]) {
+  auto load_q = [&](int b, QF (&qf)[QS]) {  // global -> registers
     const E* Qb = static_cast<const E*>(qv) + ((int64_t)b * hq + h) * L * (int64_t)D;
 #pragma unroll
     for (int s = 0; s < QS; ++s) {
@@ -300,122 +320,172 @@ __global__ void __launch_bounds__(128) k_maps(const void* qv, const void* kv, in
       }
     }
   };
-  auto load_tile = [&](const E* Kb, int kt) {  // keys kt*64 .. kt*64+63 of one sequence into LDS
-    __syncthreads();
-    constexpr int CH = D * (int)sizeof(E) / 16;  // 16-byte chunks per key row
-    for (int x = tid; x < 64 * CH; x += 128) {
-      const int r = x / CH, c = x % CH, j = kt * 64 + r;
-      uint4 u = make_uint4(0u, 0u, 0u, 0u);
-      if (j < L) u = *(reinterpret_cast<const uint4*>(Kb + (int64_t)j * D) + c);
-      E* dst = Ks + r * KSTR + c * (16 / (int)sizeof(E));
+  auto load_k = [&](int b, int kt, uint4 (&kr)[NL]) {  // keys kt*KW .. kt*KW+KW-1 of sequence b -> registers
+    const E* Kb = static_cast<const E*>(kv) + ((int64_t)b * hkv + kvh) * L * (int64_t)D;
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int x = tid + 128 * u, r = x / CH, c = x % CH, j = kt * KW + r;
+      kr[u] = j < L ? *(reinterpret_cast<const uint4*>(Kb + (int64_t)j * D) + c) : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto store_k = [&](int buf, const uint4 (&kr)[NL]) {  // registers -> LDS buffer
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int x = tid + 128 * u, r = x / CH, c = x % CH;
+      E* dst = Ks[buf] + r * KSTR + c * (16 / (int)sizeof(E));
       if constexpr (BF16) {
-        *reinterpret_cast<uint4*>(dst) = u;
+        *reinterpret_cast<uint4*>(dst) = kr[u];
       } else {
-        dst[0] = __uint_as_float(u.x);
-        dst[1] = __uint_as_float(u.y);
-        dst[2] = __uint_as_float(u.z);
-        dst[3] = __uint_as_float(u.w);
+        dst[0] = __uint_as_float(kr[u].x);
+        dst[1] = __uint_as_float(kr[u].y);
+        dst[2] = __uint_as_float(kr[u].z);
+        dst[3] = __uint_as_float(kr[u].w);
       }
     }
-    __syncthreads();
   };
-  // scaled logits of the LDS tile for this lane's row: value v of block kb is key
-  // kt*64 + kb*32 + 8(v/4) + 4g + v%4; keys past the row are -inf
-  auto scores = [&](const QF (&qf)[QS], int kt, float (&x)[2][16]) {
+  // raw logits q . k of the LDS tile for this lane's row: value v of block kb is key
+  // kt*KW + kb*32 + 8(v/4) + 4g + v%4.  Only the last tile of the row block holds keys past a row;
+  // there they are set to -inf, which every later step keeps (the scale is positive).
+  auto scores = [&](int buf, const QF (&qf)[QS], int kt, float (&x)[NKB][16]) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb) {
       mf32x16 acc;
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
 #pragma unroll
       for (int s = 0; s < QS; ++s) {
         if constexpr (BF16) {
-          const mbf16x8 kf = *reinterpret_cast<const mbf16x8*>(&Ks[(kb * 32 + r32) * KSTR + 16 * s + 8 * g]);
+          const mbf16x8 kf = *reinterpret_cast<const mbf16x8*>(&Ks[buf][(kb * 32 + r32) * KSTR + 16 * s + 8 * g]);
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], acc, 0, 0, 0);
         } else {
-          const float kf = Ks[(kb * 32 + r32) * KSTR + 2 * s + g];
+          const float kf = Ks[buf][(kb * 32 + r32) * KSTR + 2 * s + g];
           acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kf, qf[s], acc, 0, 0, 0);
         }
       }
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int j = kt * 64 + kb * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-        x[kb][v] = (j <= i) ? acc[v] * scale_log2 : -INFINITY;
+      for (int v = 0; v < 16; ++v) x[kb][v] = acc[v];
+    }
+    if (kt == nkt - 1) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int j = kt * KW + kb * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+          if (j > i) x[kb][v] = -INFINITY;
+        }
+    }
+  };
+  // One pass over n_steps (sequence, key tile) steps; step n is (bb, kt) = at(n).  For each step
+  // `body(n, bb, kt, buf, qf)` runs on the staged tile.
+  auto pipeline = [&](int n_steps, auto at, auto body) {
+    QF qc[QS], qn[QS];
+    uint4 kr[NL];
+    int bb, kt;
+    at(0, bb, kt);
+    load_q(bb, qc);
+    load_k(bb, kt, kr);
+    store_k(0, kr);
+    __syncthreads();
+    for (int n = 0; n < n_steps; ++n) {
+      at(n, bb, kt);
+      int bn = bb, ktn = kt;
+      const bool more = n + 1 < n_steps;
+      if (more) {
+        at(n + 1, bn, ktn);
+        load_k(bn, ktn, kr);
+        if (bn != bb) load_q(bn, qn);
       }
+      body(n, bb, kt, n & 1, qc);
+      if (more) {
+        store_k((n + 1) & 1, kr);
+        if (bn != bb) {
+#pragma unroll
+          for (int s = 0; s < QS; ++s) qc[s] = qn[s];
+        }
+      }
+      __syncthreads();
     }
   };
 
   for (int b0 = 0; b0 < B; b0 += kMapChunk) {
     const int nb = min(kMapChunk, B - b0);
-    // pass 1: row max and 1/sum of each sequence of the chunk
-    for (int bb = 0; bb < nb; ++bb) {
-      QF qf[QS];
-      load_q(b0 + bb, qf);
-      float m = -INFINITY, l = 0.0f;
-      for (int kt = 0; kt <= rb; ++kt) {
-        load_tile(kbase(b0 + bb), kt);
-        float x[2][16];
-        scores(qf, kt, x);
-        float tmax = -INFINITY;
+    // pass 1: row max and 1/sum of each sequence of the chunk (steps: sequence-major)
+    float m = -INFINITY, l = 0.0f;
+    pipeline(
+        nb * nkt, [&](int n, int& bb, int& kt) { bb = b0 + n / nkt; kt = n % nkt; },
+        [&](int n, int bb, int kt, int buf, const QF (&qf)[QS]) {
+          float x[NKB][16];
+          scores(buf, qf, kt, x);
+          float tmax = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, x[kb][v]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));  // the row's other keys sit in lane ^ 32
-        const float mn = fmaxf(m, tmax);  // finite: key kt*64 <= i for every kt <= rb
-        float part = 0.0f;
+            for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, x[kb][v]);
+          tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));  // the row's other keys sit in lane ^ 32
+          // the scaled maximum (scaling by a positive factor keeps the order); finite: key kt*KW <= i
+          // for every tile of the row block
+          const float mn = fmaxf(m, tmax * scale_log2);
+          float part = 0.0f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) part += __builtin_amdgcn_exp2f(x[kb][v] - mn);
-        part += __shfl_xor(part, 32, 64);
-        l = (m == -INFINITY ? 0.0f : l * __builtin_amdgcn_exp2f(m - mn)) + part;
-        m = mn;
-      }
-      st_m[bb][tid] = m;  // read back by this lane only
-      st_il[bb][tid] = 1.0f / l;
-    }
-    // pass 2: per key tile, the chunk's probabilities summed in registers
-    for (int kt = 0; kt <= rb; ++kt) {
-      float acc[2][16];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[kb][v] = 0.0f;
-      for (int bb = 0; bb < nb; ++bb) {
-        QF qf[QS];
-        load_q(b0 + bb, qf);
-        load_tile(kbase(b0 + bb), kt);
-        float x[2][16];
-        scores(qf, kt, x);
-        const float m = st_m[bb][tid], il = st_il[bb][tid];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) acc[kb][v] += __builtin_amdgcn_exp2f(x[kb][v] - m) * il;
-      }
-      if (row_ok) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int qd = 0; qd < 4; ++qd) {
-            const int j0 = kt * 64 + kb * 32 + 8 * qd + 4 * g;
-            if (vec_rows && j0 + 3 < L) {
-              float4* dst = reinterpret_cast<float4*>(mrow + j0);
-              float4 cur = b0 == 0 ? make_float4(0.0f, 0.0f, 0.0f, 0.0f) : *dst;
-              cur.x += acc[kb][4 * qd + 0] * invB;
-              cur.y += acc[kb][4 * qd + 1] * invB;
-              cur.z += acc[kb][4 * qd + 2] * invB;
-              cur.w += acc[kb][4 * qd + 3] * invB;
-              *dst = cur;
-            } else {
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (j0 + e < L) mrow[j0 + e] = (b0 == 0 ? 0.0f : mrow[j0 + e]) + acc[kb][4 * qd + e] * invB;
-            }
+            for (int v = 0; v < 16; ++v) part += __builtin_amdgcn_exp2f(__builtin_fmaf(x[kb][v], scale_log2, -mn));
+          part += __shfl_xor(part, 32, 64);
+          l = (m == -INFINITY ? 0.0f : l * __builtin_amdgcn_exp2f(m - mn)) + part;
+          m = mn;
+          if (kt == nkt - 1) {  // last tile of this sequence
+            st_m[bb - b0][tid] = m;  // read back by this lane only
+            st_il[bb - b0][tid] = 1.0f / l;
+            m = -INFINITY;
+            l = 0.0f;
           }
-      }
-    }
+        });
+    // pass 2: per key tile, the chunk's probabilities summed in registers (steps: tile-major)
+    float acc[NKB][16];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[kb][v] = 0.0f;
+    pipeline(
+        nkt * nb, [&](int n, int& bb, int& kt) { kt = n / nb; bb = b0 + n % nb; },
+        [&](int n, int bb, int kt, int buf, const QF (&qf)[QS]) {
+          float x[NKB][16];
+          scores(buf, qf, kt, x);
+          const float mb = st_m[bb - b0][tid], il = st_il[bb - b0][tid];
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              acc[kb][v] += __builtin_amdgcn_exp2f(__builtin_fmaf(x[kb][v], scale_log2, -mb)) * il;
+          if (bb - b0 == nb - 1) {  // last sequence of the chunk: this key tile is complete
+            if (row_ok) {
+#pragma unroll
+              for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int qd = 0; qd < 4; ++qd) {
+                  const int j0 = kt * KW + kb * 32 + 8 * qd + 4 * g;
+                  if (j0 > last) continue;  // above the block diagonal: zeros, written above
+                  if (vec_rows && j0 + 3 < L) {
+                    float4* dst = reinterpret_cast<float4*>(mrow + j0);
+                    float4 cur = b0 == 0 ? make_float4(0.0f, 0.0f, 0.0f, 0.0f) : *dst;
+                    cur.x += acc[kb][4 * qd + 0] * invB;
+                    cur.y += acc[kb][4 * qd + 1] * invB;
+                    cur.z += acc[kb][4 * qd + 2] * invB;
+                    cur.w += acc[kb][4 * qd + 3] * invB;
+                    *dst = cur;
+                  } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                      if (j0 + e < L) mrow[j0 + e] = (b0 == 0 ? 0.0f : mrow[j0 + e]) + acc[kb][4 * qd + e] * invB;
+                  }
+                }
+            }
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+              for (int v = 0; v < 16; ++v) acc[kb][v] = 0.0f;
+          }
+        });
   }
 }
 
