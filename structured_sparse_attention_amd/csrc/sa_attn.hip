@@ -251,7 +251,9 @@ __global__ void __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(2))
   __shared__ __attribute__((aligned(16))) E Vs[C::V_ELEMS];
   __shared__ __attribute__((aligned(16))) int32_t cols_sh[3][BN];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform: kept in a scalar register, so that row and LDS offsets derived from it
+  // (and M0 of the LDS-direct loads) are scalar arithmetic
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, r32 = lane & 31;
   int b, h, rb;
   decode_item(p, b, h, rb);
@@ -667,7 +669,9 @@ k_attn_bf16(Params p) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * C::STAGE];
   __shared__ __attribute__((aligned(16))) int32_t cols_sh[3][BN];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform: kept in a scalar register, so that row and LDS offsets derived from it
+  // (and M0 of the LDS-direct loads) are scalar arithmetic
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, r32 = lane & 31;
   const int rh = wave;  // this wave's 32 rows
   int b, h, rb;
@@ -719,7 +723,7 @@ k_attn_bf16(Params p) {
   // kswz(R) = kswz(k * RPL) ^ kswz(lane / CPR), and R % 4 == (lane / CPR) % 4.
   const int ld_r = lane / C::CPR, ld_p = lane % C::CPR;
   static_assert((C::LPW * C::RPL) % 16 == 0, "each wave's first tile row must be a multiple of 16");
-  const int ld_ck = 16 * (ld_p ^ kswz<D>(ld_r)), ld_cv = 16 * (ld_p ^ vswz<D>(ld_r));
+  const int ld_ck = 16 * (ld_p ^ kswz<D>(ld_r)), ld_cv = 16 * (ld_p ^ vswz<D>(ld_r)), ld_row = ld_r * C::ROWB;
   auto issue_tile = [&](const Tile& t, int st, const int32_t* cols) {
     unsigned char* Kst = lds + st * C::STAGE;
     unsigned char* Vst = Kst + C::MAT;
@@ -732,13 +736,35 @@ k_attn_bf16(Params p) {
     }
     // rows of the tile that hold keys (< S for a band tile; list entries are always < S)
     const int lim = t.kind == 2 ? t.nvalid : min(t.nvalid, S - t.j0);
+    if (lim == BN && t.kind == 1) {
+      // whole band tile: the row offset is uniform (scalar offset), the lane part a constant
 #pragma unroll
-    for (int k = 0; k < C::LPW; ++k) {
-      const int R0 = (wave * C::LPW + k) * C::RPL;
-      const int base = R0 + ld_r < lim ? key[k] * C::ROWB : (int)slab_bytes;  // past the slab: zeros
-      const int ck = ld_ck ^ (16 * kswz<D>(k * C::RPL));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsK, (lds_void_ptr)(Kst + R0 * C::ROWB), 16, base + ck, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsV, (lds_void_ptr)(Vst + R0 * C::ROWB), 16, base + ld_cv, 0, 0, 0);
+      for (int k = 0; k < C::LPW; ++k) {
+        const int R0 = (wave * C::LPW + k) * C::RPL;
+        const int so = (t.j0 + R0) * C::ROWB;
+        const int ck = ld_ck ^ (16 * kswz<D>(k * C::RPL));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsK, (lds_void_ptr)(Kst + R0 * C::ROWB), 16, ld_row + ck, so, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsV, (lds_void_ptr)(Vst + R0 * C::ROWB), 16, ld_row + ld_cv, so, 0, 0);
+      }
+    } else if (lim == BN) {
+      // whole gathered tile: every row holds a key
+#pragma unroll
+      for (int k = 0; k < C::LPW; ++k) {
+        const int R0 = (wave * C::LPW + k) * C::RPL;
+        const int base = key[k] * C::ROWB;
+        const int ck = ld_ck ^ (16 * kswz<D>(k * C::RPL));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsK, (lds_void_ptr)(Kst + R0 * C::ROWB), 16, base + ck, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsV, (lds_void_ptr)(Vst + R0 * C::ROWB), 16, base + ld_cv, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < C::LPW; ++k) {
+        const int R0 = (wave * C::LPW + k) * C::RPL;
+        const int base = R0 + ld_r < lim ? key[k] * C::ROWB : (int)slab_bytes;  // past the slab: zeros
+        const int ck = ld_ck ^ (16 * kswz<D>(k * C::RPL));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsK, (lds_void_ptr)(Kst + R0 * C::ROWB), 16, base + ck, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsV, (lds_void_ptr)(Vst + R0 * C::ROWB), 16, base + ld_cv, 0, 0, 0);
+      }
     }
   };
 
