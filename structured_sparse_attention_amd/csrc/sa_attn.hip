@@ -774,30 +774,23 @@ k_attn_bf16(Params p) {
     uint32_t w0, w1, w2;
     uint64_t xin;
     bool full;  // every key of the tile is retained for every row of the block (wave-uniform)
+    bool cand;  // band tile that may be full: decided in mask_finish from fw
+    uint32_t fw;
   };
+  // the offsets a band tile shows the block, [b0 - j0 - 63, b1 - j0], span at most BM + 63 bits,
+  // i.e. at most kWords bitmap words from word omin / 32; lane k < kWords holds word k of them
+  constexpr int kWords = (BM + BN - 1 + 31) / 32 + 1;
   auto mask_loads = [&](const Tile& t, const int32_t* cols) -> MaskIn {
-    MaskIn mi{0u, 0u, 0u, 0ull, false};
+    MaskIn mi{0u, 0u, 0u, 0ull, false, false, 0u};
     if (t.kind == 2) mi.full = (t.nvalid == BN) && (cols[BN - 1] <= b0);
     if (t.kind == 1) {
       // full when the whole tile is at or below the block's first row and every offset any row of
-      // the block sees in it, [b0 - j0 - 63, b1 - j0], is a diagonal (checked on the bitmap words)
+      // the block sees in it is a diagonal: one vector load spreads the words over lanes, and
+      // mask_finish checks them (by then the load has had the current tile's compute to land)
       if (t.nvalid == BN && t.j0 + BN - 1 <= b0) {
-        // the offsets span at most BM + 63 bits, i.e. at most (BM + 94) / 32 words from word
-        // omin/32; all of them are read at once (scalar loads) and checked without branches
-        const int omin = b0 - t.j0 - (BN - 1), omax = b1 - t.j0;
-        const int w0 = omin >> 5;
-        constexpr int kWords = (BM + BN - 1 + 31) / 32 + 1;
-        bool f = true;
-#pragma unroll
-        for (int k = 0; k < kWords; ++k) {
-          const int w = w0 + k;
-          const int a = max(omin - 32 * w, 0), e = min(omax - 32 * w, 31);
-          const uint32_t need =
-              a <= e ? ((e == 31 ? 0xffffffffu : ((1u << (e + 1)) - 1u)) & ~((1u << a) - 1u)) : 0u;
-          const uint32_t word = dbh[min(w, p.nwords - 1)];
-          f = f & ((word & need) == need);
-        }
-        mi.full = f;
+        const int w = ((b0 - t.j0 - (BN - 1)) >> 5) + min(lane, kWords - 1);
+        mi.cand = true;
+        mi.fw = dbh[min(w, p.nwords - 1)];
       }
       const int wl = i - t.j0 - (BN - 1);
       const int wi = wl >> 5;
@@ -820,6 +813,14 @@ k_attn_bf16(Params p) {
   };
   auto mask_finish = [&](const Tile& t, const MaskIn& mi, const int32_t* cols) -> uint64_t {
     if (mi.full) return ~0ull;
+    if (mi.cand) {
+      const int omin = b0 - t.j0 - (BN - 1), omax = b1 - t.j0;
+      const int w = (omin >> 5) + lane;
+      const int a = max(omin - 32 * w, 0), e = min(omax - 32 * w, 31);
+      const uint32_t need =
+          (lane < kWords && a <= e) ? ((e == 31 ? 0xffffffffu : ((1u << (e + 1)) - 1u)) & ~((1u << a) - 1u)) : 0u;
+      if (__all((mi.fw & need) == need)) return ~0ull;
+    }
     uint64_t m = 0;
     if (t.kind == 1) {
       const int base = i - t.j0;
@@ -966,7 +967,7 @@ k_attn_bf16(Params p) {
   __syncthreads();
   for (int n = 0; cur.kind != 0; ++n) {
     const int bx = (n + 1) % 3, bz = (n + 2) % 3;
-    MaskIn mi{0u, 0u, 0u, 0ull, false};
+    MaskIn mi{0u, 0u, 0u, 0ull, false, false, 0u};
     if (nxt.kind != 0) {
       mi = mask_loads(nxt, cols_sh[bx]);
       issue_tile(nxt, (n + 1) & 1, cols_sh[bx]);
