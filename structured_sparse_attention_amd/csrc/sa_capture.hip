@@ -71,6 +71,66 @@ __device__ inline float wave_max(float x) {
 // How a row's keep flags are decided in the element pass.
 enum { kRowThreshold = 0, kRowAll = 1, kRowNone = 2, kRowEach = 3 };
 
+// The keep rule of one causal row from its fp32 extremes (pass 2 below explains why a threshold is
+// exact): mode, and for kRowThreshold the smallest float that passes.  At lambda = 0.5 the search
+// starts from the inverse of the transform, a = (1 + (ymin + tau * range) / 2)^2 - eps, which is a
+// few fp64 roundings from the answer: a short walk over neighbouring floats settles it, and a
+// bisection over what is left covers any start that is further off.  The answer does not depend on
+// the start: it is the unique smallest passing value of a monotone test.
+template <int KIND>
+__device__ inline void row_rule(float amin, float amax, double eps, double lambda, double tau, int& mode,
+                                float& thr) {
+#pragma clang fp contract(off)
+  const double ymin = box_cox<KIND>(amin, eps, lambda);
+  const double ymax = box_cox<KIND>(amax, eps, lambda);
+  mode = kRowEach;
+  thr = 0.0f;
+  if (ymax == ymin) {
+    mode = 1.0 >= tau ? kRowAll : kRowNone;  // flat: t = 1 for every element
+    return;
+  }
+  if (!(amin >= 0.0f && amax < INFINITY)) return;
+  const double range = ymax - ymin;
+  auto pass = [&](uint32_t bits) { return (box_cox<KIND>(__uint_as_float(bits), eps, lambda) - ymin) / range >= tau; };
+  const uint32_t bmin = __float_as_uint(amin) & 0x7fffffffu, bmax = __float_as_uint(amax);
+  if (!pass(bmax)) {
+    mode = kRowNone;
+    return;
+  }
+  mode = kRowThreshold;
+  uint32_t lo = bmin, hi = bmax;  // the answer lies in [lo, hi], and hi passes
+  if constexpr (KIND == kBoxCoxHalf) {
+    const double sr = 1.0 + 0.5 * (ymin + tau * range);
+    const double a = sr > 0.0 ? sr * sr - eps : 0.0;
+    const uint32_t c = a <= (double)amin ? bmin : a >= (double)amax ? bmax : __float_as_uint((float)a);
+    if (pass(c)) {
+      hi = c;
+      for (int k = 0; k < 8 && hi > lo; ++k) {
+        if (!pass(hi - 1)) {
+          lo = hi;  // hi passes and the float below it does not
+          break;
+        }
+        --hi;
+      }
+    } else {
+      lo = c + 1;  // c < bmax here, since bmax passes
+      for (int k = 0; k < 8 && lo < hi; ++k) {
+        if (pass(lo)) {
+          hi = lo;  // everything below lo failed
+          break;
+        }
+        ++lo;
+      }
+    }
+  }
+  while (lo < hi) {
+    const uint32_t mid = lo + ((hi - lo) >> 1);
+    if (pass(mid)) hi = mid;
+    else lo = mid + 1;
+  }
+  thr = __uint_as_float(lo);
+}
+
 template <int KIND>
 __global__ void __launch_bounds__(kThreads)
     k_capture(const float* maps, int32_t L, double lambda, double eps, double tau, double mu, int32_t norm_scope,
@@ -169,29 +229,9 @@ __global__ void __launch_bounds__(kThreads)
   // few ulp of tau, the cells that may differ from a correctly rounded evaluation anyway.  Rows with
   // a negative or non-finite extreme test each element.
   for (int r = tid; r < L; r += kThreads) {
-    const float amin = rmin[r], amax = rmax[r];
-    const double ymin = box_cox<KIND>(amin, eps, lambda);
-    const double ymax = box_cox<KIND>(amax, eps, lambda);
-    int mode = kRowEach;
-    float thr = 0.0f;
-    if (ymax == ymin) {
-      mode = 1.0 >= tau ? kRowAll : kRowNone;  // flat: t = 1 for every element
-    } else if (amin >= 0.0f && amax < INFINITY) {
-      const double range = ymax - ymin;
-      auto pass = [&](float a) { return (box_cox<KIND>(a, eps, lambda) - ymin) / range >= tau; };
-      if (!pass(amax)) {
-        mode = kRowNone;
-      } else {
-        uint32_t lo = __float_as_uint(amin) & 0x7fffffffu, hi = __float_as_uint(amax);
-        while (lo < hi) {
-          const uint32_t mid = lo + ((hi - lo) >> 1);
-          if (pass(__uint_as_float(mid))) hi = mid;
-          else lo = mid + 1;
-        }
-        mode = kRowThreshold;
-        thr = __uint_as_float(lo);
-      }
-    }
+    int mode;
+    float thr;
+    row_rule<KIND>(rmin[r], rmax[r], eps, lambda, tau, mode, thr);
     rmode[r] = mode;
     rthr[r] = thr;
   }
@@ -235,6 +275,158 @@ __global__ void __launch_bounds__(kThreads)
   }
   __syncthreads();
   for (int r = tid; r < L; r += kThreads) {
+    const double size = (double)(L - r);
+    keep_diag[map * L + r] = ((double)hd[r] / size) >= mu;
+    keep_vert[map * L + r] = ((double)hv[r] / size) >= mu;
+    if (diag_hits) diag_hits[map * L + r] = hd[r];
+    if (vert_hits) vert_hits[map * L + r] = hv[r];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// One read of the map: the same keep flags and hits as k_capture for lambda = 0.5, per-row
+// extremes (norm_scope 0) and L <= 512 with L % 4 == 0 (the capture length of the pages is 512).
+// 256 threads per map.  A wave holds kRowBatch consecutive causal rows in registers (lane l:
+// columns 4(l + 64u) .. +3), reduces each row's extremes across the wave, lets lane q find row q's
+// rule (row_rule, all rows of the batch at once), and counts hits from the same registers:
+// diagonal hits with LDS atomics, vertical hits in registers (the lane's columns are fixed) added
+// to LDS once at the end.
+// ---------------------------------------------------------------------------
+constexpr int kRowThreads = 256, kRowBatch = 8, kRowMaxL = 512;
+
+__global__ void __launch_bounds__(kRowThreads)
+    k_capture_rows(const float* maps, int32_t L, double eps, double tau, double mu, uint8_t* keep_diag,
+                   uint8_t* keep_vert, int32_t* diag_hits, int32_t* vert_hits, uint8_t* true_mask) {
+#pragma clang fp contract(off)
+  constexpr int NU = kRowMaxL / 256;  // float4 chunks per lane and row
+  constexpr int NW = kRowThreads / 64;
+  constexpr int kDiag = kRowBatch + 3;  // diagonals of one chunk's cells in a batch
+  __shared__ int32_t hd[kRowMaxL + 64], hv[kRowMaxL];  // hd[kRowMaxL + lane]: a sink for zero adds
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t map = blockIdx.x;
+  const float* A = maps + map * (int64_t)L * L;
+  const int nq = L / 4;  // float4 per row
+  const uint32_t map_bytes = (uint32_t)L * L * 4u;
+  const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, map_bytes, 0x00020000);
+  for (int r = tid; r < kRowMaxL + 64; r += kRowThreads) hd[r] = 0;
+  for (int r = tid; r < kRowMaxL; r += kRowThreads) hv[r] = 0;
+  __syncthreads();
+  int32_t vh[NU][4] = {};  // vertical hits of this lane's columns
+  for (int i0 = kRowBatch * wave; i0 < L; i0 += kRowBatch * NW) {
+    // the batch's causal cells; cells past the row, the map or the rows read as zero (buffer range)
+    float4 a[kRowBatch][NU];
+#pragma unroll
+    for (int q = 0; q < kRowBatch; ++q)
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const int c = lane + 64 * u, i = i0 + q;
+        const uint32_t off = (i < L && c < nq && 4 * c <= i) ? (uint32_t)(i * L + 4 * c) * 4u : map_bytes;
+        a[q][u] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rsA, off, 0, 0));
+      }
+    // extremes of each causal row
+    float mn[kRowBatch], mx[kRowBatch];
+#pragma unroll
+    for (int q = 0; q < kRowBatch; ++q) {
+      mn[q] = INFINITY;
+      mx[q] = -INFINITY;
+      const int i = i0 + q;
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const int c = lane + 64 * u;
+        const float v[4] = {a[q][u].x, a[q][u].y, a[q][u].z, a[q][u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool in = (c < nq) & (4 * c + e <= i);
+          mn[q] = fminf(mn[q], in ? v[e] : INFINITY);
+          mx[q] = fmaxf(mx[q], in ? v[e] : -INFINITY);
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kRowBatch; ++q) {
+      mn[q] = wave_min(mn[q]);
+      mx[q] = wave_max(mx[q]);
+    }
+    // lane q < kRowBatch: the rule of row i0 + q
+    float amin = mn[0], amax = mx[0];
+#pragma unroll
+    for (int q = 1; q < kRowBatch; ++q)
+      if (lane == q) {
+        amin = mn[q];
+        amax = mx[q];
+      }
+    int mode = kRowNone;
+    float thr = 0.0f;
+    if (lane < kRowBatch && i0 + lane < L) row_rule<kBoxCoxHalf>(amin, amax, eps, 0.5, tau, mode, thr);
+    // keep flags and hits without per-element branches.  Cell (i0 + q, 4c + e) lies on diagonal
+    // i0 - 4c + (q - e): per chunk the lane's cells fall on kDiag diagonals, counted in registers
+    int32_t dc[NU][kDiag] = {};
+#pragma unroll
+    for (int q = 0; q < kRowBatch; ++q) {
+      const int i = i0 + q;
+      const int qm = __builtin_amdgcn_readlane(mode, q);  // uniform
+      const float qt = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(thr), q));
+      // 0/1 flags combined with bitwise operators: no branches per element
+      const uint32_t all = qm == kRowAll, thr_mode = qm == kRowThreshold, row_in = i < L;
+      uint8_t* mrow = (true_mask && i < L && qm != kRowEach) ? true_mask + (map * L + i) * (int64_t)L : nullptr;
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const int c = lane + 64 * u;
+        const float v[4] = {a[q][u].x, a[q][u].y, a[q][u].z, a[q][u].w};
+        uint32_t packed = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t in = row_in & (uint32_t)(c < nq) & (uint32_t)(4 * c + e <= i);
+          const int32_t k1 = (int32_t)(in & (all | (thr_mode & (uint32_t)(v[e] >= qt))));
+          vh[u][e] += k1;
+          dc[u][q - e + 3] += k1;
+          packed |= (uint32_t)k1 << (8 * e);
+        }
+        if (mrow && c < nq) *reinterpret_cast<uint32_t*>(mrow + 4 * c) = packed;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int c = lane + 64 * u;
+#pragma unroll
+      for (int k = 0; k < kDiag; ++k) atomicAdd(&hd[dc[u][k] ? i0 - 4 * c + k - 3 : kRowMaxL + lane], dc[u][k]);
+    }
+    // rows with a negative or non-finite extreme: each element tested in fp64, from memory
+    const uint64_t each = __ballot(lane < kRowBatch && mode == kRowEach);
+    if (each) {
+#pragma unroll 1
+      for (int q = 0; q < kRowBatch; ++q) {
+        if (!((each >> q) & 1)) continue;
+        const int i = i0 + q;
+        const float qmin = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(amin), q));
+        const float qmax = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(amax), q));
+        const double ymin = box_cox<kBoxCoxHalf>(qmin, eps, 0.5);
+        const double range = box_cox<kBoxCoxHalf>(qmax, eps, 0.5) - ymin;
+        uint8_t* mrow = true_mask ? true_mask + (map * L + i) * (int64_t)L : nullptr;
+        for (int j = lane; j < L; j += 64) {
+          uint8_t keep = 0;
+          if (j <= i) {
+            keep = (box_cox<kBoxCoxHalf>(A[(int64_t)i * L + j], eps, 0.5) - ymin) / range >= tau;
+            if (keep) {
+              atomicAdd(&hd[i - j], 1);
+              atomicAdd(&hv[j], 1);
+            }
+          }
+          if (mrow) mrow[j] = keep;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int c = lane + 64 * u;
+    if (c < nq)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (vh[u][e]) atomicAdd(&hv[4 * c + e], vh[u][e]);
+  }
+  __syncthreads();
+  for (int r = tid; r < L; r += kRowThreads) {
     const double size = (double)(L - r);
     keep_diag[map * L + r] = ((double)hd[r] / size) >= mu;
     keep_vert[map * L + r] = ((double)hv[r] / size) >= mu;
@@ -629,6 +821,11 @@ __global__ void __launch_bounds__(kDescThreads)
 hipError_t launch_capture(const float* maps, int32_t n_maps, int32_t L, double lambda, double eps, double tau,
                           double mu, int32_t norm_scope, uint8_t* keep_diag, uint8_t* keep_vert, int32_t* diag_hits,
                           int32_t* vert_hits, uint8_t* true_mask, hipStream_t stream) {
+  if (lambda == 0.5 && norm_scope == 0 && L <= kRowMaxL && L % 4 == 0) {
+    hipLaunchKernelGGL(k_capture_rows, dim3((unsigned)n_maps), dim3(kRowThreads), 0, stream, maps, L, eps, tau, mu,
+                       keep_diag, keep_vert, diag_hits, vert_hits, true_mask);
+    return hipGetLastError();
+  }
   const size_t lds = 6 * sizeof(int32_t) * (size_t)L;  // hits, then per-row min, max, threshold, mode
   auto kern = lambda == 0.5 ? k_capture<kBoxCoxHalf> : lambda == 0.0 ? k_capture<kBoxCoxLog> : k_capture<kBoxCoxPow>;
   if (lds > 65536) {
