@@ -312,17 +312,22 @@ __global__ void __launch_bounds__(kRowThreads)
   for (int r = tid; r < kRowMaxL; r += kRowThreads) hv[r] = 0;
   __syncthreads();
   int32_t vh[NU][4] = {};  // vertical hits of this lane's columns
-  for (int i0 = kRowBatch * wave; i0 < L; i0 += kRowBatch * NW) {
-    // the batch's causal cells; cells past the row, the map or the rows read as zero (buffer range)
-    float4 a[kRowBatch][NU];
+  // a batch's causal cells; cells past the row, the map or the rows read as zero (buffer range)
+  auto load_batch = [&](int i0, float4 (&dst)[kRowBatch][NU]) {
 #pragma unroll
     for (int q = 0; q < kRowBatch; ++q)
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         const int c = lane + 64 * u, i = i0 + q;
         const uint32_t off = (i < L && c < nq && 4 * c <= i) ? (uint32_t)(i * L + 4 * c) * 4u : map_bytes;
-        a[q][u] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rsA, off, 0, 0));
+        dst[q][u] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rsA, off, 0, 0));
       }
+  };
+  // the next batch's loads are in flight while this one is reduced, ruled and counted
+  float4 a[kRowBatch][NU], an[kRowBatch][NU];
+  load_batch(kRowBatch * wave, a);
+  for (int i0 = kRowBatch * wave; i0 < L; i0 += kRowBatch * NW) {
+    load_batch(i0 + kRowBatch * NW, an);
     // extremes of each causal row
     float mn[kRowBatch], mx[kRowBatch];
 #pragma unroll
@@ -416,6 +421,10 @@ __global__ void __launch_bounds__(kRowThreads)
         }
       }
     }
+#pragma unroll
+    for (int q = 0; q < kRowBatch; ++q)
+#pragma unroll
+      for (int u = 0; u < NU; ++u) a[q][u] = an[q][u];
   }
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
