@@ -325,7 +325,9 @@ __device__ inline void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Items per workgroup of k_items_lists (one per wave) and diagonal offsets staged per wave.
+// Items per workgroup of k_items_lists (one per wave) and diagonal offsets staged per wave.  When
+// the workgroup's items all belong to one head (the usual case: row-block counts are multiples of
+// kListWaves), the head's offsets are staged once for the workgroup, in the whole area.
 constexpr int kListWaves = 4;
 constexpr int kDshWave = 1536;
 
@@ -345,19 +347,30 @@ __device__ inline void store_counts_wave(const sa_index& ix, const ItemConsts& k
 
 // ---------------------------------------------------------------------------
 // Item kinds with no bitmap (blocks only, stripes only, diagonals + verticals).
-// One wave per (head, row block), kListWaves items per workgroup; the waves never
-// wait for each other.  The count pass (fill = 0) classifies the item and, for a
+// One wave per (head, row block), kListWaves items per workgroup; apart from the one
+// barrier after a workgroup-wide staging of the head's offsets, the waves never wait for
+// each other.  The count pass (fill = 0) classifies the item and, for a
 // kKindGeneral item, only records that in its scratch slot.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(64 * kListWaves) k_items_lists(sa_pattern_desc d, sa_index ix, int32_t fill,
                                                                  int32_t validate, ItemConsts kc, int32_t n_items) {
-  __shared__ int32_t Dsh_all[kListWaves][kDshWave];
+  __shared__ int32_t Dsh_all[kListWaves * kDshWave];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int32_t it = (int32_t)blockIdx.x * kListWaves + wave;
+  const int32_t it0 = (int32_t)blockIdx.x * kListWaves, it = it0 + wave;
+  const int32_t nbk = ix.n_row_blocks;
+  const bool one_head = it0 / nbk == (min(it0 + kListWaves, n_items) - 1) / nbk;  // uniform
+  const int32_t dcap = one_head ? kListWaves * kDshWave : kDshWave;  // offsets an item may stage
+  if (one_head) {
+    // the head's offsets, once for the workgroup (when they fit; otherwise no item here uses them)
+    const int32_t h = it0 / nbk, dp0 = d.diag_ptr[h], nD = d.diag_ptr[h + 1] - dp0;
+    if (nD <= dcap)
+      for (int32_t p = threadIdx.x; p < nD; p += 64 * kListWaves) Dsh_all[p] = d.diag_off[dp0 + p];
+    __syncthreads();
+  }
   if (it >= n_items) return;  // the whole wave leaves; nothing below waits for other waves
   const Item m = load_item(d, ix, kc, it);
   const int32_t S = d.S, b0 = m.b0, b1 = m.b1;
-  int32_t* Dsh = Dsh_all[wave];
+  int32_t* Dsh = one_head ? Dsh_all : Dsh_all + wave * kDshWave;
 
   uint32_t kind;
   long long blk_cols = 0, blk_pairs = 0;  // the block-mask columns' counts, used if the item is block-only
@@ -387,7 +400,7 @@ __global__ void __launch_bounds__(64 * kListWaves) k_items_lists(sa_pattern_desc
     const bool has_vert = m.vp1 > m.vp0, has_str = m.sp1 > m.sp0, has_diag = m.nD > 0;
     if (has_blk && !has_diag && !has_vert && !has_str) kind = kKindBlocks;
     else if (has_str && !has_blk && !has_diag && !has_vert) kind = kKindStripes;
-    else if (!has_blk && !has_str && m.nD <= kDshWave) kind = kKindLists;
+    else if (!has_blk && !has_str && m.nD <= dcap) kind = kKindLists;
     else kind = kKindGeneral;
     if (kind == kKindGeneral) {
       if (lane == 0) *scratch_slot(ix, kc, m) = kKindGeneral << kKindShift;
@@ -503,7 +516,7 @@ __global__ void __launch_bounds__(64 * kListWaves) k_items_lists(sa_pattern_desc
     }
   } else {  // kKindLists
     const int32_t nD = m.nD;
-    for (int32_t pb = 0; pb < nD; pb += 8 * 64) {
+    for (int32_t pb = 0; !one_head && pb < nD; pb += 8 * 64) {  // staged per wave
       int32_t r[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {

@@ -139,6 +139,21 @@ def test_index_diagonal_runs_merge(BM):
     _compare(d, BM, "diag-runs")
 
 
+@pytest.mark.parametrize("BM", [64, 128])
+def test_index_many_diagonals(BM):
+    """Heads with more diagonal offsets than one wave stages (the lists path with the offsets staged once per
+    workgroup, up to four times as many) and with more than a workgroup stages (the bitmap path): a band plus
+    scattered offsets, as runtime-captured masks have, with verticals."""
+    S, rng = 16384, np.random.default_rng(61)
+    diags = [np.concatenate([np.arange(1024), 1024 + np.sort(rng.choice(S - 1024, 1000, replace=False))]),
+             np.sort(rng.choice(S, 3000, replace=False)),
+             np.sort(rng.choice(S, 7000, replace=False)),
+             np.arange(0, S, 2)]
+    verts = [np.sort(rng.choice(S, n, replace=False)) for n in (12, 200, 64, 0)]
+    d = W.desc_from_lists(S, diags, verts)
+    _compare(d, BM, "many-diagonals")
+
+
 def test_index_unsorted_stripe_list_stays_in_range():
     """An unsorted stripe list (an invalid descriptor) built without validation: every column the index
     holds is still a valid key column of its row block."""
