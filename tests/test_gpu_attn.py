@@ -152,6 +152,22 @@ def test_band_edges_partial_tiles(d, BM):
     _run(desc, q, k, v, BM, all_rows(1, H, S), "band-edges")
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 128), ("f32", 64)])
+@pytest.mark.parametrize("BM", [64, 128])
+def test_lone_and_paired_far_diagonals(dtype, d, BM):
+    """Far diagonals without a band: a lone offset (rows below it empty), pairs 1, 63, 64 and 65 apart
+    (one segment, two segments that touch, two apart), a diagonal next to the sequence end, and a
+    head with 32 scattered offsets plus diagonal 0 (the 64K slash heads' far part).  Every row."""
+    S, H = 1100, 8
+    rng = np.random.default_rng(33)
+    diags = [np.array([300]), np.array([300, 301]), np.array([300, 363]), np.array([300, 364]),
+             np.array([300, 365]), np.array([0, S - 1]), np.concatenate([[0], np.sort(rng.choice(
+                 np.arange(70, S), 32, replace=False))]), np.array([64, 128, 192, 640])]
+    desc = W.desc_from_lists(S, diags, [np.zeros(0)] * H)
+    q, k, v = W.qkv(34, 1, H, 2, S, d, dtype)
+    _run(desc, q, k, v, BM, all_rows(1, H, S), "far-diagonals")
+
+
 def _mixed_desc(S, H, seed):
     """Every pattern kind at once in each head: diagonal runs, verticals, 128 x 128 blocks and
     256-row stripe lists (the index builds these items with LDS bitmaps)."""
