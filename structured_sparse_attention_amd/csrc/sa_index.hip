@@ -47,8 +47,6 @@ constexpr int kScanChunk = kThreads * kScanPer; // scan entries per workgroup
 constexpr int32_t kBadHead = 1 << 30;           // run_ptr marker from k_heads to k_scan_fix
 constexpr size_t kDefaultLds = 65536;           // dynamic LDS usable without raising the function's limit
 
-__device__ inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
 // number of elements <= x in the sorted array a[0, n) (a may point to LDS or global memory)
 __device__ inline int32_t upper_bound_i32(const int32_t* a, int32_t n, int32_t x) {
   int32_t lo = 0, hi = n;
@@ -68,6 +66,16 @@ __device__ inline uint32_t bit_range(int a, int b) {
 
 // true iff offset r does not continue the run of its predecessor (wrap-safe for invalid lists)
 __device__ inline bool starts_run(int32_t r, int32_t prev) { return (uint32_t)r != (uint32_t)prev + 1u; }
+
+// a[i] for lo <= i < hi, else `fill`; [lo, hi) must be a non-empty range of valid indices.  The load
+// itself is unconditional, from the index clamped into [lo, hi), so that a batch of these calls
+// leaves every load in flight at once (a load under a branch is waited for before the branch joins:
+// one round trip per element).
+template <typename T, typename I>
+__device__ inline T load_in(const T* a, I i, I lo, I hi, T fill) {
+  const T x = a[i < lo ? lo : (i < hi ? i : hi - 1)];
+  return (i >= lo && i < hi) ? x : fill;
+}
 
 // Workgroup-wide exclusive scan of one value per thread; *total receives the sum.  Contains
 // two barriers, so every read a thread made before the call precedes every write after it.
@@ -154,8 +162,8 @@ __global__ void __launch_bounds__(kThreads) k_heads(sa_pattern_desc d, sa_index 
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int32_t p = pb + u * kThreads + tid;
-      r[u] = p < p1 ? d.diag_off[p] : 0;
-      prev[u] = (p < p1 && p > p0) ? d.diag_off[p - 1] : 0;
+      r[u] = load_in<int32_t, int32_t>(d.diag_off, p, p0, p1, 0);
+      prev[u] = load_in<int32_t, int32_t>(d.diag_off, p - 1, p0, p1, 0);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -210,6 +218,15 @@ struct Item {
   int32_t cb1;          // block column that holds column b1
 };
 
+// Values the whole wave shares, loaded through the vector memory path, moved to scalar registers.
+__device__ inline int32_t uni(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ inline int64_t uni64(int64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)x);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// `it` must be the same for the whole wave.
 __device__ inline Item load_item(const sa_pattern_desc& d, const sa_index& ix, const ItemConsts& kc, int32_t it) {
   Item m;
   const int32_t S = d.S, BM = ix.row_block, nb = ix.n_row_blocks;
@@ -229,8 +246,13 @@ __device__ inline Item load_item(const sa_pattern_desc& d, const sa_index& ix, c
     m.sp0 = d.stripe_ptr[st];
     m.sp1 = d.stripe_ptr[st + 1];
   }
-  m.nD = dp1 - dp0;
-  m.D = d.diag_off + dp0;
+  // the item is the same for the whole wave: its bounds go to scalar registers
+  m.vp0 = uni(m.vp0);
+  m.vp1 = uni(m.vp1);
+  m.sp0 = uni64(m.sp0);
+  m.sp1 = uni64(m.sp1);
+  m.nD = uni(dp1 - dp0);
+  m.D = d.diag_off + uni(dp0);
   m.brow = nullptr;
   m.cb1 = 0;
   if (d.block_mask != nullptr) {
@@ -302,9 +324,25 @@ __device__ inline int64_t wave_upper_bound(const int32_t* a, int64_t n, int32_t 
   return lo;
 }
 
-// Lists path helpers: number of offsets of D (sorted, in LDS) in [lo, hi]
-__device__ inline int32_t count_in(const int32_t* D, int32_t nD, int32_t lo, int32_t hi) {
-  return hi < lo ? 0 : upper_bound_i32(D, nD, hi) - upper_bound_i32(D, nD, lo - 1);
+// four consecutive int32 written with one 16-byte store; the address need only be 4-byte aligned
+typedef int32_t int4u __attribute__((ext_vector_type(4), aligned(4)));
+
+// For each k, the number of elements <= x[k] of the sorted LDS array D[0, n).  The K searches run in
+// lockstep (the probe offsets halve together), so that their LDS reads are in flight at once instead of
+// one dependent chain per search.
+template <int K>
+__device__ inline void upper_bounds(const int32_t* D, int32_t n, const int32_t (&x)[K], int32_t (&pos)[K]) {
+#pragma unroll
+  for (int k = 0; k < K; ++k) pos[k] = 0;
+  if (n <= 0) return;
+  for (int32_t step = 1 << (31 - __builtin_clz((uint32_t)n)); step > 0; step >>= 1) {
+    int32_t v[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) v[k] = D[min(pos[k] + step, n) - 1];
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+      if (pos[k] + step <= n && v[k] <= x[k]) pos[k] += step;
+  }
 }
 
 // Wave-level helpers of k_items_lists (one item per wave, no workgroup barrier).
@@ -323,6 +361,15 @@ __device__ inline void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Block-row flags are read in chunks of kRowChunk block columns, kRowLoads byte loads per lane (all in
+// flight together): f[u] is block column cbase + u * 64 + lane, 0 past the item's last block column.
+constexpr int kRowLoads = 8;
+constexpr int kRowChunk = kRowLoads * 64;
+__device__ inline void load_row_chunk(const Item& m, int32_t cbase, int lane, uint8_t f[kRowLoads]) {
+#pragma unroll
+  for (int u = 0; u < kRowLoads; ++u) f[u] = load_in<uint8_t, int32_t>(m.brow, cbase + u * 64 + lane, 0, m.cb1 + 1, 0);
 }
 
 // Items per workgroup of k_items_lists (one per wave) and diagonal offsets staged per wave.  When
@@ -355,21 +402,55 @@ __device__ inline void store_counts_wave(const sa_index& ix, const ItemConsts& k
 __global__ void __launch_bounds__(64 * kListWaves) k_items_lists(sa_pattern_desc d, sa_index ix, int32_t fill,
                                                                  int32_t validate, ItemConsts kc, int32_t n_items) {
   __shared__ int32_t Dsh_all[kListWaves * kDshWave];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int32_t it0 = (int32_t)blockIdx.x * kListWaves, it = it0 + wave;
   const int32_t nbk = ix.n_row_blocks;
   const bool one_head = it0 / nbk == (min(it0 + kListWaves, n_items) - 1) / nbk;  // uniform
   const int32_t dcap = one_head ? kListWaves * kDshWave : kDshWave;  // offsets an item may stage
+  // Every wave loads an item (the last one when it has none, so that it can still take part in the
+  // staging), and issues with it what the item needs from global memory first: the first chunk of
+  // the block row and, in the fill pass, the item's kind and output positions.  They travel
+  // together, and with the staging of the head's offsets below.
+  const bool has_item = it < n_items;
+  const Item m = load_item(d, ix, kc, has_item ? it : n_items - 1);
+  const int32_t S = d.S, b0 = m.b0, b1 = m.b1;
+  uint8_t f[kRowLoads];  // block-row flags of columns cbase + u * 64 + lane
+  if (m.brow != nullptr) load_row_chunk(m, 0, lane, f);
+  uint32_t slot = 0;
+  int64_t fp_seg = 0, fp_bcol = 0, fp_col = 0, fp_col_end = 0;  // fill pass: the item's first outputs
+  if (fill) {
+    slot = *scratch_slot(ix, kc, m);
+    fp_seg = ix.seg_ptr[m.it];
+    fp_bcol = ix.bcol_ptr[m.it];
+    fp_col = ix.col_ptr[m.it];
+    fp_col_end = ix.col_ptr[m.it + 1];
+  }
+  const auto uniform_fill_inputs = [&]() {
+    slot = uni((int32_t)slot);
+    fp_seg = uni64(fp_seg);
+    fp_bcol = uni64(fp_bcol);
+    fp_col = uni64(fp_col);
+    fp_col_end = uni64(fp_col_end);
+  };
   if (one_head) {
-    // the head's offsets, once for the workgroup (when they fit; otherwise no item here uses them)
-    const int32_t h = it0 / nbk, dp0 = d.diag_ptr[h], nD = d.diag_ptr[h + 1] - dp0;
+    // the head's offsets, once for the workgroup (when they fit; otherwise no item here uses them);
+    // every wave's m is an item of this head
+    const int32_t nD = m.nD;
     if (nD <= dcap)
-      for (int32_t p = threadIdx.x; p < nD; p += 64 * kListWaves) Dsh_all[p] = d.diag_off[dp0 + p];
+      for (int32_t pb = 0; pb < nD; pb += 8 * 64 * kListWaves) {
+        int32_t r[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          r[u] = load_in<int32_t, int32_t>(m.D, pb + u * 64 * kListWaves + (int32_t)threadIdx.x, 0, nD, 0);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int32_t p = pb + u * 64 * kListWaves + (int32_t)threadIdx.x;
+          if (p < nD) Dsh_all[p] = r[u];
+        }
+      }
     __syncthreads();
   }
-  if (it >= n_items) return;  // the whole wave leaves; nothing below waits for other waves
-  const Item m = load_item(d, ix, kc, it);
-  const int32_t S = d.S, b0 = m.b0, b1 = m.b1;
+  if (!has_item) return;  // the whole wave leaves; nothing below waits for other waves
   int32_t* Dsh = one_head ? Dsh_all : Dsh_all + wave * kDshWave;
 
   uint32_t kind;
@@ -378,15 +459,10 @@ __global__ void __launch_bounds__(64 * kListWaves) k_items_lists(sa_pattern_desc
     int any = 0;
     if (m.brow != nullptr) {
       const int32_t bs = kc.bs;
-      for (int32_t cbase = 0; cbase <= m.cb1; cbase += 8 * 64) {  // eight loads in flight per lane
-        uint8_t f[8];
+      for (int32_t cbase = 0; cbase <= m.cb1; cbase += kRowChunk) {
+        if (cbase > 0) load_row_chunk(m, cbase, lane, f);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int32_t cb = cbase + u * 64 + lane;
-          f[u] = cb <= m.cb1 ? m.brow[cb] : 0;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < kRowLoads; ++u) {
           if (f[u]) {
             const int32_t c0 = (cbase + u * 64 + lane) * bs, c1 = min(b1, c0 + bs - 1);
             any = 1;
@@ -407,7 +483,8 @@ __global__ void __launch_bounds__(64 * kListWaves) k_items_lists(sa_pattern_desc
       return;
     }
   } else {
-    kind = *scratch_slot(ix, kc, m) >> kKindShift;
+    uniform_fill_inputs();
+    kind = slot >> kKindShift;
     if (kind == kKindGeneral) return;
   }
 
@@ -423,32 +500,68 @@ __global__ void __launch_bounds__(64 * kListWaves) k_items_lists(sa_pattern_desc
       return;
     }
     // fill: every set block but the last is full, so set block k of the row (in order) starts at
-    // output k * bs; the wave writes one block at a time, lane by column (coalesced)
-    const int64_t base = ix.col_ptr[m.it];
+    // output k * bs.
+    const int64_t base = fp_col;
     const int64_t cap = ix.capacity.n_cols;
-    int64_t done = 0;  // set blocks before the current chunk of 64 block columns
-    for (int32_t cbase = 0; cbase <= m.cb1; cbase += 8 * 64) {  // eight loads in flight per lane
-      uint8_t f[8];
+    int64_t done = 0;  // set blocks before the current chunk of block columns
+    if (bs == 64) {
+      // The set block columns of each chunk of kRowChunk are compacted into this wave's LDS area (in
+      // order: rank from the ballots), then written four blocks per store instruction: lanes
+      // 16q .. 16q + 15 write block t + q, four columns (16 bytes) each.  Only a block-only item takes
+      // this path, and its head has no diagonal offsets, so no wave of the workgroup uses the staging
+      // area for them.
+      int32_t* sel = Dsh_all + wave * kDshWave;
+      const uint64_t below = (1ull << lane) - 1ull;
+      for (int32_t cbase = 0; cbase <= m.cb1; cbase += kRowChunk) {
+        if (cbase > 0) load_row_chunk(m, cbase, lane, f);
+        int32_t n = 0;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int32_t cb = cbase + u * 64 + lane;
-        f[u] = cb <= m.cb1 ? m.brow[cb] : 0;
-      }
+        for (int u = 0; u < kRowLoads; ++u) {
+          const uint64_t set0 = __ballot(f[u] != 0);
+          if (f[u]) sel[n + __popcll(set0 & below)] = cbase + u * 64 + lane;
+          n += __popcll(set0);
+        }
+        wave_lds_sync();
+        const int q = lane >> 4, e4 = 4 * (lane & 15);
+        for (int32_t t = 0; t < n; t += 4) {
+          const int32_t tq = t + q;
+          if (tq < n) {
+            const int32_t c0 = sel[tq] * 64, c1 = min(b1, c0 + 63), c = c0 + e4;
+            const int64_t pos = base + (done + tq) * 64 + e4;
+            if (c + 3 <= c1 && pos + 3 < cap) {
+              *reinterpret_cast<int4u*>(ix.col_idx + pos) = int4u{c, c + 1, c + 2, c + 3};
+            } else {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const uint64_t set0 = __ballot(f[u] != 0);
-        uint64_t set = set0;
-        while (set) {
-          const int j = __ffsll((unsigned long long)set) - 1;
-          const int64_t k = done + __popcll(set0 & ((1ull << j) - 1ull));  // set blocks before this one
-          set &= set - 1;
-          const int32_t c0 = (cbase + u * 64 + j) * bs, c1 = min(b1, c0 + bs - 1);
-          for (int32_t c = c0 + lane; c <= c1; c += 64) {
-            const int64_t pos = base + k * bs + (c - c0);
-            if (pos < cap) ix.col_idx[pos] = c; else overflow = true;
+              for (int e = 0; e < 4; ++e) {
+                if (c + e <= c1) {
+                  if (pos + e < cap) ix.col_idx[pos + e] = c + e; else overflow = true;
+                }
+              }
+            }
           }
         }
-        done += __popcll(set0);
+        done += n;
+        wave_lds_sync();  // every lane has read `sel` before the next chunk overwrites it
+      }
+    } else {
+      for (int32_t cbase = 0; cbase <= m.cb1; cbase += kRowChunk) {
+        if (cbase > 0) load_row_chunk(m, cbase, lane, f);
+#pragma unroll
+        for (int u = 0; u < kRowLoads; ++u) {
+          const uint64_t set0 = __ballot(f[u] != 0);
+          uint64_t set = set0;
+          while (set) {
+            const int j = __ffsll((unsigned long long)set) - 1;
+            const int64_t k = done + __popcll(set0 & ((1ull << j) - 1ull));  // set blocks before this one
+            set &= set - 1;
+            const int32_t c0 = (cbase + u * 64 + j) * bs, c1 = min(b1, c0 + bs - 1);
+            for (int32_t c = c0 + lane; c <= c1; c += 64) {
+              const int64_t pos = base + k * bs + (c - c0);
+              if (pos < cap) ix.col_idx[pos] = c; else overflow = true;
+            }
+          }
+          done += __popcll(set0);
+        }
       }
     }
   } else if (kind == kKindStripes) {
@@ -474,8 +587,8 @@ __global__ void __launch_bounds__(64 * kListWaves) k_items_lists(sa_pattern_desc
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int64_t p = pb + u * 64 + lane;
-          c[u] = p < m.sp1 ? d.stripe_col[p] : -1;
-          prev[u] = (p < m.sp1 && p > m.sp0) ? d.stripe_col[p - 1] : -1;
+          c[u] = load_in<int32_t, int64_t>(d.stripe_col, p, m.sp0, m.sp1, -1);
+          prev[u] = load_in<int32_t, int64_t>(d.stripe_col, p - 1, m.sp0, m.sp1, -1);
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -492,14 +605,14 @@ __global__ void __launch_bounds__(64 * kListWaves) k_items_lists(sa_pattern_desc
       return;
     }
     // fill: the columns <= b1 of a sorted list are its first n entries
-    const int64_t base = ix.col_ptr[m.it], n = ix.col_ptr[m.it + 1] - base;
+    const int64_t base = fp_col, n = fp_col_end - base;
     const int64_t cap = ix.capacity.n_cols;
     for (int64_t qb = 0; qb < n; qb += 8 * 64) {
       int32_t c[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int64_t q = qb + u * 64 + lane;
-        c[u] = q < n ? d.stripe_col[m.sp0 + q] : 0;
+        c[u] = load_in<int32_t, int64_t>(d.stripe_col + m.sp0, q, 0, n, 0);
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -521,7 +634,7 @@ __global__ void __launch_bounds__(64 * kListWaves) k_items_lists(sa_pattern_desc
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int32_t p = pb + u * 64 + lane;
-        r[u] = p < nD ? m.D[p] : 0;
+        r[u] = load_in<int32_t, int32_t>(m.D, p, 0, nD, 0);
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -559,24 +672,39 @@ __global__ void __launch_bounds__(64 * kListWaves) k_items_lists(sa_pattern_desc
     };
 
     if (!fill) {
-      for (int32_t p = lane; p < nD; p += 64) {
-        bool st, en;
-        int32_t s0, s1;
-        seg_flags(p, st, en, s0, s1);
-        cnt[0] += st ? 1 : 0;
+      // segments start at runs of D: four offsets per lane and step, their reads issued together
+      for (int32_t pb = 0; pb < nD; pb += 4 * 64) {
+        bool start[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int32_t p = min(pb + k * 64 + lane, nD - 1);
+          start[k] = p == 0 || starts_run(Dsh[p], Dsh[max(p - 1, 0)]);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int32_t p = pb + k * 64 + lane;
+          if (p < nD && start[k]) {
+            bool st, en;
+            int32_t s0, s1;
+            seg_flags(p, st, en, s0, s1);
+            cnt[0] += st ? 1 : 0;
+          }
+        }
       }
+      // verticals: the offsets of D in [a - c, b1 - c] (a = max(b0, c)) are the rows of the block that
+      // reach c along a diagonal
       for (int32_t pb = m.vp0; pb < m.vp1; pb += 8 * 64) {
         int32_t c[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int32_t p = pb + u * 64 + lane;
-          c[u] = p < m.vp1 ? d.vert_col[p] : -1;
+          c[u] = load_in<int32_t, int32_t>(d.vert_col, p, m.vp0, m.vp1, -1);
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           if (c[u] < 0 || c[u] > b1) continue;
           const int32_t a = max(b0, c[u]);
-          const int32_t dc = count_in(Dsh, nD, a - c[u], b1 - c[u]);
+          const int32_t dc = upper_bound_i32(Dsh, nD, b1 - c[u]) - upper_bound_i32(Dsh, nD, a - c[u] - 1);
           if (dc > 0) {
             cnt[1] += 1;
             cnt[3] += (b1 - a + 1) - dc;
@@ -586,40 +714,57 @@ __global__ void __launch_bounds__(64 * kListWaves) k_items_lists(sa_pattern_desc
           }
         }
       }
-      // diagonal pairs of each row: offsets r in D_h with r <= i
-      if (nD > 0)
-        for (int32_t i = b0 + lane; i <= b1; i += 64) cnt[3] += upper_bound_i32(Dsh, nD, i);
+      // diagonal pairs of each row: offsets r in D_h with r <= i (BM <= 128: two rows per lane)
+      if (nD > 0) {
+        int32_t x[2] = {b0 + lane, b0 + 64 + lane}, ub[2];
+        upper_bounds<2>(Dsh, nD, x, ub);
+        if (x[0] <= b1) cnt[3] += ub[0];
+        if (x[1] <= b1) cnt[3] += ub[1];
+      }
       store_counts_wave(ix, kc, m, cnt, kind);
       return;
     }
     // fill: segments in ascending column order = runs in descending offset order
-    int64_t bs_lo = ix.seg_ptr[m.it], bs_hi = bs_lo;
-    for (int32_t cbase = 0; cbase < nD; cbase += 64) {
-      const int32_t p = nD - 1 - (cbase + lane);
-      bool st, en;
-      int32_t s0 = 0, s1 = 0;
-      seg_flags(p, st, en, s0, s1);
-      const uint64_t mst = __ballot(st), men = __ballot(en);
-      if (st) {
-        const int64_t pos = bs_lo + lanes_below(mst);
-        if (pos < ix.capacity.n_segs) ix.seg_lo[pos] = s0; else overflow = true;
+    int64_t bs_lo = fp_seg, bs_hi = bs_lo;
+    for (int32_t cb4 = 0; cb4 < nD; cb4 += 4 * 64) {
+      // which of the next 4 x 64 offsets start a run (reads issued together); steps with none are skipped
+      bool start[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int32_t p = nD - 1 - (cb4 + k * 64 + lane), pc = max(p, 0);
+        start[k] = p >= 0 && (pc == 0 || starts_run(Dsh[pc], Dsh[max(pc - 1, 0)]));
       }
-      if (en) {
-        const int64_t pos = bs_hi + lanes_below(men);
-        if (pos < ix.capacity.n_segs) ix.seg_hi[pos] = s1; else overflow = true;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (__ballot(start[k]) == 0ull) continue;
+        const int32_t p = nD - 1 - (cb4 + k * 64 + lane);
+        bool st = false, en = false;
+        int32_t s0 = 0, s1 = 0;
+        if (start[k]) seg_flags(p, st, en, s0, s1);
+        const uint64_t mst = __ballot(st), men = __ballot(en);
+        if (st) {
+          const int64_t pos = bs_lo + lanes_below(mst);
+          if (pos < ix.capacity.n_segs) ix.seg_lo[pos] = s0; else overflow = true;
+        }
+        if (en) {
+          const int64_t pos = bs_hi + lanes_below(men);
+          if (pos < ix.capacity.n_segs) ix.seg_hi[pos] = s1; else overflow = true;
+        }
+        bs_lo += __popcll(mst);
+        bs_hi += __popcll(men);
       }
-      bs_lo += __popcll(mst);
-      bs_hi += __popcll(men);
     }
     // verticals in list order, split into in-segment and gathered columns
-    int64_t b_in = ix.bcol_ptr[m.it], b_out = ix.col_ptr[m.it];
+    int64_t b_in = fp_bcol, b_out = fp_col;
     for (int32_t pb = m.vp0; pb < m.vp1; pb += 64) {
       const int32_t p = pb + lane;
       const int32_t c = p < m.vp1 ? d.vert_col[p] : -1;
       bool in = false, out = false;
-      if (c >= 0 && c <= b1) {
-        const int32_t a = max(b0, c);
-        if (count_in(Dsh, nD, a - c, b1 - c) > 0) in = true;
+      const bool ok = c >= 0 && c <= b1;
+      int32_t x[2] = {ok ? b1 - c : -1, ok ? max(b0, c) - c - 1 : -1}, ub[2];
+      upper_bounds<2>(Dsh, nD, x, ub);
+      if (ok) {
+        if (ub[0] > ub[1]) in = true;
         else out = true;
       }
       const uint64_t min_ = __ballot(in), mout = __ballot(out);
@@ -663,7 +808,7 @@ __device__ inline void items_body(const sa_pattern_desc& d, const sa_index& ix, 
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int32_t p = pb + u * kThreads + tid;
-      c[u] = p < m.vp1 ? d.vert_col[p] : -1;
+      c[u] = load_in<int32_t, int32_t>(d.vert_col, p, m.vp0, m.vp1, -1);
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u)
@@ -676,8 +821,8 @@ __device__ inline void items_body(const sa_pattern_desc& d, const sa_index& ix, 
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int64_t p = pb + u * kThreads + tid;
-        c[u] = p < m.sp1 ? d.stripe_col[p] : -1;
-        prev[u] = (validate && p < m.sp1 && p > m.sp0) ? d.stripe_col[p - 1] : -1;
+        c[u] = load_in<int32_t, int64_t>(d.stripe_col, p, m.sp0, m.sp1, -1);
+        prev[u] = validate ? load_in<int32_t, int64_t>(d.stripe_col, p - 1, m.sp0, m.sp1, -1) : -1;
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -899,13 +1044,16 @@ __global__ void __launch_bounds__(kThreads) k_items(sa_pattern_desc d, sa_index 
     const bool staged = nD <= kc.dcap;
 
     // --- X from the block row, U cleared, D staged in LDS
+    const int32_t blk_end = (kc.wpb_shift >= 0 ? ((nw - 1) >> kc.wpb_shift) : (nw - 1) / kc.wpb) + 1;
     for (int32_t wb = 0; wb < nw; wb += 4 * kThreads) {
-      uint32_t x[4];
+      uint32_t x[4] = {0u, 0u, 0u, 0u};
+      if (m.brow != nullptr) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int32_t w = wb + u * kThreads + tid;
-        const int32_t blk = kc.wpb_shift >= 0 ? (w >> kc.wpb_shift) : w / kc.wpb;
-        x[u] = (m.brow != nullptr && w < nw && m.brow[blk]) ? 0xffffffffu : 0u;
+        for (int u = 0; u < 4; ++u) {
+          const int32_t w = wb + u * kThreads + tid;
+          const int32_t blk = kc.wpb_shift >= 0 ? (w >> kc.wpb_shift) : w / kc.wpb;
+          x[u] = load_in<uint8_t, int32_t>(m.brow, blk, 0, blk_end, 0) ? 0xffffffffu : 0u;
+        }
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -922,7 +1070,7 @@ __global__ void __launch_bounds__(kThreads) k_items(sa_pattern_desc d, sa_index 
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int32_t p = pb + u * kThreads + tid;
-          r[u] = p < nD ? m.D[p] : 0;
+          r[u] = load_in<int32_t, int32_t>(m.D, p, 0, nD, 0);
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -961,7 +1109,7 @@ __global__ void __launch_bounds__(kThreads) k_scan_local(int64_t* a0, int64_t* a
   const int64_t base = 1 + c * kScanChunk + (int64_t)threadIdx.x * kScanPer;
   long long v[kScanPer], s = 0;
 #pragma unroll
-  for (int u = 0; u < kScanPer; ++u) v[u] = (base + u <= end) ? a[base + u] : 0;
+  for (int u = 0; u < kScanPer; ++u) v[u] = load_in<int64_t, int64_t>(a, base + u, 1, end + 1, 0);
 #pragma unroll
   for (int u = 0; u < kScanPer; ++u) s += v[u];
   long long tot;
@@ -993,7 +1141,7 @@ __global__ void __launch_bounds__(kThreads) k_scan_fix(int64_t* a0, int64_t* a1,
   __shared__ long long sh[kWaves];
   __shared__ int32_t sh32[kWaves];
   const int tid = threadIdx.x;
-  const int64_t C = cdiv64(n, kScanChunk);
+  const int64_t C = (n + kScanChunk - 1) / kScanChunk;
   for (int which = 0; which < 3; ++which) {
     int64_t* a = pick(a0, a1, a2, which);
     long long carry = 0;
@@ -1011,7 +1159,7 @@ __global__ void __launch_bounds__(kThreads) k_scan_fix(int64_t* a0, int64_t* a1,
   int32_t carry = 0, bad = 0;
   for (int32_t hb = 0; hb < n_heads; hb += kThreads) {
     const int32_t hh = hb + tid;
-    int32_t v = hh < n_heads ? run_ptr[hh + 1] : 0;
+    int32_t v = load_in<int32_t, int32_t>(run_ptr, hh + 1, 1, n_heads + 1, 0);
     bad |= v & kBadHead;
     v &= ~kBadHead;
     int32_t tot;
