@@ -75,6 +75,69 @@ __device__ inline uint64_t range_mask(int a, int b) {  // bits [a, b], 0 <= a <=
   return (~0ull >> (63 - b)) & (~0ull << a);
 }
 
+// LDS written by some lanes of a wave becomes visible to every lane of that wave
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// A work item's list of one or two int32 arrays (segment bounds, in-segment columns), read in
+// order by the whole wave.  The wave keeps 64 consecutive entries in its own LDS area and refills
+// it when the walk passes its end, so that the walk waits on global memory once per 64 entries, not
+// once per entry (a segment change, an in-segment column).  issue() starts the loads of the first
+// chunk into registers, so that they travel with other loads; commit() waits for them and stores it.
+template <int N, bool REFILL>
+struct ListStream {
+  const int32_t* src[N];
+  int32_t* sh;  // N * 64 entries of this wave's LDS
+  int64_t end, base;
+  int32_t v[N];
+  __device__ void issue(int64_t at) {
+    base = at;
+    const int64_t q = min(at + (int64_t)(threadIdx.x & 63), max(end - 1, (int64_t)0));
+#pragma unroll
+    for (int k = 0; k < N; ++k) v[k] = end > 0 ? src[k][q] : 0;
+  }
+  __device__ void commit() {
+#pragma unroll
+    for (int k = 0; k < N; ++k) sh[k * 64 + (threadIdx.x & 63)] = v[k];
+    wave_lds_sync();
+  }
+  // entry `at` of array k (base <= at < end); wave-uniform.  Past the chunk, the next 64 entries
+  // replace it (REFILL), or the entry is read from global memory directly (for a kernel whose loop
+  // has no registers to spare for the refill).
+  __device__ int32_t get(int k, int64_t at) {
+    if (!REFILL && at - base >= 64) return __builtin_amdgcn_readfirstlane(src[k][at]);
+    if (at - base >= 64) {
+      base = at;
+      const int64_t q = min(at + (int64_t)(threadIdx.x & 63), end - 1);
+#pragma unroll
+      for (int kk = 0; kk < N; ++kk) sh[kk * 64 + (threadIdx.x & 63)] = src[kk][q];
+      wave_lds_sync();
+    }
+    return __builtin_amdgcn_readfirstlane(sh[k * 64 + (int)(at - base)]);
+  }
+};
+
+// The in-segment columns of a work item, consumed tile by tile in key order.
+template <bool REFILL>
+struct BcolStream {
+  ListStream<1, REFILL> ls;
+  int64_t pos;
+  // bits (c - j0) of the entries c < j0 + n, consumed
+  __device__ uint64_t take(int j0, int n) {
+    uint64_t x = 0;
+    while (pos < ls.end) {
+      const int c = ls.get(0, pos);
+      if (c >= j0 + n) break;
+      x |= 1ull << (c - j0);
+      ++pos;
+    }
+    return x;
+  }
+};
+
 // max/sum of a value and its copy in lane l ^ 32
 __device__ inline float pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -187,19 +250,19 @@ struct Tile {
   int64_t seg, pc;
 };
 
+template <bool REFILL>
 struct TileWalk {
   int64_t s1, c0, c1;
-  const int32_t* seg_lo;
-  const int32_t* seg_hi;
+  ListStream<2, REFILL> segs;  // seg_lo, seg_hi
 
-  __device__ Tile first(int64_t s0) const {
+  __device__ Tile first(int64_t s0) {
     Tile t;
     t.seg = s0;
     t.pc = c0;
     if (s0 < s1) {
       t.kind = 1;
-      t.j0 = uni(seg_lo[s0]);
-      t.shi = uni(seg_hi[s0]);
+      t.j0 = segs.get(0, s0);
+      t.shi = segs.get(1, s0);
       t.nvalid = min(BN, t.shi - t.j0 + 1);
     } else {
       start_gather(t);
@@ -218,13 +281,13 @@ struct TileWalk {
       t.nvalid = 0;
     }
   }
-  __device__ Tile next(Tile t) const {
+  __device__ Tile next(Tile t) {
     if (t.kind == 1) {
       if (t.j0 + BN <= t.shi) {
         t.j0 += BN;
       } else if (++t.seg < s1) {
-        t.j0 = uni(seg_lo[t.seg]);
-        t.shi = uni(seg_hi[t.seg]);
+        t.j0 = segs.get(0, t.seg);
+        t.shi = segs.get(1, t.seg);
       } else {
         start_gather(t);
         return t;
@@ -250,6 +313,7 @@ __global__ void __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(2))
   __shared__ __attribute__((aligned(16))) E Ks[C::K_ELEMS];
   __shared__ __attribute__((aligned(16))) E Vs[C::V_ELEMS];
   __shared__ __attribute__((aligned(16))) int32_t cols_sh[3][BN];
+  __shared__ int32_t list_sh[BM / 32][3 * 64];  // per wave: segment bounds, in-segment columns
 
   // the wave index is uniform: kept in a scalar register, so that row and LDS offsets derived from it
   // (and M0 of the LDS-direct loads) are scalar arithmetic
@@ -260,6 +324,10 @@ __global__ void __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(2))
   const int S = p.S;
   const int b0 = rb * BM, b1 = min(S, b0 + BM) - 1;
   const int i = b0 + wave * 32 + r32;  // this lane's query row
+  // the item's list bounds, loaded together with Q (one round trip)
+  const int64_t item = (int64_t)h * p.nb + rb;
+  const int64_t lb_b0 = p.bcol_ptr[item], lb_b1 = p.bcol_ptr[item + 1], lb_s0 = p.seg_ptr[item],
+                lb_s1 = p.seg_ptr[item + 1], lb_c0 = p.col_ptr[item], lb_c1 = p.col_ptr[item + 1];
   const bool row_ok = i <= b1;
   const int kvh = h / (p.hq / p.hkv);
 
@@ -291,15 +359,25 @@ __global__ void __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(2))
     for (int v = 0; v < 16; ++v) oacc[x][v] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
-  const int64_t item = (int64_t)h * p.nb + rb;
-  int64_t bp = uni64(p.bcol_ptr[item]);
-  const int64_t bp_end = uni64(p.bcol_ptr[item + 1]);
-  TileWalk walk;
-  walk.s1 = uni64(p.seg_ptr[item + 1]);
-  walk.c0 = uni64(p.col_ptr[item]);
-  walk.c1 = uni64(p.col_ptr[item + 1]);
-  walk.seg_lo = p.seg_lo;
-  walk.seg_hi = p.seg_hi;
+  // the first 64 segment bounds and in-segment columns of the item, loaded together
+  TileWalk<false> walk;
+  walk.s1 = uni64(lb_s1);
+  walk.c0 = uni64(lb_c0);
+  walk.c1 = uni64(lb_c1);
+  walk.segs.src[0] = p.seg_lo;
+  walk.segs.src[1] = p.seg_hi;
+  walk.segs.sh = list_sh[wave];
+  walk.segs.end = walk.s1;
+  BcolStream<false> bcs;
+  bcs.ls.src[0] = p.bcol_idx;
+  bcs.ls.sh = list_sh[wave] + 128;
+  bcs.ls.end = uni64(lb_b1);
+  bcs.pos = uni64(lb_b0);
+  const int64_t seg0 = uni64(lb_s0);
+  walk.segs.issue(seg0);
+  bcs.ls.issue(bcs.pos);
+  walk.segs.commit();
+  bcs.ls.commit();
 
   // ---- tile fetch: global -> registers (issued one tile ahead), registers -> LDS.
   // Buffer loads: an offset past the end of the kv head's slab reads as zero, so padding keys
@@ -402,14 +480,7 @@ __global__ void __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(2))
       mi.w1 = (c1 == wi + 1) ? a1 : 0u;
       mi.w2 = (c2 == wi + 2) ? a2 : 0u;
       // in-segment columns of this tile (sorted list, consumed in tile order)
-      uint64_t xin = 0;
-      while (bp < bp_end) {
-        const int c = p.bcol_idx[bp];
-        if (c >= t.j0 + t.nvalid) break;
-        xin |= 1ull << (c - t.j0);
-        ++bp;
-      }
-      mi.xin = xin;
+      mi.xin = bcs.take(t.j0, t.nvalid);
     }
     return mi;
   };
@@ -567,7 +638,7 @@ __global__ void __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(2))
   auto load_cols = [&](const Tile& t, int32_t* dst) {
     if (t.kind == 2 && tid < BN) dst[tid] = tid < t.nvalid ? p.col_idx[t.pc + tid] : 0;
   };
-  Tile cur = walk.first(uni64(p.seg_ptr[item]));
+  Tile cur = walk.first(seg0);
   Tile nxt = walk.next(cur);
   Tile nn = walk.next(nxt);
   load_cols(cur, cols_sh[0]);
@@ -668,6 +739,7 @@ k_attn_bf16(Params p) {
   using C = Cfg3<D, BM>;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * C::STAGE];
   __shared__ __attribute__((aligned(16))) int32_t cols_sh[3][BN];
+  __shared__ int32_t list_sh[BM / 32][3 * 64];  // per wave: segment bounds, in-segment columns
 
   // the wave index is uniform: kept in a scalar register, so that row and LDS offsets derived from it
   // (and M0 of the LDS-direct loads) are scalar arithmetic
@@ -679,6 +751,10 @@ k_attn_bf16(Params p) {
   const int S = p.S;
   const int b0 = rb * BM, b1 = min(S, b0 + BM) - 1;
   const int i = b0 + rh * 32 + r32;
+  // the item's list bounds, loaded together with Q (one round trip)
+  const int64_t item = (int64_t)h * p.nb + rb;
+  const int64_t lb_b0 = p.bcol_ptr[item], lb_b1 = p.bcol_ptr[item + 1], lb_s0 = p.seg_ptr[item],
+                lb_s1 = p.seg_ptr[item + 1], lb_c0 = p.col_ptr[item], lb_c1 = p.col_ptr[item + 1];
   const bool row_ok = i <= b1;
   const int kvh = h / (p.hq / p.hkv);
   using E = unsigned short;
@@ -702,15 +778,25 @@ k_attn_bf16(Params p) {
     for (int v = 0; v < 16; ++v) oacc[x][v] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
-  const int64_t item = (int64_t)h * p.nb + rb;
-  int64_t bp = uni64(p.bcol_ptr[item]);
-  const int64_t bp_end = uni64(p.bcol_ptr[item + 1]);
-  TileWalk walk;
-  walk.s1 = uni64(p.seg_ptr[item + 1]);
-  walk.c0 = uni64(p.col_ptr[item]);
-  walk.c1 = uni64(p.col_ptr[item + 1]);
-  walk.seg_lo = p.seg_lo;
-  walk.seg_hi = p.seg_hi;
+  // the first 64 segment bounds and in-segment columns of the item, loaded together
+  TileWalk<true> walk;
+  walk.s1 = uni64(lb_s1);
+  walk.c0 = uni64(lb_c0);
+  walk.c1 = uni64(lb_c1);
+  walk.segs.src[0] = p.seg_lo;
+  walk.segs.src[1] = p.seg_hi;
+  walk.segs.sh = list_sh[wave];
+  walk.segs.end = walk.s1;
+  BcolStream<true> bcs;
+  bcs.ls.src[0] = p.bcol_idx;
+  bcs.ls.sh = list_sh[wave] + 128;
+  bcs.ls.end = uni64(lb_b1);
+  bcs.pos = uni64(lb_b0);
+  const int64_t seg0 = uni64(lb_s0);
+  walk.segs.issue(seg0);
+  bcs.ls.issue(bcs.pos);
+  walk.segs.commit();
+  bcs.ls.commit();
 
   constexpr uint32_t kBufFlags = 0x00020000u;
   const uint32_t slab_bytes = (uint32_t)S * D * 2u;
@@ -800,14 +886,7 @@ k_attn_bf16(Params p) {
       mi.w0 = (c0 == wi) ? a0 : 0u;
       mi.w1 = (c1 == wi + 1) ? a1 : 0u;
       mi.w2 = (c2 == wi + 2) ? a2 : 0u;
-      uint64_t xin = 0;
-      while (bp < bp_end) {
-        const int c = p.bcol_idx[bp];
-        if (c >= t.j0 + t.nvalid) break;
-        xin |= 1ull << (c - t.j0);
-        ++bp;
-      }
-      mi.xin = xin;
+      mi.xin = bcs.take(t.j0, t.nvalid);
     }
     return mi;
   };
@@ -951,7 +1030,7 @@ k_attn_bf16(Params p) {
   auto load_cols = [&](const Tile& t, int32_t* dst) {
     if (t.kind == 2 && tid < BN) dst[tid] = tid < t.nvalid ? p.col_idx[t.pc + tid] : 0;
   };
-  Tile cur = walk.first(uni64(p.seg_ptr[item]));
+  Tile cur = walk.first(seg0);
   Tile nxt = walk.next(cur);
   Tile nn = walk.next(nxt);
   load_cols(cur, cols_sh[0]);
