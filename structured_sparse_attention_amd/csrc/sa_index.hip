@@ -432,6 +432,8 @@ __global__ void __launch_bounds__(64 * kListWaves) k_items_lists(sa_pattern_desc
     fp_col = uni64(fp_col);
     fp_col_end = uni64(fp_col_end);
   };
+  __shared__ int32_t n_runs_sh;  // runs of D staged after it (one-head workgroups), or -1
+  __shared__ int32_t scan_sh[kListWaves];
   if (one_head) {
     // the head's offsets, once for the workgroup (when they fit; otherwise no item here uses them);
     // every wave's m is an item of this head
@@ -448,6 +450,30 @@ __global__ void __launch_bounds__(64 * kListWaves) k_items_lists(sa_pattern_desc
           if (p < nD) Dsh_all[p] = r[u];
         }
       }
+    __syncthreads();
+    // the maximal runs of D, as run_lo at Dsh_all[nD + k] and run_hi at Dsh_all[nD + nruns + k] (when
+    // they fit after D): thread t takes a contiguous range of offsets, the run starts before it come
+    // from a workgroup scan, and the run ending at an offset is the last one started at or before it
+    if (nD > 0 && nD <= dcap) {
+      const int32_t per = (nD + 64 * kListWaves - 1) / (64 * kListWaves);
+      const int32_t p0 = min(nD, (int32_t)threadIdx.x * per), p1 = min(nD, p0 + per);
+      int32_t starts = 0;
+      for (int32_t q = p0; q < p1; ++q) starts += (q == 0 || starts_run(Dsh_all[q], Dsh_all[q - 1])) ? 1 : 0;
+      int32_t total;
+      int32_t k = block_exscan<int32_t>(starts, &total, scan_sh);
+      if (nD + 2 * total <= dcap) {
+        int32_t* RL = Dsh_all + nD;
+        int32_t* RH = Dsh_all + nD + total;
+        for (int32_t q = p0; q < p1; ++q) {
+          const int32_t r = Dsh_all[q];
+          if (q == 0 || starts_run(r, Dsh_all[q - 1])) RL[k++] = r;
+          if (q == nD - 1 || starts_run(Dsh_all[q + 1], r)) RH[k - 1] = r;
+        }
+      }
+      if (threadIdx.x == 0) n_runs_sh = nD + 2 * total <= dcap ? total : -1;
+    } else if (threadIdx.x == 0) {
+      n_runs_sh = -1;
+    }
     __syncthreads();
   }
   if (!has_item) return;  // the whole wave leaves; nothing below waits for other waves
@@ -671,7 +697,30 @@ __global__ void __launch_bounds__(64 * kListWaves) k_items_lists(sa_pattern_desc
       en = !(p > 0 && max(0, b0 - Dsh[p - 1]) <= s1 + 1);
     };
 
+    // with the runs staged: the same flags from run k and its neighbours, no search
+    const int32_t nr = one_head ? n_runs_sh : -1;
+    const int32_t* RL = Dsh + nD;
+    const int32_t* RH = Dsh + nD + max(nr, 0);
+    auto run_flags = [&](int32_t k, bool& st, bool& en, int32_t& s0, int32_t& s1) {
+      st = en = false;
+      if (k < 0 || k >= nr) return;
+      const int32_t lo = RL[k], hi = RH[k];
+      if (lo > b1) return;
+      s0 = max(0, b0 - hi);
+      s1 = min(b1, b1 - lo);
+      st = !(k + 1 < nr && RL[k + 1] <= b1 && s0 <= min(b1, b1 - RL[k + 1]) + 1);
+      en = !(k > 0 && max(0, b0 - RH[k - 1]) <= s1 + 1);
+    };
+
     if (!fill) {
+      if (nr >= 0) {
+        for (int32_t k = lane; k < nr; k += 64) {
+          bool st, en;
+          int32_t s0, s1;
+          run_flags(k, st, en, s0, s1);
+          cnt[0] += st ? 1 : 0;
+        }
+      } else {
       // segments start at runs of D: four offsets per lane and step, their reads issued together
       for (int32_t pb = 0; pb < nD; pb += 4 * 64) {
         bool start[4];
@@ -690,6 +739,7 @@ __global__ void __launch_bounds__(64 * kListWaves) k_items_lists(sa_pattern_desc
             cnt[0] += st ? 1 : 0;
           }
         }
+      }
       }
       // verticals: the offsets of D in [a - c, b1 - c] (a = max(b0, c)) are the rows of the block that
       // reach c along a diagonal
@@ -726,7 +776,23 @@ __global__ void __launch_bounds__(64 * kListWaves) k_items_lists(sa_pattern_desc
     }
     // fill: segments in ascending column order = runs in descending offset order
     int64_t bs_lo = fp_seg, bs_hi = bs_lo;
-    for (int32_t cb4 = 0; cb4 < nD; cb4 += 4 * 64) {
+    for (int32_t kb = 0; nr >= 0 && kb < nr; kb += 64) {
+      bool st, en;
+      int32_t s0 = 0, s1 = 0;
+      run_flags(nr - 1 - (kb + lane), st, en, s0, s1);
+      const uint64_t mst = __ballot(st), men = __ballot(en);
+      if (st) {
+        const int64_t pos = bs_lo + lanes_below(mst);
+        if (pos < ix.capacity.n_segs) ix.seg_lo[pos] = s0; else overflow = true;
+      }
+      if (en) {
+        const int64_t pos = bs_hi + lanes_below(men);
+        if (pos < ix.capacity.n_segs) ix.seg_hi[pos] = s1; else overflow = true;
+      }
+      bs_lo += __popcll(mst);
+      bs_hi += __popcll(men);
+    }
+    for (int32_t cb4 = 0; nr < 0 && cb4 < nD; cb4 += 4 * 64) {
       // which of the next 4 x 64 offsets start a run (reads issued together); steps with none are skipped
       bool start[4];
 #pragma unroll
@@ -834,9 +900,27 @@ __device__ inline void items_body(const sa_pattern_desc& d, const sa_index& ix, 
     if (bad && !fill) atomicOr(ix.status, SA_STATUS_DESC_INVALID);
   }
   // --- U: columns i - r for i in [b0, b1] and r in a run [lo, hi] of D_h: [b0 - hi, b1 - lo], clipped
-  // to [0, b1].  A thread that holds the first offset of a run finds the run's end by binary search:
-  // D[q] - q is non-decreasing and constant exactly along a run.
-  for (int32_t p = tid; p < nD; p += kThreads) {
+  // to [0, b1].  Staged offsets: a thread that holds the first offset of a run finds the run's end by
+  // binary search (D[q] - q is non-decreasing and constant exactly along a run).  Offsets in global
+  // memory: each offset r <= b1 sets its own columns [b0 - r, b1 - r] (the union is the same), eight
+  // loads in flight per thread and no search.
+  if constexpr (!STAGED) {
+    for (int32_t pb = 0; pb < nD; pb += 8 * kThreads) {
+      int32_t r[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) r[u] = load_in<int32_t, int32_t>(Dq, pb + u * kThreads + tid, 0, nD, INT32_MAX);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (r[u] > b1) continue;
+        const int32_t a = max(0, b0 - r[u]), e = b1 - r[u];
+        for (int32_t w = a >> 5; w <= (e >> 5); ++w) {
+          const int32_t ba = max(a, w * 32) - w * 32, be = min(e, w * 32 + 31) - w * 32;
+          atomicOr(&U[w], bit_range(ba, be));
+        }
+      }
+    }
+  }
+  for (int32_t p = tid; STAGED && p < nD; p += kThreads) {
     const int32_t lo = Dq[p];
     if (p > 0 && !starts_run(lo, Dq[p - 1])) continue;  // not the first offset of a run
     if (lo > b1) continue;
@@ -875,19 +959,40 @@ __device__ inline void items_body(const sa_pattern_desc& d, const sa_index& ix, 
           cnt[3] += b1 - max(j, b0) + 1;
         }
       }
-      // in-segment columns of X: every causal row minus the rows whose offset is a diagonal
+      // in-segment columns of X: every causal row minus the rows whose offset is a diagonal (with the
+      // offsets in global memory, those rows are taken off per offset below)
       while (in) {
         int bit = __ffs(in) - 1;
         in &= in - 1;
         int32_t j = w * 32 + bit;
         int32_t a = max(j, b0);
-        int32_t dcount = upper_bound_i32(Dq, nD, b1 - j) - upper_bound_i32(Dq, nD, a - j - 1);
+        const int32_t dcount = STAGED ? upper_bound_i32(Dq, nD, b1 - j) - upper_bound_i32(Dq, nD, a - j - 1) : 0;
         cnt[3] += (b1 - a + 1) - dcount;
       }
     }
-    // diagonal pairs of each row: offsets r in D_h with r <= i
-    if (nD > 0)
-      for (int32_t i = b0 + tid; i <= b1; i += kThreads) cnt[3] += upper_bound_i32(Dq, nD, i);
+    if constexpr (STAGED) {
+      // diagonal pairs of each row: offsets r in D_h with r <= i
+      if (nD > 0)
+        for (int32_t i = b0 + tid; i <= b1; i += kThreads) cnt[3] += upper_bound_i32(Dq, nD, i);
+    } else {
+      // per offset r <= b1: its rows max(r, b0) .. b1 (diagonal pairs), less the in-segment columns j
+      // in [b0 - r, b1 - r], whose pair (j + r, j) was counted with the column above
+      for (int32_t pb = 0; pb < nD; pb += 8 * kThreads) {
+        int32_t r[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) r[u] = load_in<int32_t, int32_t>(Dq, pb + u * kThreads + tid, 0, nD, INT32_MAX);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (r[u] > b1) continue;
+          cnt[3] += b1 - max(r[u], b0) + 1;
+          const int32_t a = max(0, b0 - r[u]), e = b1 - r[u];
+          for (int32_t w = a >> 5; w <= (e >> 5); ++w) {
+            const int32_t ba = max(a, w * 32) - w * 32, be = min(e, w * 32 + 31) - w * 32;
+            cnt[3] -= __popc(X[w] & U[w] & bit_range(ba, be));
+          }
+        }
+      }
+    }
     store_counts(ix, kc, m, cnt, kKindGeneral, red_sh);
     return;
   }
