@@ -286,13 +286,13 @@ __global__ void __launch_bounds__(kThreads)
 // ---------------------------------------------------------------------------
 // One read of the map: the same keep flags and hits as k_capture for lambda = 0.5, per-row
 // extremes (norm_scope 0) and L <= 512 with L % 4 == 0 (the capture length of the pages is 512).
-// 256 threads per map.  A wave holds kRowBatch consecutive causal rows in registers (lane l:
-// columns 4(l + 64u) .. +3), reduces each row's extremes across the wave, lets lane q find row q's
-// rule (row_rule, all rows of the batch at once), and counts hits from the same registers:
-// diagonal hits with LDS atomics, vertical hits in registers (the lane's columns are fixed) added
-// to LDS once at the end.
+// 512 threads per map (about 100 VGPRs, so two maps share a CU).  A wave holds kRowBatch consecutive
+// causal rows in registers (lane l: columns 4(l + 64u) .. +3), reduces each row's extremes across the
+// wave, lets lane q find row q's rule (row_rule, all rows of the batch at once), and counts hits from
+// the same registers: diagonal hits with LDS atomics, vertical hits in registers (the lane's columns
+// are fixed) added to LDS once at the end.
 // ---------------------------------------------------------------------------
-constexpr int kRowThreads = 256, kRowBatch = 8, kRowMaxL = 512;
+constexpr int kRowThreads = 512, kRowBatch = 2, kRowMaxL = 512;
 
 __global__ void __launch_bounds__(kRowThreads)
     k_capture_rows(const float* maps, int32_t L, double eps, double tau, double mu, uint8_t* keep_diag,
