@@ -301,8 +301,10 @@ __global__ void __launch_bounds__(kRowThreads)
   constexpr int NU = kRowMaxL / 256;  // float4 chunks per lane and row
   constexpr int NW = kRowThreads / 64;
   constexpr int kDiag = kRowBatch + 3;  // diagonals of one chunk's cells in a batch
+  static_assert(kRowMaxL / NW <= 255, "a lane's vertical hits per column fit a byte");
   __shared__ int32_t hd[kRowMaxL + 64], hv[kRowMaxL];  // hd[kRowMaxL + lane]: a sink for zero adds
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform (a scalar register), so that row indices and row predicates are scalar
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t map = blockIdx.x;
   const float* A = maps + map * (int64_t)L * L;
   const int nq = L / 4;  // float4 per row
@@ -311,7 +313,8 @@ __global__ void __launch_bounds__(kRowThreads)
   for (int r = tid; r < kRowMaxL + 64; r += kRowThreads) hd[r] = 0;
   for (int r = tid; r < kRowMaxL; r += kRowThreads) hv[r] = 0;
   __syncthreads();
-  int32_t vh[NU][4] = {};  // vertical hits of this lane's columns
+  // vertical hits of this lane's columns, one byte per column (a lane sees at most L / NW <= 64 rows)
+  uint32_t vh[NU] = {};
   // a batch's causal cells; cells past the row, the map or the rows read as zero (buffer range)
   auto load_batch = [&](int i0, float4 (&dst)[kRowBatch][NU]) {
 #pragma unroll
@@ -338,13 +341,14 @@ __global__ void __launch_bounds__(kRowThreads)
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         const int c = lane + 64 * u;
-        const float v[4] = {a[q][u].x, a[q][u].y, a[q][u].z, a[q][u].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool in = (c < nq) & (4 * c + e <= i);
-          mn[q] = fminf(mn[q], in ? v[e] : INFINITY);
-          mx[q] = fmaxf(mx[q], in ? v[e] : -INFINITY);
-        }
+        // a chunk with a cell in the row starts in the row; its cells past the row repeat its first
+        // cell, which leaves the chunk's extremes unchanged, so one select per chunk remains
+        const float4 w = a[q][u];
+        const float w1 = 4 * c + 1 <= i ? w.y : w.x, w2 = 4 * c + 2 <= i ? w.z : w.x,
+                    w3 = 4 * c + 3 <= i ? w.w : w.x;
+        const bool cin = (c < nq) & (4 * c <= i);
+        mn[q] = fminf(mn[q], cin ? fminf(fminf(w.x, w1), fminf(w2, w3)) : INFINITY);
+        mx[q] = fmaxf(mx[q], cin ? fmaxf(fmaxf(w.x, w1), fmaxf(w2, w3)) : -INFINITY);
       }
     }
 #pragma unroll
@@ -371,24 +375,31 @@ __global__ void __launch_bounds__(kRowThreads)
       const int i = i0 + q;
       const int qm = __builtin_amdgcn_readlane(mode, q);  // uniform
       const float qt = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(thr), q));
-      // 0/1 flags combined with bitwise operators: no branches per element
-      const uint32_t all = qm == kRowAll, thr_mode = qm == kRowThreshold, row_in = i < L;
+      // 0/1 flags combined with bitwise operators: no branches per element.  The row's rule is
+      // uniform, so the element code is written once per rule (a threshold compare, or none)
+      const uint32_t all = qm == kRowAll, row_in = i < L;
       uint8_t* mrow = (true_mask && i < L && qm != kRowEach) ? true_mask + (map * L + i) * (int64_t)L : nullptr;
+      auto cells = [&](auto thr_row) {
 #pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        const int c = lane + 64 * u;
-        const float v[4] = {a[q][u].x, a[q][u].y, a[q][u].z, a[q][u].w};
-        uint32_t packed = 0;
+        for (int u = 0; u < NU; ++u) {
+          const int c = lane + 64 * u;
+          const float v[4] = {a[q][u].x, a[q][u].y, a[q][u].z, a[q][u].w};
+          uint32_t packed = 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t in = row_in & (uint32_t)(c < nq) & (uint32_t)(4 * c + e <= i);
-          const int32_t k1 = (int32_t)(in & (all | (thr_mode & (uint32_t)(v[e] >= qt))));
-          vh[u][e] += k1;
-          dc[u][q - e + 3] += k1;
-          packed |= (uint32_t)k1 << (8 * e);
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t in = row_in & (uint32_t)(c < nq) & (uint32_t)(4 * c + e <= i);
+            const int32_t k1 = (int32_t)(decltype(thr_row)::value ? (in & (uint32_t)(v[e] >= qt)) : (in & all));
+            dc[u][q - e + 3] += k1;
+            packed |= (uint32_t)k1 << (8 * e);
+          }
+          vh[u] += packed;
+          if (mrow && c < nq) *reinterpret_cast<uint32_t*>(mrow + 4 * c) = packed;
         }
-        if (mrow && c < nq) *reinterpret_cast<uint32_t*>(mrow + 4 * c) = packed;
-      }
+      };
+      if (qm == kRowThreshold)
+        cells(std::true_type{});
+      else
+        cells(std::false_type{});
     }
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
@@ -432,7 +443,7 @@ __global__ void __launch_bounds__(kRowThreads)
     if (c < nq)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (vh[u][e]) atomicAdd(&hv[4 * c + e], vh[u][e]);
+        if ((vh[u] >> (8 * e)) & 0xffu) atomicAdd(&hv[4 * c + e], (int32_t)((vh[u] >> (8 * e)) & 0xffu));
   }
   __syncthreads();
   for (int r = tid; r < L; r += kRowThreads) {
