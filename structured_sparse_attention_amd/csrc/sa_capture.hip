@@ -29,10 +29,12 @@
 // row's kept elements are those at or above one fp32 threshold, found per row by bisection with the
 // same fp64 steps; the element pass then compares in fp32 and needs no fp64 at all.
 //
-// Layout: one 1024-thread workgroup per map.  Pass 1: the fp32 min/max of every row (wave w takes rows
-// w, w+16, ..., four rows at a time, lanes over columns); pass 2: one thread per row transforms the
-// extremes and finds the threshold; pass 3: the element pass (lanes over columns, four loads in
-// flight per lane), hits accumulating with LDS atomics.  The causal half of the map is read twice.
+// Layout: at lambda = 0.5 with per-row extremes and L <= 512 (the pages' case), k_capture_tiles reads
+// the causal half once, through LDS tiles of 16 rows (described above it).  Every other case runs
+// k_capture: one 1024-thread workgroup per map.  Pass 1: the fp32 min/max of every row (wave w takes
+// rows w, w+16, ..., four rows at a time, lanes over columns); pass 2: one thread per row transforms
+// the extremes and finds the threshold; pass 3: the element pass (lanes over columns, four loads in
+// flight per lane), hits accumulating with LDS atomics.  That kernel reads the causal half twice.
 #include <type_traits>
 
 #include "sa_internal.h"
@@ -93,7 +95,8 @@ __device__ inline void row_rule(float amin, float amax, double eps, double lambd
   const double range = ymax - ymin;
   auto pass = [&](uint32_t bits) { return (box_cox<KIND>(__uint_as_float(bits), eps, lambda) - ymin) / range >= tau; };
   const uint32_t bmin = __float_as_uint(amin) & 0x7fffffffu, bmax = __float_as_uint(amax);
-  if (!pass(bmax)) {
+  // the row maximum's score is (ymax - ymin) / range = range / range = 1 exactly (same fp64 steps)
+  if (!(1.0 >= tau)) {
     mode = kRowNone;
     return;
   }
@@ -103,8 +106,17 @@ __device__ inline void row_rule(float amin, float amax, double eps, double lambd
     const double sr = 1.0 + 0.5 * (ymin + tau * range);
     const double a = sr > 0.0 ? sr * sr - eps : 0.0;
     const uint32_t c = a <= (double)amin ? bmin : a >= (double)amax ? bmax : __float_as_uint((float)a);
-    if (pass(c)) {
-      hi = c;
+    // c and its two neighbours tested together (three independent evaluations instead of a chain);
+    // a passing value bounds the answer from above, a failing one from below
+    const uint32_t cm = c > lo ? c - 1 : c, cp = c < hi ? c + 1 : c;
+    const bool qm = pass(cm), qc = pass(c), qp = pass(cp);
+    if (qp) hi = cp;
+    else lo = cp + 1;
+    if (qc) hi = c;
+    else lo = max(lo, c + 1);
+    if (qm) hi = cm;
+    else lo = max(lo, cm + 1);
+    if (qc) {
       for (int k = 0; k < 8 && hi > lo; ++k) {
         if (!pass(hi - 1)) {
           lo = hi;  // hi passes and the float below it does not
@@ -113,7 +125,6 @@ __device__ inline void row_rule(float amin, float amax, double eps, double lambd
         --hi;
       }
     } else {
-      lo = c + 1;  // c < bmax here, since bmax passes
       for (int k = 0; k < 8 && lo < hi; ++k) {
         if (pass(lo)) {
           hi = lo;  // everything below lo failed
@@ -283,175 +294,200 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
-// ---------------------------------------------------------------------------
-// One read of the map: the same keep flags and hits as k_capture for lambda = 0.5, per-row
-// extremes (norm_scope 0) and L <= 512 with L % 4 == 0 (the capture length of the pages is 512).
-// 512 threads per map (about 100 VGPRs, so two maps share a CU).  A wave holds kRowBatch consecutive
-// causal rows in registers (lane l: columns 4(l + 64u) .. +3), reduces each row's extremes across the
-// wave, lets lane q find row q's rule (row_rule, all rows of the batch at once), and counts hits from
-// the same registers: diagonal hits with LDS atomics, vertical hits in registers (the lane's columns
-// are fixed) added to LDS once at the end.
-// ---------------------------------------------------------------------------
-constexpr int kRowThreads = 512, kRowBatch = 2, kRowMaxL = 512;
+constexpr int kRowMaxL = 512;  // longest map the tiled single-read kernel takes
 
-__global__ void __launch_bounds__(kRowThreads)
-    k_capture_rows(const float* maps, int32_t L, double eps, double tau, double mu, uint8_t* keep_diag,
-                   uint8_t* keep_vert, int32_t* diag_hits, int32_t* vert_hits, uint8_t* true_mask) {
+// ---------------------------------------------------------------------------
+// Tiled single read of the map (k_capture_tiles): the same keep flags and hits as k_capture for
+// lambda = 0.5, per-row extremes and L <= 512 with L % 4 == 0.  512 threads per map take the causal
+// half in chunks of 16 rows, in a pipeline (two maps share a CU, so each covers the other's waits):
+//   chunk n      is counted from LDS tile n % 2 with its rules;
+//   chunk n + 1  waits in the other tile with its extremes, and one wave finds its 16 row rules
+//                (lane = row, row_rule) while the others count chunk n;
+//   chunks n + 2 and n + 3  are in flight into two register sets: thread (row t = tid / 32, phase
+//                s = tid % 32) loads float4 columns s + 32k of chunk row t; when chunk n + 2 lands,
+//                the registers go to the tile chunk n has freed and its extremes come from the same
+//                values (32-lane reductions; min and max are exact in any order), and the loads of
+//                chunk n + 4 take their place (two chunks of time to arrive).
+// Hits: lane `col` counts column col (vertical hits) and diagonal offset col (cell (i, i - col) of
+// chunk row t sits at tile[t][i - col]): each counter belongs to one lane for the whole map and stays
+// in a register, so no atomics.  A wave whose columns all lie past a chunk's last row skips it; the
+// rule wave is the last wave, which has no cells in most chunks.
+// ---------------------------------------------------------------------------
+constexpr int kTileRows = 16, kTileThreads = 512;
+
+__global__ void __launch_bounds__(kTileThreads)
+    k_capture_tiles(const float* maps, int32_t L, double eps, double tau, double mu, uint8_t* keep_diag,
+                    uint8_t* keep_vert, int32_t* diag_hits, int32_t* vert_hits, uint8_t* true_mask) {
 #pragma clang fp contract(off)
-  constexpr int NU = kRowMaxL / 256;  // float4 chunks per lane and row
-  constexpr int NW = kRowThreads / 64;
-  constexpr int kDiag = kRowBatch + 3;  // diagonals of one chunk's cells in a batch
-  static_assert(kRowMaxL / NW <= 255, "a lane's vertical hits per column fit a byte");
-  __shared__ int32_t hd[kRowMaxL + 64], hv[kRowMaxL];  // hd[kRowMaxL + lane]: a sink for zero adds
-  // the wave index is uniform (a scalar register), so that row indices and row predicates are scalar
+  constexpr int PH = kTileThreads / kTileRows;  // threads per chunk row: 32
+  constexpr int NK = kRowMaxL / (4 * PH);       // float4 per thread and chunk: 4
+  constexpr int kRuleWave = kTileThreads / 64 - 1;
+  static_assert(kTileThreads == kRowMaxL && PH * NK * 4 == kRowMaxL, "lane = column = diagonal offset");
+  // tile[b][0] is a guard row: a diagonal lane reads row t at column i0 + t - r, which lies in row t - 1
+  // (or the guard row) when r > i0 + t.  Non-causal cells (column > row, past L) and the guard rows
+  // hold NaN, which fails every threshold compare, so the whole-chunk hit pass needs no range tests.
+  __shared__ __attribute__((aligned(16))) float tile[2][kTileRows + 1][kRowMaxL];
+  __shared__ float ex_min[2][kTileRows], ex_max[2][kTileRows];
+  __shared__ int32_t rl_mode[2][kTileRows], rl_fast[2];
+  __shared__ __attribute__((aligned(16))) float rl_thr[2][kTileRows];
+  __shared__ double rl_ymin[2][kTileRows], rl_range[2][kTileRows];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t_ld = tid / PH, s_ld = tid % PH;
   const int64_t map = blockIdx.x;
   const float* A = maps + map * (int64_t)L * L;
   const int nq = L / 4;  // float4 per row
   const uint32_t map_bytes = (uint32_t)L * L * 4u;
   const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, map_bytes, 0x00020000);
-  for (int r = tid; r < kRowMaxL + 64; r += kRowThreads) hd[r] = 0;
-  for (int r = tid; r < kRowMaxL; r += kRowThreads) hv[r] = 0;
-  __syncthreads();
-  // vertical hits of this lane's columns, one byte per column (a lane sees at most L / NW <= 64 rows)
-  uint32_t vh[NU] = {};
-  // a batch's causal cells; cells past the row, the map or the rows read as zero (buffer range)
-  auto load_batch = [&](int i0, float4 (&dst)[kRowBatch][NU]) {
+  const int nch = (L + kTileRows - 1) / kTileRows;
+  // causal cells of chunk row t; cells past the row's last float4, the map or the rows read as zero
+  float4 ra[NK], rb[NK];
+  auto load_chunk = [&](int n, float4(&a)[NK]) {
+    const int i = n * kTileRows + t_ld;
 #pragma unroll
-    for (int q = 0; q < kRowBatch; ++q)
-#pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        const int c = lane + 64 * u, i = i0 + q;
-        const uint32_t off = (i < L && c < nq && 4 * c <= i) ? (uint32_t)(i * L + 4 * c) * 4u : map_bytes;
-        dst[q][u] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rsA, off, 0, 0));
-      }
+    for (int k = 0; k < NK; ++k) {
+      const int c = s_ld + PH * k;
+      const uint32_t off = (i < L && c < nq && 4 * c <= i) ? (uint32_t)(i * L + 4 * c) * 4u : map_bytes;
+      a[k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rsA, off, 0, 0));
+    }
   };
-  // the next batch's loads are in flight while this one is reduced, ruled and counted
-  float4 a[kRowBatch][NU], an[kRowBatch][NU];
-  load_batch(kRowBatch * wave, a);
-  for (int i0 = kRowBatch * wave; i0 < L; i0 += kRowBatch * NW) {
-    load_batch(i0 + kRowBatch * NW, an);
-    // extremes of each causal row
-    float mn[kRowBatch], mx[kRowBatch];
+  // chunk row t_ld from the registers into tile `buf`, its non-causal cells (column > row, past L) as
+  // NaN, and its extremes from the same values: fminf and fmaxf skip NaN, so the masked cells leave
+  // them unchanged (as do NaN cells of the map itself)
+  auto land_chunk = [&](int n, int buf, const float4(&a)[NK]) {
+    const int i = n * kTileRows + t_ld;
+    const float nan = __builtin_nanf("");
+    float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
-    for (int q = 0; q < kRowBatch; ++q) {
-      mn[q] = INFINITY;
-      mx[q] = -INFINITY;
-      const int i = i0 + q;
-#pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        const int c = lane + 64 * u;
-        // a chunk with a cell in the row starts in the row; its cells past the row repeat its first
-        // cell, which leaves the chunk's extremes unchanged, so one select per chunk remains
-        const float4 w = a[q][u];
-        const float w1 = 4 * c + 1 <= i ? w.y : w.x, w2 = 4 * c + 2 <= i ? w.z : w.x,
-                    w3 = 4 * c + 3 <= i ? w.w : w.x;
-        const bool cin = (c < nq) & (4 * c <= i);
-        mn[q] = fminf(mn[q], cin ? fminf(fminf(w.x, w1), fminf(w2, w3)) : INFINITY);
-        mx[q] = fmaxf(mx[q], cin ? fmaxf(fmaxf(w.x, w1), fmaxf(w2, w3)) : -INFINITY);
-      }
+    for (int k = 0; k < NK; ++k) {
+      const int c = s_ld + PH * k;
+      const bool cv = (i < L) & (c < nq);
+      const float4 w = a[k];
+      const float4 st = make_float4(cv & (4 * c <= i) ? w.x : nan, cv & (4 * c + 1 <= i) ? w.y : nan,
+                                    cv & (4 * c + 2 <= i) ? w.z : nan, cv & (4 * c + 3 <= i) ? w.w : nan);
+      mn = fminf(mn, fminf(fminf(st.x, st.y), fminf(st.z, st.w)));
+      mx = fmaxf(mx, fmaxf(fmaxf(st.x, st.y), fmaxf(st.z, st.w)));
+      *reinterpret_cast<float4*>(&tile[buf][t_ld + 1][4 * c]) = st;
     }
 #pragma unroll
-    for (int q = 0; q < kRowBatch; ++q) {
-      mn[q] = wave_min(mn[q]);
-      mx[q] = wave_max(mx[q]);
+    for (int o = PH / 2; o > 0; o >>= 1) {
+      mn = fminf(mn, __shfl_xor(mn, o, PH));
+      mx = fmaxf(mx, __shfl_xor(mx, o, PH));
     }
-    // lane q < kRowBatch: the rule of row i0 + q
-    float amin = mn[0], amax = mx[0];
-#pragma unroll
-    for (int q = 1; q < kRowBatch; ++q)
-      if (lane == q) {
-        amin = mn[q];
-        amax = mx[q];
-      }
+    if (s_ld == 0) {
+      ex_min[n & 1][t_ld] = mn;
+      ex_max[n & 1][t_ld] = mx;
+    }
+  };
+  // the rule wave: row rules of chunk n (lane = row)
+  auto rules = [&](int n) {
+    if (wave != kRuleWave || lane >= kTileRows) return;
     int mode = kRowNone;
     float thr = 0.0f;
-    if (lane < kRowBatch && i0 + lane < L) row_rule<kBoxCoxHalf>(amin, amax, eps, 0.5, tau, mode, thr);
-    // keep flags and hits without per-element branches.  Cell (i0 + q, 4c + e) lies on diagonal
-    // i0 - 4c + (q - e): per chunk the lane's cells fall on kDiag diagonals, counted in registers
-    int32_t dc[NU][kDiag] = {};
-#pragma unroll
-    for (int q = 0; q < kRowBatch; ++q) {
-      const int i = i0 + q;
-      const int qm = __builtin_amdgcn_readlane(mode, q);  // uniform
-      const float qt = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(thr), q));
-      // 0/1 flags combined with bitwise operators: no branches per element.  The row's rule is
-      // uniform, so the element code is written once per rule (a threshold compare, or none)
-      const uint32_t all = qm == kRowAll, row_in = i < L;
-      uint8_t* mrow = (true_mask && i < L && qm != kRowEach) ? true_mask + (map * L + i) * (int64_t)L : nullptr;
-      auto cells = [&](auto thr_row) {
-#pragma unroll
-        for (int u = 0; u < NU; ++u) {
-          const int c = lane + 64 * u;
-          const float v[4] = {a[q][u].x, a[q][u].y, a[q][u].z, a[q][u].w};
-          uint32_t packed = 0;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t in = row_in & (uint32_t)(c < nq) & (uint32_t)(4 * c + e <= i);
-            const int32_t k1 = (int32_t)(decltype(thr_row)::value ? (in & (uint32_t)(v[e] >= qt)) : (in & all));
-            dc[u][q - e + 3] += k1;
-            packed |= (uint32_t)k1 << (8 * e);
-          }
-          vh[u] += packed;
-          if (mrow && c < nq) *reinterpret_cast<uint32_t*>(mrow + 4 * c) = packed;
-        }
-      };
-      if (qm == kRowThreshold)
-        cells(std::true_type{});
-      else
-        cells(std::false_type{});
-    }
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int c = lane + 64 * u;
-#pragma unroll
-      for (int k = 0; k < kDiag; ++k) atomicAdd(&hd[dc[u][k] ? i0 - 4 * c + k - 3 : kRowMaxL + lane], dc[u][k]);
-    }
-    // rows with a negative or non-finite extreme: each element tested in fp64, from memory
-    const uint64_t each = __ballot(lane < kRowBatch && mode == kRowEach);
-    if (each) {
-#pragma unroll 1
-      for (int q = 0; q < kRowBatch; ++q) {
-        if (!((each >> q) & 1)) continue;
-        const int i = i0 + q;
-        const float qmin = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(amin), q));
-        const float qmax = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(amax), q));
-        const double ymin = box_cox<kBoxCoxHalf>(qmin, eps, 0.5);
-        const double range = box_cox<kBoxCoxHalf>(qmax, eps, 0.5) - ymin;
-        uint8_t* mrow = true_mask ? true_mask + (map * L + i) * (int64_t)L : nullptr;
-        for (int j = lane; j < L; j += 64) {
-          uint8_t keep = 0;
-          if (j <= i) {
-            keep = (box_cox<kBoxCoxHalf>(A[(int64_t)i * L + j], eps, 0.5) - ymin) / range >= tau;
-            if (keep) {
-              atomicAdd(&hd[i - j], 1);
-              atomicAdd(&hv[j], 1);
-            }
-          }
-          if (mrow) mrow[j] = keep;
-        }
+    double ymin = 0.0, range = 0.0;
+    if (n * kTileRows + lane < L) {
+      const float amin = ex_min[n & 1][lane], amax = ex_max[n & 1][lane];
+      row_rule<kBoxCoxHalf>(amin, amax, eps, 0.5, tau, mode, thr);
+      if (mode == kRowEach) {
+        ymin = box_cox<kBoxCoxHalf>(amin, eps, 0.5);
+        range = box_cox<kBoxCoxHalf>(amax, eps, 0.5) - ymin;
       }
     }
-#pragma unroll
-    for (int q = 0; q < kRowBatch; ++q)
-#pragma unroll
-      for (int u = 0; u < NU; ++u) a[q][u] = an[q][u];
-  }
-#pragma unroll
-  for (int u = 0; u < NU; ++u) {
-    const int c = lane + 64 * u;
-    if (c < nq)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if ((vh[u] >> (8 * e)) & 0xffu) atomicAdd(&hv[4 * c + e], (int32_t)((vh[u] >> (8 * e)) & 0xffu));
+    rl_mode[n & 1][lane] = mode;
+    rl_thr[n & 1][lane] = thr;
+    rl_ymin[n & 1][lane] = ymin;
+    rl_range[n & 1][lane] = range;
+    // every row of the chunk decided by its threshold (rows past L are never visited)
+    const uint64_t thr_rows = __ballot(mode == kRowThreshold || n * kTileRows + lane >= L);
+    if (lane == 0) rl_fast[n & 1] = (thr_rows & ((1ull << kTileRows) - 1)) == ((1ull << kTileRows) - 1);
+  };
+  const int col = 64 * wave + lane;  // this lane's column and diagonal offset
+  int32_t hv = 0, hd = 0;
+
+  // prologue: guard rows; chunk 0 landed and ruled, chunk 1 landed, chunks 2 and 3 in flight (ra holds
+  // the even chunks, rb the odd ones)
+  tile[0][0][tid] = __builtin_nanf("");
+  tile[1][0][tid] = __builtin_nanf("");
+  load_chunk(0, ra);
+  if (nch > 1) load_chunk(1, rb);
+  land_chunk(0, 0, ra);
+  if (nch > 2) load_chunk(2, ra);
+  __syncthreads();
+  rules(0);
+  if (nch > 1) {
+    land_chunk(1, 1, rb);
+    if (nch > 3) load_chunk(3, rb);
   }
   __syncthreads();
-  for (int r = tid; r < L; r += kRowThreads) {
-    const double size = (double)(L - r);
-    keep_diag[map * L + r] = ((double)hd[r] / size) >= mu;
-    keep_vert[map * L + r] = ((double)hv[r] / size) >= mu;
-    if (diag_hits) diag_hits[map * L + r] = hd[r];
-    if (vert_hits) vert_hits[map * L + r] = hv[r];
+  auto step = [&](int n, float4(&a)[NK]) {  // a: the registers of chunk n + 2 (same parity as n)
+    if (n + 1 < nch) rules(n + 1);
+    // ---- hits of chunk n
+    const int i0 = n * kTileRows, rows = min(kTileRows, L - i0);
+    const float* tl = &tile[n & 1][1][0];  // chunk row 0
+    const float thr_v = rl_thr[n & 1][lane % kTileRows];
+    if (true_mask == nullptr && rl_fast[n & 1] && rows == kTileRows) {
+      // a whole chunk, every row by its threshold: the lane's cells of a few rows are read first, then
+      // each counts iff it is at or above its row's threshold (cells outside the causal rows are NaN)
+      if (64 * wave <= i0 + kTileRows - 1) {
+        const float* bv = tl + col;         // column col of row t: bv[t * kRowMaxL]
+        const float* bd = tl + (i0 - col);  // diagonal col of row t: bd[t * (kRowMaxL + 1)]
+        const float4* th = reinterpret_cast<const float4*>(&rl_thr[n & 1][0]);  // same address in every lane
+#pragma unroll
+        for (int g = 0; g < kTileRows / 4; ++g) {
+          float v[4], w[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            v[t] = bv[(4 * g + t) * kRowMaxL];
+            w[t] = bd[(4 * g + t) * (kRowMaxL + 1)];
+          }
+          const float4 t4 = th[g];
+          hv += (int32_t)(v[0] >= t4.x) + (int32_t)(v[1] >= t4.y) + (int32_t)(v[2] >= t4.z) + (int32_t)(v[3] >= t4.w);
+          hd += (int32_t)(w[0] >= t4.x) + (int32_t)(w[1] >= t4.y) + (int32_t)(w[2] >= t4.z) + (int32_t)(w[3] >= t4.w);
+        }
+      }
+    } else if (!(64 * wave > i0 + rows - 1 && true_mask == nullptr)) {
+      const int mode_v = rl_mode[n & 1][lane % kTileRows];
+      for (int t = 0; t < rows; ++t) {
+        const int i = i0 + t;
+        const int m = __builtin_amdgcn_readlane(mode_v, t);
+        const float thr = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(thr_v), t));
+        // column col <= i, and offset col <= i (its column i - col >= 0)
+        const bool in = col <= i;
+        const float v = tl[t * kRowMaxL + col];
+        const float w = tl[t * kRowMaxL + max(i - col, 0)];
+        int32_t kv = 0, kd = 0;
+        if (m == kRowThreshold) {
+          kv = in & (v >= thr);
+          kd = in & (w >= thr);
+        } else if (m == kRowAll) {
+          kv = in;
+          kd = in;
+        } else if (m == kRowEach) {
+          const double ymin = rl_ymin[n & 1][t], range = rl_range[n & 1][t];
+          kv = in && (box_cox<kBoxCoxHalf>(v, eps, 0.5) - ymin) / range >= tau;
+          kd = in && (box_cox<kBoxCoxHalf>(w, eps, 0.5) - ymin) / range >= tau;
+        }
+        hv += kv;
+        hd += kd;
+        if (true_mask != nullptr && col < L) true_mask[(map * L + i) * (int64_t)L + col] = (uint8_t)kv;
+      }
+    }
+    __syncthreads();  // chunk n counted: its tile is free; rules of chunk n + 1 written
+    if (n + 2 < nch) {
+      land_chunk(n + 2, n & 1, a);
+      if (n + 4 < nch) load_chunk(n + 4, a);
+    }
+    __syncthreads();  // chunk n + 2 in its tile
+  };
+  for (int n = 0; n < nch; n += 2) {
+    step(n, ra);
+    if (n + 1 < nch) step(n + 1, rb);
+  }
+  if (col < L) {
+    const double size = (double)(L - col);
+    keep_diag[map * L + col] = ((double)hd / size) >= mu;
+    keep_vert[map * L + col] = ((double)hv / size) >= mu;
+    if (diag_hits) diag_hits[map * L + col] = hd;
+    if (vert_hits) vert_hits[map * L + col] = hv;
   }
 }
 
@@ -842,7 +878,7 @@ hipError_t launch_capture(const float* maps, int32_t n_maps, int32_t L, double l
                           double mu, int32_t norm_scope, uint8_t* keep_diag, uint8_t* keep_vert, int32_t* diag_hits,
                           int32_t* vert_hits, uint8_t* true_mask, hipStream_t stream) {
   if (lambda == 0.5 && norm_scope == 0 && L <= kRowMaxL && L % 4 == 0) {
-    hipLaunchKernelGGL(k_capture_rows, dim3((unsigned)n_maps), dim3(kRowThreads), 0, stream, maps, L, eps, tau, mu,
+    hipLaunchKernelGGL(k_capture_tiles, dim3((unsigned)n_maps), dim3(kTileThreads), 0, stream, maps, L, eps, tau, mu,
                        keep_diag, keep_vert, diag_hits, vert_hits, true_mask);
     return hipGetLastError();
   }
