@@ -381,6 +381,9 @@ __global__ void __launch_bounds__(kTileThreads)
   // the rule wave: row rules of chunk n (lane = row)
   auto rules = [&](int n) {
     if (wave != kRuleWave || lane >= kTileRows) return;
+    // the rule chain (dependent fp64 steps) paces the pipeline: issue it ahead of the counting waves
+    // that share its SIMD
+    __builtin_amdgcn_s_setprio(3);
     int mode = kRowNone;
     float thr = 0.0f;
     double ymin = 0.0, range = 0.0;
@@ -399,6 +402,7 @@ __global__ void __launch_bounds__(kTileThreads)
     // every row of the chunk decided by its threshold (rows past L are never visited)
     const uint64_t thr_rows = __ballot(mode == kRowThreshold || n * kTileRows + lane >= L);
     if (lane == 0) rl_fast[n & 1] = (thr_rows & ((1ull << kTileRows) - 1)) == ((1ull << kTileRows) - 1);
+    __builtin_amdgcn_s_setprio(0);
   };
   const int col = 64 * wave + lane;  // this lane's column and diagonal offset
   int32_t hv = 0, hd = 0;
