@@ -219,16 +219,16 @@ def small_workloads(sa, torch):
     return out
 
 
-def capture_ms(sa, torch, reps=5):
+def capture_ms(sa, torch, reps=20):
     import workloads as W
     maps = W.capture_maps(layers=16, heads=32, n_avg=4)
     md = torch.from_numpy(maps).cuda()
-    sa.pattern_capture(md)
+    out = sa.pattern_capture(md)   # outputs reused below, so the timed calls allocate nothing
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(reps):
-        sa.pattern_capture(md)
+        sa.pattern_capture(md, out=out)
     b.record()
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / reps
@@ -246,7 +246,7 @@ def maps_from_qk_ms(sa, torch, reps=5):
     kd = torch.from_numpy(k.view(np.int16)).cuda().view(torch.bfloat16).repeat(1, 16, 1, 1).contiguous()
     maps = torch.empty((512, 512, 512), dtype=torch.float32, device="cuda")
     sa.attention_maps(qd, kd, out=maps)
-    sa.pattern_capture(maps)
+    cap = sa.pattern_capture(maps)
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     ev[0].record()
@@ -254,7 +254,7 @@ def maps_from_qk_ms(sa, torch, reps=5):
         sa.attention_maps(qd, kd, out=maps)
     ev[1].record()
     for _ in range(reps):
-        sa.pattern_capture(maps)
+        sa.pattern_capture(maps, out=cap)
     ev[2].record()
     torch.cuda.synchronize()
     maps_ms, cap_ms = ev[0].elapsed_time(ev[1]) / reps, ev[1].elapsed_time(ev[2]) / reps

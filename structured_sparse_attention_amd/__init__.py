@@ -370,17 +370,32 @@ def attention_maps(q: torch.Tensor, k: torch.Tensor, softmax_scale: Optional[flo
 
 
 def pattern_capture(maps: torch.Tensor, lam: float = 0.5, eps: float = 1e-8, tau: float = 0.3, mu: float = 0.8,
-                    norm_scope: int = 0, return_hits: bool = True, return_mask: bool = False, stream=None) -> dict:
-    """sa_pattern_capture on float32 maps [n, L, L] in device memory."""
+                    norm_scope: int = 0, return_hits: bool = True, return_mask: bool = False, out: Optional[dict] = None,
+                    stream=None) -> dict:
+    """sa_pattern_capture on float32 maps [n, L, L] in device memory.  `out`: a dict returned by an earlier
+    call with the same shapes and flags, whose tensors are written again instead of new ones."""
     if maps.dtype != torch.float32 or maps.dim() != 3 or maps.shape[1] != maps.shape[2] or not maps.is_contiguous():
         raise ValueError("maps must be a contiguous float32 [n, L, L] tensor")
     n, L, _ = maps.shape
     dev = maps.device
-    kd = torch.empty((n, L), dtype=torch.uint8, device=dev)
-    kv = torch.empty((n, L), dtype=torch.uint8, device=dev)
-    hd = torch.empty((n, L), dtype=torch.int32, device=dev) if return_hits else None
-    hv = torch.empty((n, L), dtype=torch.int32, device=dev) if return_hits else None
-    tm = torch.empty((n, L, L), dtype=torch.uint8, device=dev) if return_mask else None
+    if out is not None:
+        kd, kv, hd, hv, tm = (out.get(x) for x in ("keep_diag", "keep_vert", "diag_hits", "vert_hits", "true_mask"))
+        want = [(kd, (n, L), torch.uint8), (kv, (n, L), torch.uint8)]
+        want += [(hd, (n, L), torch.int32), (hv, (n, L), torch.int32)] if return_hits else []
+        want += [(tm, (n, L, L), torch.uint8)] if return_mask else []
+        for t, shape, dt in want:
+            if t is None or tuple(t.shape) != shape or t.dtype != dt or not t.is_contiguous() or t.device != dev:
+                raise ValueError("out does not match the maps and the requested outputs")
+        if not return_hits:
+            hd = hv = None
+        if not return_mask:
+            tm = None
+    else:
+        kd = torch.empty((n, L), dtype=torch.uint8, device=dev)
+        kv = torch.empty((n, L), dtype=torch.uint8, device=dev)
+        hd = torch.empty((n, L), dtype=torch.int32, device=dev) if return_hits else None
+        hv = torch.empty((n, L), dtype=torch.int32, device=dev) if return_hits else None
+        tm = torch.empty((n, L, L), dtype=torch.uint8, device=dev) if return_mask else None
     _check(_lib.sa_pattern_capture(maps.data_ptr(), n, L, lam, eps, tau, mu, norm_scope, kd.data_ptr(),
                                    kv.data_ptr(), _ptr(hd), _ptr(hv), _ptr(tm), _stream(stream)),
            "sa_pattern_capture")

@@ -195,3 +195,22 @@ def test_capture_to_attention_end_to_end():
     idx = torch.from_numpy(rows.astype(np.int64)).cuda()
     go = o[idx[:, 0], idx[:, 1], idx[:, 2]].float().cpu().numpy().astype(np.float64)
     assert_close_bf16(go, ro, "end-to-end")
+
+
+def test_capture_into_given_outputs():
+    """`out` of an earlier call is written again: a second map set through the same tensors gives the
+    oracle's flags, hits and mask for that set."""
+    m = sa()
+    rng = np.random.default_rng(12)
+    a = (rng.random((6, 128, 128)) ** 3).astype(np.float32)
+    b = (rng.random((6, 128, 128)) ** 2).astype(np.float32)
+    note("capture into given outputs")
+    out = m.pattern_capture(torch.from_numpy(a).cuda(), return_mask=True)
+    got = m.pattern_capture(torch.from_numpy(b).cuda(), return_mask=True, out=out)
+    torch.cuda.synchronize()
+    ref = oracle.capture(b, want_mask=True)
+    for key in ("keep_diag", "keep_vert", "diag_hits", "vert_hits", "true_mask"):
+        assert got[key].data_ptr() == out[key].data_ptr()
+        np.testing.assert_array_equal(got[key].cpu().numpy(), ref[key], err_msg=key)
+    with pytest.raises(ValueError):
+        m.pattern_capture(torch.from_numpy(b[:3]).cuda(), out=out)   # shapes differ
