@@ -484,6 +484,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="skip the S=131072 and capture measurements")
     ap.add_argument("--capture-sweep", action="store_true",
                     help="only run the capture sensitivity sweep (PCL, lambda, tau, mu) and print it as JSON")
+    ap.add_argument("--capture-only", action="store_true",
+                    help="only time the capture of the 512 workload maps and of the 512 maps from Q/K (JSON)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one device copy of 1 GiB (reference for hardware byte counters)")
     args = ap.parse_args()
@@ -497,6 +499,9 @@ def main():
 
     if args.capture_sweep:
         print(json.dumps(capture_sweep(sa, torch)))
+        return
+    if args.capture_only:
+        print(json.dumps(dict(capture=capture_ms(sa, torch), capture_from_qk=maps_from_qk_ms(sa, torch))))
         return
 
     cfg = WORKLOADS[args.config]
