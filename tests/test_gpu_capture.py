@@ -52,8 +52,10 @@ def test_capture_workload_maps(scope, eps):
     _capture_both(maps, norm_scope=scope, eps=eps)
 
 
-@pytest.mark.parametrize("L", [1, 5, 64, 333, 1024])
+@pytest.mark.parametrize("L", [1, 4, 5, 12, 64, 100, 300, 333, 508, 1024])
 def test_capture_odd_sizes(L):
+    """Sizes on both kernels: L % 4 == 0 and L <= 512 take the single-read tiled kernel (4, 12, 100, 300 and
+    508 end in a partial chunk of rows), the others the three-pass kernel."""
     rng = np.random.default_rng(L)
     A = rng.random((3, L, L)).astype(np.float32)
     A = np.tril(A) / np.maximum(1, np.tril(A).sum(axis=2, keepdims=True))
