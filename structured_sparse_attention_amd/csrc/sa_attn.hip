@@ -810,7 +810,7 @@ k_attn_bf16(Params p) {
   const int ld_r = lane / C::CPR, ld_p = lane % C::CPR;
   static_assert((C::LPW * C::RPL) % 16 == 0, "each wave's first tile row must be a multiple of 16");
   const int ld_ck = 16 * (ld_p ^ kswz<D>(ld_r)), ld_cv = 16 * (ld_p ^ vswz<D>(ld_r)), ld_row = ld_r * C::ROWB;
-  auto issue_tile = [&](const Tile& t, int st, const int32_t* cols) {
+  auto issue_tile = [&](const Tile& t, int st, const int32_t* cols) __attribute__((always_inline)) {
     unsigned char* Kst = lds + st * C::STAGE;
     unsigned char* Vst = Kst + C::MAT;
     int key[C::LPW];
@@ -866,7 +866,7 @@ k_attn_bf16(Params p) {
   // the offsets a band tile shows the block, [b0 - j0 - 63, b1 - j0], span at most BM + 63 bits,
   // i.e. at most kWords bitmap words from word omin / 32; lane k < kWords holds word k of them
   constexpr int kWords = (BM + BN - 1 + 31) / 32 + 1;
-  auto mask_loads = [&](const Tile& t, const int32_t* cols) -> MaskIn {
+  auto mask_loads = [&](const Tile& t, const int32_t* cols) __attribute__((always_inline)) -> MaskIn {
     MaskIn mi{0u, 0u, 0u, 0ull, false, false, 0u};
     if (t.kind == 2) mi.full = (t.nvalid == BN) && (cols[BN - 1] <= b0);
     if (t.kind == 1) {
@@ -890,7 +890,7 @@ k_attn_bf16(Params p) {
     }
     return mi;
   };
-  auto mask_finish = [&](const Tile& t, const MaskIn& mi, const int32_t* cols) -> uint64_t {
+  auto mask_finish = [&](const Tile& t, const MaskIn& mi, const int32_t* cols) __attribute__((always_inline)) -> uint64_t {
     if (mi.full) return ~0ull;
     if (mi.cand) {
       const int omin = b0 - t.j0 - (BN - 1), omax = b1 - t.j0;
@@ -937,7 +937,7 @@ k_attn_bf16(Params p) {
     voff[x] = (4 * (q16 >> 1) + es) * C::ROWB + 16 * ((d >> 3) ^ vswz<D>(es)) + 8 * ((d >> 2) & 1);
   }
 
-  auto compute_tile = [&](int st, uint64_t m) {
+  auto compute_tile = [&](int st, uint64_t m) __attribute__((always_inline)) {
     const unsigned char* Kst = lds + st * C::STAGE;
     const unsigned char* Vst = Kst + C::MAT;
     f32x16 sacc[C::NKB];
@@ -1044,16 +1044,19 @@ k_attn_bf16(Params p) {
   }
   __builtin_amdgcn_s_waitcnt(0xF70);  // this thread's tile loads have landed in LDS
   __syncthreads();
-  for (int n = 0; cur.kind != 0; ++n) {
+  // one tile step; the LDS stage of tile n is n & 1, passed as a constant (the loop below takes two
+  // steps per iteration), so the stage offsets fold into the LDS instructions' immediate offsets
+  auto tile_step = [&](int n, auto stage) __attribute__((always_inline)) {
+    constexpr int st = decltype(stage)::value;
     const int bx = (n + 1) % 3, bz = (n + 2) % 3;
     MaskIn mi{0u, 0u, 0u, 0ull, false, false, 0u};
     if (nxt.kind != 0) {
       mi = mask_loads(nxt, cols_sh[bx]);
-      issue_tile(nxt, (n + 1) & 1, cols_sh[bx]);
+      issue_tile(nxt, st ^ 1, cols_sh[bx]);
     }
     int32_t ncol = 0;
     if (nn.kind == 2 && tid < BN && tid < nn.nvalid) ncol = p.col_idx[nn.pc + tid];
-    compute_tile(n & 1, m_cur);
+    compute_tile(st, m_cur);
     const uint64_t m_next = nxt.kind != 0 ? mask_finish(nxt, mi, cols_sh[bx]) : 0ull;
     if (nn.kind == 2 && tid < BN) cols_sh[bz][tid] = ncol;
     __builtin_amdgcn_s_waitcnt(0xF70);
@@ -1062,6 +1065,11 @@ k_attn_bf16(Params p) {
     cur = nxt;
     nxt = nn;
     nn = walk.next(nn);
+  };
+  for (int n = 0; cur.kind != 0; n += 2) {
+    tile_step(n, std::integral_constant<int, 0>{});
+    if (cur.kind == 0) break;
+    tile_step(n + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- normalise and store
