@@ -1045,14 +1045,18 @@ k_attn_bf16(Params p) {
   __builtin_amdgcn_s_waitcnt(0xF70);  // this thread's tile loads have landed in LDS
   __syncthreads();
   // one tile step; the LDS stage of tile n is n & 1, passed as a constant (the loop below takes two
-  // steps per iteration), so the stage offsets fold into the LDS instructions' immediate offsets
+  // steps per iteration), so the stage offsets of the tile's reads fold into the LDS instructions'
+  // immediate offsets.  The next tile's loads take the stage as a run-time value: their LDS bases (M0)
+  // are then computed per tile instead of being held for both stages, which would spill SGPRs.
   auto tile_step = [&](int n, auto stage) __attribute__((always_inline)) {
     constexpr int st = decltype(stage)::value;
     const int bx = (n + 1) % 3, bz = (n + 2) % 3;
     MaskIn mi{0u, 0u, 0u, 0ull, false, false, 0u};
     if (nxt.kind != 0) {
       mi = mask_loads(nxt, cols_sh[bx]);
-      issue_tile(nxt, st ^ 1, cols_sh[bx]);
+      int ld_stage = st ^ 1;
+      asm volatile("" : "+s"(ld_stage));  // opaque to the optimizer: no constant to hoist per stage
+      issue_tile(nxt, ld_stage, cols_sh[bx]);
     }
     int32_t ncol = 0;
     if (nn.kind == 2 && tid < BN && tid < nn.nvalid) ncol = p.col_idx[nn.pc + tid];
