@@ -526,7 +526,9 @@ __global__ void __launch_bounds__(128) k_maps(const void* qv, const void* kv, in
   constexpr int CH = D * (int)sizeof(E) / 16;         // 16-byte chunks per key row
   constexpr int NL = KW * CH / 128;                   // chunks of a tile per thread
   __shared__ __attribute__((aligned(16))) E Ks[2][KW * KSTR];
-  __shared__ float st_m[kMapChunk][128], st_il[kMapChunk][128];  // per lane: its row's max, 1/sum
+  // per lane: its row's max less log2 of its sum, per sequence of the chunk, so that pass 2's
+  // probability is one exp2 (p = 2^(x scale - max) / sum = 2^(x scale - (max + log2 sum)))
+  __shared__ float st_m[kMapChunk][128];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, r32 = lane & 31;
   const int nrb = (L + 63) / 64;
@@ -686,8 +688,7 @@ __global__ void __launch_bounds__(128) k_maps(const void* qv, const void* kv, in
           l = (m == -INFINITY ? 0.0f : l * __builtin_amdgcn_exp2f(m - mn)) + part;
           m = mn;
           if (kt == nkt - 1) {  // last tile of this sequence
-            st_m[bb - b0][tid] = m;  // read back by this lane only
-            st_il[bb - b0][tid] = 1.0f / l;
+            st_m[bb - b0][tid] = m + __builtin_amdgcn_logf(l);  // read back by this lane only
             m = -INFINITY;
             l = 0.0f;
           }
@@ -703,12 +704,11 @@ __global__ void __launch_bounds__(128) k_maps(const void* qv, const void* kv, in
         [&](int n, int bb, int kt, int buf, const QF (&qf)[QS]) {
           float x[NKB][16];
           scores(buf, qf, kt, x);
-          const float mb = st_m[bb - b0][tid], il = st_il[bb - b0][tid];
+          const float mb = st_m[bb - b0][tid];
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
-              acc[kb][v] += __builtin_amdgcn_exp2f(__builtin_fmaf(x[kb][v], scale_log2, -mb)) * il;
+            for (int v = 0; v < 16; ++v) acc[kb][v] += __builtin_amdgcn_exp2f(__builtin_fmaf(x[kb][v], scale_log2, -mb));
           if (bb - b0 == nb - 1) {  // last sequence of the chunk: this key tile is complete
             if (row_ok) {
 #pragma unroll
