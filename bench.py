@@ -236,7 +236,7 @@ def capture_ms(sa, torch, reps=20):
     return dict(ms=ms, maps=int(maps.shape[0]), L=512, read_GBps=causal_bytes / (ms * 1e-3) / 1e9)
 
 
-def maps_from_qk_ms(sa, torch, reps=5):
+def maps_from_qk_ms(sa, torch, reps=10, warm=3):
     """Capture maps from Q/K: 16 layers x 32 query heads (8 kv heads per layer) stacked into one
     call, batch 16, L = 512, d = 64 (bf16), then the capture of those 512 maps.  One layer's
     structured Q/K is generated and repeated over the 16 layers (the work does not depend on values)."""
@@ -245,7 +245,8 @@ def maps_from_qk_ms(sa, torch, reps=5):
     qd = torch.from_numpy(q.view(np.int16)).cuda().view(torch.bfloat16).repeat(1, 16, 1, 1).contiguous()
     kd = torch.from_numpy(k.view(np.int16)).cuda().view(torch.bfloat16).repeat(1, 16, 1, 1).contiguous()
     maps = torch.empty((512, 512, 512), dtype=torch.float32, device="cuda")
-    sa.attention_maps(qd, kd, out=maps)
+    for _ in range(warm):
+        sa.attention_maps(qd, kd, out=maps)
     cap = sa.pattern_capture(maps)
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
