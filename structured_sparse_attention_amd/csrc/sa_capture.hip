@@ -500,13 +500,15 @@ __global__ void __launch_bounds__(kTileThreads)
 // average attention maps of the first L positions, accumulated over the inputs;
 // "Assumptions & free parameters": the batch mean stands in for each sequence):
 //   maps[h][i][j] = (1/B) sum_b softmax_j(q_bhi . k_bgj * scale), j <= i; 0 above.
-// One workgroup (two waves, 64 query rows) per (head, 64-row block).  Scores are
-// S^T = K Q^T on MFMA (lane = query row, as in the attention kernels) over 64-key
-// tiles staged in LDS.  Sequences are taken kMapChunk at a time: pass 1 finds the
-// row max and 1/sum (exp2 domain) of every sequence of the chunk and keeps them in
-// LDS; pass 2 walks the key tiles once, recomputes each sequence's scores and sums
-// p_b / B in registers, so a map element is written once per chunk (added to the
-// previous chunks' sum after the first).  No other workgroup touches these rows.
+// One workgroup (four waves) per (head, pair of 64-row blocks): waves 0-1 take the
+// lower block, waves 2-3 the upper one, and both share every K tile (the lower block's
+// waves skip the upper block's diagonal tile).  Scores are S^T = K Q^T on MFMA (lane =
+// query row, as in the attention kernels) over 64-key tiles staged in LDS.  Sequences
+// are taken kMapChunk at a time: pass 1 finds the row max and sum (exp2 domain) of
+// every sequence of the chunk and keeps max + log2 sum in LDS; pass 2 walks the key
+// tiles once, recomputes each sequence's scores and sums p_b / B in registers, so a
+// map element is written once per chunk (added to the previous chunks' sum after the
+// first).  No other workgroup touches these rows.
 // Each pass is one software-pipelined loop over its (sequence, key tile) steps: the
 // K tile and the Q fragment of step n + 1 are loaded into registers while step n is
 // computed from the other LDS buffer, with one barrier per step.
@@ -514,51 +516,60 @@ __global__ void __launch_bounds__(kTileThreads)
 typedef __bf16 mbf16x8 __attribute__((ext_vector_type(8)));
 typedef float mf32x16 __attribute__((ext_vector_type(16)));
 constexpr int kMapChunk = 16;
+constexpr int kMapThreads = 256;  // four waves: two row blocks of 64 query rows
 
 template <int D, bool BF16>
-__global__ void __launch_bounds__(128) k_maps(const void* qv, const void* kv, int32_t B, int32_t hq, int32_t hkv,
-                                              int32_t L, float scale_log2, float* maps) {
+__global__ void __launch_bounds__(kMapThreads) __attribute__((amdgpu_waves_per_eu(3)))
+k_maps(const void* qv, const void* kv, int32_t B, int32_t hq, int32_t hkv, int32_t L, float scale_log2, float* maps) {
   using E = typename std::conditional<BF16, uint16_t, float>::type;
   using QF = typename std::conditional<BF16, mbf16x8, float>::type;
   constexpr int QS = BF16 ? D / 16 : D / 2;           // MFMA k-steps over d
   constexpr int KSTR = BF16 ? D + 8 : D + 1;          // LDS row stride of the K tile (elements)
   constexpr int KW = 64, NKB = 2;                     // keys and 32-key blocks per key tile
   constexpr int CH = D * (int)sizeof(E) / 16;         // 16-byte chunks per key row
-  constexpr int NL = KW * CH / 128;                   // chunks of a tile per thread
+  constexpr int NL = KW * CH / kMapThreads;           // chunks of a tile per thread
   __shared__ __attribute__((aligned(16))) E Ks[2][KW * KSTR];
   // per lane: its row's max less log2 of its sum, per sequence of the chunk, so that pass 2's
   // probability is one exp2 (p = 2^(x scale - max) / sum = 2^(x scale - (max + log2 sum)))
-  __shared__ float st_m[kMapChunk][128];
+  __shared__ float st_m[kMapChunk][kMapThreads];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, r32 = lane & 31;
   const int nrb = (L + 63) / 64;
+  const int npr = (nrb + 1) / 2;  // pairs of row blocks, one per workgroup
   // Workgroup k runs on XCD k % 8.  When the kv heads split evenly over the 8 XCDs, XCD x takes
   // the row blocks of kv heads x, x + 8, ... (one group at a time, heaviest row blocks first), so
   // the K tiles of a group, shared by its query heads and row blocks, stay in that XCD's L2.
-  int h, rb;
+  int h, pr;
   if (hkv % 8 == 0) {
-    const int hpg = hq / hkv, per_group = hpg * nrb;
+    const int hpg = hq / hkv, per_group = hpg * npr;
     const int x = (int)(blockIdx.x % 8u), slot = (int)(blockIdx.x / 8u);
     const int gl = slot / per_group, rem = slot % per_group;
-    rb = nrb - 1 - rem / hpg;
+    pr = npr - 1 - rem / hpg;
     h = (x + 8 * gl) * hpg + rem % hpg;
   } else {
-    h = blockIdx.x / nrb;
-    rb = blockIdx.x % nrb;
+    h = blockIdx.x / npr;
+    pr = blockIdx.x % npr;
   }
   const int kvh = h / (hq / hkv);
-  const int i = rb * 64 + wave * 32 + r32;  // this lane's query row
-  const bool row_ok = i < L;
+  // waves 0-1 take row block 2 pr, waves 2-3 row block 2 pr + 1 (absent past the map): both share the
+  // workgroup's K tiles
+  const int rb = 2 * pr + (wave >> 1);
+  const int i = rb * 64 + (wave & 1) * 32 + r32;  // this lane's query row
+  const bool row_ok = rb < nrb && i < L;
   const float invB = 1.0f / (float)B;
   const bool vec_rows = (L & 3) == 0;  // map rows 16-byte aligned
   float* mrow = maps + ((int64_t)h * L + (row_ok ? i : 0)) * L;
-  const int last = min(L, rb * 64 + 64) - 1;  // last query row (and last key) of the row block
-  const int nkt = last / KW + 1;               // key tiles of this row block
+  const int last = min(L, rb * 64 + 64) - 1;          // last query row (and last key) of this wave's row block
+  const int nkt_w = rb < nrb ? last / KW + 1 : 0;     // key tiles of this wave's row block
+  const int nkt = (min(L, 2 * pr * 64 + 128) - 1) / KW + 1;  // key tiles of the workgroup (its upper block)
 
-  // zeros above the block diagonal (keys of the tiles past this row block)
-  for (int r = 0; r < 64 && rb * 64 + r < L; ++r) {
-    float* zrow = maps + ((int64_t)h * L + rb * 64 + r) * L;
-    for (int jj = (rb + 1) * 64 + tid; jj < L; jj += 128) zrow[jj] = 0.0f;
+  // zeros above the block diagonal (keys of the tiles past each row block)
+  for (int q = 0; q < 2; ++q) {
+    const int rq = 2 * pr + q;
+    for (int r = 0; r < 64 && rq * 64 + r < L; ++r) {
+      float* zrow = maps + ((int64_t)h * L + rq * 64 + r) * L;
+      for (int jj = (rq + 1) * 64 + tid; jj < L; jj += kMapThreads) zrow[jj] = 0.0f;
+    }
   }
 
   auto load_q = [&](int b, QF (&qf)[QS]) {  // global -> registers
@@ -578,14 +589,14 @@ __global__ void __launch_bounds__(128) k_maps(const void* qv, const void* kv, in
     const E* Kb = static_cast<const E*>(kv) + ((int64_t)b * hkv + kvh) * L * (int64_t)D;
 #pragma unroll
     for (int u = 0; u < NL; ++u) {
-      const int x = tid + 128 * u, r = x / CH, c = x % CH, j = kt * KW + r;
+      const int x = tid + kMapThreads * u, r = x / CH, c = x % CH, j = kt * KW + r;
       kr[u] = j < L ? *(reinterpret_cast<const uint4*>(Kb + (int64_t)j * D) + c) : make_uint4(0u, 0u, 0u, 0u);
     }
   };
   auto store_k = [&](int buf, const uint4 (&kr)[NL]) {  // registers -> LDS buffer
 #pragma unroll
     for (int u = 0; u < NL; ++u) {
-      const int x = tid + 128 * u, r = x / CH, c = x % CH;
+      const int x = tid + kMapThreads * u, r = x / CH, c = x % CH;
       E* dst = Ks[buf] + r * KSTR + c * (16 / (int)sizeof(E));
       if constexpr (BF16) {
         *reinterpret_cast<uint4*>(dst) = kr[u];
@@ -619,7 +630,7 @@ __global__ void __launch_bounds__(128) k_maps(const void* qv, const void* kv, in
 #pragma unroll
       for (int v = 0; v < 16; ++v) x[kb][v] = acc[v];
     }
-    if (kt == nkt - 1) {
+    if (kt == nkt_w - 1) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -668,6 +679,7 @@ __global__ void __launch_bounds__(128) k_maps(const void* qv, const void* kv, in
     pipeline(
         nb * nkt, [&](int n, int& bb, int& kt) { bb = b0 + n / nkt; kt = n % nkt; },
         [&](int n, int bb, int kt, int buf, const QF (&qf)[QS]) {
+          if (kt >= nkt_w) return;  // the upper block's diagonal tile lies above this wave's rows
           float x[NKB][16];
           scores(buf, qf, kt, x);
           float tmax = -INFINITY;
@@ -687,7 +699,7 @@ __global__ void __launch_bounds__(128) k_maps(const void* qv, const void* kv, in
           part += __shfl_xor(part, 32, 64);
           l = (m == -INFINITY ? 0.0f : l * __builtin_amdgcn_exp2f(m - mn)) + part;
           m = mn;
-          if (kt == nkt - 1) {  // last tile of this sequence
+          if (kt == nkt_w - 1) {  // last tile of this sequence for this wave's rows
             st_m[bb - b0][tid] = m + __builtin_amdgcn_logf(l);  // read back by this lane only
             m = -INFINITY;
             l = 0.0f;
@@ -702,6 +714,7 @@ __global__ void __launch_bounds__(128) k_maps(const void* qv, const void* kv, in
     pipeline(
         nkt * nb, [&](int n, int& bb, int& kt) { kt = n / nb; bb = b0 + n % nb; },
         [&](int n, int bb, int kt, int buf, const QF (&qf)[QS]) {
+          if (kt >= nkt_w) return;  // nothing of this wave's rows in the tile (acc stays zero)
           float x[NKB][16];
           scores(buf, qf, kt, x);
           const float mb = st_m[bb - b0][tid];
@@ -745,8 +758,9 @@ template <int D, bool BF16>
 hipError_t launch_maps_t(const void* q, const void* k, int32_t B, int32_t hq, int32_t hkv, int32_t L, float scale,
                          float* maps, hipStream_t stream) {
   const int nrb = (L + 63) / 64;
-  k_maps<D, BF16><<<dim3((unsigned)(hq * nrb)), dim3(128), 0, stream>>>(q, k, B, hq, hkv, L,
-                                                                          scale * 1.44269504088896340736f, maps);
+  const int npr = (nrb + 1) / 2;
+  k_maps<D, BF16><<<dim3((unsigned)(hq * npr)), dim3(kMapThreads), 0, stream>>>(q, k, B, hq, hkv, L,
+                                                                                 scale * 1.44269504088896340736f, maps);
   return hipGetLastError();
 }
 
